@@ -1,0 +1,181 @@
+"""Plain CPU oracle of the forward pass of one Grok-1 mixture-of-experts FFN layer.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this module.
+It shares no code with the HIP library and never imports it; both sides take their inputs from ``synth``.
+
+Everything is evaluated in float64 on the exact values of the stored inputs, with plain PyTorch CPU operations
+(a float64 matrix product is the only library primitive used as a step).  Pages followed:
+
+* [bridge] "A functional bridge between openai/grok and xai-org/grok-1" (github.com/Jah-yee/grok README),
+  architecture diagram: each expert is GELU(x W1) ⊙ (x Wv) W2; 8 experts, top-2 routing.
+* [moe] "Grok-1: 314B Total Parameters, 25B Active Per Token (MoE Explained)",
+  section "Expert Routing Details": logits = gate(x) (a Dense layer to the expert count), gates = softmax(logits),
+  then top_k(gates, k=2) returns (top-k gates, top-k indices); no gating noise outside training.
+  Section "How MoE Works in Practice": the layer output is the sum, over the selected experts, of each expert's
+  output times that expert's router weight.
+* [card] "Grok-1-BF16" (TevunahAi conversion notes), section "Conversion Details": int8 weights times bf16 scales,
+  scales broadcast over the grouped axis, JAX [in, out] layout; section "Verification": tensor shapes.
+
+Readings where the pages leave a step open (each is also listed in the design notes):
+  * GELU is the exact erf form (the pages name GELU without saying which).
+  * The two combine weights are the softmax probabilities of the selected experts over all E experts, not
+    renormalised over the two ([moe] returns top_k of the full softmax and multiplies by it).
+  * Selection is by descending logit with the lower expert index first on equal logits (softmax is strictly
+    increasing, so this equals selecting on the probabilities, without ties created by rounding them).
+  * Weights are stored [E, in, out]: W1, Wv are [E, d, f], W2 is [E, f, d]; int8 scales are [E, 1, out].
+  * In the bf16 and int8 layers the intermediate h = GELU(a) ⊙ b is rounded once to bf16 (round to nearest
+    even, directly from float64) before the down projection; the fp32 layer keeps h unrounded.
+  * The optional per-expert router bias is added to the logits before the softmax.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+F32, BF16, W8 = 0, 1, 2
+
+__all__ = [
+    "F32", "BF16", "W8", "as_f64", "bf16_round", "gelu", "route", "expert_ffn", "dequant", "forward",
+]
+
+
+def as_f64(a, kind: str) -> torch.Tensor:
+    """Exact float64 value of a stored tensor.  kind: 'f32' (float32), 'bf16' (uint16 bit patterns), 'i8'."""
+    a = np.ascontiguousarray(a)
+    if kind == "f32":
+        return torch.from_numpy(a.astype(np.float32, copy=False)).to(torch.float64)
+    if kind == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    if kind == "i8":
+        return torch.from_numpy(a.astype(np.int8, copy=False)).to(torch.float64)
+    raise ValueError(kind)
+
+
+def bf16_round(v: torch.Tensor) -> torch.Tensor:
+    """Round float64 values to the bfloat16 grid (8 significant bits) with one round-to-nearest-even step.
+
+    Uses frexp: v = m * 2**e with 0.5 <= |m| < 1, so m * 2**8 carries exactly the 8 significant bits plus the
+    fraction to be rounded.  The values met here are far inside bf16's normal range.
+    """
+    m, e = torch.frexp(v)
+    return torch.ldexp(torch.round(torch.ldexp(m, torch.full_like(e, 8))), e - 8)
+
+
+def gelu(z: torch.Tensor) -> torch.Tensor:
+    """Exact GELU: z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2))."""
+    return 0.5 * z * (1.0 + torch.special.erf(z / math.sqrt(2.0)))
+
+
+def route(x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor | None = None, k: int = 2) -> dict:
+    """Router of [moe] "Expert Routing Details": gate logits, softmax over all experts, top-k.
+
+    x [T, d] and router_w [E, d] in float64.  Returns logits [T, E], probs [T, E], idx [T, k] (int64, descending
+    logit, lower index first on ties), p [T, k] = probs at idx, and the smallest logit gaps (diagnostics).
+    """
+    logits = x @ router_w.T
+    if bias is not None:
+        logits = logits + bias[None, :]
+    T, E = logits.shape
+    mx = logits.max(dim=1, keepdim=True).values
+    ex = torch.exp(logits - mx)
+    probs = ex / ex.sum(dim=1, keepdim=True)
+    idx = torch.empty((T, k), dtype=torch.int64)
+    taken = torch.zeros((T, E), dtype=torch.bool)
+    rows = torch.arange(T)
+    for j in range(k):
+        best = torch.full((T,), -1, dtype=torch.int64)
+        bestv = torch.full((T,), -math.inf, dtype=torch.float64)
+        for e in range(E):  # ascending e with strict '>' keeps the lower index on equal logits
+            le = logits[:, e]
+            better = (~taken[:, e]) & ((best < 0) | (le > bestv))
+            best = torch.where(better, torch.full_like(best, e), best)
+            bestv = torch.where(better, le, bestv)
+        idx[:, j] = best
+        taken[rows, best] = True
+    p = probs.gather(1, idx)
+    srt = torch.sort(logits, dim=1, descending=True).values
+    gap12 = (srt[:, 0] - srt[:, 1]).min().item() if E > 1 else math.inf
+    gap_k = (srt[:, k - 1] - srt[:, k]).min().item() if E > k else math.inf
+    return {"logits": logits, "probs": probs, "idx": idx, "p": p, "min_gap_top": gap12, "min_gap_cut": gap_k}
+
+
+def expert_ffn(x: torch.Tensor, w1: torch.Tensor, wv: torch.Tensor, w2: torch.Tensor, round_h: bool) -> tuple:
+    """One expert of [bridge]'s diagram on rows x [n, d]: h = GELU(x W1) ⊙ (x Wv); y = h W2.
+
+    w1, wv [d, f] and w2 [f, d] in float64 ([in, out]).  Returns (h, y).
+    """
+    a = x @ w1
+    b = x @ wv
+    h = gelu(a) * b
+    if round_h:
+        h = bf16_round(h)
+    return h, h @ w2
+
+
+def dequant(q, s) -> torch.Tensor:
+    """[card] "Conversion Details": weight = int8 value times its bf16 scale, the scale broadcast over the in axis.
+
+    q [in, out] int8 (numpy), s [1, out] bf16 bits (numpy).  Exact in float64.
+    """
+    return as_f64(q, "i8") * as_f64(s, "bf16")
+
+
+def _expert_weights(inp: dict, dtype: int, e: int):
+    if dtype == F32:
+        return tuple(as_f64(inp[n][e], "f32") for n in ("w1", "wv", "w2"))
+    if dtype == BF16:
+        return tuple(as_f64(inp[n][e], "bf16") for n in ("w1", "wv", "w2"))
+    if dtype == W8:
+        return (dequant(inp["w1"][e], inp["s1"][e]), dequant(inp["wv"][e], inp["sv"][e]),
+                dequant(inp["w2"][e], inp["s2"][e]))
+    raise ValueError(dtype)
+
+
+def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False) -> dict:
+    """The whole layer: routing on every token, expert FFNs and combine on ``rows`` (all rows if None).
+
+    inp: dict of numpy arrays as produced by ``synth.make_inputs`` (x, router_w, w1, wv, w2, s1, sv, s2,
+    router_bias).  Returns float64 tensors: out [len(rows), d]; idx [T, k]; p [T, k]; counts [E]; logits; probs;
+    and, if asked, h [len(rows), k, f] and y [len(rows), k, d] per (row, selected expert).
+    """
+    akind = "f32" if dtype == F32 else "bf16"
+    x = as_f64(inp["x"], akind)
+    rw = as_f64(inp["router_w"], akind)
+    bias = inp.get("router_bias")
+    bias = None if bias is None else torch.from_numpy(np.asarray(bias, dtype=np.float32)).to(torch.float64)
+    T, d = x.shape
+    E = rw.shape[0]
+    r = route(x, rw, bias, k)
+    idx, p = r["idx"], r["p"]
+    counts = torch.bincount(idx.reshape(-1), minlength=E)
+    rows = torch.arange(T) if rows is None else torch.as_tensor(np.asarray(rows), dtype=torch.int64)
+    n = rows.numel()
+    sel = idx[rows]  # [n, k]
+    out = torch.zeros((n, d), dtype=torch.float64)
+    f = inp["w1"].shape[2]
+    hs = torch.zeros((n, k, f), dtype=torch.float64) if return_h else None
+    ys = torch.zeros((n, k, d), dtype=torch.float64) if return_h else None
+    round_h = dtype != F32
+    ys_all = torch.zeros((n, k, d), dtype=torch.float64)
+    for e in range(E):
+        hit = (sel == e).nonzero()  # (row position, slot j) pairs choosing expert e
+        if hit.numel() == 0:
+            continue
+        w1, wv, w2 = _expert_weights(inp, dtype, e)
+        h, y = expert_ffn(x[rows[hit[:, 0]]], w1, wv, w2, round_h)
+        del w1, wv, w2
+        ys_all[hit[:, 0], hit[:, 1]] = y
+        if return_h:
+            hs[hit[:, 0], hit[:, 1]] = h
+    # combine of [moe] "How MoE Works in Practice": sum over the k selected experts of p_j * y_j
+    pr = p[rows]
+    for j in range(k):
+        out += pr[:, j:j + 1] * ys_all[:, j]
+    res = {"out": out, "idx": idx, "p": p, "counts": counts, "logits": r["logits"], "probs": r["probs"],
+           "rows": rows, "min_gap_top": r["min_gap_top"], "min_gap_cut": r["min_gap_cut"]}
+    if return_h:
+        res["h"] = hs
+        res["y"] = ys_all
+    return res
