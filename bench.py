@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Throughput of the Grok-1 MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16|prefill_bf16|int8_w8|skew_bf16|tiny_f32]
+
+A step is one pass of the whole layer (router, binning, fused up-projection with GELU product, down-projection,
+combine) over one batch of seeded synthetic tokens, with weights and inputs already resident in HBM.  The step
+calls the library's five step entry points in order (bit-identical to grok_moe_forward) on the current stream,
+so that HIP events can time the expert kernels inside the timed region.  Prints one JSON line.
+
+The default workload is the Grok-1-shape decode step (T=8, d=6144, f=32768, E=8, top-2, bf16).  Unless
+--no-prefill is given, the same run also times the T=8192 prefill on the same weights and reports it under
+"prefill".  The CPU oracle is timed on a bounded sample of the same workload ("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Grok-1 MoE layer tokens/s (T=8 decode, T=8192 prefill); % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ("expert_stream.hip", "expert_tiled.hip", "common.h")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_transformer_gemv_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the companion T=8192 prefill measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+class Layer:
+    """Device-resident inputs and preallocated buffers of one workload, and the timed step."""
+
+    def __init__(self, gm, w, inp, dv):
+        import torch
+        self.gm, self.w, self.inp, self.dv = gm, w, inp, dv
+        T, d, f, E = w.T, w.d, w.f, w.E
+        dev = dv["x"].device
+        self.S = gm.down_splits(T, d, f, E, 2, w.dtype)
+        i32 = torch.int32
+        self.idx = torch.empty((T, 2), dtype=i32, device=dev)
+        self.p = torch.empty((T, 2), dtype=torch.float32, device=dev)
+        self.counts = torch.empty((E,), dtype=i32, device=dev)
+        self.offsets = torch.empty((E + 1,), dtype=i32, device=dev)
+        self.perm = torch.empty((2 * T,), dtype=i32, device=dev)
+        self.inv = torch.empty((T, 2), dtype=i32, device=dev)
+        self.h = torch.empty((2 * T, f), dtype=torch.float32 if w.dtype == gm.F32 else torch.bfloat16, device=dev)
+        self.y = torch.empty((self.S, 2 * T, d), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.s1 = self.sv = self.s2 = None
+        if dv["scales"] is not None:
+            self.s1, self.sv, self.s2 = dv["scales"]
+        mk = lambda: torch.cuda.Event(enable_timing=True)
+        self.ev = [mk() for _ in range(6)]
+        self.lib = gm.lib()
+
+    def step(self, timed=False):
+        import ctypes
+        gm, dv, L, w = self.gm, self.dv, self.lib, self.w
+        P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        s = ctypes.c_void_p(__import__("torch").cuda.current_stream().cuda_stream)
+        T, d, f, E, dt = w.T, w.d, w.f, w.E, w.dtype
+        ev = self.ev
+        if timed:
+            ev[0].record()
+        st = L.grok_moe_route(P(dv["x"]), P(dv["router_w"]), P(dv["router_bias"]), T, d, E, 2, dt, P(self.idx),
+                              P(self.p), s)
+        st |= L.grok_moe_bin(P(self.idx), T, E, 2, P(self.counts), P(self.offsets), P(self.perm), P(self.inv), s)
+        if timed:
+            ev[1].record()
+        st |= L.grok_moe_expert_up(P(dv["x"]), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), P(self.counts),
+                                   P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
+        if timed:
+            ev[2].record()
+        st |= L.grok_moe_expert_down(P(self.h), P(dv["w2"]), P(self.s2), P(self.counts), P(self.offsets), T, d, f,
+                                     E, 2, dt, self.S, P(self.y), s)
+        if timed:
+            ev[3].record()
+        st |= L.grok_moe_combine(P(self.y), self.S, P(self.p), P(self.inv), T, d, 2, P(self.out), s)
+        if timed:
+            ev[4].record()
+        if st != 0:
+            raise RuntimeError(f"library call failed (status bits {st})")
+
+    def run_with_kernel_times(self, steps, warmup):
+        """Time `steps` steps (wall, bracketed by synchronize) and the average per-launch duration of each expert
+        kernel (HIP events on the launch stream, read after the timed region)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        mk = lambda: torch.cuda.Event(enable_timing=True)
+        evs = [[mk() for _ in range(5)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.ev = evs[i]
+            self.step(timed=True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k = np.array([[e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]), e[0].elapsed_time(e[1]),
+                       e[3].elapsed_time(e[4])] for e in evs])
+        return wall, k.mean(axis=0)  # ms: up, down, route+bin, combine
+
+
+def n_hit(layer) -> int:
+    return int((layer.counts.cpu().numpy() > 0).sum())
+
+
+def up_bytes(w, nh, T):
+    wb = 1 if w.dtype == 2 else (4 if w.dtype == 0 else 2)
+    b = nh * 2 * w.d * w.f * wb + T * w.d * 2 + 2 * T * w.f * 2
+    if w.dtype == 2:
+        b += nh * 2 * w.f * 2
+    return b
+
+
+def down_bytes(w, nh, T, S):
+    wb = 1 if w.dtype == 2 else (4 if w.dtype == 0 else 2)
+    b = nh * w.f * w.d * wb + 2 * T * w.f * 2 + S * 2 * T * w.d * 4
+    if w.dtype == 2:
+        b += nh * w.d * 2
+    return b
+
+
+def up_flops(w, T):
+    return 2.0 * (2 * T) * w.d * w.f * 2
+
+
+def load_traffic(workload: str, kernel: str, launches_bytes: float):
+    """HBM traffic per launch from the committed counter summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except Exception:
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, oracle, synth):
+    """The oracle as it stands, on a bounded sample of the workload (routing for all tokens, expert path on a few
+    rows), timed on this host's cores."""
+    import torch
+    rows = synth.sampled_rows(w.T, 2 if w.T <= 64 else 4)
+    t0 = time.perf_counter()
+    oracle.forward(inp, w.dtype, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} of {w.T} token rows of {w.name} through the float64 oracle (routing on all "
+                      f"{w.T} tokens, both selected experts per row), {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is designed but not built "
+                                   "(tensor-parallel over d_ff with a reduce-scatter of the fp32 output)",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_transformer_gemv_amd as gm
+    import synth
+    from tests._helpers import dev_inputs
+
+    gm.lib()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[a.workload]
+    log(f"workload {w.name}: drawing weights")
+    t0 = time.perf_counter()
+    wts = synth.make_weights(w)
+    inp = synth.make_inputs(w, weights=wts)
+    dv = dev_inputs(inp, w.dtype)
+    log(f"inputs resident ({time.perf_counter() - t0:.1f} s)")
+
+    if a.copy_probe_mib:
+        src = torch.empty(a.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    layer = Layer(gm, w, inp, dv)
+    wall, kms = layer.run_with_kernel_times(a.steps, a.warmup)
+    ms = wall * 1e3 / a.steps
+    nh = n_hit(layer)
+    T = w.T
+    res = {"metric": METRIC, "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": {0: "f32", 1: "bf16", 2: "bf16 x int8-weight"}[w.dtype], "data": "synthetic",
+           "config": {"workload": w.name, "T": T, "d_model": w.d, "d_ff": w.f, "experts": w.E, "top_k": 2,
+                      "experts_hit": nh, "down_splits": layer.S}}
+    kernels = {"expert_up_ms": kms[0], "expert_down_ms": kms[1], "route_bin_ms": kms[2], "combine_ms": kms[3]}
+    if w.T <= 64:  # weight-streaming regime: HBM-bound, the up-projection (W1 and Wv) is the dominant kernel
+        ub = up_bytes(w, nh, T)
+        ach = ub / (kms[0] * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": "up_stream_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                           "traffic": load_traffic(w.name, "up", ub), "algorithmic_bytes": ub}
+        db = down_bytes(w, nh, T, layer.S)
+        kernels["expert_down_GBps"] = db / (kms[1] * 1e-3) / 1e9
+        kernels["layer_GBps"] = (ub + db) / (ms * 1e-3) / 1e9
+    else:
+        fl = up_flops(w, T)
+        ach = fl / (kms[0] * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "kernel": "tiled_kernel<2>", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                           "traffic": load_traffic(w.name, "up", fl), "algorithmic_flops": fl}
+        kernels["layer_TFLOPs"] = 3 * fl / 2 / (ms * 1e-3) / 1e12
+    res["kernels"] = kernels
+    log(f"{w.name}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down {kms[1]:.3f} ms")
+
+    if not a.no_prefill and w.name == "decode_bf16":
+        pw = synth.WORKLOADS["prefill_bf16"]
+        pinp = synth.make_inputs(pw, weights=wts)
+        pdv = dict(dv)
+        pdv["x"] = dev_inputs({**pinp, "w1": None, "wv": None, "w2": None}, synth.BF16)["x"]
+        pl = Layer(gm, pw, pinp, pdv)
+        pwall, pk = pl.run_with_kernel_times(a.prefill_steps, 2)
+        pms = pwall * 1e3 / a.prefill_steps
+        fl = up_flops(pw, pw.T)
+        res["prefill"] = {"workload": pw.name, "T": pw.T, "value": pw.T / (pms / 1e3), "unit": "tokens/s",
+                          "ms_per_step": pms, "steps": a.prefill_steps,
+                          "layer_TFLOPs": 3 * fl / 2 / (pms * 1e-3) / 1e12,
+                          "roofline": {"bound": "mfma", "kernel": "tiled_kernel<2>",
+                                       "achieved": fl / (pk[0] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": fl / (pk[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                          "kernels": {"expert_up_ms": pk[0], "expert_down_ms": pk[1], "route_bin_ms": pk[2],
+                                      "combine_ms": pk[3],
+                                      "expert_down_TFLOPs": fl / 2 / (pk[1] * 1e-3) / 1e12}}
+        log(f"prefill: {pms:.3f} ms/step, {res['prefill']['value']:.0f} tokens/s")
+        del pl, pdv
+        torch.cuda.empty_cache()
+
+    if not a.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, inp, oracle, synth)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

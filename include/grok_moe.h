@@ -1,0 +1,129 @@
+/*
+ * grok_moe.h -- C ABI of the MI355X (gfx950) forward pass of one Grok-1 mixture-of-experts FFN layer.
+ *
+ * The layer (pages cited by title and section):
+ *   - Router: logits = x . gate^T (a Dense layer from d_model to the E experts), softmax over all E experts,
+ *     then the top-2 experts per token; the call returns the top-k gates and their indices
+ *     ("Grok-1: 314B Total Parameters, 25B Active Per Token (MoE Explained)", section "Expert Routing Details").
+ *   - Expert: y = (GELU(x W1) (*) (x Wv)) W2, 8 experts of which 2 are active per token
+ *     ("A functional bridge between openai/grok and xai-org/grok-1", the architecture diagram).
+ *   - Combine: the layer output is the sum over the selected experts of the expert output times that
+ *     expert's router probability ("... (MoE Explained)", section "How MoE Works in Practice").
+ *   - Shapes: d_model 6144, d_ff 32768, 8 experts, top-2; router gate [8, 6144]
+ *     ("Grok-1-BF16", section "Verification"); int8 weights with bf16 scales, scale broadcast over the
+ *     grouped axis, JAX [in, out] layout ("Grok-1-BF16", section "Conversion Details").
+ *
+ * Conventions for every entry point:
+ *   - All tensors are row-major and contiguous.  Tensor pointers are DEVICE pointers (HBM of the current HIP
+ *     device), 16-byte aligned, owned by the caller, and must stay valid until the enqueued work completes.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call only ENQUEUES work on it and
+ *     returns without synchronising; results are visible after the stream reaches that point.
+ *   - Argument errors are detected on the host before anything is enqueued: the call returns a negative
+ *     status, enqueues nothing and writes nothing.  A failed kernel launch returns GROK_MOE_EHIP.
+ *   - The library allocates no memory and keeps no mutable global state: calls on different streams with
+ *     distinct workspaces may run concurrently.
+ *   - Weight layout is [E, in, out]: W1 and Wv are [E, d, f], W2 is [E, f, d].  Scales (int8 only) are
+ *     [E, 1, f] for W1 and Wv and [E, 1, d] for W2: one bf16 scale per (expert, output channel).
+ *   - Supported shapes: k == 2, 2 <= E <= 64.  bf16 and int8 layers need d and f to be multiples of 256;
+ *     the fp32 layer needs multiples of 64.  T may be any value >= 0 (T == 0 enqueues nothing).
+ *     Other shapes return GROK_MOE_EUNSUPPORTED; they are never padded silently.
+ */
+#ifndef GROK_MOE_H
+#define GROK_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of a layer.
+ *   GROK_MOE_F32 : x, router_w, W1, Wv, W2 float32.  h (the GELU product) is kept in float32.
+ *   GROK_MOE_BF16: x, router_w, W1, Wv, W2 bfloat16 (raw 16-bit patterns).  h is rounded once to bf16.
+ *   GROK_MOE_W8  : x, router_w bfloat16; W1, Wv, W2 int8 with bf16 scales s1, sv, s2; h rounded to bf16.
+ * Accumulation is fp32 in every expert matrix product; the router accumulates in fp64. */
+typedef enum { GROK_MOE_F32 = 0, GROK_MOE_BF16 = 1, GROK_MOE_W8 = 2 } grok_moe_dtype;
+
+enum {
+  GROK_MOE_OK = 0,
+  GROK_MOE_EINVAL = -1,       /* NULL or misaligned pointer, negative size, unknown dtype */
+  GROK_MOE_EUNSUPPORTED = -2, /* valid but unsupported shape (k != 2, E outside [2,64], d/f granularity) */
+  GROK_MOE_EWORKSPACE = -3,   /* workspace smaller than grok_moe_workspace_size() */
+  GROK_MOE_EHIP = -4          /* a HIP launch failed */
+};
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* grok_moe_strerror(int status);
+
+/* Bytes of device workspace grok_moe_forward() needs for this shape (0 if the shape is invalid or T == 0).
+ * The workspace holds routing results, the token permutation, h [k*T, f] and the partial expert outputs. */
+size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
+
+/* The whole layer: router -> token binning -> fused up-projection with GELU product -> down-projection ->
+ * gate-weighted combine, all on `stream`.
+ *   x          [T, d]     f32 | bf16
+ *   router_w   [E, d]     f32 | bf16 (the gate weight, [out, in])
+ *   w1, wv     [E, d, f]  f32 | bf16 | int8
+ *   w2         [E, f, d]  f32 | bf16 | int8
+ *   s1, sv     [E, 1, f]  bf16, s2 [E, 1, d] bf16: int8 scales (GROK_MOE_W8 only; must be NULL otherwise)
+ *   out        [T, d]     f32, overwritten: out[t] = p[t,0] * y_{e0}(x_t) + p[t,1] * y_{e1}(x_t)
+ *   router_bias [E] f32 or NULL: added to the logits before the softmax
+ *   topk_idx   [T, k] int32 or NULL (out): selected experts, descending logit, lower index first on ties
+ *   topk_p     [T, k] f32 or NULL (out): their softmax probabilities over all E experts (not renormalised)
+ *   expert_counts [E] int32 or NULL (out): number of tokens routed to each expert
+ *   workspace  device buffer of at least grok_moe_workspace_size() bytes, 256-byte aligned, not shared
+ *              with another call in flight.
+ * Results are deterministic: identical inputs give bit-identical outputs (no floating-point atomics). */
+int grok_moe_forward(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                     const void* s1, const void* sv, const void* s2,
+                     int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                     float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- The steps of the layer, one entry point each (grok_moe_forward enqueues exactly these). ---------------
+ * A "slot" is one (token, selected expert) assignment; there are k*T of them, grouped by expert in ascending
+ * expert order and, within an expert, in ascending token order. */
+
+/* Router ("... (MoE Explained)", section "Expert Routing Details"): gate GEMV with fp64 accumulation, softmax
+ * over all E, top-2 with the lower-index tie-break.  x [T,d], router_w [E,d] (f32 if dtype == GROK_MOE_F32,
+ * else bf16); router_bias [E] f32 or NULL.  Writes topk_idx [T,k] int32 and topk_p [T,k] f32 (both required). */
+int grok_moe_route(const void* x, const void* router_w, const float* router_bias, int64_t T, int64_t d, int E,
+                   int k, int dtype, int32_t* topk_idx, float* topk_p, void* stream);
+
+/* Token binning (the dispatch of each token to its selected experts, "... (MoE Explained)", section
+ * "How MoE Works in Practice"): histogram of topk_idx [T,k], exclusive prefix sum, stable permutation.
+ * Writes counts [E], offsets [E+1] (offsets[e] = first slot of expert e, offsets[E] = k*T),
+ * perm [k*T] (slot -> token) and inv [T,k] ((token, j) -> slot).  topk_idx entries must lie in [0, E). */
+int grok_moe_bin(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* inv, void* stream);
+
+/* Fused up-projection ("A functional bridge ...", architecture diagram; int8 form per "Grok-1-BF16",
+ * section "Conversion Details"): for every slot s of expert e with token t = perm[s],
+ *   a = x[t] . W1[e] (* s1[e]),  b = x[t] . Wv[e] (* sv[e]),  h[s] = GELU_erf(a) * b,
+ * fp32 accumulation; h [k*T, f] is bf16 (rounded once, to nearest even) or f32 for GROK_MOE_F32.
+ * counts/offsets/perm are grok_moe_bin's outputs. */
+int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                       int64_t T, int64_t d, int64_t f, int E, int k, int dtype, void* h, void* stream);
+
+/* Number of partial sums grok_moe_expert_down() splits the f axis into for this shape (>= 1). */
+int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
+
+/* Down-projection: y[p, s] = sum over the p-th chunk of f of h[s] . W2[e] (* s2[e]), fp32, for every slot s
+ * of expert e.  y is [splits, k*T, d] f32 with splits = grok_moe_down_splits(...) (passed back in `splits`
+ * as a check; a different value returns GROK_MOE_EINVAL). */
+int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const int32_t* counts,
+                         const int32_t* offsets, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                         int splits, float* y, void* stream);
+
+/* Gate-weighted combine ("... (MoE Explained)", section "How MoE Works in Practice"):
+ * out[t] = sum_j topk_p[t,j] * (sum_p y[p, inv[t,j]]), the partials summed in ascending p. out [T,d] f32. */
+int grok_moe_combine(const float* y, int splits, const float* topk_p, const int32_t* inv, int64_t T, int64_t d,
+                     int k, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROK_MOE_H */

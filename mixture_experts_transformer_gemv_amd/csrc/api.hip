@@ -1,0 +1,222 @@
+// C ABI of the Grok-1 MoE layer library (declarations and contracts in include/grok_moe.h).
+//
+// Host side only: argument validation, workspace layout, choice of kernel family, and the launches on the
+// caller's stream.  Nothing here allocates memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/grok_moe.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+constexpr int kStreamMaxTokens = 64;  // at most this many tokens: few rows per expert -> weight streaming kernels
+
+struct Plan {
+  int64_t slots;
+  bool stream;  // streaming kernels (else LDS-tiled grouped GEMM or the fp32 kernels)
+  int mt;       // 16-row MFMA tiles per pass of the streaming kernels
+  int splits;   // partial sums of the down-projection
+  size_t o_idx, o_p, o_counts, o_offsets, o_perm, o_inv, o_h, o_y, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int check_shape(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
+  if (dtype != GROK_MOE_F32 && dtype != GROK_MOE_BF16 && dtype != GROK_MOE_W8) return GROK_MOE_EINVAL;
+  if (T < 0 || d <= 0 || f <= 0) return GROK_MOE_EINVAL;
+  if (k != 2 || E < 2 || E > 64) return GROK_MOE_EUNSUPPORTED;
+  if (T > kMaxTokens || d > (int64_t(1) << 20) || f > (int64_t(1) << 20)) return GROK_MOE_EUNSUPPORTED;
+  const int64_t g = dtype == GROK_MOE_F32 ? 64 : 256;
+  if (d % g != 0 || f % g != 0) return GROK_MOE_EUNSUPPORTED;
+  return GROK_MOE_OK;
+}
+
+int down_splits(int64_t T, int64_t f, int dtype) {
+  if (dtype == GROK_MOE_F32 || T > kStreamMaxTokens) return 1;
+  // chunks of at least 2048 rows of W2 (a multiple of 64), at most 16 chunks
+  int s = 1;
+  while (s < 16 && (f / (2 * s)) % 64 == 0 && f / (2 * s) >= 2048) s *= 2;
+  return s;
+}
+
+Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
+  Plan p;
+  p.slots = 2 * T;
+  p.stream = dtype != GROK_MOE_F32 && T <= kStreamMaxTokens;
+  p.mt = T <= 16 ? 1 : 2;
+  p.splits = down_splits(T, f, dtype);
+  size_t o = 0;
+  p.o_idx = o; o = align256(o + size_t(p.slots) * 4);
+  p.o_p = o; o = align256(o + size_t(p.slots) * 4);
+  p.o_counts = o; o = align256(o + size_t(E) * 4);
+  p.o_offsets = o; o = align256(o + size_t(E + 1) * 4);
+  p.o_perm = o; o = align256(o + size_t(p.slots) * 4);
+  p.o_inv = o; o = align256(o + size_t(p.slots) * 4);
+  p.o_h = o; o = align256(o + size_t(p.slots) * f * (dtype == GROK_MOE_F32 ? 4 : 2));
+  p.o_y = o; o = align256(o + size_t(p.splits) * p.slots * d * 4);
+  p.total = o;
+  return p;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+inline bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+int check_scales(int dtype, const void* s1, const void* sv, const void* s2) {
+  if (dtype == GROK_MOE_W8) return (ok_ptr(s1) && ok_ptr(sv) && ok_ptr(s2)) ? GROK_MOE_OK : GROK_MOE_EINVAL;
+  return (s1 == nullptr && sv == nullptr && s2 == nullptr) ? GROK_MOE_OK : GROK_MOE_EINVAL;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? GROK_MOE_OK : GROK_MOE_EHIP; }
+
+// ---- the steps, without argument checks (callers have validated)
+hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv, const int32_t* counts,
+                 const int32_t* offsets, const int32_t* perm, const Plan& p, int64_t d, int64_t f, int E, int dtype,
+                 void* h, hipStream_t s) {
+  if (dtype == GROK_MOE_F32)
+    return gm::launch_up_f32(static_cast<const float*>(x), static_cast<const float*>(w1),
+                             static_cast<const float*>(wv), counts, offsets, perm, int(d), int(f), E, int(p.slots),
+                             static_cast<float*>(h), s);
+  const bool i8 = dtype == GROK_MOE_W8;
+  if (p.stream)
+    return gm::launch_up_stream(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
+                                static_cast<const uint16_t*>(sv), counts, offsets, perm, int(d), int(f), E, i8, p.mt,
+                                static_cast<uint16_t*>(h), s);
+  return gm::launch_up_tiled(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
+                             static_cast<const uint16_t*>(sv), counts, offsets, perm, int(d), int(f), E,
+                             int(p.slots), i8, static_cast<uint16_t*>(h), s);
+}
+
+hipError_t do_down(const void* h, const void* w2, const void* s2, const int32_t* counts, const int32_t* offsets,
+                   const Plan& p, int64_t d, int64_t f, int E, int dtype, float* y, hipStream_t s) {
+  if (dtype == GROK_MOE_F32)
+    return gm::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2), counts, offsets, int(d),
+                               int(f), E, int(p.slots), y, s);
+  const bool i8 = dtype == GROK_MOE_W8;
+  if (p.stream)
+    return gm::launch_down_stream(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2), counts,
+                                  offsets, int(d), int(f), E, int(p.slots), p.splits, i8, p.mt, y, s);
+  return gm::launch_down_tiled(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2), counts,
+                               offsets, int(d), int(f), E, int(p.slots), i8, y, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* grok_moe_strerror(int status) {
+  switch (status) {
+    case GROK_MOE_OK: return "ok";
+    case GROK_MOE_EINVAL: return "invalid argument (NULL or misaligned pointer, negative size or unknown dtype)";
+    case GROK_MOE_EUNSUPPORTED: return "unsupported shape (needs k == 2, 2 <= E <= 64, d and f multiples of 256 "
+                                       "for bf16/int8 or of 64 for fp32)";
+    case GROK_MOE_EWORKSPACE: return "workspace too small";
+    case GROK_MOE_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
+  if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK || T == 0) return 0;
+  return make_plan(T, d, f, E, dtype).total;
+}
+
+int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
+  if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK) return 1;
+  return make_plan(T, d, f, E, dtype).splits;
+}
+
+int grok_moe_forward(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                     const void* s1, const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k,
+                     int dtype, float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(T, d, f, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(w2) || !ok_ptr(out))
+    return GROK_MOE_EINVAL;
+  if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
+  if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
+  const Plan p = make_plan(T, d, f, E, dtype);
+  if (workspace_bytes < p.total) return GROK_MOE_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + p.o_idx);
+  float* pr = topk_p ? topk_p : reinterpret_cast<float*>(ws + p.o_p);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.o_counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + p.o_offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + p.o_perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + p.o_inv);
+  void* h = ws + p.o_h;
+  float* y = reinterpret_cast<float*>(ws + p.o_y);
+
+  hipError_t e = gm::launch_router(x, router_w, router_bias, int(T), int(d), E, dtype != GROK_MOE_F32, idx, pr, s);
+  if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
+  if (e == hipSuccess) e = do_up(x, w1, wv, s1, sv, counts, offsets, perm, p, d, f, E, dtype, h, s);
+  if (e == hipSuccess) e = do_down(h, w2, s2, counts, offsets, p, d, f, E, dtype, y, s);
+  if (e == hipSuccess) e = gm::launch_combine(y, p.splits, pr, inv, int(T), int(d), out, s);
+  if (e == hipSuccess && expert_counts)
+    e = hipMemcpyAsync(expert_counts, counts, size_t(E) * 4, hipMemcpyDeviceToDevice, s);
+  return hip_status(e);
+}
+
+int grok_moe_route(const void* x, const void* router_w, const float* router_bias, int64_t T, int64_t d, int E, int k,
+                   int dtype, int32_t* topk_idx, float* topk_p, void* stream) {
+  int st = check_shape(T, d, dtype == GROK_MOE_F32 ? 64 : 256, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(topk_idx) || !ok_ptr(topk_p) || !ok_opt(router_bias))
+    return GROK_MOE_EINVAL;
+  return hip_status(gm::launch_router(x, router_w, router_bias, int(T), int(d), E, dtype != GROK_MOE_F32, topk_idx,
+                                      topk_p, static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_bin(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* inv, void* stream) {
+  if (T < 0) return GROK_MOE_EINVAL;
+  if (k != 2 || E < 2 || E > 64 || T > kMaxTokens) return GROK_MOE_EUNSUPPORTED;
+  if (!ok_ptr(counts) || !ok_ptr(offsets)) return GROK_MOE_EINVAL;
+  if (T > 0 && (!ok_ptr(topk_idx) || !ok_ptr(perm) || !ok_ptr(inv))) return GROK_MOE_EINVAL;
+  return hip_status(gm::launch_bin(topk_idx, int(T), E, counts, offsets, perm, inv, static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d,
+                       int64_t f, int E, int k, int dtype, void* h, void* stream) {
+  int st = check_shape(T, d, f, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(perm) || !ok_ptr(h))
+    return GROK_MOE_EINVAL;
+  if ((st = check_scales(dtype, s1, sv, dtype == GROK_MOE_W8 ? s1 : nullptr)) != GROK_MOE_OK) return st;
+  const Plan p = make_plan(T, d, f, E, dtype);
+  return hip_status(do_up(x, w1, wv, s1, sv, counts, offsets, perm, p, d, f, E, dtype, h,
+                          static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const int32_t* counts, const int32_t* offsets,
+                         int64_t T, int64_t d, int64_t f, int E, int k, int dtype, int splits, float* y, void* stream) {
+  int st = check_shape(T, d, f, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  const Plan p = make_plan(T, d, f, E, dtype);
+  if (splits != p.splits) return GROK_MOE_EINVAL;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(h) || !ok_ptr(w2) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(y)) return GROK_MOE_EINVAL;
+  if (dtype == GROK_MOE_W8 ? !ok_ptr(s2) : s2 != nullptr) return GROK_MOE_EINVAL;
+  return hip_status(do_down(h, w2, s2, counts, offsets, p, d, f, E, dtype, y, static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_combine(const float* y, int splits, const float* topk_p, const int32_t* inv, int64_t T, int64_t d, int k,
+                     float* out, void* stream) {
+  if (T < 0 || d <= 0 || splits < 1 || splits > 64) return GROK_MOE_EINVAL;
+  if (k != 2 || T > kMaxTokens || d % 4 != 0) return GROK_MOE_EUNSUPPORTED;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(y) || !ok_ptr(topk_p) || !ok_ptr(inv) || !ok_ptr(out)) return GROK_MOE_EINVAL;
+  return hip_status(gm::launch_combine(y, splits, topk_p, inv, int(T), int(d), out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

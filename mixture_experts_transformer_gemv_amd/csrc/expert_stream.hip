@@ -1,0 +1,272 @@
+// Expert matrix products of the Grok-1 MoE layer for few tokens per expert (decode-sized batches), gfx950.
+//
+// Expert FFN, page "A functional bridge between openai/grok and xai-org/grok-1" (architecture diagram):
+// y = (GELU(x W1) (*) (x Wv)) W2.  int8 weights times per-(expert, output channel) bf16 scales, page
+// "Grok-1-BF16", section "Conversion Details".
+//
+// With at most a few dozen tokens per expert the products are bound by streaming the weights from HBM: every
+// weight is used by at most 2 * 16 tokens.  So the weights go straight from HBM into registers, without LDS
+// staging.  Each lane loads an 8 (k) x 8 (n) block as eight 16-byte row pieces (8-byte for int8), transposes
+// it in registers (v_perm_b32; int8 values are converted to bf16 exactly on the way) so that it holds 8 k
+// values for each of 8 columns, and feeds 8 MFMAs 16x16x32 against the same A fragment (16 token rows).
+// Lane l covers columns n0 + 8 (l & 15) .. +7 and k rows 8 (l >> 4) .. +7 of each 32-deep step, so a wave
+// owns 128 columns; the four 16-lane groups read four different row blocks of 256 contiguous bytes.
+//
+// Up-projection: one wave per 128 columns of both W1 and Wv over the whole d axis (GELU needs the full sum);
+// h = bf16(GELU(a) * b) is written for the valid token rows.  Down-projection: one wave per 128 columns of W2
+// over one of S chunks of the f axis; fp32 partial sums go to y[S, slots, d] and are added by the combine.
+#include "common.h"
+#include "launch.h"
+
+namespace gm {
+
+template <bool INT8> struct WRow;
+template <> struct WRow<false> {  // bf16: 16 bytes = 8 columns
+  typedef u32x4_t T;
+  static __device__ __forceinline__ T load(const void* base, size_t i) {
+    return *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + i);
+  }
+  static __device__ __forceinline__ void transpose(const T r[8], u32x4_t t[8]) { transpose8x8_bf16(r, t); }
+};
+template <> struct WRow<true> {  // int8: 8 bytes = 8 columns
+  typedef u32x2_t T;
+  static __device__ __forceinline__ T load(const void* base, size_t i) {
+    return *reinterpret_cast<const u32x2_t*>(static_cast<const int8_t*>(base) + i);
+  }
+  static __device__ __forceinline__ void transpose(const T r[8], u32x4_t t[8]) { transpose8x8_i8_to_bf16(r, t); }
+};
+
+// 8 scales (bf16) of consecutive columns -> float.
+__device__ __forceinline__ void load_scales8(const uint16_t* s, float o[8]) {
+  const u32x4_t w = *reinterpret_cast<const u32x4_t*>(s);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { o[2 * j] = bf16lo(w[j]); o[2 * j + 1] = bf16hi(w[j]); }
+}
+
+template <bool INT8, int MT>
+struct UpStep {
+  typename WRow<INT8>::T b1[8], b2[8];
+  u32x4_t a[MT];
+};
+
+template <bool INT8, int MT>
+__global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restrict__ x, const void* __restrict__ w1,
+                                                        const void* __restrict__ wv, const uint16_t* __restrict__ s1,
+                                                        const uint16_t* __restrict__ sv,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ perm, int d, int f,
+                                                        uint16_t* __restrict__ h) {
+  typedef WRow<INT8> W;
+  const int e = blockIdx.y;
+  const int n_e = counts[e];
+  if (n_e == 0) return;
+  const int off = offsets[e];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int n0 = (blockIdx.x * 4 + wave) * 128;
+  if (n0 >= f) return;  // no workgroup barrier in this kernel
+  const int col = n0 + 8 * c16;
+  const size_t ebase = size_t(e) * d * f;
+  const size_t lane_base = ebase + size_t(8 * g) * f + col;  // row 8g of each 32-deep step, column col
+
+  for (int mb = 0; mb < n_e; mb += 16 * MT) {
+    const uint16_t* arow[MT];
+    bool aval[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mb + mt * 16 + c16;
+      aval[mt] = m < n_e;
+      arow[mt] = x + size_t(aval[mt] ? perm[off + m] : 0) * d + 8 * g;
+    }
+    f32x4_t acc1[MT][8], acc2[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { acc1[mt][c] = f32x4_t{0, 0, 0, 0}; acc2[mt][c] = f32x4_t{0, 0, 0, 0}; }
+
+    auto load = [&](UpStep<INT8, MT>& st, int k0) {
+      const size_t rb = lane_base + size_t(k0) * f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        st.b1[r] = W::load(w1, rb + size_t(r) * f);
+        st.b2[r] = W::load(wv, rb + size_t(r) * f);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
+    };
+    auto compute = [&](const UpStep<INT8, MT>& st) {
+      u32x4_t t[8];
+      W::transpose(st.b1, t);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc1[mt][c] = mfma16x16x32(st.a[mt], t[c], acc1[mt][c]);
+      W::transpose(st.b2, t);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc2[mt][c] = mfma16x16x32(st.a[mt], t[c], acc2[mt][c]);
+    };
+
+    // d is a multiple of 64: two 32-deep steps per iteration, the next step's loads in flight during compute.
+    UpStep<INT8, MT> sa, sb;
+    load(sa, 0);
+    for (int k0 = 0; k0 < d; k0 += 64) {
+      load(sb, k0 + 32);
+      compute(sa);
+      if (k0 + 64 < d) load(sa, k0 + 64);
+      compute(sb);
+    }
+
+    float sc1[8], scv[8];
+    if (INT8) {
+      load_scales8(s1 + size_t(e) * f + col, sc1);
+      load_scales8(sv + size_t(e) * f + col, scv);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mb + mt * 16 + 4 * g + v;
+        if (m < n_e) {
+          float hv[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float a = acc1[mt][c][v], b = acc2[mt][c][v];
+            if (INT8) { a *= sc1[c]; b *= scv[c]; }
+            hv[c] = gelu_erf(a) * b;
+          }
+          u32x4_t o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = pack_bf16(hv[2 * j], hv[2 * j + 1]);
+          *reinterpret_cast<u32x4_t*>(h + size_t(off + m) * f + col) = o;
+        }
+      }
+    }
+  }
+}
+
+template <bool INT8, int MT>
+struct DownStep {
+  typename WRow<INT8>::T b[8];
+  u32x4_t a[MT];
+};
+
+template <bool INT8, int MT>
+__global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __restrict__ h, const void* __restrict__ w2,
+                                                          const uint16_t* __restrict__ s2,
+                                                          const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ offsets, int d, int f, int S,
+                                                          int64_t split_stride, float* __restrict__ y) {
+  typedef WRow<INT8> W;
+  const int e = blockIdx.z;
+  const int n_e = counts[e];
+  if (n_e == 0) return;
+  const int off = offsets[e];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int n0 = (blockIdx.x * 4 + wave) * 128;
+  if (n0 >= d) return;
+  const int col = n0 + 8 * c16;
+  const int kchunk = f / S;
+  const int kbeg = blockIdx.y * kchunk;
+  const size_t lane_base = size_t(e) * f * d + size_t(8 * g) * d + col;
+
+  for (int mb = 0; mb < n_e; mb += 16 * MT) {
+    const uint16_t* arow[MT];
+    bool aval[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mb + mt * 16 + c16;
+      aval[mt] = m < n_e;
+      arow[mt] = h + size_t(off + (aval[mt] ? m : 0)) * f + 8 * g;
+    }
+    f32x4_t acc[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[mt][c] = f32x4_t{0, 0, 0, 0};
+
+    auto load = [&](DownStep<INT8, MT>& st, int k0) {
+      const size_t rb = lane_base + size_t(k0) * d;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) st.b[r] = W::load(w2, rb + size_t(r) * d);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
+    };
+    auto compute = [&](const DownStep<INT8, MT>& st) {
+      u32x4_t t[8];
+      W::transpose(st.b, t);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt][c] = mfma16x16x32(st.a[mt], t[c], acc[mt][c]);
+    };
+
+    DownStep<INT8, MT> sa, sb;
+    const int kend = kbeg + kchunk;  // kchunk is a multiple of 64
+    load(sa, kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += 64) {
+      load(sb, k0 + 32);
+      compute(sa);
+      if (k0 + 64 < kend) load(sa, k0 + 64);
+      compute(sb);
+    }
+
+    float sc[8];
+    if (INT8) load_scales8(s2 + size_t(e) * d + col, sc);
+    float* ys = y + int64_t(blockIdx.y) * split_stride;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mb + mt * 16 + 4 * g + v;
+        if (m < n_e) {
+          f32x4_t o0, o1;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            o0[c] = INT8 ? acc[mt][c][v] * sc[c] : acc[mt][c][v];
+            o1[c] = INT8 ? acc[mt][c + 4][v] * sc[c + 4] : acc[mt][c + 4][v];
+          }
+          float* dst = ys + size_t(off + m) * d + col;
+          *reinterpret_cast<f32x4_t*>(dst) = o0;
+          *reinterpret_cast<f32x4_t*>(dst + 4) = o1;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
+                            const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                            int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s) {
+  const dim3 grid((f + 511) / 512, E), block(256);
+  if (int8) {
+    if (mt == 1) up_stream_kernel<true, 1><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
+    else up_stream_kernel<true, 2><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
+  } else {
+    if (mt == 1) up_stream_kernel<false, 1><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
+    else up_stream_kernel<false, 2><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
+                              const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, int mt,
+                              float* y, hipStream_t s) {
+  const dim3 grid((d + 511) / 512, S, E), block(256);
+  const int64_t stride = int64_t(slots) * d;
+  if (int8) {
+    if (mt == 1) down_stream_kernel<true, 1><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
+    else down_stream_kernel<true, 2><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
+  } else {
+    if (mt == 1) down_stream_kernel<false, 1><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
+    else down_stream_kernel<false, 2><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gm

@@ -1,0 +1,65 @@
+// Internal launchers of the gfx950 kernels (host side).  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gm {
+
+// Router: fp64 gate GEMV, softmax over E, top-2 (lower index first on ties).  is_bf16 selects the input type.
+hipError_t launch_router(const void* x, const void* rw, const float* bias, int T, int d, int E, bool is_bf16,
+                         int32_t* idx, float* p, hipStream_t s);
+
+// Histogram + scan + stable permutation of the k = 2 assignments per token (one workgroup).
+hipError_t launch_bin(const int32_t* idx, int T, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
+                      int32_t* inv, hipStream_t s);
+
+// Combine: out[t] = sum_j p[t,j] * sum_s y[s, inv[t,j]].
+hipError_t launch_combine(const float* y, int S, const float* p, const int32_t* inv, int T, int d, float* out,
+                          hipStream_t s);
+
+// Streaming (few tokens per expert) expert kernels: weights go HBM -> registers -> MFMA, no LDS tiling.
+// mt = number of 16-row MFMA tiles held per pass (1 or 2).
+hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
+                            const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                            int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s);
+hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
+                              const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, int mt,
+                              float* y, hipStream_t s);
+
+// LDS-tiled grouped GEMMs (many tokens per expert).  max_mtiles = upper bound of the number of 128-row tiles.
+hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
+                           const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                           int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s);
+hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
+                             const int32_t* offsets, int d, int f, int E, int slots, bool int8, float* y,
+                             hipStream_t s);
+
+// fp32 layer (VALU, LDS tiles).
+hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, const int32_t* counts,
+                         const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, float* h,
+                         hipStream_t s);
+hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* counts, const int32_t* offsets, int d,
+                           int f, int E, int slots, float* y, hipStream_t s);
+
+// Tile scheduling shared by the grouped kernels: the m-th row tile (of height bm) over all experts in
+// ascending expert order.  Returns false if m is past the last tile.  counts has E entries.
+__device__ __forceinline__ bool find_row_tile(const int32_t* counts, const int32_t* offsets, int E, int bm, int m,
+                                              int* e_out, int* row0_out, int* rows_out) {
+  int base = 0;
+  for (int e = 0; e < E; ++e) {
+    const int n = counts[e];
+    const int tiles = (n + bm - 1) / bm;
+    if (m < base + tiles) {
+      const int r = (m - base) * bm;
+      *e_out = e;
+      *row0_out = offsets[e] + r;
+      *rows_out = min(bm, n - r);
+      return true;
+    }
+    base += tiles;
+  }
+  return false;
+}
+
+}  // namespace gm

@@ -130,6 +130,7 @@ class Workload:
     router_bias: tuple | None = None
     sampled_rows: int | None = None  # check the expert path on this many seeded rows (None = all rows)
     seed: int = 0
+    w_std: float = 0.02  # std of bf16 expert weights
     note: str = ""
     tags: dict = field(default_factory=dict)
 
@@ -173,25 +174,25 @@ def make_weights(w: Workload) -> dict:
     d, f, E, dt, seed = w.d, w.f, w.E, w.dtype, w.seed
     out = {}
     if dt == F32:
-        out["router_w"] = normal(f"router_w/{d}", (E, d), 1.0 / math.sqrt(d), F32, seed)
-        out["w1"] = normal(f"w1/{d}x{f}", (E, d, f), 1.0 / math.sqrt(d), F32, seed)
-        out["wv"] = normal(f"wv/{d}x{f}", (E, d, f), 1.0 / math.sqrt(d), F32, seed)
-        out["w2"] = normal(f"w2/{f}x{d}", (E, f, d), 1.0 / math.sqrt(f), F32, seed)
+        out["router_w"] = normal(f"router_w/{d}/E={E}", (E, d), 1.0 / math.sqrt(d), F32, seed)
+        out["w1"] = normal(f"w1/{d}x{f}/E={E}", (E, d, f), 1.0 / math.sqrt(d), F32, seed)
+        out["wv"] = normal(f"wv/{d}x{f}/E={E}", (E, d, f), 1.0 / math.sqrt(d), F32, seed)
+        out["w2"] = normal(f"w2/{f}x{d}/E={E}", (E, f, d), 1.0 / math.sqrt(f), F32, seed)
         out["s1"] = out["sv"] = out["s2"] = None
     elif dt == BF16:
-        out["router_w"] = normal(f"router_w/{d}", (E, d), 1.0 / math.sqrt(d), BF16, seed)
-        out["w1"] = normal(f"w1/{d}x{f}", (E, d, f), 0.02, BF16, seed)
-        out["wv"] = normal(f"wv/{d}x{f}", (E, d, f), 0.02, BF16, seed)
-        out["w2"] = normal(f"w2/{f}x{d}", (E, f, d), 0.02, BF16, seed)
+        out["router_w"] = normal(f"router_w/{d}/E={E}", (E, d), 1.0 / math.sqrt(d), BF16, seed)
+        out["w1"] = normal(f"w1/{d}x{f}/E={E}", (E, d, f), w.w_std, BF16, seed)
+        out["wv"] = normal(f"wv/{d}x{f}/E={E}", (E, d, f), w.w_std, BF16, seed)
+        out["w2"] = normal(f"w2/{f}x{d}/E={E}", (E, f, d), w.w_std, BF16, seed)
         out["s1"] = out["sv"] = out["s2"] = None
     elif dt == W8:
-        out["router_w"] = normal(f"router_w/{d}", (E, d), 1.0 / math.sqrt(d), BF16, seed)
-        out["w1"] = uniform_int8(f"q1/{d}x{f}", (E, d, f), -127, 127, seed)
-        out["wv"] = uniform_int8(f"qv/{d}x{f}", (E, d, f), -127, 127, seed)
-        out["w2"] = uniform_int8(f"q2/{f}x{d}", (E, f, d), -127, 127, seed)
-        out["s1"] = uniform_bf16(f"s1/{f}", (E, 1, f), 1e-4, 5e-4, seed)
-        out["sv"] = uniform_bf16(f"sv/{f}", (E, 1, f), 1e-4, 5e-4, seed)
-        out["s2"] = uniform_bf16(f"s2/{d}", (E, 1, d), 1e-4, 5e-4, seed)
+        out["router_w"] = normal(f"router_w/{d}/E={E}", (E, d), 1.0 / math.sqrt(d), BF16, seed)
+        out["w1"] = uniform_int8(f"q1/{d}x{f}/E={E}", (E, d, f), -127, 127, seed)
+        out["wv"] = uniform_int8(f"qv/{d}x{f}/E={E}", (E, d, f), -127, 127, seed)
+        out["w2"] = uniform_int8(f"q2/{f}x{d}/E={E}", (E, f, d), -127, 127, seed)
+        out["s1"] = uniform_bf16(f"s1/{f}/E={E}", (E, 1, f), 1e-4, 5e-4, seed)
+        out["sv"] = uniform_bf16(f"sv/{f}/E={E}", (E, 1, f), 1e-4, 5e-4, seed)
+        out["s2"] = uniform_bf16(f"s2/{d}/E={E}", (E, 1, d), 1e-4, 5e-4, seed)
     else:
         raise ValueError(f"unknown dtype {dt}")
     return out

@@ -1,0 +1,109 @@
+"""The C ABI library without a GPU: it loads, exports every entry point its header declares, and rejects bad
+arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grok_moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import mixture_experts_transformer_gemv_amd as gm
+    if not os.path.exists(gm.LIB_PATH):
+        from mixture_experts_transformer_gemv_amd import build
+        build.build()
+    return gm.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(grok_moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("grok_moe_forward", "grok_moe_workspace_size", "grok_moe_strerror", "grok_moe_route", "grok_moe_bin",
+              "grok_moe_expert_up", "grok_moe_expert_down", "grok_moe_combine", "grok_moe_down_splits"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_strerror(L):
+    import mixture_experts_transformer_gemv_amd as gm
+    assert gm.strerror(0) == "ok"
+    for s in (-1, -2, -3, -4, 7):
+        assert gm.strerror(s)
+
+
+def test_workspace_size_and_splits(L):
+    import mixture_experts_transformer_gemv_amd as gm
+    assert gm.workspace_size(0, 6144, 32768) == 0
+    assert gm.workspace_size(8, 6144, 32768, 8, 3) == 0  # k != 2
+    assert gm.workspace_size(8, 6100, 32768) == 0        # d not a multiple of 256
+    ws_dec = gm.workspace_size(8, 6144, 32768)
+    assert ws_dec >= 16 * 32768 * 2 + 16 * 6144 * 4 * gm.down_splits(8, 6144, 32768)
+    assert gm.down_splits(8, 6144, 32768) == 16
+    assert gm.down_splits(8192, 6144, 32768) == 1
+    assert gm.down_splits(64, 128, 512, 8, 2, gm.F32) == 1
+    ws_pre = gm.workspace_size(8192, 6144, 32768)
+    assert ws_pre >= 16384 * 32768 * 2 + 16384 * 6144 * 4
+    assert gm.workspace_size(64, 128, 512, 8, 2, gm.F32) >= 128 * 512 * 4 + 128 * 128 * 4
+
+
+def _fwd(L, **kw):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+    a = dict(x=fake, router_w=fake, w1=fake, wv=fake, w2=fake, s1=None, sv=None, s2=None, T=8, d=256, f=512, E=8,
+             k=2, dtype=1, out=fake, bias=None, idx=None, p=None, cnt=None, ws=ctypes.c_void_p(0x200000),
+             ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.grok_moe_forward(a["x"], a["router_w"], a["w1"], a["wv"], a["w2"], a["s1"], a["sv"], a["s2"], a["T"],
+                              a["d"], a["f"], a["E"], a["k"], a["dtype"], a["out"], a["bias"], a["idx"], a["p"],
+                              a["cnt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_forward_rejects_bad_arguments_on_host(L):
+    assert _fwd(L, dtype=5) == -1
+    assert _fwd(L, T=-1) == -1
+    assert _fwd(L, k=3) == -2
+    assert _fwd(L, E=1) == -2
+    assert _fwd(L, E=65) == -2
+    assert _fwd(L, d=300) == -2
+    assert _fwd(L, f=320) == -2                    # bf16 needs multiples of 256
+    assert _fwd(L, x=None) == -1
+    assert _fwd(L, out=ctypes.c_void_p(0x100004)) == -1   # misaligned
+    assert _fwd(L, s1=ctypes.c_void_p(0x100000)) == -1    # scales given for a bf16 layer
+    assert _fwd(L, dtype=2) == -1                           # int8 layer without scales
+    assert _fwd(L, ws=None) == -1
+    assert _fwd(L, ws=ctypes.c_void_p(0x200010)) == -1      # workspace not 256-byte aligned
+    assert _fwd(L, ws_bytes=1024) == -3                     # too small
+    assert _fwd(L, T=0) == 0                                # nothing to do
+    assert _fwd(L, T=0, x=None) == 0
+
+
+def test_step_entry_points_reject_bad_arguments_on_host(L):
+    fake = ctypes.c_void_p(0x100000)
+    assert L.grok_moe_route(None, fake, None, 8, 256, 8, 2, 1, fake, fake, None) == -1
+    assert L.grok_moe_route(fake, fake, None, 8, 256, 8, 3, 1, fake, fake, None) == -2
+    assert L.grok_moe_bin(fake, -1, 8, 2, fake, fake, fake, fake, None) == -1
+    assert L.grok_moe_bin(fake, 8, 99, 2, fake, fake, fake, fake, None) == -2
+    assert L.grok_moe_expert_up(fake, fake, fake, None, None, fake, fake, None, 8, 256, 512, 8, 2, 1, fake, None) == -1
+    S = L.grok_moe_down_splits(8, 256, 512, 8, 2, 1)
+    assert L.grok_moe_expert_down(fake, fake, None, fake, fake, 8, 256, 512, 8, 2, 1, S + 1, fake, None) == -1
+    assert L.grok_moe_combine(fake, 0, fake, fake, 8, 256, 2, fake, None) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import mixture_experts_transformer_gemv_amd as gm
+    monkeypatch.setattr(gm, "_lib", None)
+    monkeypatch.setattr(gm, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(gm.GrokMoeError):
+        gm.lib()

@@ -331,7 +331,7 @@ def test_sampled_rows_equal_full_rows():
     rows = synth.sampled_rows(64, 13)
     part = oracle.forward(inp, F32, rows=rows)
     assert torch.equal(part["idx"], full["idx"])
-    assert torch.allclose(part["out"], full["out"][torch.from_numpy(rows)], rtol=0, atol=0)
+    assert torch.allclose(part["out"], full["out"][torch.from_numpy(rows)], rtol=1e-13, atol=1e-15)
 
 
 def test_worked_example_by_hand():
