@@ -27,13 +27,21 @@ hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t*
                               const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, int mt,
                               float* y, hipStream_t s);
 
-// LDS-tiled grouped GEMMs (many tokens per expert).  max_mtiles = upper bound of the number of 128-row tiles.
+// LDS-tiled grouped GEMMs (many tokens per expert); int8 weights use register-staged tiles, bf16 weights the
+// direct-to-LDS kernels below.
 hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                            const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                            int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s);
 hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
                              const int32_t* offsets, int d, int f, int E, int slots, bool int8, float* y,
                              hipStream_t s);
+
+// The bf16 forms of the tiled kernels: direct global -> LDS copies, LDS transpose reads.
+hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const int32_t* counts,
+                               const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
+                               uint16_t* h, hipStream_t s);
+hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const int32_t* counts, const int32_t* offsets,
+                                 int d, int f, int E, int slots, float* y, hipStream_t s);
 
 // fp32 layer (VALU, LDS tiles).
 hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, const int32_t* counts,

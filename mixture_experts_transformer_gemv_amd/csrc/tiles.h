@@ -1,0 +1,109 @@
+// Tile scheduling and epilogue shared by the two LDS-tiled grouped-GEMM kernels (gfx950).
+//
+// Expert FFN, page "A functional bridge between openai/grok and xai-org/grok-1" (architecture diagram):
+// y = (GELU(x W1) (*) (x Wv)) W2; int8 weights times per-(expert, output channel) bf16 scales, page
+// "Grok-1-BF16", section "Conversion Details".
+//
+// A workgroup of 4 waves computes a 256-row x 256-column output tile of the expert-sorted assignment slots:
+//   * up-projection (NMAT = 2): 128 columns of W1 and the same 128 columns of Wv; h = bf16(GELU(a) * b);
+//   * down-projection (NMAT = 1): 256 columns of W2; fp32 output.
+// Each wave holds a 128 x 128 accumulator tile as 4 x 4 MFMA 32x32 blocks (256 fp32 per lane).
+#pragma once
+
+#include "common.h"
+
+namespace gm {
+namespace tile {
+
+constexpr int BM = 256;   // rows per tile
+constexpr int BNT = 256;  // output columns per tile (all matrices)
+constexpr int NGROUP = 4; // column tiles per group in the tile order
+
+// Map workgroup p to (expert, first row slot, valid rows, column tile); false if p has no tile.
+// Workgroup p runs on XCD p % 8 (round-robin dispatch).  Each XCD gets a contiguous range of tiles, ordered
+// expert -> group of NGROUP column tiles -> row tile -> column tile, so the ~32 tiles resident on one XCD share
+// their A rows (NGROUP ways) and their weight columns (up to 8 ways) in that XCD's L2.
+__device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* offsets, int E, int NT, int p,
+                                         int* e_out, int* row0_out, int* rows_out, int* nt_out) {
+  int total = 0;
+  for (int e = 0; e < E; ++e) total += (counts[e] + BM - 1) / BM;
+  total *= NT;
+  const int chunk = (total + 7) >> 3;
+  const int q = p >> 3;
+  if (q >= chunk) return false;
+  int L = (p & 7) * chunk + q;
+  if (L >= total) return false;
+  for (int e = 0; e < E; ++e) {
+    const int n = counts[e];
+    const int mt = (n + BM - 1) / BM;
+    const int te = mt * NT;
+    if (L < te) {
+      const int ng = L / (mt * NGROUP);
+      const int gsz = min(NGROUP, NT - ng * NGROUP);
+      const int rem = L - ng * mt * NGROUP;
+      const int m = rem / gsz;
+      *nt_out = ng * NGROUP + (rem - m * gsz);
+      *e_out = e;
+      *row0_out = offsets[e] + m * BM;
+      *rows_out = min(BM, n - m * BM);
+      return true;
+    }
+    L -= te;
+  }
+  return false;
+}
+
+// Upper bound of the number of tiles, rounded to a multiple of 8 (the grid); the exact count depends on the
+// per-expert counts, which only the device knows.
+static inline unsigned grid_tiles(int slots, int E, int NT) {
+  const unsigned g = unsigned(slots / BM + E) * unsigned(NT);
+  return (g + 7u) & ~7u;
+}
+
+// Epilogue.  acc[i][j]: wave (wm, wn) rows wm*128 + 32 i .., column sub-tile j (NMAT = 2: j = 0,1 are W1
+// columns wn*64 + 32 j, j = 2,3 the same Wv columns; NMAT = 1: columns wn*128 + 32 j).  Lane holds column
+// (lane & 31) of each sub-tile, rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5) of each 32-row block.
+template <int NMAT, bool INT8>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][4], int wm, int wn, int lane, int e, int row0,
+                                           int rows, int nbase, int N, const uint16_t* sc0, const uint16_t* sc1,
+                                           void* out) {
+  const int lr = lane & 31, rhalf = 4 * (lane >> 5);
+  if (NMAT == 2) {
+    uint16_t* h = static_cast<uint16_t*>(out);
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+      const int n = nbase + wn * 64 + jn * 32 + lr;
+      float s_a = 1.0f, s_b = 1.0f;
+      if (INT8) { s_a = bf16f(sc0[size_t(e) * N + n]); s_b = bf16f(sc1[size_t(e) * N + n]); }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
+          if (r < rows) {
+            const float a = acc[i][jn][v] * s_a, b = acc[i][2 + jn][v] * s_b;
+            h[size_t(row0 + r) * N + n] = uint16_t(f2bf(gelu_erf(a) * b));
+          }
+        }
+      }
+    }
+  } else {
+    float* y = static_cast<float*>(out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = nbase + wn * 128 + j * 32 + lr;
+      const float s = INT8 ? bf16f(sc0[size_t(e) * N + n]) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
+          if (r < rows) y[size_t(row0 + r) * N + n] = INT8 ? acc[i][j][v] * s : acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace tile
+}  // namespace gm
