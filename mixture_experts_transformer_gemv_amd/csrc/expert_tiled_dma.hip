@@ -3,18 +3,21 @@
 // Expert FFN, page "A functional bridge between openai/grok and xai-org/grok-1" (architecture diagram):
 // y = (GELU(x W1) (*) (x Wv)) W2.
 //
-// Tile shape, order and epilogue: tiles.h.  K steps of 32 in a 4-deep LDS ring (4 x 32 KB).  Both operands
-// are copied straight from global memory into LDS with global_load_lds_dwordx4 (no registers, no VALU), 16
-// bytes per lane:
+// Tile shape and order: tiles.h.  K steps of 32 in a 4-deep LDS ring (4 x 32 KB).  Both operands are copied
+// straight from global memory into LDS with global_load_lds_dwordx4 (no registers, no VALU), 16 bytes per lane,
+// addressed as a wave-uniform base plus a per-lane 32-bit offset:
 //   * A tile [256 rows][32 k], 64-byte rows; the 16-byte k chunk c of row r sits in slot c ^ ((r >> 2) & 3);
-//   * B tile [32 k][256 columns], 512-byte rows; the 8-column chunk c of row k sits in slot c ^ (4 (k & 3)).
-// The XOR swizzles are chosen on the global side (which chunk each lane fetches), so that the MFMA operand
-// reads below hit distinct LDS banks.  A fragments are 16-byte reads; the weights are stored [in, out]
-// (columns contiguous), so their MFMA fragments (8 consecutive k of one column per lane) come from two
-// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane
-// 4 r + j / 4 (r = 0..3), i.e. 4 consecutive k of one column when four lanes address four consecutive k rows.
-// One workgroup barrier per K step, placed between the step's two 16-deep halves: the first half of step kt+1
-// is read from LDS while the second half of step kt is multiplied.
+//   * weights as two [32 k][128 column] sub-tiles (up: W1 and Wv; down: two halves of the W2 columns) with
+//     256-byte rows; the 8-column chunk c of row k sits in slot c ^ (4 (k & 3)).
+// The XOR swizzles are chosen on the global side (which chunk each lane fetches) so that the MFMA operand reads
+// hit distinct LDS banks.  A fragments are 16-byte reads; the weights are stored [in, out] (columns contiguous),
+// so their MFMA fragments (8 consecutive k of one column per lane) come from two ds_read_b64_tr_b16: within each
+// 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane 4 r + j / 4 (r = 0..3), i.e. 4
+// consecutive k of one column when four lanes address four consecutive k rows.
+// Schedule: one workgroup barrier per K step, between its two 16-deep halves; every MFMA is followed by at most
+// one LDS fragment read or one copy (pinned with sched_barrier), so the copies of step kt+3 and the fragments of
+// the next half-step are issued in the shadow of the 32-cycle MFMAs.  Up-projection epilogue: the GELU product
+// tile is staged in the idle ring and written as 16-byte row pieces.
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -29,21 +32,21 @@ using tile::BM;
 using tile::BNT;
 constexpr int BK = 32;                  // K per ring stage
 constexpr int NSTAGE = 4;               // ring depth
-constexpr int A_STAGE = BM * BK * 2;    // bytes
-constexpr int B_STAGE = BK * BNT * 2;   // bytes
-constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int A_STAGE = BM * BK * 2;    // bytes: [256 rows][32 k]
+constexpr int B_SUB = BK * 128 * 2;     // bytes: one [32 k][128 columns] weight sub-tile
+constexpr int STAGE = A_STAGE + 2 * B_SUB;
 }
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte global -> LDS copy: lane i of the wave writes LDS bytes [dst + 16 i, dst + 16 i + 16); dst is
-// wave-uniform.  Issued as inline assembly so that the compiler does not wait for every copy in flight before
-// each LDS read (it cannot tell the ring stages apart); completion is awaited explicitly with vmcnt before the
-// workgroup barrier of the stage.  No "memory" clobber: the barrier sequence below orders the LDS accesses.
-__device__ __forceinline__ void g2lds16(const void* src, const lds_u8* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "m0");
+// 16-byte global -> LDS copy of one wave: lane i reads base + voff (bytes; base wave-uniform) and writes LDS
+// bytes [dst + 16 i, dst + 16 i + 16) (dst wave-uniform).  Inline assembly so that the compiler does not wait for
+// every copy in flight before each LDS read (it cannot tell the ring stages apart); completion is awaited with
+// an explicit vmcnt before the stage barrier.  No destination register; no "memory" clobber (the barrier
+// sequence orders the LDS accesses).
+__device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(dst) : "m0");
 }
 
 // LDS transpose read (see the header comment).
@@ -51,11 +54,12 @@ __device__ __forceinline__ u32x2_t lds_tr16(const lds_u8* p) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p)));
 }
 
-// Wait until at most n copies issued by this wave are in flight (n = copies of the later stages).
-__device__ __forceinline__ void wait_copies(int later_stages) {
-  if (later_stages >= 2) asm volatile("s_waitcnt vmcnt(16)");
-  else if (later_stages == 1) asm volatile("s_waitcnt vmcnt(8)");
-  else asm volatile("s_waitcnt vmcnt(0)");
+template <int N> __device__ __forceinline__ void wait_vm() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)");
+  else static_assert(N < 0, "unsupported wait count");
 }
 
 // Workgroup barrier ordering LDS accesses only (a __syncthreads would also wait for all copies in flight).
@@ -81,39 +85,39 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
   lds_u8* lds = (lds_u8*)(smem);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nbase = ntile * BNM;
 
-  // ---- copy sources.  A: wave w copies rows 64 w + 16 i + lane/4 (i = 0..3), LDS slot lane & 3 of the row.
-  const uint16_t* a_src[4];
+  // ---- copies.  A: wave w, piece i copies rows 64 w + 16 i + lane/4; lane's slot (lane & 3) of the 64-byte row
+  // holds k chunk (lane & 3) ^ ((row >> 2) & 3).  Byte offsets from A (32 bits: x and h are < 4 GiB).
+  uint32_t a_voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 64 * wave + 16 * i + (lane >> 2);
     const int rr = min(r, rows - 1);  // rows past the expert's end repeat a valid row; never stored
-    const size_t arow = (NMAT == 2) ? size_t(perm[row0 + rr]) : size_t(row0 + rr);
-    a_src[i] = A + arow * K + 8 * ((lane & 3) ^ ((r >> 2) & 3));
+    const uint32_t arow = (NMAT == 2) ? uint32_t(perm[row0 + rr]) : uint32_t(row0 + rr);
+    a_voff[i] = (arow * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u;
   }
-  // B: wave w copies k rows 8 w + 2 i + lane/32 (i = 0..3), LDS slot lane & 31 of the 512-byte row.
-  const uint16_t* b_src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k = 8 * wave + 2 * i + (lane >> 5);
-    const int c = (lane & 31) ^ (4 * (k & 3));
-    const uint16_t* bm = (NMAT == 2 && c >= 16) ? B1 : B0;
-    const int col = nbase + 8 * ((NMAT == 2) ? (c & 15) : c);
-    b_src[i] = bm + size_t(e) * K * N + size_t(k) * N + col;
-  }
-  auto issue = [&](int stage, int k0) {
-    const lds_u8* as = lds + stage * STAGE;
-    const lds_u8* bs = as + A_STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) g2lds16(a_src[i] + k0, as + (64 * wave + 16 * i) * (BK * 2));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) g2lds16(b_src[i] + size_t(k0) * N, bs + (8 * wave + 2 * i) * (BNT * 2));
+  // B: weight sub-tile sub = wave >> 1 (NMAT = 2: W1 / Wv columns nbase..+127; NMAT = 1: W2 columns
+  // nbase + 128 sub ..+127); piece i copies k rows 16 (wave & 1) + 4 i + lane/16, lane's slot (lane & 15) of the
+  // 256-byte row holds column chunk (lane & 15) ^ (4 (k & 3)).
+  const int sub = wave >> 1;
+  const uint16_t* bmat = (NMAT == 2 && sub == 1) ? B1 : B0;
+  const uint16_t* b_base = bmat + size_t(e) * K * N + size_t(16 * (wave & 1)) * N + nbase + ((NMAT == 1) ? 128 * sub : 0);
+  const uint32_t b_voff = uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
+  const uint32_t a_dst = lds0 + uint32_t(64 * wave) * (BK * 2);
+  const uint32_t b_dst = lds0 + A_STAGE + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * 256;
+  // piece n of the copies of K step kt into ring slot stage (n < 4: A piece n; else B piece n - 4)
+  auto copy_piece = [&](int stage, int kt, int n) {
+    const uint32_t so = uint32_t(stage) * STAGE;
+    if (n < 4) g2lds16(A + size_t(kt) * BK, a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
+    else g2lds16(b_base + size_t(kt) * BK * N + size_t(4 * (n - 4)) * N, b_voff, b_dst + so + uint32_t(4 * (n - 4)) * 256);
   };
 
-  // ---- fragment addresses.  Waves 2 x 2: wave rows wm*128 .. +127, 4 column sub-tiles of 32.
+  // ---- fragments.  Waves 2 x 2: wave rows wm*128 .. +127, 4 column sub-tiles of 32.
   const int wm = wave >> 1, wn = wave & 1;
   int a_off[4][2];  // A row wm*128 + 32 i + (lane & 31), k chunk 2 ks + (lane >> 5)
 #pragma unroll
@@ -123,31 +127,40 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
       const int r = wm * 128 + 32 * i + (lane & 31);
       a_off[i][ks] = r * (BK * 2) + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
     }
-  // B halves h: lane addresses k row 16 ks + 8 g + 4 h + (s >> 2) and columns col .. +3, where G = lane >> 4,
-  // g = G >> 1, s = lane & 15 and col = (sub-tile base) + 16 (G & 1) + 4 (s & 3)
+  // B halves h: lane addresses k row 16 ks + 8 g + 4 h + (s >> 2) and columns col .. +3 of its sub-tile, where
+  // G = lane >> 4, g = G >> 1, s = lane & 15 and col = (sub-tile column base) + 16 (G & 1) + 4 (s & 3)
   int b_off[4][2][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int colbase = (NMAT == 2) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+    const int bsub = (NMAT == 2) ? (j >> 1) : wn;
+    const int lc = (NMAT == 2) ? (wn * 64 + (j & 1) * 32) : (j * 32);
     const int G = lane >> 4, s = lane & 15;
-    const int col = colbase + 16 * (G & 1) + 4 * (s & 3);
+    const int col = lc + 16 * (G & 1) + 4 * (s & 3);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = 16 * ks + 8 * (G >> 1) + 4 * h + (s >> 2);
-        b_off[j][ks][h] = A_STAGE + k * (BNT * 2) + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
+        b_off[j][ks][h] = A_STAGE + bsub * B_SUB + k * 256 + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
       }
   }
-  auto frags = [&](const lds_u8* st, int ks, u32x4_t fa[4], u32x4_t fb[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[i][ks]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x2_t lo = lds_tr16(st + b_off[j][ks][0]);
-      const u32x2_t hi = lds_tr16(st + b_off[j][ks][1]);
-      fb[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  // fragment piece p of half-step ks from ring slot st, in the order the MFMAs consume them:
+  // A0, B0 (two halves), B1, B2, B3, A1, A2, A3
+  u32x4_t fa[2][4], fb[2][4];
+  u32x2_t bh[2][4][2];
+  auto read_piece = [&](int buf, const lds_u8* st, int ks, int p) {
+    if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
+    else if (p <= 8) {
+      const int j = (p - 1) >> 1, h = (p - 1) & 1;
+      bh[buf][j][h] = lds_tr16(st + b_off[j][ks][h]);
+    } else {
+      const int i = p - 8;
+      fa[buf][i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[i][ks]);
     }
+  };
+  auto join_b = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[buf][j] = u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
   };
 
   f32x16_t acc[4][4];
@@ -157,34 +170,75 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  auto mma = [&](const u32x4_t fa[4], const u32x4_t fb[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
-  };
 
-  // ---- main loop.  Copies issued so far are always stages 0 .. min(kt + NSTAGE - 2, KT - 1).
+  // ---- main loop.  Step kt: half-step 0 multiplies fragments buffer 0 while the 12 fragment pieces of
+  // half-step 1 are read; then the wave waits for its copies of step kt+1 and joins the barrier; half-step 1
+  // multiplies buffer 1 while the copies of step kt+3 are issued and half-step 0 of step kt+1 is read.  Each MFMA
+  // is followed by at most one copy or one LDS read, in a fixed order.  Copies past the last step re-read the last
+  // step into a ring slot that is never read again, so every step issues 8 copies and the wait count is constant.
   const int KT = K / BK;
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < KT) issue(s, s * BK);
-  wait_copies(min(KT - 1, NSTAGE - 2));
+#pragma unroll
+    for (int n = 0; n < 8; ++n) copy_piece(s, min(s, KT - 1), n);
+  wait_vm<8 * (NSTAGE - 2)>();  // step 0 landed (steps 1 .. NSTAGE-2 may be in flight)
   lds_barrier();
-  u32x4_t fa0[4], fb0[4], fa1[4], fb1[4];
-  frags(lds, 0, fa0, fb0);
+#pragma unroll
+  for (int p = 0; p < 12; ++p) read_piece(0, lds, 0, p);
+  join_b(0);
   for (int kt = 0; kt < KT; ++kt) {
     const lds_u8* st = lds + (kt % NSTAGE) * STAGE;
-    frags(st, 1, fa1, fb1);
-    mma(fa0, fb0);
-    wait_copies(min(KT - 1, kt + NSTAGE - 2) - (kt + 1));
-    lds_barrier();  // stage kt+1 landed for every wave; every wave finished reading stage kt-1
-    if (kt + NSTAGE - 1 < KT) issue((kt + NSTAGE - 1) % NSTAGE, (kt + NSTAGE - 1) * BK);
-    if (kt + 1 < KT) frags(lds + ((kt + 1) % NSTAGE) * STAGE, 0, fa0, fb0);
-    mma(fa1, fb1);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
+      if (m < 12) read_piece(1, st, 1, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    join_b(1);
+    wait_vm<8 * (NSTAGE - 3)>();  // step kt+1 landed (steps kt+2 .. may be in flight)
+    lds_barrier();                       // ... for every wave; every wave finished reading step kt-1
+    const int cstage = (kt + NSTAGE - 1) % NSTAGE, ck = min(kt + NSTAGE - 1, KT - 1);
+    const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * STAGE;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
+      if (m < 8) copy_piece(cstage, ck, m);
+      if (m < 12) read_piece(0, nst, 0, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    join_b(0);
   }
+  asm volatile("s_waitcnt vmcnt(0)");
 
-  tile::store_tile<NMAT, false>(acc, wm, wn, lane, e, row0, rows, nbase, N, nullptr, nullptr, out);
+  if constexpr (NMAT == 2) {
+    // h tile [256 rows][128 columns] bf16 staged in the (now idle) ring, then written as 16-byte row pieces
+    lds_barrier();
+    __attribute__((address_space(3))) uint16_t* ht = (__attribute__((address_space(3))) uint16_t*)(lds);
+    const int lr = lane & 31, rhalf = 4 * (lane >> 5);
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+      const int c = wn * 64 + jn * 32 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
+          ht[r * 128 + c] = uint16_t(f2bf(gelu_erf(acc[i][jn][v]) * acc[i][2 + jn][v]));
+        }
+    }
+    lds_barrier();
+    uint16_t* h = static_cast<uint16_t*>(out);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int chunk = q * 256 + tid;          // 16-byte chunk: row chunk / 16, columns 8 (chunk % 16) ..
+      const int r = chunk >> 4, c8 = (chunk & 15) * 8;
+      if (r < rows)
+        *reinterpret_cast<u32x4_t*>(h + size_t(row0 + r) * N + nbase + c8) =
+            *(const __attribute__((address_space(3))) u32x4_t*)(ht + r * 128 + c8);
+    }
+  } else {
+    tile::store_tile<NMAT, false>(acc, wm, wn, lane, e, row0, rows, nbase, N, nullptr, nullptr, out);
+  }
 }
 
 hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const int32_t* counts,

@@ -4,9 +4,10 @@
 // logits come from a Dense gate with one output per expert, the gates are the softmax of the logits (no noise
 // at inference), and top_k with k = 2 returns the two largest gates with their indices.
 //
-// One wave64 per token.  Each lane accumulates its strided share of the d products in fp64: a product of two
-// bf16 (or two fp32) values is exact in fp64, so the only rounding is fp64 summation.  A fixed butterfly
-// reduction makes the result deterministic.  Selection uses the fp64 logits (descending, lower expert index on
+// One workgroup of 4 waves per token (enough waves in flight even for a decode step of 8 tokens).  Each lane
+// accumulates its strided share of the d products in fp64: a product of two bf16 (or two fp32) values is exact
+// in fp64, so the only rounding is fp64 summation.  A fixed butterfly reduction inside each wave and a fixed
+// order across the 4 waves make the result deterministic.  Selection uses the fp64 logits (descending, lower expert index on
 // equal logits), which is the same order as the probabilities since softmax is strictly increasing.
 #include "common.h"
 #include "launch.h"
@@ -34,14 +35,17 @@ template <bool BF16, int EMAX>
 __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict__ x, const void* __restrict__ rw,
                                                           const float* __restrict__ bias, int T, int d, int E,
                                                           int32_t* __restrict__ idx, float* __restrict__ p) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave leaves; the kernel has no workgroup barrier
+  // One workgroup (4 waves) per token; wave w accumulates the k in its quarter of d, lane-strided by 8.
+  __shared__ double part[4][EMAX];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
   double acc[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) acc[e] = 0.0;
   const int64_t xrow = int64_t(t) * d;
-  for (int k0 = lane * 8; k0 < d; k0 += 512) {
+  const int q = d >> 2;  // d is a multiple of 64, so each quarter is a multiple of 16
+  const int kend = (wave + 1) * q;
+  for (int k0 = wave * q + lane * 8; k0 < kend; k0 += 512) {
     float xv[8];
     Vec8<BF16>::load(x, xrow + k0, xv);
 #pragma unroll
@@ -59,10 +63,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc[e] += __shfl_xor(acc[e], off, 64);
   }
-  if (lane != 0) return;
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   double l[EMAX];
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e) l[e] = (e < E) ? acc[e] + (bias ? double(bias[e]) : 0.0) : 0.0;
+  for (int e = 0; e < EMAX; ++e)
+    l[e] = (e < E) ? ((part[0][e] + part[1][e]) + (part[2][e] + part[3][e])) + (bias ? double(bias[e]) : 0.0) : 0.0;
   int e1 = 0;
 #pragma unroll
   for (int e = 1; e < EMAX; ++e)
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
 template <bool BF16>
 static hipError_t launch_router_t(const void* x, const void* rw, const float* bias, int T, int d, int E, int32_t* idx,
                                   float* p, hipStream_t s) {
-  const dim3 grid((T + 3) / 4), block(256);
+  const dim3 grid(T), block(256);
   if (E <= 8) router_topk_kernel<BF16, 8><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
   else if (E <= 16) router_topk_kernel<BF16, 16><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
   else if (E <= 32) router_topk_kernel<BF16, 32><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
