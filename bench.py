@@ -29,16 +29,15 @@ sys.path.insert(0, ROOT)
 METRIC = "Grok-1 MoE layer tokens/s (T=8 decode, T=8192 prefill); % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ("expert_stream.hip", "expert_tiled.hip", "common.h")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for n in KERNEL_SOURCES:
+    for n in files:
         with open(os.path.join(ROOT, "mixture_experts_transformer_gemv_amd", "csrc", n), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -156,18 +155,20 @@ def up_flops(w, T):
     return 2.0 * (2 * T) * w.d * w.f * 2
 
 
-def load_traffic(workload: str, kernel: str, launches_bytes: float):
-    """HBM traffic per launch from the committed counter summary, if it was taken on the current kernel source."""
+def load_traffic(workload: str, kernel: str):
+    """HBM-side bytes per launch of a kernel from its committed counter record (profiles/traffic_*.json:
+    FETCH_SIZE and WRITE_SIZE scaled by the same counters on a plain copy of known size), or None if there is no
+    record or the kernel's sources changed since the counters were taken."""
     p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(p):
         return None
     try:
         rec = json.load(open(p))
+        if rec.get("source_hash") != source_hash(rec["source_files"]):
+            return None
+        return rec.get("bytes_per_launch")
     except Exception:
         return None
-    if rec.get("source_hash") != source_hash():
-        return None
-    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(w, inp, oracle, synth):
@@ -230,16 +231,16 @@ def main():
         ach = ub / (kms[0] * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "up_stream_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": load_traffic(w.name, "up", ub), "algorithmic_bytes": ub}
+                           "traffic": load_traffic(w.name, "up"), "algorithmic_bytes": ub}
         db = down_bytes(w, nh, T, layer.S)
         kernels["expert_down_GBps"] = db / (kms[1] * 1e-3) / 1e9
         kernels["layer_GBps"] = (ub + db) / (ms * 1e-3) / 1e9
     else:
         fl = up_flops(w, T)
         ach = fl / (kms[0] * 1e-3) / 1e12
-        res["roofline"] = {"bound": "mfma", "kernel": "tiled_kernel<2>", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+        res["roofline"] = {"bound": "mfma", "kernel": "tiled_dma_kernel<2>" if w.dtype == 1 else "tiled_reg_kernel<2>", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
-                           "traffic": load_traffic(w.name, "up", fl), "algorithmic_flops": fl}
+                           "traffic": load_traffic(w.name, "up"), "algorithmic_flops": fl}
         kernels["layer_TFLOPs"] = 3 * fl / 2 / (ms * 1e-3) / 1e12
     res["kernels"] = kernels
     log(f"{w.name}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down {kms[1]:.3f} ms")
@@ -256,9 +257,10 @@ def main():
         res["prefill"] = {"workload": pw.name, "T": pw.T, "value": pw.T / (pms / 1e3), "unit": "tokens/s",
                           "ms_per_step": pms, "steps": a.prefill_steps,
                           "layer_TFLOPs": 3 * fl / 2 / (pms * 1e-3) / 1e12,
-                          "roofline": {"bound": "mfma", "kernel": "tiled_kernel<2>",
+                          "roofline": {"bound": "mfma", "kernel": "tiled_dma_kernel<2>",
                                        "achieved": fl / (pk[0] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                                       "unit": "TFLOP/s", "frac": fl / (pk[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                                       "unit": "TFLOP/s", "frac": fl / (pk[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                       "traffic": load_traffic(pw.name, "up"), "algorithmic_flops": fl},
                           "kernels": {"expert_up_ms": pk[0], "expert_down_ms": pk[1], "route_bin_ms": pk[2],
                                       "combine_ms": pk[3],
                                       "expert_down_TFLOPs": fl / 2 / (pk[1] * 1e-3) / 1e12}}
