@@ -34,6 +34,8 @@ int check_shape(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
 }
 
 int down_splits(int64_t T, int64_t f, int dtype) {
+  // LDS-tiled bf16 down-projection: K split in two, so that its tiles fill the chip in more, shorter rounds
+  if (dtype == GROK_MOE_BF16 && T > kStreamMaxTokens) return 2;
   if (dtype == GROK_MOE_F32 || T > kStreamMaxTokens) return 1;
   // chunks of at least 2048 rows of W2 (a multiple of 64), at most 16 chunks
   int s = 1;
@@ -99,7 +101,7 @@ hipError_t do_down(const void* h, const void* w2, const void* s2, const int32_t*
     return gm::launch_down_stream(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2), counts,
                                   offsets, int(d), int(f), E, int(p.slots), p.splits, i8, p.mt, y, s);
   return gm::launch_down_tiled(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2), counts,
-                               offsets, int(d), int(f), E, int(p.slots), i8, y, s);
+                               offsets, int(d), int(f), E, int(p.slots), p.splits, i8, y, s);
 }
 
 }  // namespace

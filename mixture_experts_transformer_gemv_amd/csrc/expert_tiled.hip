@@ -177,9 +177,9 @@ hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, co
 }
 
 hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
-                             const int32_t* offsets, int d, int f, int E, int slots, bool int8, float* y,
+                             const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, float* y,
                              hipStream_t s) {
-  if (!int8) return launch_down_tiled_dma(h, w2, counts, offsets, d, f, E, slots, y, s);
+  if (!int8) return launch_down_tiled_dma(h, w2, counts, offsets, d, f, E, slots, S, y, s);
   const dim3 grid(tile::grid_tiles(slots, E, d / BNT)), block(256);
   tiled_reg_kernel<1, true><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, counts, offsets, nullptr, f, d, E, y);
   return hipGetLastError();

@@ -15,8 +15,10 @@
 // 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane 4 r + j / 4 (r = 0..3), i.e. 4
 // consecutive k of one column when four lanes address four consecutive k rows.
 // Schedule: one workgroup barrier per K step, between its two 16-deep halves; every MFMA is followed by at most
-// one LDS fragment read or one copy (pinned with sched_barrier), so the copies of step kt+3 and the fragments of
-// the next half-step are issued in the shadow of the 32-cycle MFMAs.  Up-projection epilogue: the GELU product
+// one LDS fragment read or one copy (pinned with sched_barrier), so the copies (half of step kt+3 after the
+// barrier, the other half in the next half-step) and the fragments of the next half-step are issued in the
+// shadow of the 32-cycle MFMAs.  The down-projection may split K over gridDim.y workgroups (fp32 partial sums,
+// added by the combine) so that its smaller number of tiles still fills the chip.  Up-projection epilogue: the GELU product
 // tile is staged in the idle ring and written as 16-byte row pieces.
 #include "common.h"
 #include "launch.h"
@@ -57,6 +59,7 @@ __device__ __forceinline__ u32x2_t lds_tr16(const lds_u8* p) {
 template <int N> __device__ __forceinline__ void wait_vm() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)");
   else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)");
   else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)");
   else static_assert(N < 0, "unsupported wait count");
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ perm, int K, int N, int E,
-                                                        void* __restrict__ out) {
+                                                        void* __restrict__ out, int64_t split_stride) {
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   int e, row0, rows, ntile;
   if (!tile::map_tile(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole WG
@@ -90,6 +93,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nbase = ntile * BNM;
+  // split blockIdx.y of gridDim.y covers k in [ksplit * Ks, (ksplit + 1) * Ks)
+  const int Ks = K / gridDim.y;
+  const int kbase = blockIdx.y * Ks;
 
   // ---- copies.  A: wave w, piece i copies rows 64 w + 16 i + lane/4; lane's slot (lane & 3) of the 64-byte row
   // holds k chunk (lane & 3) ^ ((row >> 2) & 3).  Byte offsets from A (32 bits: x and h are < 4 GiB).
@@ -113,8 +119,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   // piece n of the copies of K step kt into ring slot stage (n < 4: A piece n; else B piece n - 4)
   auto copy_piece = [&](int stage, int kt, int n) {
     const uint32_t so = uint32_t(stage) * STAGE;
-    if (n < 4) g2lds16(A + size_t(kt) * BK, a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
-    else g2lds16(b_base + size_t(kt) * BK * N + size_t(4 * (n - 4)) * N, b_voff, b_dst + so + uint32_t(4 * (n - 4)) * 256);
+    if (n < 4) g2lds16(A + size_t(kbase + kt * BK), a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
+    else g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - 4)) * N, b_voff, b_dst + so + uint32_t(4 * (n - 4)) * 256);
   };
 
   // ---- fragments.  Waves 2 x 2: wave rows wm*128 .. +127, 4 column sub-tiles of 32.
@@ -176,22 +182,26 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   // multiplies buffer 1 while the copies of step kt+3 are issued and half-step 0 of step kt+1 is read.  Each MFMA
   // is followed by at most one copy or one LDS read, in a fixed order.  Copies past the last step re-read the last
   // step into a ring slot that is never read again, so every step issues 8 copies and the wait count is constant.
-  const int KT = K / BK;
+  const int KT = Ks / BK;
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
 #pragma unroll
-    for (int n = 0; n < 8; ++n) copy_piece(s, min(s, KT - 1), n);
-  wait_vm<8 * (NSTAGE - 2)>();  // step 0 landed (steps 1 .. NSTAGE-2 may be in flight)
+    for (int n = 0; n < 8; ++n)
+      if (s < NSTAGE - 2 || n < 4) copy_piece(s, min(s, KT - 1), n);
+  wait_vm<8 * (NSTAGE - 3) + 4>();  // step 0 landed (step 1 and half of step 2 may be in flight)
   lds_barrier();
 #pragma unroll
   for (int p = 0; p < 12; ++p) read_piece(0, lds, 0, p);
   join_b(0);
   for (int kt = 0; kt < KT; ++kt) {
     const lds_u8* st = lds + (kt % NSTAGE) * STAGE;
+    // second half of the copies of step kt+2 (its first half was issued after the barrier of step kt-1)
+    const int pstage = (kt + NSTAGE - 2) % NSTAGE, pk = min(kt + NSTAGE - 2, KT - 1);
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
       if (m < 12) read_piece(1, st, 1, m);
+      if (m >= 12) copy_piece(pstage, pk, m - 8);
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(1);
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
-      if (m < 8) copy_piece(cstage, ck, m);
+      if (m < 4) copy_piece(cstage, ck, m);
       if (m < 12) read_piece(0, nst, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -237,7 +247,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
             *(const __attribute__((address_space(3))) u32x4_t*)(ht + r * 128 + c8);
     }
   } else {
-    tile::store_tile<NMAT, false>(acc, wm, wn, lane, e, row0, rows, nbase, N, nullptr, nullptr, out);
+    tile::store_tile<NMAT, false>(acc, wm, wn, lane, e, row0, rows, nbase, N, nullptr, nullptr,
+                                  static_cast<float*>(out) + blockIdx.y * split_stride);
   }
 }
 
@@ -246,15 +257,15 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
                                uint16_t* h, hipStream_t s) {
   const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
   tiled_dma_kernel<2><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(wv),
-                                             counts, offsets, perm, d, f, E, h);
+                                             counts, offsets, perm, d, f, E, h, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const int32_t* counts, const int32_t* offsets,
-                                 int d, int f, int E, int slots, float* y, hipStream_t s) {
-  const dim3 grid(tile::grid_tiles(slots, E, d / BNT)), block(256);
+                                 int d, int f, int E, int slots, int S, float* y, hipStream_t s) {
+  const dim3 grid(tile::grid_tiles(slots, E, d / BNT), S), block(256);
   tiled_dma_kernel<1><<<grid, block, 0, s>>>(h, static_cast<const uint16_t*>(w2), nullptr, counts, offsets, nullptr,
-                                             f, d, E, y);
+                                             f, d, E, y, int64_t(slots) * d);
   return hipGetLastError();
 }
 

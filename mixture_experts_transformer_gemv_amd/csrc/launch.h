@@ -33,7 +33,7 @@ hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, co
                            const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                            int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s);
 hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
-                             const int32_t* offsets, int d, int f, int E, int slots, bool int8, float* y,
+                             const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, float* y,
                              hipStream_t s);
 
 // The bf16 forms of the tiled kernels: direct global -> LDS copies, LDS transpose reads.
@@ -41,7 +41,7 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
                                const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
                                uint16_t* h, hipStream_t s);
 hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const int32_t* counts, const int32_t* offsets,
-                                 int d, int f, int E, int slots, float* y, hipStream_t s);
+                                 int d, int f, int E, int slots, int S, float* y, hipStream_t s);
 
 // fp32 layer (VALU, LDS tiles).
 hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, const int32_t* counts,

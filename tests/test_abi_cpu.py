@@ -52,7 +52,8 @@ def test_workspace_size_and_splits(L):
     ws_dec = gm.workspace_size(8, 6144, 32768)
     assert ws_dec >= 16 * 32768 * 2 + 16 * 6144 * 4 * gm.down_splits(8, 6144, 32768)
     assert gm.down_splits(8, 6144, 32768) == 16
-    assert gm.down_splits(8192, 6144, 32768) == 1
+    assert gm.down_splits(8192, 6144, 32768) == 2   # LDS-tiled bf16 path splits K in two
+    assert gm.down_splits(8192, 6144, 32768, 8, 2, gm.W8) == 1
     assert gm.down_splits(64, 128, 512, 8, 2, gm.F32) == 1
     ws_pre = gm.workspace_size(8192, 6144, 32768)
     assert ws_pre >= 16384 * 32768 * 2 + 16384 * 6144 * 4
