@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
   typedef BRow<INT8> W;
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   int e, row0, rows, ntile;
-  if (!tile::map_tile(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole workgroup
+  if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole workgroup
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BNT * LDK];

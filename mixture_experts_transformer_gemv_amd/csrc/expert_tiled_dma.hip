@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
                                                         void* __restrict__ out, int64_t split_stride) {
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   int e, row0, rows, ntile;
-  if (!tile::map_tile(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole WG
+  if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole WG
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
   lds_u8* lds = (lds_u8*)(smem);

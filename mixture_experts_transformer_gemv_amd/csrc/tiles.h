@@ -17,12 +17,16 @@ namespace tile {
 
 constexpr int BM = 256;   // rows per tile
 constexpr int BNT = 256;  // output columns per tile (all matrices)
-constexpr int NGROUP = 4; // column tiles per group in the tile order
+// Column tiles per group in the tile order: the up-projection streams W1|Wv (6.4 GB) while its token rows fit
+// in the 256 MB last-level cache, so it favours weight reuse (4); the down-projection's rows (h, 1.07 GB at
+// T = 8192) do not fit, so it favours row reuse (8).  Measured on MI355X.
+template <int NMAT> struct Group { static constexpr int N = NMAT == 2 ? 4 : 8; };
 
 // Map workgroup p to (expert, first row slot, valid rows, column tile); false if p has no tile.
 // Workgroup p runs on XCD p % 8 (round-robin dispatch).  Each XCD gets a contiguous range of tiles, ordered
 // expert -> group of NGROUP column tiles -> row tile -> column tile, so the ~32 tiles resident on one XCD share
-// their A rows (NGROUP ways) and their weight columns (up to 8 ways) in that XCD's L2.
+// their A rows (NGROUP ways) and their weight columns (32 / NGROUP ways) in that XCD's L2.
+template <int NGROUP>
 __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* offsets, int E, int NT, int p,
                                          int* e_out, int* row0_out, int* rows_out, int* nt_out) {
   int total = 0;
