@@ -14,7 +14,11 @@ Everything is evaluated in float64 on the exact values of the stored inputs, wit
   Section "How MoE Works in Practice": the layer output is the sum, over the selected experts, of each expert's
   output times that expert's router weight.
 * [card] "Grok-1-BF16" (TevunahAi conversion notes), section "Conversion Details": int8 weights times bf16 scales,
-  scales broadcast over the grouped axis, JAX [in, out] layout; section "Verification": tensor shapes.
+  scales broadcast over the grouped axis, JAX [in, out] layout; section "Verification": tensor shapes and the
+  four RMSNorms of a layer (pre_moe_norm and post_moe_norm around moe_block); section "Architecture": "Four norms
+  per layer".
+* [bridge] lists RMSNorm among Grok-1's components; [moe] section "Why JAX Instead of PyTorch" shows the block as
+  x = x + moe(norm(x)).
 
 Readings where the pages leave a step open (each is also listed in the design notes):
   * GELU is the exact erf form (the pages name GELU without saying which).
@@ -26,6 +30,9 @@ Readings where the pages leave a step open (each is also listed in the design no
   * In the bf16 and int8 layers the intermediate h = GELU(a) ⊙ b is rounded once to bf16 (round to nearest
     even, directly from float64) before the down projection; the fp32 layer keeps h unrounded.
   * The optional per-expert router bias is added to the logits before the softmax.
+  * The MoE block: out = x + RMSNorm_post(MoE(RMSNorm_pre(x))), RMSNorm(v) = v / sqrt(mean(v^2) + eps) * scale
+    (pre-norm output rounded once to the layer's activation type, post-norm on the fp32 MoE output); eps is not
+    on the pages and is an argument.
 """
 from __future__ import annotations
 
@@ -37,7 +44,8 @@ import torch
 F32, BF16, W8 = 0, 1, 2
 
 __all__ = [
-    "F32", "BF16", "W8", "as_f64", "bf16_round", "gelu", "route", "expert_ffn", "dequant", "forward",
+    "F32", "BF16", "W8", "as_f64", "bf16_round", "gelu", "route", "expert_ffn", "dequant", "forward", "rmsnorm",
+    "block_forward",
 ]
 
 
@@ -179,3 +187,43 @@ def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False
         res["h"] = hs
         res["y"] = ys_all
     return res
+
+
+def rmsnorm(v: torch.Tensor, scale: torch.Tensor, eps: float) -> torch.Tensor:
+    """RMSNorm over the last axis: v / sqrt(mean(v^2) + eps) * scale, in float64."""
+    return v / torch.sqrt((v * v).mean(dim=-1, keepdim=True) + eps) * scale
+
+
+def block_forward(inp: dict, dtype: int, pre_scale, post_scale, eps: float, rows=None, k: int = 2) -> dict:
+    """The MoE part of a Grok-1 layer with its two norms and the residual:
+    out = x + RMSNorm_post(MoE(RMSNorm_pre(x))).
+
+    pre_scale, post_scale: [d] arrays in the activation type (float32 for the fp32 layer, bf16 bits otherwise).
+    The pre-norm output is what the router and the experts see, stored in the activation type: rounded once to
+    bf16 (nearest even, from float64) in the bf16 and int8 layers, rounded to float32 in the fp32 layer.
+    Returns the forward() dict of the MoE on the normed input, with 'out' replaced by the block output and the
+    normed input under 'xn' (float64)."""
+    akind = "f32" if dtype == F32 else "bf16"
+    x = as_f64(inp["x"], akind)
+    g_pre = as_f64(np.asarray(pre_scale), akind)
+    g_post = as_f64(np.asarray(post_scale), akind)
+    xn = rmsnorm(x, g_pre, eps)
+    if dtype == F32:
+        xn_stored = xn.to(torch.float32).numpy()  # the fp32 layer stores its activations in float32
+    else:
+        xn_stored = _to_bf16_bits(bf16_round(xn))
+    inner = dict(inp)
+    inner["x"] = xn_stored
+    r = forward(inner, dtype, rows=rows, k=k)
+    rows_t = r["rows"]
+    moe = r["out"]
+    r["moe_out"] = moe
+    r["out"] = x[rows_t] + rmsnorm(moe, g_post, eps)
+    r["xn"] = as_f64(xn_stored, akind)
+    return r
+
+
+def _to_bf16_bits(v: torch.Tensor) -> np.ndarray:
+    """float64 values already on the bf16 grid -> their bf16 bit patterns (exact)."""
+    f32 = v.to(torch.float32).numpy()  # exact: bf16 values are float32 values
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)

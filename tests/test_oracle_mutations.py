@@ -108,3 +108,38 @@ def test_dropped_combine_term_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "forward", one_term)
     with pytest.raises(AssertionError):
         pins.test_identical_experts_scale_by_gate_sum()
+
+
+from tests import test_oracle_block_pins as bpins
+
+
+@pytest.mark.parametrize("bad", [
+    lambda v, g, eps: v / ((v * v).mean(dim=-1, keepdim=True) + eps) * g,            # no square root
+    lambda v, g, eps: v / (torch.sqrt((v * v).mean(dim=-1, keepdim=True)) + eps) * g,  # eps outside the root
+    lambda v, g, eps: v / torch.sqrt((v * v).sum(dim=-1, keepdim=True) + eps) * g,     # sum instead of mean
+])
+def test_rmsnorm_mistakes_are_caught(bad, monkeypatch):
+    monkeypatch.setattr(om, "rmsnorm", bad)
+    monkeypatch.setattr(oracle, "rmsnorm", bad)
+    caught = 0
+    for t in (bpins.test_rmsnorm_3_4_5_triangle, bpins.test_rmsnorm_eps_closed_form_and_zero_row,
+              bpins.test_block_against_numpy):
+        try:
+            t()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1
+
+
+def test_dropped_residual_is_caught(monkeypatch):
+    orig = om.block_forward
+
+    def no_residual(inp, dtype, pre, post, eps, rows=None, k=2):
+        r = orig(inp, dtype, pre, post, eps, rows, k)
+        r["out"] = r["out"] - om.as_f64(inp["x"], "f32" if dtype == om.F32 else "bf16")[r["rows"]]
+        return r
+
+    monkeypatch.setattr(om, "block_forward", no_residual)
+    monkeypatch.setattr(oracle, "block_forward", no_residual)
+    with pytest.raises(AssertionError):
+        bpins.test_block_against_numpy()
