@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the companion T=8192 prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--block", action="store_true",
+                    help="time the MoE block (pre-MoE RMSNorm, MoE, post-MoE RMSNorm, residual) instead of the layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -60,9 +62,10 @@ def parse():
 class Layer:
     """Device-resident inputs and preallocated buffers of one workload, and the timed step."""
 
-    def __init__(self, gm, w, inp, dv):
+    def __init__(self, gm, w, inp, dv, norms=None):
         import torch
         self.gm, self.w, self.inp, self.dv = gm, w, inp, dv
+        self.norms = norms  # (pre_scale, post_scale, eps) device tensors for the block form
         T, d, f, E = w.T, w.d, w.f, w.E
         dev = dv["x"].device
         self.S = gm.down_splits(T, d, f, E, 2, w.dtype)
@@ -76,6 +79,7 @@ class Layer:
         self.h = torch.empty((2 * T, f), dtype=torch.float32 if w.dtype == gm.F32 else torch.bfloat16, device=dev)
         self.y = torch.empty((self.S, 2 * T, d), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.xn = torch.empty_like(dv["x"]) if norms is not None else None
         self.s1 = self.sv = self.s2 = None
         if dv["scales"] is not None:
             self.s1, self.sv, self.s2 = dv["scales"]
@@ -92,12 +96,18 @@ class Layer:
         ev = self.ev
         if timed:
             ev[0].record()
-        st = L.grok_moe_route(P(dv["x"]), P(dv["router_w"]), P(dv["router_bias"]), T, d, E, 2, dt, P(self.idx),
-                              P(self.p), s)
+        if self.norms is None:
+            xa = dv["x"]
+            st = L.grok_moe_route(P(dv["x"]), P(dv["router_w"]), P(dv["router_bias"]), T, d, E, 2, dt, P(self.idx),
+                                  P(self.p), s)
+        else:
+            xa = self.xn
+            st = L.grok_moe_route_norm(P(dv["x"]), P(self.norms[0]), self.norms[2], P(dv["router_w"]),
+                                       P(dv["router_bias"]), T, d, E, 2, dt, P(self.xn), P(self.idx), P(self.p), s)
         st |= L.grok_moe_bin(P(self.idx), T, E, 2, P(self.counts), P(self.offsets), P(self.perm), P(self.inv), s)
         if timed:
             ev[1].record()
-        st |= L.grok_moe_expert_up(P(dv["x"]), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), P(self.counts),
+        st |= L.grok_moe_expert_up(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), P(self.counts),
                                    P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
         if timed:
             ev[2].record()
@@ -105,7 +115,11 @@ class Layer:
                                      E, 2, dt, self.S, P(self.y), s)
         if timed:
             ev[3].record()
-        st |= L.grok_moe_combine(P(self.y), self.S, P(self.p), P(self.inv), T, d, 2, P(self.out), s)
+        if self.norms is None:
+            st |= L.grok_moe_combine(P(self.y), self.S, P(self.p), P(self.inv), T, d, 2, P(self.out), s)
+        else:
+            st |= L.grok_moe_combine_norm(P(self.y), self.S, P(self.p), P(self.inv), P(dv["x"]), P(self.norms[1]),
+                                          self.norms[2], T, d, 2, dt, P(self.out), s)
         if timed:
             ev[4].record()
         if st != 0:
@@ -171,13 +185,17 @@ def load_traffic(workload: str, kernel: str):
         return None
 
 
-def cpu_baseline(w, inp, oracle, synth):
+def cpu_baseline(w, inp, oracle, synth, block=False):
     """The oracle as it stands, on a bounded sample of the workload (routing for all tokens, expert path on a few
     rows), timed on this host's cores."""
     import torch
     rows = synth.sampled_rows(w.T, 2 if w.T <= 64 else 4)
     t0 = time.perf_counter()
-    oracle.forward(inp, w.dtype, rows=rows)
+    if block:
+        ns = synth.make_norm_scales(w)
+        oracle.block_forward(inp, w.dtype, ns["pre_scale"], ns["post_scale"], ns["eps"], rows=rows)
+    else:
+        oracle.forward(inp, w.dtype, rows=rows)
     dt = time.perf_counter() - t0
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": f"{len(rows)} of {w.T} token rows of {w.name} through the float64 oracle (routing on all "
@@ -215,7 +233,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    layer = Layer(gm, w, inp, dv)
+    norms = None
+    if a.block:
+        ns = synth.make_norm_scales(w)
+        if w.dtype == synth.F32:
+            conv = lambda v: torch.from_numpy(v).cuda()
+        else:
+            conv = lambda v: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
+        norms = (conv(ns["pre_scale"]), conv(ns["post_scale"]), ns["eps"])
+    layer = Layer(gm, w, inp, dv, norms)
     wall, kms = layer.run_with_kernel_times(a.steps, a.warmup)
     ms = wall * 1e3 / a.steps
     nh = n_hit(layer)
@@ -223,8 +249,9 @@ def main():
     res = {"metric": METRIC, "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": {0: "f32", 1: "bf16", 2: "bf16 x int8-weight"}[w.dtype], "data": "synthetic",
-           "config": {"workload": w.name, "T": T, "d_model": w.d, "d_ff": w.f, "experts": w.E, "top_k": 2,
-                      "experts_hit": nh, "down_splits": layer.S}}
+           "config": {"workload": w.name + ("_block" if a.block else ""), "T": T, "d_model": w.d, "d_ff": w.f,
+                      "experts": w.E, "top_k": 2, "experts_hit": nh, "down_splits": layer.S,
+                      "rmsnorm_residual": bool(a.block)}}
     kernels = {"expert_up_ms": kms[0], "expert_down_ms": kms[1], "route_bin_ms": kms[2], "combine_ms": kms[3]}
     if w.T <= 64:  # weight-streaming regime: HBM-bound, the up-projection (W1 and Wv) is the dominant kernel
         ub = up_bytes(w, nh, T)
@@ -245,7 +272,7 @@ def main():
     res["kernels"] = kernels
     log(f"{w.name}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down {kms[1]:.3f} ms")
 
-    if not a.no_prefill and w.name == "decode_bf16":
+    if not a.no_prefill and w.name == "decode_bf16" and not a.block:
         pw = synth.WORKLOADS["prefill_bf16"]
         pinp = synth.make_inputs(pw, weights=wts)
         pdv = dict(dv)
@@ -271,7 +298,7 @@ def main():
     if not a.no_cpu_baseline:
         import oracle
         log("timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(w, inp, oracle, synth)
+        res["cpu_baseline"] = cpu_baseline(w, inp, oracle, synth, a.block)
     print(json.dumps(res), flush=True)
 
 

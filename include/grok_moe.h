@@ -122,6 +122,38 @@ int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const in
 int grok_moe_combine(const float* y, int splits, const float* topk_p, const int32_t* inv, int64_t T, int64_t d,
                      int k, float* out, void* stream);
 
+/* ---- The MoE part of a Grok-1 layer with its two norms and the residual ------------------------------------
+ * Page "Grok-1-BF16", section "Architecture" (four norms per layer: pre-attention, post-attention, pre-MoE,
+ * post-MoE) and section "Verification" (pre_moe_norm.scale and post_moe_norm.scale of shape [6144] around
+ * moe_block); page "... (MoE Explained)", section "Why JAX Instead of PyTorch" (x = x + moe(norm(x))):
+ *   xn  = RMSNorm(x; pre_scale),  out = x + RMSNorm(MoE(xn); post_scale),
+ *   RMSNorm(v; g) = v / sqrt(mean(v^2) + eps) * g over the d axis.
+ * eps is not on the pages (any eps >= 0).  pre_scale, post_scale [d] are in the activation type (f32 for
+ * GROK_MOE_F32, bf16 otherwise).  xn is stored once rounded to the activation type (bf16 round-to-nearest-even
+ * from a float64 evaluation) and is what the router and the experts see; the post-norm and the residual add are
+ * evaluated in float64 and written as fp32. */
+
+/* Workspace of grok_moe_block_forward (the layer's workspace plus xn). */
+size_t grok_moe_block_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
+
+/* The block: same arguments and conventions as grok_moe_forward plus pre_scale, post_scale and eps; out [T,d]
+ * fp32 = x + RMSNorm(MoE(RMSNorm(x; pre_scale)); post_scale).  Routing outputs refer to the normed input. */
+int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,
+                           const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
+                           const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                           float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                           int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step: pre-MoE RMSNorm fused with the router.  Writes xn [T,d] (activation type), topk_idx, topk_p. */
+int grok_moe_route_norm(const void* x, const void* pre_scale, double eps, const void* router_w,
+                        const float* router_bias, int64_t T, int64_t d, int E, int k, int dtype, void* xn,
+                        int32_t* topk_idx, float* topk_p, void* stream);
+
+/* Step: combine fused with the post-MoE RMSNorm and the residual add (x is the block input [T,d]). */
+int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const int32_t* inv, const void* x,
+                          const void* post_scale, double eps, int64_t T, int64_t d, int k, int dtype, float* out,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "F32", "BF16", "W8", "LIB_PATH", "lib", "forward", "route", "bin_tokens", "expert_up", "expert_down",
-    "combine", "workspace_size", "down_splits", "strerror", "dtype_of", "GrokMoeError",
+    "combine", "workspace_size", "down_splits", "strerror", "dtype_of", "GrokMoeError", "block_forward",
+    "block_workspace_size", "route_norm", "combine_norm",
 ]
 
 F32, BF16, W8 = 0, 1, 2
@@ -36,6 +37,14 @@ _SIGS = {
     "grok_moe_expert_down": (_int, [_c_void_p] * 5 + [_i64, _i64, _i64, _int, _int, _int, _int]
                              + [_c_void_p] * 2),
     "grok_moe_combine": (_int, [_c_void_p, _int, _c_void_p, _c_void_p, _i64, _i64, _int, _c_void_p, _c_void_p]),
+    "grok_moe_block_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _int, _int, _int]),
+    "grok_moe_block_forward": (_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_double] + [_c_void_p] * 7
+                               + [_i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 6
+                               + [ctypes.c_size_t, _c_void_p]),
+    "grok_moe_route_norm": (_int, [_c_void_p, _c_void_p, ctypes.c_double, _c_void_p, _c_void_p, _i64, _i64, _int,
+                                   _int, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "grok_moe_combine_norm": (_int, [_c_void_p, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, ctypes.c_double,
+                                     _i64, _i64, _int, _int, _c_void_p, _c_void_p]),
 }
 
 _lib = None
@@ -212,4 +221,64 @@ def combine(y, topk_p, inv, out=None):
     if out is None:
         out = torch.empty((T, d), dtype=torch.float32, device=y.device)
     _check(lib().grok_moe_combine(_p(y), S, _p(topk_p), _p(inv), T, d, 2, _p(out), _stream()), "grok_moe_combine")
+    return out
+
+
+def block_workspace_size(T: int, d: int, f: int, E: int = 8, k: int = 2, dtype: int = BF16) -> int:
+    return int(lib().grok_moe_block_workspace_size(T, d, f, E, k, dtype))
+
+
+def block_forward(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, scales=None, router_bias=None,
+                  return_routing=False, workspace=None):
+    """The MoE part of a Grok-1 layer with its norms and residual: out = x + RMSNorm(MoE(RMSNorm(x; pre_scale));
+    post_scale), fp32 [T, d].  pre_scale, post_scale: [d] in the activation type of x."""
+    T, d, f, E = _layer_shapes(x, router_w, w1, wv, w2)
+    dt = dtype_of(x, w1)
+    for t, n in ((x, "x"), (router_w, "router_w"), (w1, "w1"), (wv, "wv"), (w2, "w2")):
+        _need(t, n)
+    _need(pre_scale, "pre_scale", x.dtype, (d,))
+    _need(post_scale, "post_scale", x.dtype, (d,))
+    s1 = sv = s2 = None
+    if dt == W8:
+        s1, sv, s2 = scales
+    dev = x.device
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, 2), dtype=torch.int32, device=dev) if return_routing else None
+    pr = torch.empty((T, 2), dtype=torch.float32, device=dev) if return_routing else None
+    cnt = torch.empty((E,), dtype=torch.int32, device=dev) if return_routing else None
+    need = block_workspace_size(T, d, f, E, 2, dt)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    st = lib().grok_moe_block_forward(_p(x), _p(pre_scale), _p(post_scale), float(eps), _p(router_w), _p(w1),
+                                      _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), T, d, f, E, 2, dt, _p(out),
+                                      _p(router_bias), _p(idx), _p(pr), _p(cnt), _p(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "grok_moe_block_forward")
+    if return_routing:
+        return out, idx, pr, cnt
+    return out
+
+
+def route_norm(x, pre_scale, eps, router_w, router_bias=None):
+    """Pre-MoE RMSNorm fused with the router step: (xn [T,d], topk_idx [T,2], topk_p [T,2])."""
+    T, d = x.shape
+    E = router_w.shape[0]
+    dt = F32 if x.dtype == torch.float32 else BF16
+    xn = torch.empty_like(x)
+    idx = torch.empty((T, 2), dtype=torch.int32, device=x.device)
+    pr = torch.empty((T, 2), dtype=torch.float32, device=x.device)
+    _check(lib().grok_moe_route_norm(_p(x), _p(pre_scale), float(eps), _p(router_w), _p(router_bias), T, d, E, 2,
+                                     dt, _p(xn), _p(idx), _p(pr), _stream()), "grok_moe_route_norm")
+    return xn, idx, pr
+
+
+def combine_norm(y, topk_p, inv, x, post_scale, eps, out=None):
+    """Combine fused with the post-MoE RMSNorm and the residual add: out [T, d] fp32."""
+    S, slots, d = y.shape
+    T = topk_p.shape[0]
+    dt = F32 if x.dtype == torch.float32 else BF16
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=y.device)
+    _check(lib().grok_moe_combine_norm(_p(y), S, _p(topk_p), _p(inv), _p(x), _p(post_scale), float(eps), T, d, 2, dt,
+                                       _p(out), _stream()), "grok_moe_combine_norm")
     return out

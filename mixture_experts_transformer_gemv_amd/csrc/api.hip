@@ -19,6 +19,7 @@ struct Plan {
   int mt;       // 16-row MFMA tiles per pass of the streaming kernels
   int splits;   // partial sums of the down-projection
   size_t o_idx, o_p, o_counts, o_offsets, o_perm, o_inv, o_h, o_y, total;
+  size_t o_xn, total_block;  // the block form adds the normed input [T, d]
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -59,6 +60,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
   p.o_h = o; o = align256(o + size_t(p.slots) * f * (dtype == GROK_MOE_F32 ? 4 : 2));
   p.o_y = o; o = align256(o + size_t(p.splits) * p.slots * d * 4);
   p.total = o;
+  p.o_xn = o; o = align256(o + size_t(T) * d * (dtype == GROK_MOE_F32 ? 4 : 2));
+  p.total_block = o;
   return p;
 }
 
@@ -219,6 +222,82 @@ int grok_moe_combine(const float* y, int splits, const float* topk_p, const int3
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(y) || !ok_ptr(topk_p) || !ok_ptr(inv) || !ok_ptr(out)) return GROK_MOE_EINVAL;
   return hip_status(gm::launch_combine(y, splits, topk_p, inv, int(T), int(d), out, static_cast<hipStream_t>(stream)));
+}
+
+size_t grok_moe_block_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
+  if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK || T == 0) return 0;
+  return make_plan(T, d, f, E, dtype).total_block;
+}
+
+int grok_moe_route_norm(const void* x, const void* pre_scale, double eps, const void* router_w,
+                        const float* router_bias, int64_t T, int64_t d, int E, int k, int dtype, void* xn,
+                        int32_t* topk_idx, float* topk_p, void* stream) {
+  int st = check_shape(T, d, dtype == GROK_MOE_F32 ? 64 : 256, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  if (!(eps >= 0.0)) return GROK_MOE_EINVAL;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(pre_scale) || !ok_ptr(router_w) || !ok_ptr(xn) || !ok_ptr(topk_idx) || !ok_ptr(topk_p) ||
+      !ok_opt(router_bias))
+    return GROK_MOE_EINVAL;
+  return hip_status(gm::launch_router_norm(x, pre_scale, eps, router_w, router_bias, int(T), int(d), E,
+                                           dtype != GROK_MOE_F32, xn, topk_idx, topk_p,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const int32_t* inv, const void* x,
+                          const void* post_scale, double eps, int64_t T, int64_t d, int k, int dtype, float* out,
+                          void* stream) {
+  if (T < 0 || d <= 0 || splits < 1 || splits > 64 || !(eps >= 0.0)) return GROK_MOE_EINVAL;
+  if (dtype != GROK_MOE_F32 && dtype != GROK_MOE_BF16 && dtype != GROK_MOE_W8) return GROK_MOE_EINVAL;
+  if (k != 2 || T > kMaxTokens || d % 4 != 0) return GROK_MOE_EUNSUPPORTED;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(y) || !ok_ptr(topk_p) || !ok_ptr(inv) || !ok_ptr(x) || !ok_ptr(post_scale) || !ok_ptr(out))
+    return GROK_MOE_EINVAL;
+  return hip_status(gm::launch_combine_norm(y, splits, topk_p, inv, int(T), int(d), x, dtype != GROK_MOE_F32,
+                                            post_scale, eps, out, static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,
+                           const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
+                           const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                           float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                           int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(T, d, f, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  if (!(eps >= 0.0)) return GROK_MOE_EINVAL;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(pre_scale) || !ok_ptr(post_scale) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) ||
+      !ok_ptr(w2) || !ok_ptr(out))
+    return GROK_MOE_EINVAL;
+  if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
+  if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
+  const Plan p = make_plan(T, d, f, E, dtype);
+  if (workspace_bytes < p.total_block) return GROK_MOE_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + p.o_idx);
+  float* pr = topk_p ? topk_p : reinterpret_cast<float*>(ws + p.o_p);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.o_counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + p.o_offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + p.o_perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + p.o_inv);
+  void* h = ws + p.o_h;
+  float* y = reinterpret_cast<float*>(ws + p.o_y);
+  void* xn = ws + p.o_xn;
+
+  hipError_t e = gm::launch_router_norm(x, pre_scale, eps, router_w, router_bias, int(T), int(d), E,
+                                        dtype != GROK_MOE_F32, xn, idx, pr, s);
+  if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
+  if (e == hipSuccess) e = do_up(xn, w1, wv, s1, sv, counts, offsets, perm, p, d, f, E, dtype, h, s);
+  if (e == hipSuccess) e = do_down(h, w2, s2, counts, offsets, p, d, f, E, dtype, y, s);
+  if (e == hipSuccess)
+    e = gm::launch_combine_norm(y, p.splits, pr, inv, int(T), int(d), x, dtype != GROK_MOE_F32, post_scale, eps, out,
+                                s);
+  if (e == hipSuccess && expert_counts)
+    e = hipMemcpyAsync(expert_counts, counts, size_t(E) * 4, hipMemcpyDeviceToDevice, s);
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -42,4 +42,70 @@ hipError_t launch_combine(const float* y, int S, const float* p, const int32_t* 
   return hipGetLastError();
 }
 
+// Combine followed by the post-MoE RMSNorm and the residual add of the layer ("Grok-1-BF16", section
+// "Architecture": a norm after the MoE block; "... (MoE Explained)", section "Why JAX Instead of PyTorch": the
+// block output is x plus the MoE branch): out[t] = x[t] + (o / sqrt(mean(o^2) + eps)) * g with o the combined
+// MoE output.  One workgroup per token: pass 1 forms o (written to out) and the fp64 sum of squares (fixed
+// order); pass 2 rewrites each thread's own elements.
+__global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restrict__ y, int S, int64_t split_stride,
+                                                           const float* __restrict__ p,
+                                                           const int32_t* __restrict__ inv, int d,
+                                                           const void* __restrict__ xres, bool bf16,
+                                                           const void* __restrict__ g, double eps,
+                                                           float* __restrict__ out) {
+  __shared__ double ssq[4];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float p0 = p[2 * t], p1 = p[2 * t + 1];
+  const float* y0 = y + int64_t(inv[2 * t]) * d;
+  const float* y1 = y + int64_t(inv[2 * t + 1]) * d;
+  float* orow = out + int64_t(t) * d;
+  double ss = 0.0;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    f32x4_t a = *reinterpret_cast<const f32x4_t*>(y0 + c);
+    f32x4_t b = *reinterpret_cast<const f32x4_t*>(y1 + c);
+    for (int s = 1; s < S; ++s) {
+      a += *reinterpret_cast<const f32x4_t*>(y0 + s * split_stride + c);
+      b += *reinterpret_cast<const f32x4_t*>(y1 + s * split_stride + c);
+    }
+    f32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = __fmaf_rn(p1, b[i], p0 * a[i]);
+      ss = __fma_rn(double(o[i]), double(o[i]), ss);
+    }
+    *reinterpret_cast<f32x4_t*>(orow + c) = o;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) ssq[wave] = ss;
+  __syncthreads();
+  const double rms = sqrt(((ssq[0] + ssq[1]) + (ssq[2] + ssq[3])) / double(d) + eps);
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const f32x4_t o = *reinterpret_cast<const f32x4_t*>(orow + c);
+    float xv[4], gv[4];
+    if (bf16) {
+      const u32x2_t xw = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(xres) + int64_t(t) * d + c);
+      const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(g) + c);
+      xv[0] = bf16lo(xw[0]); xv[1] = bf16hi(xw[0]); xv[2] = bf16lo(xw[1]); xv[3] = bf16hi(xw[1]);
+      gv[0] = bf16lo(gw[0]); gv[1] = bf16hi(gw[0]); gv[2] = bf16lo(gw[1]); gv[3] = bf16hi(gw[1]);
+    } else {
+      const f32x4_t xw = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(xres) + int64_t(t) * d + c);
+      const f32x4_t gw = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(g) + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { xv[i] = xw[i]; gv[i] = gw[i]; }
+    }
+    f32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = float(double(xv[i]) + (double(o[i]) / rms) * double(gv[i]));
+    *reinterpret_cast<f32x4_t*>(orow + c) = r;
+  }
+}
+
+hipError_t launch_combine_norm(const float* y, int S, const float* p, const int32_t* inv, int T, int d,
+                               const void* xres, bool bf16, const void* g, double eps, float* out, hipStream_t s) {
+  const int64_t split_stride = int64_t(2) * T * d;
+  combine_norm_kernel<<<T, 256, 0, s>>>(y, S, split_stride, p, inv, d, xres, bf16, g, eps, out);
+  return hipGetLastError();
+}
+
 }  // namespace gm

@@ -10,6 +10,14 @@ namespace gm {
 hipError_t launch_router(const void* x, const void* rw, const float* bias, int T, int d, int E, bool is_bf16,
                          int32_t* idx, float* p, hipStream_t s);
 
+// Router with the pre-MoE RMSNorm in front: writes xn [T,d] (activation type) and routes on it.
+hipError_t launch_router_norm(const void* x, const void* g, double eps, const void* rw, const float* bias, int T,
+                              int d, int E, bool is_bf16, void* xn, int32_t* idx, float* p, hipStream_t s);
+
+// Combine, then the post-MoE RMSNorm and the residual add: out = x + RMSNorm(combined, g, eps).
+hipError_t launch_combine_norm(const float* y, int S, const float* p, const int32_t* inv, int T, int d,
+                               const void* xres, bool bf16, const void* g, double eps, float* out, hipStream_t s);
+
 // Histogram + scan + stable permutation of the k = 2 assignments per token (one workgroup).
 hipError_t launch_bin(const int32_t* idx, int T, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                       int32_t* inv, hipStream_t s);

@@ -31,6 +31,36 @@ template <> struct Vec8<false> {
   }
 };
 
+// Selection from the per-wave partial logits: softmax over all E (fp64), the two largest logits with the lower
+// expert index first on equal logits.
+template <int EMAX>
+__device__ __forceinline__ void select_top2(const double (&part)[4][EMAX], const float* bias, int E, int t,
+                                            int32_t* idx, float* p) {
+  double l[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    l[e] = (e < E) ? ((part[0][e] + part[1][e]) + (part[2][e] + part[3][e])) + (bias ? double(bias[e]) : 0.0) : 0.0;
+  int e1 = 0;
+#pragma unroll
+  for (int e = 1; e < EMAX; ++e)
+    if (e < E && l[e] > l[e1]) e1 = e;
+  int e2 = -1;
+  double l2 = 0.0, l1 = l[0];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < E && e != e1 && (e2 < 0 || l[e] > l2)) { e2 = e; l2 = l[e]; }
+    if (e == e1) l1 = l[e];
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < E) s += exp(l[e] - l1);
+  idx[2 * t] = e1;
+  idx[2 * t + 1] = e2;
+  p[2 * t] = float(1.0 / s);
+  p[2 * t + 1] = float(exp(l2 - l1) / s);
+}
+
 template <bool BF16, int EMAX>
 __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict__ x, const void* __restrict__ rw,
                                                           const float* __restrict__ bias, int T, int d, int E,
@@ -68,30 +98,101 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
     for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  double l[EMAX];
+  if (threadIdx.x == 0) select_top2<EMAX>(part, bias, E, t, idx, p);
+}
+
+// float64 -> bf16 bit pattern with a single round-to-nearest-even step (bf16 keeps 8 significant bits, so 45
+// of the 53 are dropped).  Finite values inside the float range.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  u += 0xFFFFFFFFFFFull + ((u >> 45) & 1ull);  // half of 2^45, minus one, plus the kept LSB
+  u &= ~((1ull << 45) - 1ull);
+  return static_cast<uint16_t>(__float_as_uint(static_cast<float>(__longlong_as_double(static_cast<long long>(u)))) >> 16);
+}
+
+// Router with the pre-MoE RMSNorm in front ("Grok-1-BF16", section "Architecture": four norms per layer, one
+// before the MoE block): xn = x / sqrt(mean(x^2) + eps) * g in float64, stored once rounded to the activation
+// type (bf16 round-to-nearest-even, or float32), and the router runs on the stored xn.  One workgroup per token:
+// all 256 threads first reduce the sum of squares (fixed order), then each wave normalises its quarter of d,
+// writes it, and accumulates the gate products exactly as router_topk_kernel.
+template <bool BF16, int EMAX>
+__global__ __launch_bounds__(256) void router_norm_kernel(const void* __restrict__ x, const void* __restrict__ g,
+                                                          double eps, const void* __restrict__ rw,
+                                                          const float* __restrict__ bias, int T, int d, int E,
+                                                          void* __restrict__ xn, int32_t* __restrict__ idx,
+                                                          float* __restrict__ p) {
+  __shared__ double part[4][EMAX];
+  __shared__ double ssq[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int64_t xrow = int64_t(t) * d;
+  double ss = 0.0;
+  for (int k0 = threadIdx.x * 8; k0 < d; k0 += 2048) {
+    float xv[8];
+    Vec8<BF16>::load(x, xrow + k0, xv);
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e)
-    l[e] = (e < E) ? ((part[0][e] + part[1][e]) + (part[2][e] + part[3][e])) + (bias ? double(bias[e]) : 0.0) : 0.0;
-  int e1 = 0;
+    for (int i = 0; i < 8; ++i) ss = __fma_rn(double(xv[i]), double(xv[i]), ss);
+  }
 #pragma unroll
-  for (int e = 1; e < EMAX; ++e)
-    if (e < E && l[e] > l[e1]) e1 = e;
-  int e2 = -1;
-  double l2 = 0.0, l1 = l[0];
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) ssq[wave] = ss;
+  __syncthreads();
+  const double rms = sqrt(((ssq[0] + ssq[1]) + (ssq[2] + ssq[3])) / double(d) + eps);
+
+  double acc[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) acc[e] = 0.0;
+  const int q = d >> 2;
+  const int kend = (wave + 1) * q;
+  for (int k0 = wave * q + lane * 8; k0 < kend; k0 += 512) {
+    float xv[8], gv[8], nv[8];
+    Vec8<BF16>::load(x, xrow + k0, xv);
+    Vec8<BF16>::load(g, k0, gv);
+    if (BF16) {
+      u32x4_t o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = f64_to_bf16((double(xv[2 * j]) / rms) * double(gv[2 * j]));
+        const uint32_t hi = f64_to_bf16((double(xv[2 * j + 1]) / rms) * double(gv[2 * j + 1]));
+        o[j] = lo | (hi << 16);
+        nv[2 * j] = bf16lo(o[j]);
+        nv[2 * j + 1] = bf16hi(o[j]);
+      }
+      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(xn) + xrow + k0) = o;
+    } else {
+      f32x4_t o0, o1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o0[i] = float((double(xv[i]) / rms) * double(gv[i]));
+        o1[i] = float((double(xv[4 + i]) / rms) * double(gv[4 + i]));
+        nv[i] = o0[i];
+        nv[4 + i] = o1[i];
+      }
+      float* dst = static_cast<float*>(xn) + xrow + k0;
+      *reinterpret_cast<f32x4_t*>(dst) = o0;
+      *reinterpret_cast<f32x4_t*>(dst + 4) = o1;
+    }
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E) {
+        float wv[8];
+        Vec8<BF16>::load(rw, int64_t(e) * d + k0, wv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[e] = __fma_rn(double(nv[i]), double(wv[i]), acc[e]);
+      }
+    }
+  }
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
-    if (e < E && e != e1 && (e2 < 0 || l[e] > l2)) { e2 = e; l2 = l[e]; }
-    if (e == e1) l1 = l[e];
-  }
-  double s = 0.0;
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e)
-    if (e < E) s += exp(l[e] - l1);
-  idx[2 * t] = e1;
-  idx[2 * t + 1] = e2;
-  p[2 * t] = float(1.0 / s);
-  p[2 * t + 1] = float(exp(l2 - l1) / s);
+    for (int off = 32; off >= 1; off >>= 1) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) select_top2<EMAX>(part, bias, E, t, idx, p);
 }
 
 template <bool BF16>
@@ -109,6 +210,23 @@ hipError_t launch_router(const void* x, const void* rw, const float* bias, int T
                          int32_t* idx, float* p, hipStream_t s) {
   return is_bf16 ? launch_router_t<true>(x, rw, bias, T, d, E, idx, p, s)
                  : launch_router_t<false>(x, rw, bias, T, d, E, idx, p, s);
+}
+
+template <bool BF16>
+static hipError_t launch_router_norm_t(const void* x, const void* g, double eps, const void* rw, const float* bias,
+                                       int T, int d, int E, void* xn, int32_t* idx, float* p, hipStream_t s) {
+  const dim3 grid(T), block(256);
+  if (E <= 8) router_norm_kernel<BF16, 8><<<grid, block, 0, s>>>(x, g, eps, rw, bias, T, d, E, xn, idx, p);
+  else if (E <= 16) router_norm_kernel<BF16, 16><<<grid, block, 0, s>>>(x, g, eps, rw, bias, T, d, E, xn, idx, p);
+  else if (E <= 32) router_norm_kernel<BF16, 32><<<grid, block, 0, s>>>(x, g, eps, rw, bias, T, d, E, xn, idx, p);
+  else router_norm_kernel<BF16, 64><<<grid, block, 0, s>>>(x, g, eps, rw, bias, T, d, E, xn, idx, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_norm(const void* x, const void* g, double eps, const void* rw, const float* bias, int T,
+                              int d, int E, bool is_bf16, void* xn, int32_t* idx, float* p, hipStream_t s) {
+  return is_bf16 ? launch_router_norm_t<true>(x, g, eps, rw, bias, T, d, E, xn, idx, p, s)
+                 : launch_router_norm_t<false>(x, g, eps, rw, bias, T, d, E, xn, idx, p, s);
 }
 
 }  // namespace gm

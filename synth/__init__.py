@@ -203,3 +203,15 @@ def sampled_rows(T: int, n: int, seed: int = 1) -> np.ndarray:
     if n >= T:
         return np.arange(T, dtype=np.int64)
     return np.sort(np.random.default_rng(seed).choice(T, n, replace=False)).astype(np.int64)
+
+
+def make_norm_scales(w: Workload, eps: float = 1e-5) -> dict:
+    """Scales of the pre-MoE and post-MoE RMSNorms, [d] each, drawn as 1 + 0.1 N(0, 1) in the activation type,
+    and the eps used with them (the pages give no eps; 1e-5 is a common choice)."""
+    act = F32 if w.dtype == F32 else BF16
+    out = {}
+    for name in ("pre_scale", "post_scale"):
+        v = normal(f"{name}/{w.d}", (w.d,), 0.1, F32, w.seed) + np.float32(1.0)
+        out[name] = v if act == F32 else f32_to_bf16_bits(v)
+    out["eps"] = eps
+    return out
