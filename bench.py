@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--block", action="store_true",
                     help="time the MoE block (pre-MoE RMSNorm, MoE, post-MoE RMSNorm, residual) instead of the layer")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time torch.matmul (hipBLASLt) bf16 on the prefill's per-expert GEMM shapes, for context")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -202,8 +204,46 @@ def cpu_baseline(w, inp, oracle, synth, block=False):
                       f"{w.T} tokens, both selected experts per row), {dt:.1f} s"}
 
 
+def library_gemm(steps, warmup):
+    """torch.matmul (hipBLASLt) on dense bf16 GEMMs of the shapes one expert sees in the T=8192 prefill
+    (2T/E = 2048 rows): one of the two up-projection matrices, and the down-projection with bf16 and fp32 output;
+    plus the whole up-projection's rows as one dense GEMM.  Context for the grouped kernels' TFLOP/s, not part of
+    the layer."""
+    import torch
+    d, f, M = 6144, 32768, 2048
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = {}
+    for name, m, k, n, odt in (("up_one_matrix", M, d, f, torch.bfloat16), ("down_bf16_out", M, f, d, torch.bfloat16),
+                               ("down_f32_out", M, f, d, torch.float32), ("up_all_rows_one_matrix", 8 * M, d, f,
+                                                                          torch.bfloat16)):
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+        if odt == torch.float32:
+            fn = lambda: torch.mm(a, b, out_dtype=torch.float32)
+        else:
+            c = torch.empty(m, n, device="cuda", dtype=odt)
+            fn = lambda: torch.mm(a, b, out=c)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"M": m, "K": k, "N": n, "ms": ms, "TFLOP/s": 2 * m * k * n / (ms * 1e-3) / 1e12}
+        log(f"{name}: {ms:.3f} ms, {res[name]['TFLOP/s']:.0f} TFLOP/s")
+        del a, b
+    print(json.dumps({"library_gemm": res, "library": "torch.mm (hipBLASLt)", "dtype": "bf16"}))
+
+
 def main():
     a = parse()
+    if a.library_gemm:
+        library_gemm(a.steps, a.warmup)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is designed but not built "
                                    "(tensor-parallel over d_ff with a reduce-scatter of the fp32 output)",
