@@ -26,7 +26,8 @@ Readings where the pages leave a step open (each is also listed in the design no
     renormalised over the two ([moe] returns top_k of the full softmax and multiplies by it).
   * Selection is by descending logit with the lower expert index first on equal logits (softmax is strictly
     increasing, so this equals selecting on the probabilities, without ties created by rounding them).
-  * Weights are stored [E, in, out]: W1, Wv are [E, d, f], W2 is [E, f, d]; int8 scales are [E, 1, out].
+  * Weights are stored [E, in, out]: W1, Wv are [E, d, f], W2 is [E, f, d]; int8 scales are [Es, G, out] with
+    Es = E (per expert) or 1 (shared) and G contiguous groups along the in axis (G = 1: per output channel).
   * In the bf16 and int8 layers the intermediate h = GELU(a) ⊙ b is rounded once to bf16 (round to nearest
     even, directly from float64) before the down projection; the fp32 layer keeps h unrounded.
   * The optional per-expert router bias is added to the logits before the softmax.
@@ -44,8 +45,8 @@ import torch
 F32, BF16, W8 = 0, 1, 2
 
 __all__ = [
-    "F32", "BF16", "W8", "as_f64", "bf16_round", "gelu", "route", "expert_ffn", "dequant", "forward", "rmsnorm",
-    "block_forward",
+    "F32", "BF16", "W8", "as_f64", "bf16_round", "gelu", "route", "expert_ffn", "dequant", "expert_scales",
+    "forward", "rmsnorm", "block_forward",
 ]
 
 
@@ -123,11 +124,29 @@ def expert_ffn(x: torch.Tensor, w1: torch.Tensor, wv: torch.Tensor, w2: torch.Te
 
 
 def dequant(q, s) -> torch.Tensor:
-    """[card] "Conversion Details": weight = int8 value times its bf16 scale, the scale broadcast over the in axis.
+    """[card] "Conversion Details": weight = int8 value times its bf16 scale, the scale broadcast over its group.
 
-    q [in, out] int8 (numpy), s [1, out] bf16 bits (numpy).  Exact in float64.
+    q [in, out] int8 (numpy); s [G, out] bf16 bits (numpy), G >= 1 dividing `in`: rows k of q take the scales of
+    group k // (in / G) (G = 1: one scale per output channel).  Exact in float64.
     """
-    return as_f64(q, "i8") * as_f64(s, "bf16")
+    q = as_f64(q, "i8")
+    sc = as_f64(s, "bf16")
+    K = q.shape[0]
+    G = sc.shape[0]
+    if K % G:
+        raise ValueError(f"{G} scale groups do not divide the input size {K}")
+    return q * torch.repeat_interleave(sc, K // G, dim=0)
+
+
+def expert_scales(s, e: int) -> np.ndarray:
+    """The [G, out] scales of expert e from a scale tensor of one of the shapes [card] lists: [Es, G, out]
+    ((8,1,N), (8,8,N)) or [Es, out] ((1,N), (8,N), read as one group).  Es = 1 means shared by all experts."""
+    s = np.asarray(s)
+    if s.ndim == 2:
+        s = s[:, None, :]
+    if s.ndim != 3:
+        raise ValueError(f"scale tensor of rank {s.ndim}")
+    return s[e if s.shape[0] > 1 else 0]
 
 
 def _expert_weights(inp: dict, dtype: int, e: int):
@@ -136,8 +155,8 @@ def _expert_weights(inp: dict, dtype: int, e: int):
     if dtype == BF16:
         return tuple(as_f64(inp[n][e], "bf16") for n in ("w1", "wv", "w2"))
     if dtype == W8:
-        return (dequant(inp["w1"][e], inp["s1"][e]), dequant(inp["wv"][e], inp["sv"][e]),
-                dequant(inp["w2"][e], inp["s2"][e]))
+        return tuple(dequant(inp[n][e], expert_scales(inp[sn], e)) for n, sn in (("w1", "s1"), ("wv", "sv"),
+                                                                                  ("w2", "s2")))
     raise ValueError(dtype)
 
 

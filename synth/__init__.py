@@ -131,6 +131,11 @@ class Workload:
     sampled_rows: int | None = None  # check the expert path on this many seeded rows (None = all rows)
     seed: int = 0
     w_std: float = 0.02  # std of bf16 expert weights
+    # int8 scale layout [Es, G, out]: Es = E (per expert) or 1 (shared by all experts); G contiguous groups along
+    # the input axis of W1/Wv (groups_up) and of W2 (groups_down)
+    scale_experts: int | None = None
+    groups_up: int = 1
+    groups_down: int = 1
     note: str = ""
     tags: dict = field(default_factory=dict)
 
@@ -146,6 +151,8 @@ WORKLOADS = {
                              note="Grok-1 shape prefill: T=8192 (maximum context), bf16"),
     "int8_w8": Workload("int8_w8", T=64, d=6144, f=32768, dtype=W8,
                         note="Grok-1 shape, int8 weights with per-(expert, channel) bf16 scales, T=64"),
+    "int8_w8_g8": Workload("int8_w8_g8", T=64, d=6144, f=32768, dtype=W8, groups_up=8, groups_down=8,
+                           note="Grok-1 shape, int8 weights with (8, 8, N) group-wise bf16 scales, T=64"),
     "skew_bf16": Workload("skew_bf16", T=4096, d=6144, f=32768, dtype=BF16, sampled_rows=256,
                           router_bias=(3.0, 0.0, 0.0, 0.0, 0.0, 1.5, 0.0, 0.0),
                           note="skewed routing: logit bias +3 on expert 0, +1.5 on expert 5, T=4096"),
@@ -190,9 +197,13 @@ def make_weights(w: Workload) -> dict:
         out["w1"] = uniform_int8(f"q1/{d}x{f}/E={E}", (E, d, f), -127, 127, seed)
         out["wv"] = uniform_int8(f"qv/{d}x{f}/E={E}", (E, d, f), -127, 127, seed)
         out["w2"] = uniform_int8(f"q2/{f}x{d}/E={E}", (E, f, d), -127, 127, seed)
-        out["s1"] = uniform_bf16(f"s1/{f}/E={E}", (E, 1, f), 1e-4, 5e-4, seed)
-        out["sv"] = uniform_bf16(f"sv/{f}/E={E}", (E, 1, f), 1e-4, 5e-4, seed)
-        out["s2"] = uniform_bf16(f"s2/{d}/E={E}", (E, 1, d), 1e-4, 5e-4, seed)
+        Es = E if w.scale_experts is None else w.scale_experts
+        g1, g2 = w.groups_up, w.groups_down
+        tag1 = "" if (Es, g1) == (E, 1) else f"/G={g1}"
+        tag2 = "" if (Es, g2) == (E, 1) else f"/G={g2}"
+        out["s1"] = uniform_bf16(f"s1/{f}/E={Es}{tag1}", (Es, g1, f), 1e-4, 5e-4, seed)
+        out["sv"] = uniform_bf16(f"sv/{f}/E={Es}{tag1}", (Es, g1, f), 1e-4, 5e-4, seed)
+        out["s2"] = uniform_bf16(f"s2/{d}/E={Es}{tag2}", (Es, g2, d), 1e-4, 5e-4, seed)
     else:
         raise ValueError(f"unknown dtype {dt}")
     return out

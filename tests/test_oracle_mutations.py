@@ -143,3 +143,31 @@ def test_dropped_residual_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "block_forward", no_residual)
     with pytest.raises(AssertionError):
         bpins.test_block_against_numpy()
+
+
+def _dequant_group_mod(q, s):
+    """Planted mistake: group of row k taken as k mod G."""
+    qq = om.as_f64(q, "i8")
+    sc = om.as_f64(s, "bf16")
+    G = sc.shape[0]
+    return qq * sc[torch.arange(qq.shape[0]) % G]
+
+
+def _dequant_first_group(q, s):
+    """Planted mistake: the first group's scales used for every row."""
+    return om.as_f64(q, "i8") * om.as_f64(s, "bf16")[0:1]
+
+
+@pytest.mark.parametrize("bad", [_dequant_group_mod, _dequant_first_group])
+def test_grouped_scale_mistakes_are_caught(bad, monkeypatch):
+    from tests import test_oracle_scale_pins as sp
+    monkeypatch.setattr(om, "dequant", bad)
+    monkeypatch.setattr(oracle, "dequant", bad)
+    caught = 0
+    for pin in (sp.test_group_index_closed_form, sp.test_dequant_brute_force_loops,
+                sp.test_grouped_layer_against_numpy_brute_force):
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1
