@@ -83,8 +83,12 @@ class Layer:
         self.out = torch.empty((T, d), dtype=torch.float32, device=dev)
         self.xn = torch.empty_like(dv["x"]) if norms is not None else None
         self.s1 = self.sv = self.s2 = None
+        self.grouped = None  # (scale_experts, groups_up, groups_down) of grouped int8 scales
         if dv["scales"] is not None:
             self.s1, self.sv, self.s2 = dv["scales"]
+            es = E if w.scale_experts is None else w.scale_experts
+            if (es, w.groups_up, w.groups_down) != (E, 1, 1):
+                self.grouped = (es, w.groups_up, w.groups_down)
         mk = lambda: torch.cuda.Event(enable_timing=True)
         self.ev = [mk() for _ in range(6)]
         self.lib = gm.lib()
@@ -109,12 +113,22 @@ class Layer:
         st |= L.grok_moe_bin(P(self.idx), T, E, 2, P(self.counts), P(self.offsets), P(self.perm), P(self.inv), s)
         if timed:
             ev[1].record()
-        st |= L.grok_moe_expert_up(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), P(self.counts),
-                                   P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
+        if self.grouped is None:
+            st |= L.grok_moe_expert_up(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), P(self.counts),
+                                       P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
+        else:
+            st |= L.grok_moe_expert_up_w8_grouped(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv),
+                                                  self.grouped[0], self.grouped[1], P(self.counts), P(self.offsets),
+                                                  P(self.perm), T, d, f, E, 2, P(self.h), s)
         if timed:
             ev[2].record()
-        st |= L.grok_moe_expert_down(P(self.h), P(dv["w2"]), P(self.s2), P(self.counts), P(self.offsets), T, d, f,
-                                     E, 2, dt, self.S, P(self.y), s)
+        if self.grouped is None:
+            st |= L.grok_moe_expert_down(P(self.h), P(dv["w2"]), P(self.s2), P(self.counts), P(self.offsets), T, d,
+                                         f, E, 2, dt, self.S, P(self.y), s)
+        else:
+            st |= L.grok_moe_expert_down_w8_grouped(P(self.h), P(dv["w2"]), P(self.s2), self.grouped[0],
+                                                    self.grouped[2], P(self.counts), P(self.offsets), T, d, f, E, 2,
+                                                    self.S, P(self.y), s)
         if timed:
             ev[3].record()
         if self.norms is None:
@@ -154,8 +168,8 @@ def n_hit(layer) -> int:
 def up_bytes(w, nh, T):
     wb = 1 if w.dtype == 2 else (4 if w.dtype == 0 else 2)
     b = nh * 2 * w.d * w.f * wb + T * w.d * 2 + 2 * T * w.f * 2
-    if w.dtype == 2:
-        b += nh * 2 * w.f * 2
+    if w.dtype == 2:  # scales: [Es, G, f] for W1 and Wv, read for every hit expert (once if shared)
+        b += (nh if w.scale_experts is None else 1) * 2 * w.groups_up * w.f * 2
     return b
 
 
@@ -163,7 +177,7 @@ def down_bytes(w, nh, T, S):
     wb = 1 if w.dtype == 2 else (4 if w.dtype == 0 else 2)
     b = nh * w.f * w.d * wb + 2 * T * w.f * 2 + S * 2 * T * w.d * 4
     if w.dtype == 2:
-        b += nh * w.d * 2
+        b += (nh if w.scale_experts is None else 1) * w.groups_down * w.d * 2
     return b
 
 

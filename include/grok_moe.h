@@ -154,6 +154,39 @@ int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const
                           const void* post_scale, double eps, int64_t T, int64_t d, int k, int dtype, float* out,
                           void* stream);
 
+/* ---- int8 weights with grouped scales -------------------------------------------------------------------------
+ * Page "Grok-1-BF16", section "Conversion Details": int8 weights times bf16 scales with grouped broadcasting,
+ * scale shapes (1,N), (8,N), (8,1,N) and (8,8,N).  Here a scale tensor is [scale_experts, groups, out]:
+ *   W[e, k, n] = q[e, k, n] * s[scale_experts == 1 ? 0 : e, k / (in / groups), n]
+ * with scale_experts = E (one tensor per expert) or 1 (shared by all experts), and `groups` contiguous groups of
+ * in/groups input rows.  (8,1,N) and (8,N) are scale_experts = 8, groups = 1 (the layout of grok_moe_forward);
+ * (1,N) is scale_experts = 1, groups = 1; (8,8,N) is scale_experts = 8, groups = 8.
+ *   s1, sv  [scale_experts, groups_up, f]   bf16, groups_up divides d and d / groups_up is a multiple of 64
+ *   s2      [scale_experts, groups_down, d] bf16, groups_down divides f and f / groups_down is a multiple of 64
+ * Other group counts return GROK_MOE_EUNSUPPORTED; scale_experts other than 1 or E, or a group count < 1,
+ * GROK_MOE_EINVAL.  A zero scale is allowed (its group contributes nothing).  Accumulation is fp32; with more
+ * than one group the kernels keep each column's accumulator in units of the current group's scale (one fp32
+ * rounding per group boundary), so non-zero scales of one column must not differ by more than ~1e30 in ratio.
+ * Workspace: grok_moe_workspace_size(..., GROK_MOE_W8); splits: grok_moe_down_splits(..., GROK_MOE_W8). */
+
+/* The whole layer with int8 weights and grouped scales; otherwise as grok_moe_forward with dtype GROK_MOE_W8. */
+int grok_moe_forward_w8_grouped(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                                const void* s1, const void* sv, const void* s2, int scale_experts, int groups_up,
+                                int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, float* out,
+                                const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step: the fused up-projection (as grok_moe_expert_up, dtype GROK_MOE_W8) with grouped scales s1, sv. */
+int grok_moe_expert_up_w8_grouped(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                                  int scale_experts, int groups_up, const int32_t* counts, const int32_t* offsets,
+                                  const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k, void* h,
+                                  void* stream);
+
+/* Step: the down-projection (as grok_moe_expert_down, dtype GROK_MOE_W8) with grouped scales s2. */
+int grok_moe_expert_down_w8_grouped(const void* h, const void* w2, const void* s2, int scale_experts,
+                                    int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T,
+                                    int64_t d, int64_t f, int E, int k, int splits, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

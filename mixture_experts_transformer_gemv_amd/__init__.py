@@ -45,6 +45,12 @@ _SIGS = {
                                    _int, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "grok_moe_combine_norm": (_int, [_c_void_p, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, ctypes.c_double,
                                      _i64, _i64, _int, _int, _c_void_p, _c_void_p]),
+    "grok_moe_forward_w8_grouped": (_int, [_c_void_p] * 8 + [_int, _int, _int, _i64, _i64, _i64, _int, _int]
+                                    + [_c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]),
+    "grok_moe_expert_up_w8_grouped": (_int, [_c_void_p] * 5 + [_int, _int] + [_c_void_p] * 3
+                                      + [_i64, _i64, _i64, _int, _int, _c_void_p, _c_void_p]),
+    "grok_moe_expert_down_w8_grouped": (_int, [_c_void_p] * 3 + [_int, _int] + [_c_void_p] * 2
+                                        + [_i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p]),
 }
 
 _lib = None
@@ -125,21 +131,45 @@ def _layer_shapes(x, router_w, w1, wv, w2):
     return T, d, f, E
 
 
+def scale_layout(s, E: int, n: int, name: str):
+    """(scale_experts, groups) of an int8 scale tensor [Es, G, n] or [Es, n] (one group); Es is 1 or E."""
+    if s is None:
+        raise GrokMoeError(f"{name}: int8 weights need scales")
+    if s.dim() == 2:
+        s = s.unsqueeze(1)
+    if s.dim() != 3 or s.shape[2] != n or s.shape[0] not in (1, E):
+        raise GrokMoeError(f"{name}: scale shape {tuple(s.shape)} is not [1 or {E}, G, {n}] or [1 or {E}, {n}]")
+    _need(s, name, torch.bfloat16)
+    return int(s.shape[0]), int(s.shape[1])
+
+
+def _grouped(scales, E, d, f):
+    """Scale layout of (s1, sv, s2): None for the per-(expert, channel) layout [E, 1, out], else
+    (scale_experts, groups_up, groups_down)."""
+    s1, sv, s2 = scales
+    l1, lv, l2 = scale_layout(s1, E, f, "s1"), scale_layout(sv, E, f, "sv"), scale_layout(s2, E, d, "s2")
+    if l1 != lv or l1[0] != l2[0]:
+        raise GrokMoeError("s1 and sv need the same layout, and s2 the same expert count")
+    if l1 == (E, 1) and l2 == (E, 1):
+        return None
+    return l1[0], l1[1], l2[1]
+
+
 def forward(x, router_w, w1, wv, w2, scales=None, router_bias=None, return_routing=False, workspace=None):
     """The whole layer.  Returns out [T, d] fp32, or (out, topk_idx [T,2] int32, topk_p [T,2] fp32,
-    expert_counts [E] int32) if return_routing.  scales = (s1, sv, s2) for int8 weights."""
+    expert_counts [E] int32) if return_routing.  scales = (s1, sv, s2) for int8 weights, each [Es, G, out] or
+    [Es, out] bf16 (Es = E or 1 shared; G groups along the input axis)."""
     T, d, f, E = _layer_shapes(x, router_w, w1, wv, w2)
     dt = dtype_of(x, w1)
     for t, n in ((x, "x"), (router_w, "router_w"), (w1, "w1"), (wv, "wv"), (w2, "w2")):
         _need(t, n)
     s1 = sv = s2 = None
+    grouped = None
     if dt == W8:
         if scales is None:
             raise GrokMoeError("int8 weights need scales (s1, sv, s2)")
         s1, sv, s2 = scales
-        _need(s1, "s1", torch.bfloat16, (E, 1, f))
-        _need(sv, "sv", torch.bfloat16, (E, 1, f))
-        _need(s2, "s2", torch.bfloat16, (E, 1, d))
+        grouped = _grouped(scales, E, d, f)
     if router_bias is not None:
         _need(router_bias, "router_bias", torch.float32, (E,))
     dev = x.device
@@ -150,10 +180,17 @@ def forward(x, router_w, w1, wv, w2, scales=None, router_bias=None, return_routi
     need = workspace_size(T, d, f, E, 2, dt)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    st = lib().grok_moe_forward(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
-                                T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
-                                _p(workspace), workspace.numel() * workspace.element_size(), _stream())
-    _check(st, "grok_moe_forward")
+    if grouped is None:
+        st = lib().grok_moe_forward(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
+                                    T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
+                                    _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+        _check(st, "grok_moe_forward")
+    else:
+        st = lib().grok_moe_forward_w8_grouped(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
+                                               *grouped, T, d, f, E, 2, _p(out), _p(router_bias), _p(idx), _p(pr),
+                                               _p(cnt), _p(workspace), workspace.numel() * workspace.element_size(),
+                                               _stream())
+        _check(st, "grok_moe_forward_w8_grouped")
     if return_routing:
         return out, idx, pr, cnt
     return out
@@ -193,12 +230,21 @@ def expert_up(x, w1, wv, counts, offsets, perm, scales=None, h=None):
     E, _, f = w1.shape
     dt = dtype_of(x, w1)
     s1 = sv = None
+    lay = (E, 1)
     if dt == W8:
         s1, sv = scales[0], scales[1]
+        lay = scale_layout(s1, E, f, "s1")
+        if scale_layout(sv, E, f, "sv") != lay:
+            raise GrokMoeError("s1 and sv need the same layout")
     if h is None:
         h = torch.empty((2 * T, f), dtype=torch.float32 if dt == F32 else torch.bfloat16, device=x.device)
-    _check(lib().grok_moe_expert_up(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), _p(counts), _p(offsets), _p(perm),
-                                    T, d, f, E, 2, dt, _p(h), _stream()), "grok_moe_expert_up")
+    if lay == (E, 1):
+        _check(lib().grok_moe_expert_up(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), _p(counts), _p(offsets), _p(perm),
+                                        T, d, f, E, 2, dt, _p(h), _stream()), "grok_moe_expert_up")
+    else:
+        _check(lib().grok_moe_expert_up_w8_grouped(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), *lay, _p(counts),
+                                                   _p(offsets), _p(perm), T, d, f, E, 2, _p(h), _stream()),
+               "grok_moe_expert_up_w8_grouped")
     return h
 
 
@@ -209,8 +255,13 @@ def expert_down(h, w2, counts, offsets, T: int, x_dtype, s2=None, y=None):
     S = down_splits(T, d, f, E, 2, dt)
     if y is None:
         y = torch.empty((S, 2 * T, d), dtype=torch.float32, device=h.device)
-    _check(lib().grok_moe_expert_down(_p(h), _p(w2), _p(s2), _p(counts), _p(offsets), T, d, f, E, 2, dt, S, _p(y),
-                                      _stream()), "grok_moe_expert_down")
+    lay = scale_layout(s2, E, d, "s2") if dt == W8 else (E, 1)
+    if lay == (E, 1):
+        _check(lib().grok_moe_expert_down(_p(h), _p(w2), _p(s2), _p(counts), _p(offsets), T, d, f, E, 2, dt, S,
+                                          _p(y), _stream()), "grok_moe_expert_down")
+    else:
+        _check(lib().grok_moe_expert_down_w8_grouped(_p(h), _p(w2), _p(s2), *lay, _p(counts), _p(offsets), T, d, f,
+                                                     E, 2, S, _p(y), _stream()), "grok_moe_expert_down_w8_grouped")
     return y
 
 

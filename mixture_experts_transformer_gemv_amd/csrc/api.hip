@@ -76,10 +76,31 @@ int check_scales(int dtype, const void* s1, const void* sv, const void* s2) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? GROK_MOE_OK : GROK_MOE_EHIP; }
 
+// int8 scale tensors [scale_experts, groups, out]; the default layout is per expert with one group.
+struct ScaleSpec {
+  int experts;  // 1 (shared by all experts) or E
+  int g_up;     // groups along d of W1 / Wv
+  int g_down;   // groups along f of W2
+};
+
+int check_groups(const ScaleSpec& sp, int64_t d, int64_t f, int E) {
+  if ((sp.experts != 1 && sp.experts != E) || sp.g_up < 1 || sp.g_down < 1) return GROK_MOE_EINVAL;
+  if (d % sp.g_up != 0 || (d / sp.g_up) % 64 != 0) return GROK_MOE_EUNSUPPORTED;
+  if (f % sp.g_down != 0 || (f / sp.g_down) % 64 != 0) return GROK_MOE_EUNSUPPORTED;
+  return GROK_MOE_OK;
+}
+
+inline gm::ScaleLayout up_layout(const ScaleSpec& sp, int64_t d, int64_t f) {
+  return gm::ScaleLayout{sp.experts == 1 ? 0 : int64_t(sp.g_up) * f, int(d / sp.g_up)};
+}
+inline gm::ScaleLayout down_layout(const ScaleSpec& sp, int64_t d, int64_t f) {
+  return gm::ScaleLayout{sp.experts == 1 ? 0 : int64_t(sp.g_down) * d, int(f / sp.g_down)};
+}
+
 // ---- the steps, without argument checks (callers have validated)
-hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv, const int32_t* counts,
-                 const int32_t* offsets, const int32_t* perm, const Plan& p, int64_t d, int64_t f, int E, int dtype,
-                 void* h, hipStream_t s) {
+hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv, const ScaleSpec& sp,
+                 const int32_t* counts, const int32_t* offsets, const int32_t* perm, const Plan& p, int64_t d,
+                 int64_t f, int E, int dtype, void* h, hipStream_t s) {
   if (dtype == GROK_MOE_F32)
     return gm::launch_up_f32(static_cast<const float*>(x), static_cast<const float*>(w1),
                              static_cast<const float*>(wv), counts, offsets, perm, int(d), int(f), E, int(p.slots),
@@ -87,24 +108,57 @@ hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, 
   const bool i8 = dtype == GROK_MOE_W8;
   if (p.stream)
     return gm::launch_up_stream(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
-                                static_cast<const uint16_t*>(sv), counts, offsets, perm, int(d), int(f), E, i8, p.mt,
-                                static_cast<uint16_t*>(h), s);
+                                static_cast<const uint16_t*>(sv), up_layout(sp, d, f), counts, offsets, perm, int(d),
+                                int(f), E, i8, p.mt, static_cast<uint16_t*>(h), s);
   return gm::launch_up_tiled(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
-                             static_cast<const uint16_t*>(sv), counts, offsets, perm, int(d), int(f), E,
-                             int(p.slots), i8, static_cast<uint16_t*>(h), s);
+                             static_cast<const uint16_t*>(sv), up_layout(sp, d, f), counts, offsets, perm, int(d),
+                             int(f), E, int(p.slots), i8, static_cast<uint16_t*>(h), s);
 }
 
-hipError_t do_down(const void* h, const void* w2, const void* s2, const int32_t* counts, const int32_t* offsets,
-                   const Plan& p, int64_t d, int64_t f, int E, int dtype, float* y, hipStream_t s) {
+hipError_t do_down(const void* h, const void* w2, const void* s2, const ScaleSpec& sp, const int32_t* counts,
+                   const int32_t* offsets, const Plan& p, int64_t d, int64_t f, int E, int dtype, float* y,
+                   hipStream_t s) {
   if (dtype == GROK_MOE_F32)
     return gm::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2), counts, offsets, int(d),
                                int(f), E, int(p.slots), y, s);
   const bool i8 = dtype == GROK_MOE_W8;
   if (p.stream)
-    return gm::launch_down_stream(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2), counts,
-                                  offsets, int(d), int(f), E, int(p.slots), p.splits, i8, p.mt, y, s);
-  return gm::launch_down_tiled(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2), counts,
-                               offsets, int(d), int(f), E, int(p.slots), p.splits, i8, y, s);
+    return gm::launch_down_stream(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),
+                                  down_layout(sp, d, f), counts, offsets, int(d), int(f), E, int(p.slots), p.splits,
+                                  i8, p.mt, y, s);
+  return gm::launch_down_tiled(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),
+                               down_layout(sp, d, f), counts, offsets, int(d), int(f), E, int(p.slots), p.splits, i8,
+                               y, s);
+}
+
+// The whole layer (grok_moe_forward and its grouped-scale form); arguments validated by the caller.
+int run_layer(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
+              const void* sv, const void* s2, const ScaleSpec& sp, int64_t T, int64_t d, int64_t f, int E, int dtype,
+              float* out, const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
+  const Plan p = make_plan(T, d, f, E, dtype);
+  if (workspace_bytes < p.total) return GROK_MOE_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + p.o_idx);
+  float* pr = topk_p ? topk_p : reinterpret_cast<float*>(ws + p.o_p);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.o_counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + p.o_offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + p.o_perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + p.o_inv);
+  void* h = ws + p.o_h;
+  float* y = reinterpret_cast<float*>(ws + p.o_y);
+
+  hipError_t e = gm::launch_router(x, router_w, router_bias, int(T), int(d), E, dtype != GROK_MOE_F32, idx, pr, s);
+  if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
+  if (e == hipSuccess) e = do_up(x, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h, s);
+  if (e == hipSuccess) e = do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, dtype, y, s);
+  if (e == hipSuccess) e = gm::launch_combine(y, p.splits, pr, inv, int(T), int(d), out, s);
+  if (e == hipSuccess && expert_counts)
+    e = hipMemcpyAsync(expert_counts, counts, size_t(E) * 4, hipMemcpyDeviceToDevice, s);
+  return hip_status(e);
 }
 
 }  // namespace
@@ -144,29 +198,26 @@ int grok_moe_forward(const void* x, const void* router_w, const void* w1, const 
     return GROK_MOE_EINVAL;
   if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
   if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
-  const Plan p = make_plan(T, d, f, E, dtype);
-  if (workspace_bytes < p.total) return GROK_MOE_EWORKSPACE;
+  return run_layer(x, router_w, w1, wv, w2, s1, sv, s2, ScaleSpec{E, 1, 1}, T, d, f, E, dtype, out, router_bias,
+                   topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + p.o_idx);
-  float* pr = topk_p ? topk_p : reinterpret_cast<float*>(ws + p.o_p);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.o_counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + p.o_offsets);
-  int32_t* perm = reinterpret_cast<int32_t*>(ws + p.o_perm);
-  int32_t* inv = reinterpret_cast<int32_t*>(ws + p.o_inv);
-  void* h = ws + p.o_h;
-  float* y = reinterpret_cast<float*>(ws + p.o_y);
-
-  hipError_t e = gm::launch_router(x, router_w, router_bias, int(T), int(d), E, dtype != GROK_MOE_F32, idx, pr, s);
-  if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
-  if (e == hipSuccess) e = do_up(x, w1, wv, s1, sv, counts, offsets, perm, p, d, f, E, dtype, h, s);
-  if (e == hipSuccess) e = do_down(h, w2, s2, counts, offsets, p, d, f, E, dtype, y, s);
-  if (e == hipSuccess) e = gm::launch_combine(y, p.splits, pr, inv, int(T), int(d), out, s);
-  if (e == hipSuccess && expert_counts)
-    e = hipMemcpyAsync(expert_counts, counts, size_t(E) * 4, hipMemcpyDeviceToDevice, s);
-  return hip_status(e);
+int grok_moe_forward_w8_grouped(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                                const void* s1, const void* sv, const void* s2, int scale_experts, int groups_up,
+                                int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, float* out,
+                                const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(T, d, f, E, k, GROK_MOE_W8);
+  if (st != GROK_MOE_OK) return st;
+  const ScaleSpec sp{scale_experts, groups_up, groups_down};
+  if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(w2) || !ok_ptr(out))
+    return GROK_MOE_EINVAL;
+  if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
+  if ((st = check_scales(GROK_MOE_W8, s1, sv, s2)) != GROK_MOE_OK) return st;
+  return run_layer(x, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, GROK_MOE_W8, out, router_bias, topk_idx,
+                   topk_p, expert_counts, workspace, workspace_bytes, stream);
 }
 
 int grok_moe_route(const void* x, const void* router_w, const float* router_bias, int64_t T, int64_t d, int E, int k,
@@ -199,7 +250,24 @@ int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void
     return GROK_MOE_EINVAL;
   if ((st = check_scales(dtype, s1, sv, dtype == GROK_MOE_W8 ? s1 : nullptr)) != GROK_MOE_OK) return st;
   const Plan p = make_plan(T, d, f, E, dtype);
-  return hip_status(do_up(x, w1, wv, s1, sv, counts, offsets, perm, p, d, f, E, dtype, h,
+  return hip_status(do_up(x, w1, wv, s1, sv, ScaleSpec{E, 1, 1}, counts, offsets, perm, p, d, f, E, dtype, h,
+                          static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_expert_up_w8_grouped(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                                  int scale_experts, int groups_up, const int32_t* counts, const int32_t* offsets,
+                                  const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k, void* h,
+                                  void* stream) {
+  int st = check_shape(T, d, f, E, k, GROK_MOE_W8);
+  if (st != GROK_MOE_OK) return st;
+  const ScaleSpec sp{scale_experts, groups_up, 1};
+  if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(perm) ||
+      !ok_ptr(h) || !ok_ptr(s1) || !ok_ptr(sv))
+    return GROK_MOE_EINVAL;
+  const Plan p = make_plan(T, d, f, E, GROK_MOE_W8);
+  return hip_status(do_up(x, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, GROK_MOE_W8, h,
                           static_cast<hipStream_t>(stream)));
 }
 
@@ -212,7 +280,24 @@ int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const in
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(h) || !ok_ptr(w2) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(y)) return GROK_MOE_EINVAL;
   if (dtype == GROK_MOE_W8 ? !ok_ptr(s2) : s2 != nullptr) return GROK_MOE_EINVAL;
-  return hip_status(do_down(h, w2, s2, counts, offsets, p, d, f, E, dtype, y, static_cast<hipStream_t>(stream)));
+  return hip_status(do_down(h, w2, s2, ScaleSpec{E, 1, 1}, counts, offsets, p, d, f, E, dtype, y,
+                            static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_expert_down_w8_grouped(const void* h, const void* w2, const void* s2, int scale_experts,
+                                    int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T,
+                                    int64_t d, int64_t f, int E, int k, int splits, float* y, void* stream) {
+  int st = check_shape(T, d, f, E, k, GROK_MOE_W8);
+  if (st != GROK_MOE_OK) return st;
+  const ScaleSpec sp{scale_experts, 1, groups_down};
+  if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
+  const Plan p = make_plan(T, d, f, E, GROK_MOE_W8);
+  if (splits != p.splits) return GROK_MOE_EINVAL;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(h) || !ok_ptr(w2) || !ok_ptr(s2) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(y))
+    return GROK_MOE_EINVAL;
+  return hip_status(do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, GROK_MOE_W8, y,
+                            static_cast<hipStream_t>(stream)));
 }
 
 int grok_moe_combine(const float* y, int splits, const float* topk_p, const int32_t* inv, int64_t T, int64_t d, int k,
@@ -290,8 +375,9 @@ int grok_moe_block_forward(const void* x, const void* pre_scale, const void* pos
   hipError_t e = gm::launch_router_norm(x, pre_scale, eps, router_w, router_bias, int(T), int(d), E,
                                         dtype != GROK_MOE_F32, xn, idx, pr, s);
   if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
-  if (e == hipSuccess) e = do_up(xn, w1, wv, s1, sv, counts, offsets, perm, p, d, f, E, dtype, h, s);
-  if (e == hipSuccess) e = do_down(h, w2, s2, counts, offsets, p, d, f, E, dtype, y, s);
+  if (e == hipSuccess)
+    e = do_up(xn, w1, wv, s1, sv, ScaleSpec{E, 1, 1}, counts, offsets, perm, p, d, f, E, dtype, h, s);
+  if (e == hipSuccess) e = do_down(h, w2, s2, ScaleSpec{E, 1, 1}, counts, offsets, p, d, f, E, dtype, y, s);
   if (e == hipSuccess)
     e = gm::launch_combine_norm(y, p.splits, pr, inv, int(T), int(d), x, dtype != GROK_MOE_F32, post_scale, eps, out,
                                 s);

@@ -1,7 +1,7 @@
 // Expert matrix products of the Grok-1 MoE layer for few tokens per expert (decode-sized batches), gfx950.
 //
 // Expert FFN, page "A functional bridge between openai/grok and xai-org/grok-1" (architecture diagram):
-// y = (GELU(x W1) (*) (x Wv)) W2.  int8 weights times per-(expert, output channel) bf16 scales, page
+// y = (GELU(x W1) (*) (x Wv)) W2.  int8 weights times bf16 scales broadcast over groups of input rows, page
 // "Grok-1-BF16", section "Conversion Details".
 //
 // With at most a few dozen tokens per expert the products are bound by streaming the weights from HBM: every
@@ -15,6 +15,13 @@
 // Up-projection: one wave per 128 columns of both W1 and Wv over the whole d axis (GELU needs the full sum);
 // h = bf16(GELU(a) * b) is written for the valid token rows.  Down-projection: one wave per 128 columns of W2
 // over one of S chunks of the f axis; fp32 partial sums go to y[S, slots, d] and are added by the combine.
+//
+// int8 scales: with one group along the input axis the scale multiplies the fp32 accumulator once, in the
+// epilogue.  With several groups (GROUPED) the accumulator is kept in units of the current group's scale: on
+// entering group g it is multiplied by s[g-1]/s[g] for each column, the MFMAs then add that group's integer
+// products, and the epilogue multiplies by the last group's scale, so that the result is sum_g s[g] * P[g].
+// A zero scale is replaced by one and that group's int8 values of the column are masked to zero, which gives
+// the same sum.  This costs one rounding per group boundary, far below the bf16 rounding of h.
 #include "common.h"
 #include "launch.h"
 
@@ -49,14 +56,27 @@ struct UpStep {
   u32x4_t a[MT];
 };
 
-template <bool INT8, int MT>
+// Scales of a group for the 8 columns of a lane: the values with zero replaced by one, and a byte mask (per
+// int8 column of a row piece) that keeps the columns whose scale is not zero.
+__device__ __forceinline__ void group_scales8(const uint16_t* s, float o[8], u32x2_t& mask) {
+  load_scales8(s, o);
+  mask = u32x2_t{0u, 0u};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (__float_as_uint(o[c]) & 0x7fffffffu) mask[c >> 2] |= 0xffu << (8 * (c & 3));
+    else o[c] = 1.0f;
+  }
+}
+
+template <bool INT8, int MT, bool GROUPED>
 __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restrict__ x, const void* __restrict__ w1,
                                                         const void* __restrict__ wv, const uint16_t* __restrict__ s1,
-                                                        const uint16_t* __restrict__ sv,
+                                                        const uint16_t* __restrict__ sv, ScaleLayout sl,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ perm, int d, int f,
                                                         uint16_t* __restrict__ h) {
+  static_assert(INT8 || !GROUPED, "grouped scales belong to int8 weights");
   typedef WRow<INT8> W;
   const int e = blockIdx.y;
   const int n_e = counts[e];
@@ -69,6 +89,8 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
   const int col = n0 + 8 * c16;
   const size_t ebase = size_t(e) * d * f;
   const size_t lane_base = ebase + size_t(8 * g) * f + col;  // row 8g of each 32-deep step, column col
+  const uint16_t* s1e = INT8 ? s1 + size_t(e) * sl.estride + col : nullptr;  // group 0's scales of the lane
+  const uint16_t* sve = INT8 ? sv + size_t(e) * sl.estride + col : nullptr;
 
   for (int mb = 0; mb < n_e; mb += 16 * MT) {
     const uint16_t* arow[MT];
@@ -96,14 +118,45 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
       for (int mt = 0; mt < MT; ++mt)
         st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
     };
+    float cur1[8], curv[8];  // GROUPED: the current group's scales (zero replaced by one)
+    u32x2_t m1, mv;          // GROUPED: byte masks of the columns with a non-zero scale in the current group
+    auto enter_group = [&](int grp, bool rescale) {
+      float n1[8], nv[8];
+      group_scales8(s1e + size_t(grp) * f, n1, m1);
+      group_scales8(sve + size_t(grp) * f, nv, mv);
+      if (rescale) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float r1 = cur1[c] / n1[c], rv = curv[c] / nv[c];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) { acc1[mt][c] *= r1; acc2[mt][c] *= rv; }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { cur1[c] = n1[c]; curv[c] = nv[c]; }
+    };
     auto compute = [&](const UpStep<INT8, MT>& st) {
       u32x4_t t[8];
-      W::transpose(st.b1, t);
+      if constexpr (GROUPED) {
+        typename W::T b[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) b[r] = st.b1[r] & m1;
+        W::transpose(b, t);
+      } else {
+        W::transpose(st.b1, t);
+      }
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc1[mt][c] = mfma16x16x32(st.a[mt], t[c], acc1[mt][c]);
-      W::transpose(st.b2, t);
+      if constexpr (GROUPED) {
+        typename W::T b[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) b[r] = st.b2[r] & mv;
+        W::transpose(b, t);
+      } else {
+        W::transpose(st.b2, t);
+      }
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -111,9 +164,15 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
     };
 
     // d is a multiple of 64: two 32-deep steps per iteration, the next step's loads in flight during compute.
+    // group boundaries (GROUPED) are multiples of 64 rows, so they fall on iteration starts.
     UpStep<INT8, MT> sa, sb;
+    int gnext = 0;  // GROUPED: first row of the next group
     load(sa, 0);
     for (int k0 = 0; k0 < d; k0 += 64) {
+      if (GROUPED && k0 == gnext) {
+        enter_group(k0 / sl.gsize, k0 != 0);
+        gnext += sl.gsize;
+      }
       load(sb, k0 + 32);
       compute(sa);
       if (k0 + 64 < d) load(sa, k0 + 64);
@@ -121,9 +180,12 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
     }
 
     float sc1[8], scv[8];
-    if (INT8) {
-      load_scales8(s1 + size_t(e) * f + col, sc1);
-      load_scales8(sv + size_t(e) * f + col, scv);
+    if (GROUPED) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { sc1[c] = cur1[c]; scv[c] = curv[c]; }
+    } else if (INT8) {
+      load_scales8(s1e, sc1);
+      load_scales8(sve, scv);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -154,12 +216,13 @@ struct DownStep {
   u32x4_t a[MT];
 };
 
-template <bool INT8, int MT>
+template <bool INT8, int MT, bool GROUPED>
 __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __restrict__ h, const void* __restrict__ w2,
-                                                          const uint16_t* __restrict__ s2,
+                                                          const uint16_t* __restrict__ s2, ScaleLayout sl,
                                                           const int32_t* __restrict__ counts,
                                                           const int32_t* __restrict__ offsets, int d, int f, int S,
                                                           int64_t split_stride, float* __restrict__ y) {
+  static_assert(INT8 || !GROUPED, "grouped scales belong to int8 weights");
   typedef WRow<INT8> W;
   const int e = blockIdx.z;
   const int n_e = counts[e];
@@ -173,6 +236,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
   const int kchunk = f / S;
   const int kbeg = blockIdx.y * kchunk;
   const size_t lane_base = size_t(e) * f * d + size_t(8 * g) * d + col;
+  const uint16_t* s2e = INT8 ? s2 + size_t(e) * sl.estride + col : nullptr;  // group 0's scales of the lane
 
   for (int mb = 0; mb < n_e; mb += 16 * MT) {
     const uint16_t* arow[MT];
@@ -197,9 +261,32 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
       for (int mt = 0; mt < MT; ++mt)
         st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
     };
+    float cur[8];  // GROUPED: the current group's scales (zero replaced by one)
+    u32x2_t msk;   // GROUPED: byte mask of the columns with a non-zero scale in the current group
+    auto enter_group = [&](int grp, bool rescale) {
+      float ns[8];
+      group_scales8(s2e + size_t(grp) * d, ns, msk);
+      if (rescale) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float r = cur[c] / ns[c];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][c] *= r;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) cur[c] = ns[c];
+    };
     auto compute = [&](const DownStep<INT8, MT>& st) {
       u32x4_t t[8];
-      W::transpose(st.b, t);
+      if constexpr (GROUPED) {
+        typename W::T b[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) b[r] = st.b[r] & msk;
+        W::transpose(b, t);
+      } else {
+        W::transpose(st.b, t);
+      }
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -208,8 +295,14 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 
     DownStep<INT8, MT> sa, sb;
     const int kend = kbeg + kchunk;  // kchunk is a multiple of 64
+    int gnext = kbeg;                // GROUPED: the chunk starts inside group kbeg / gsize
     load(sa, kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += 64) {
+      if (GROUPED && k0 == gnext) {
+        const int grp = k0 / sl.gsize;
+        enter_group(grp, k0 != kbeg);
+        gnext = (grp + 1) * sl.gsize;
+      }
       load(sb, k0 + 32);
       compute(sa);
       if (k0 + 64 < kend) load(sa, k0 + 64);
@@ -217,7 +310,12 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
     }
 
     float sc[8];
-    if (INT8) load_scales8(s2 + size_t(e) * d + col, sc);
+    if (GROUPED) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sc[c] = cur[c];
+    } else if (INT8) {
+      load_scales8(s2e, sc);
+    }
     float* ys = y + int64_t(blockIdx.y) * split_stride;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -241,31 +339,39 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 }
 
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                            const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
-                            int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s) {
+                            const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* perm, int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s) {
   const dim3 grid((f + 511) / 512, E), block(256);
-  if (int8) {
-    if (mt == 1) up_stream_kernel<true, 1><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
-    else up_stream_kernel<true, 2><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
+  const bool grouped = int8 && sl.gsize < d;
+#define GM_UP(I8, MT, GR) up_stream_kernel<I8, MT, GR><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, \
+                                                                          perm, d, f, h)
+  if (grouped) {
+    if (mt == 1) GM_UP(true, 1, true); else GM_UP(true, 2, true);
+  } else if (int8) {
+    if (mt == 1) GM_UP(true, 1, false); else GM_UP(true, 2, false);
   } else {
-    if (mt == 1) up_stream_kernel<false, 1><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
-    else up_stream_kernel<false, 2><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, h);
+    if (mt == 1) GM_UP(false, 1, false); else GM_UP(false, 2, false);
   }
+#undef GM_UP
   return hipGetLastError();
 }
 
-hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
-                              const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, int mt,
-                              float* y, hipStream_t s) {
+hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+                              const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
+                              bool int8, int mt, float* y, hipStream_t s) {
   const dim3 grid((d + 511) / 512, S, E), block(256);
   const int64_t stride = int64_t(slots) * d;
-  if (int8) {
-    if (mt == 1) down_stream_kernel<true, 1><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
-    else down_stream_kernel<true, 2><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
+  const bool grouped = int8 && sl.gsize < f;
+#define GM_DOWN(I8, MT, GR) down_stream_kernel<I8, MT, GR><<<grid, block, 0, s>>>(h, w2, s2, sl, counts, offsets, d, \
+                                                                              f, S, stride, y)
+  if (grouped) {
+    if (mt == 1) GM_DOWN(true, 1, true); else GM_DOWN(true, 2, true);
+  } else if (int8) {
+    if (mt == 1) GM_DOWN(true, 1, false); else GM_DOWN(true, 2, false);
   } else {
-    if (mt == 1) down_stream_kernel<false, 1><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
-    else down_stream_kernel<false, 2><<<grid, block, 0, s>>>(h, w2, s2, counts, offsets, d, f, S, stride, y);
+    if (mt == 1) GM_DOWN(false, 1, false); else GM_DOWN(false, 2, false);
   }
+#undef GM_DOWN
   return hipGetLastError();
 }
 

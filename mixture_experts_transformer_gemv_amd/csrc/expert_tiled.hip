@@ -1,16 +1,20 @@
 // LDS-tiled grouped GEMM with register-staged weight tiles (used for int8 weights), gfx950.
 //
 // Expert FFN, page "A functional bridge between openai/grok and xai-org/grok-1" (architecture diagram):
-// y = (GELU(x W1) (*) (x Wv)) W2; int8 weights times per-(expert, output channel) bf16 scales, page
+// y = (GELU(x W1) (*) (x Wv)) W2; int8 weights times bf16 scales broadcast over groups of input rows, page
 // "Grok-1-BF16", section "Conversion Details".
 //
 // Tile shape, order and epilogue: tiles.h.  K steps of 64, double-buffered in LDS (2 x 72 KB).  Weights are
 // stored [in, out] while the MFMA wants 8 consecutive k per lane, so each thread loads an 8 (k) x 8 (n) block as
 // eight row pieces, converts int8 to bf16 exactly (|q| <= 128 has at most 8 significant bits) while transposing
 // it in registers, and writes eight 16-byte column pieces into the [n][k] LDS tile.  LDS rows are padded by 16
-// bytes so that 16-byte MFMA operand reads of consecutive rows fall into distinct banks.  The per-channel scales
-// multiply the fp32 accumulators in the epilogue.  bf16 weights take the direct-to-LDS kernel of
-// expert_tiled_dma.hip instead.
+// bytes so that 16-byte MFMA operand reads of consecutive rows fall into distinct banks.  With one scale group
+// along K the per-channel scales multiply the fp32 accumulators in the epilogue.  With several (GROUPED) the
+// accumulators are kept in units of the current group's scale: entering group g multiplies each column by
+// s[g-1]/s[g], the epilogue multiplies by the last group's scale; a zero scale is replaced by one and the
+// column's int8 values of that group are masked to zero while they are converted.  bf16 weights take the
+// direct-to-LDS kernel of expert_tiled_dma.hip instead.  The GROUPED form uses 128-row tiles (64 x 128 per
+// wave) so that the accumulators leave registers for the rescaling.
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -42,29 +46,34 @@ template <> struct BRow<true> {
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1).  B0/B1: weights [E, K, N].
 // out: h bf16 [slots, N] (NMAT = 2) or y f32 [slots, N] (NMAT = 1).
-template <int NMAT, bool INT8>
+template <int NMAT, bool INT8, bool GROUPED>
 __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restrict__ A, const void* __restrict__ B0,
                                                     const void* __restrict__ B1, const uint16_t* __restrict__ sc0,
-                                                    const uint16_t* __restrict__ sc1,
+                                                    const uint16_t* __restrict__ sc1, ScaleLayout sl,
                                                     const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ offsets,
                                                     const int32_t* __restrict__ perm, int K, int N, int E,
                                                     void* __restrict__ out) {
+  static_assert(INT8 || !GROUPED, "grouped scales belong to int8 weights");
   typedef BRow<INT8> W;
-  constexpr int BNM = BNT / NMAT;  // columns per matrix
+  constexpr int BNM = BNT / NMAT;       // columns per matrix
+  constexpr int TBM = GROUPED ? 128 : BM;  // rows per tile
+  constexpr int MI = TBM / 64;          // 32-row MFMA blocks per wave
+  constexpr int NA = TBM / 32;          // 16-byte A pieces per thread and K step
   int e, row0, rows, ntile;
-  if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole workgroup
+  if (!tile::map_tile<tile::Group<NMAT>::N, TBM>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile))
+    return;  // whole workgroup
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][TBM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BNT * LDK];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nbase = ntile * BNM;
 
-  // ---- global A pieces: 8 x 16 bytes per thread (rows tid/8 + 32 i, k piece tid % 8)
-  const uint16_t* a_src[8];
+  // ---- global A pieces: NA x 16 bytes per thread (rows tid/8 + 32 i, k piece tid % 8)
+  const uint16_t* a_src[NA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NA; ++i) {
     const int r = (tid >> 3) + 32 * i;
     const int rr = min(r, rows - 1);  // rows past the expert's end repeat a valid row; never stored
     const size_t arow = (NMAT == 2) ? size_t(perm[row0 + rr]) : size_t(row0 + rr);
@@ -78,42 +87,72 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
   const size_t b_base = size_t(e) * K * N + size_t(8 * kb) * N + gcol;
   const int b_lds_row = wave * 64 + nb * 8;  // first of the 8 LDS rows (columns) this thread writes
 
-  u32x4_t ra[8];
+  // GROUPED: scales of the 8 columns of this thread's B block (group 0), and the byte mask of those with a
+  // non-zero scale in the group of the K step held in rb
+  const uint16_t* bscale = INT8 ? ((NMAT == 2 && mat == 1) ? sc1 : sc0) + size_t(e) * sl.estride + gcol : nullptr;
+  u32x2_t bmask = {~0u, ~0u};
+  auto set_bmask = [&](int grp) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(bscale + size_t(grp) * N);
+    bmask = u32x2_t{0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t b = (w[c >> 1] >> (16 * (c & 1))) & 0xffffu;
+      if (b & 0x7fffu) bmask[c >> 2] |= 0xffu << (8 * (c & 3));
+    }
+  };
+
+  u32x4_t ra[NA];
   typename W::T rb[8];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
+    for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
 #pragma unroll
     for (int r = 0; r < 8; ++r) rb[r] = W::load(bmat, b_base + size_t(k0 + r) * N);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NA; ++i)
       *reinterpret_cast<u32x4_t*>(&As[buf][((tid >> 3) + 32 * i) * LDK + 8 * (tid & 7)]) = ra[i];
     u32x4_t t[8];
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) rb[r] &= bmask;
+    }
     W::transpose(rb, t);
 #pragma unroll
     for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4_t*>(&Bs[buf][(b_lds_row + c) * LDK + 8 * kb]) = t[c];
   };
 
-  // ---- MFMA tiling: waves 2 x 2; wave rows wm*128 .. +127; 4 column sub-tiles of 32
+  // ---- MFMA tiling: waves 2 x 2; wave rows wm*TBM/2 .. +TBM/2-1; 4 column sub-tiles of 32
   const int wm = wave >> 1, wn = wave & 1;
   int bsub[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) bsub[j] = (NMAT == 2) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
-  f32x16_t acc[4][4];
+  f32x16_t acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int lr = lane & 31, lk = 8 * (lane >> 5);
-  auto frags = [&](int buf, int ks, u32x4_t a[4], u32x4_t b[4]) {
+  // the output column of each accumulator sub-tile held by this lane, as a pointer to its group-0 scale
+  const uint16_t* jscale[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const u32x4_t*>(&As[buf][(wm * 128 + i * 32 + lr) * LDK + ks + lk]);
+  for (int j = 0; j < 4; ++j) {
+    if (NMAT == 2) jscale[j] = ((j >> 1) ? sc1 : sc0) + size_t(e) * sl.estride + nbase + wn * 64 + (j & 1) * 32 + lr;
+    else jscale[j] = sc0 + size_t(e) * sl.estride + nbase + wn * 128 + j * 32 + lr;
+  }
+  float cur[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // GROUPED: scale (zero -> one) of the group being accumulated
+  auto group_scale = [&](int j, int grp) {
+    const uint16_t b = jscale[j][size_t(grp) * N];
+    return (b & 0x7fffu) ? bf16f(b) : 1.0f;
+  };
+  auto frags = [&](int buf, int ks, u32x4_t a[MI], u32x4_t b[4]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      a[i] = *reinterpret_cast<const u32x4_t*>(&As[buf][(wm * 32 * MI + i * 32 + lr) * LDK + ks + lk]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4_t*>(&Bs[buf][(bsub[j] + lr) * LDK + ks + lk]);
   };
@@ -123,65 +162,108 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
   // step kt+2 is fetched from global memory, all interleaved with the 64 MFMAs of step kt.  The body has no
   // branches (the prefetch past the last step re-reads it; it is never stored).
   const int KT = K / BK;
+  const int gsteps = sl.gsize / BK;  // K steps per scale group (GROUPED)
+  if constexpr (GROUPED) {
+    set_bmask(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cur[j] = group_scale(j, 0);
+  }
   gload(0);
   lstore(0);
   gload(min(1, KT - 1) * BK);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    u32x4_t fa[2][4], fb[2][4];
+    if constexpr (GROUPED) {
+      if (kt > 0 && kt % gsteps == 0) {  // step kt opens group kt / gsteps: change the accumulators' unit
+        const int grp = kt / gsteps;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float nv = group_scale(j, grp);
+          const float r = cur[j] / nv;
+          cur[j] = nv;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) acc[i][j] *= r;
+        }
+      }
+      if ((kt + 1) < KT && (kt + 1) % gsteps == 0) set_bmask((kt + 1) / gsteps);  // rb holds step kt + 1
+    }
+    u32x4_t fa[2][MI], fb[2][4];
     frags(buf, 0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) frags(buf, (ks + 1) * 16, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
     }
     lstore(buf ^ 1);
     gload(min(kt + 2, KT - 1) * BK);
     // interleave: 8 fragment reads, then MFMAs each followed by the remaining fragment reads, then by
-    // transposes and LDS stores, then by the global loads of the step after next
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // transposes and LDS stores, then by the global loads of the step after next (the GROUPED form is left to
+    // the compiler's schedule)
+    if constexpr (!GROUPED) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __syncthreads();
   }
 
-  tile::store_tile<NMAT, INT8>(acc, wm, wn, lane, e, row0, rows, nbase, N, sc0, sc1, out);
+  if constexpr (INT8) {  // the scale of the last group (GROUPED) or of the only one, then the plain epilogue
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sj = GROUPED ? cur[j] : bf16f(jscale[j][0]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[i][j] *= sj;
+    }
+  }
+  tile::store_tile<NMAT, false, MI>(acc, wm, wn, lane, e, row0, rows, nbase, N, nullptr, nullptr, out);
 }
 
 hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                           const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
-                           int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s) {
+                           const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
+                           const int32_t* perm, int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s) {
   if (!int8) return launch_up_tiled_dma(x, w1, wv, counts, offsets, perm, d, f, E, slots, h, s);
-  const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
-  tiled_reg_kernel<2, true><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, counts, offsets, perm, d, f, E, h);
+  if (sl.gsize < d) {
+    const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2), 128)), block(256);
+    tiled_reg_kernel<2, true, true><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, E, h);
+  } else {
+    const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
+    tiled_reg_kernel<2, true, false><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, E, h);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
-                             const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, float* y,
-                             hipStream_t s) {
+hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+                             const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
+                             bool int8, float* y, hipStream_t s) {
   if (!int8) return launch_down_tiled_dma(h, w2, counts, offsets, d, f, E, slots, S, y, s);
-  const dim3 grid(tile::grid_tiles(slots, E, d / BNT)), block(256);
-  tiled_reg_kernel<1, true><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, counts, offsets, nullptr, f, d, E, y);
+  if (sl.gsize < f) {
+    const dim3 grid(tile::grid_tiles(slots, E, d / BNT, 128)), block(256);
+    tiled_reg_kernel<1, true, true><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, offsets, nullptr,
+                                                           f, d, E, y);
+  } else {
+    const dim3 grid(tile::grid_tiles(slots, E, d / BNT)), block(256);
+    tiled_reg_kernel<1, true, false><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, offsets,
+                                                            nullptr, f, d, E, y);
+  }
   return hipGetLastError();
 }
 

@@ -6,6 +6,14 @@
 
 namespace gm {
 
+// Layout of int8 scales [Es, G, N] ("Grok-1-BF16", section "Conversion Details": scales broadcast over groups):
+// the scale of (expert e, group g, column n) is at e * estride + g * N + n (estride = G * N, or 0 when all
+// experts share one scale tensor); a group is gsize consecutive input rows (gsize == K: one group).
+struct ScaleLayout {
+  int64_t estride;
+  int gsize;
+};
+
 // Router: fp64 gate GEMV, softmax over E, top-2 (lower index first on ties).  is_bf16 selects the input type.
 hipError_t launch_router(const void* x, const void* rw, const float* bias, int T, int d, int E, bool is_bf16,
                          int32_t* idx, float* p, hipStream_t s);
@@ -29,20 +37,20 @@ hipError_t launch_combine(const float* y, int S, const float* p, const int32_t* 
 // Streaming (few tokens per expert) expert kernels: weights go HBM -> registers -> MFMA, no LDS tiling.
 // mt = number of 16-row MFMA tiles held per pass (1 or 2).
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                            const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
-                            int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s);
-hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
-                              const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, int mt,
-                              float* y, hipStream_t s);
+                            const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* perm, int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s);
+hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+                              const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
+                              bool int8, int mt, float* y, hipStream_t s);
 
 // LDS-tiled grouped GEMMs (many tokens per expert); int8 weights use register-staged tiles, bf16 weights the
 // direct-to-LDS kernels below.
 hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                           const uint16_t* sv, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
-                           int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s);
-hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, const int32_t* counts,
-                             const int32_t* offsets, int d, int f, int E, int slots, int S, bool int8, float* y,
-                             hipStream_t s);
+                           const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
+                           const int32_t* perm, int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s);
+hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+                             const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
+                             bool int8, float* y, hipStream_t s);
 
 // The bf16 forms of the tiled kernels: direct global -> LDS copies, LDS transpose reads.
 hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const int32_t* counts,

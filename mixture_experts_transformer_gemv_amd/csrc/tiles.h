@@ -7,7 +7,8 @@
 // A workgroup of 4 waves computes a 256-row x 256-column output tile of the expert-sorted assignment slots:
 //   * up-projection (NMAT = 2): 128 columns of W1 and the same 128 columns of Wv; h = bf16(GELU(a) * b);
 //   * down-projection (NMAT = 1): 256 columns of W2; fp32 output.
-// Each wave holds a 128 x 128 accumulator tile as 4 x 4 MFMA 32x32 blocks (256 fp32 per lane).
+// Each wave holds a 128 x 128 accumulator tile as 4 x 4 MFMA 32x32 blocks (256 fp32 per lane).  A kernel may use
+// half-height tiles (128 rows, 64 x 128 per wave) where it needs accumulator registers for other work.
 #pragma once
 
 #include "common.h"
@@ -22,15 +23,16 @@ constexpr int BNT = 256;  // output columns per tile (all matrices)
 // T = 8192) do not fit, so it favours row reuse (8).  Measured on MI355X.
 template <int NMAT> struct Group { static constexpr int N = NMAT == 2 ? 4 : 8; };
 
-// Map workgroup p to (expert, first row slot, valid rows, column tile); false if p has no tile.
+// Map workgroup p to (expert, first row slot, valid rows, column tile) for row tiles of TBM rows; false if p has
+// no tile.
 // Workgroup p runs on XCD p % 8 (round-robin dispatch).  Each XCD gets a contiguous range of tiles, ordered
 // expert -> group of NGROUP column tiles -> row tile -> column tile, so the ~32 tiles resident on one XCD share
 // their A rows (NGROUP ways) and their weight columns (32 / NGROUP ways) in that XCD's L2.
-template <int NGROUP>
+template <int NGROUP, int TBM = BM>
 __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* offsets, int E, int NT, int p,
                                          int* e_out, int* row0_out, int* rows_out, int* nt_out) {
   int total = 0;
-  for (int e = 0; e < E; ++e) total += (counts[e] + BM - 1) / BM;
+  for (int e = 0; e < E; ++e) total += (counts[e] + TBM - 1) / TBM;
   total *= NT;
   const int chunk = (total + 7) >> 3;
   const int q = p >> 3;
@@ -39,7 +41,7 @@ __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* o
   if (L >= total) return false;
   for (int e = 0; e < E; ++e) {
     const int n = counts[e];
-    const int mt = (n + BM - 1) / BM;
+    const int mt = (n + TBM - 1) / TBM;
     const int te = mt * NT;
     if (L < te) {
       const int ng = L / (mt * NGROUP);
@@ -48,8 +50,8 @@ __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* o
       const int m = rem / gsz;
       *nt_out = ng * NGROUP + (rem - m * gsz);
       *e_out = e;
-      *row0_out = offsets[e] + m * BM;
-      *rows_out = min(BM, n - m * BM);
+      *row0_out = offsets[e] + m * TBM;
+      *rows_out = min(TBM, n - m * TBM);
       return true;
     }
     L -= te;
@@ -59,16 +61,16 @@ __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* o
 
 // Upper bound of the number of tiles, rounded to a multiple of 8 (the grid); the exact count depends on the
 // per-expert counts, which only the device knows.
-static inline unsigned grid_tiles(int slots, int E, int NT) {
-  const unsigned g = unsigned(slots / BM + E) * unsigned(NT);
+static inline unsigned grid_tiles(int slots, int E, int NT, int bm = BM) {
+  const unsigned g = unsigned(slots / bm + E) * unsigned(NT);
   return (g + 7u) & ~7u;
 }
 
-// Epilogue.  acc[i][j]: wave (wm, wn) rows wm*128 + 32 i .., column sub-tile j (NMAT = 2: j = 0,1 are W1
-// columns wn*64 + 32 j, j = 2,3 the same Wv columns; NMAT = 1: columns wn*128 + 32 j).  Lane holds column
+// Epilogue.  acc[i][j] (i < MI row blocks of 32): wave (wm, wn) rows wm*32*MI + 32 i .., column sub-tile j
+// (NMAT = 2: j = 0,1 are W1 columns wn*64 + 32 j, j = 2,3 the same Wv columns; NMAT = 1: columns wn*128 + 32 j).  Lane holds column
 // (lane & 31) of each sub-tile, rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5) of each 32-row block.
-template <int NMAT, bool INT8>
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][4], int wm, int wn, int lane, int e, int row0,
+template <int NMAT, bool INT8, int MI = 4>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[MI][4], int wm, int wn, int lane, int e, int row0,
                                            int rows, int nbase, int N, const uint16_t* sc0, const uint16_t* sc1,
                                            void* out) {
   const int lr = lane & 31, rhalf = 4 * (lane >> 5);
@@ -80,10 +82,10 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][4], int wm, 
       float s_a = 1.0f, s_b = 1.0f;
       if (INT8) { s_a = bf16f(sc0[size_t(e) * N + n]); s_b = bf16f(sc1[size_t(e) * N + n]); }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
+          const int r = wm * 32 * MI + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
           if (r < rows) {
             const float a = acc[i][jn][v] * s_a, b = acc[i][2 + jn][v] * s_b;
             h[size_t(row0 + r) * N + n] = uint16_t(f2bf(gelu_erf(a) * b));
@@ -98,10 +100,10 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][4], int wm, 
       const int n = nbase + wn * 128 + j * 32 + lr;
       const float s = INT8 ? bf16f(sc0[size_t(e) * N + n]) : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
+          const int r = wm * 32 * MI + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
           if (r < rows) y[size_t(row0 + r) * N + n] = INT8 ? acc[i][j][v] * s : acc[i][j][v];
         }
       }

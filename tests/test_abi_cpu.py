@@ -108,3 +108,36 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gm, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(gm.GrokMoeError):
         gm.lib()
+
+
+def _fwd_g(L, se=8, g1=2, g2=4, **kw):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+    a = dict(T=8, d=512, f=1024, E=8, k=2, ws_bytes=0)
+    a.update(kw)
+    return L.grok_moe_forward_w8_grouped(fake, fake, fake, fake, fake, fake, fake, fake, se, g1, g2, a["T"], a["d"],
+                                         a["f"], a["E"], a["k"], fake, None, None, None, None,
+                                         ctypes.c_void_p(0x200000), a["ws_bytes"], None)
+
+
+def test_grouped_scale_layouts_rejected_on_host(L):
+    assert _fwd_g(L) == -3                    # valid layout: only the (zero-byte) workspace is short
+    assert _fwd_g(L, se=1) == -3              # shared scales
+    assert _fwd_g(L, se=3) == -1              # scale_experts neither 1 nor E
+    assert _fwd_g(L, g1=0) == -1
+    assert _fwd_g(L, g2=-2) == -1
+    assert _fwd_g(L, g1=3) == -2              # does not divide d
+    assert _fwd_g(L, g1=16) == -2             # d / 16 = 32 rows: not a multiple of 64
+    assert _fwd_g(L, g2=32) == -2             # f / 32 = 32 rows
+    assert _fwd_g(L, g1=8, g2=16) == -3       # 64-row groups are accepted
+    assert _fwd_g(L, k=3) == -2
+    assert _fwd_g(L, T=0) == 0
+    fake = ctypes.c_void_p(0x100000)
+    assert L.grok_moe_expert_up_w8_grouped(fake, fake, fake, fake, fake, 8, 3, fake, fake, fake, 8, 512, 1024, 8, 2,
+                                           fake, None) == -2
+    assert L.grok_moe_expert_up_w8_grouped(fake, fake, fake, None, fake, 8, 2, fake, fake, fake, 8, 512, 1024, 8, 2,
+                                           fake, None) == -1
+    S = L.grok_moe_down_splits(8, 512, 1024, 8, 2, 2)
+    assert L.grok_moe_expert_down_w8_grouped(fake, fake, fake, 2, 4, fake, fake, 8, 512, 1024, 8, 2, S, fake,
+                                             None) == -1
+    assert L.grok_moe_expert_down_w8_grouped(fake, fake, fake, 8, 4, fake, fake, 8, 512, 1024, 8, 2, S + 1, fake,
+                                             None) == -1
