@@ -44,11 +44,12 @@ template <> struct WRow<true> {  // int8: 8 bytes = 8 columns
 };
 
 // 8 scales (bf16) of consecutive columns -> float.
-__device__ __forceinline__ void load_scales8(const uint16_t* s, float o[8]) {
-  const u32x4_t w = *reinterpret_cast<const u32x4_t*>(s);
+__device__ __forceinline__ void unpack_scales8(const u32x4_t& w, float o[8]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) { o[2 * j] = bf16lo(w[j]); o[2 * j + 1] = bf16hi(w[j]); }
 }
+__device__ __forceinline__ u32x4_t load_raw8(const uint16_t* s) { return *reinterpret_cast<const u32x4_t*>(s); }
+__device__ __forceinline__ void load_scales8(const uint16_t* s, float o[8]) { unpack_scales8(load_raw8(s), o); }
 
 template <bool INT8, int MT>
 struct UpStep {
@@ -58,13 +59,26 @@ struct UpStep {
 
 // Scales of a group for the 8 columns of a lane: the values with zero replaced by one, and a byte mask (per
 // int8 column of a row piece) that keeps the columns whose scale is not zero.
-__device__ __forceinline__ void group_scales8(const uint16_t* s, float o[8], u32x2_t& mask) {
-  load_scales8(s, o);
+__device__ __forceinline__ void group_scales8(const u32x4_t& raw, float o[8], u32x2_t& mask) {
+  unpack_scales8(raw, o);
   mask = u32x2_t{0u, 0u};
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     if (__float_as_uint(o[c]) & 0x7fffffffu) mask[c >> 2] |= 0xffu << (8 * (c & 3));
     else o[c] = 1.0f;
+  }
+}
+
+// Transpose of a weight block, its int8 columns first masked (byte mask m) if MASKED.
+template <bool INT8, bool MASKED>
+__device__ __forceinline__ void block_transpose(const typename WRow<INT8>::T r[8], const u32x2_t& m, u32x4_t t[8]) {
+  if constexpr (MASKED) {
+    typename WRow<INT8>::T b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = r[i] & m;
+    WRow<INT8>::transpose(b, t);
+  } else {
+    WRow<INT8>::transpose(r, t);
   }
 }
 
@@ -118,12 +132,15 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
       for (int mt = 0; mt < MT; ++mt)
         st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
     };
-    float cur1[8], curv[8];  // GROUPED: the current group's scales (zero replaced by one)
-    u32x2_t m1, mv;          // GROUPED: byte masks of the columns with a non-zero scale in the current group
-    auto enter_group = [&](int grp, bool rescale) {
+    // GROUPED: the current group's scales (zero replaced by one), the byte masks of its columns with a non-zero
+    // scale, and the raw scales of the next group (loaded a group ahead)
+    float cur1[8], curv[8];
+    u32x2_t m1, mv;
+    u32x4_t pend1, pendv;
+    auto enter_group = [&](bool rescale) {
       float n1[8], nv[8];
-      group_scales8(s1e + size_t(grp) * f, n1, m1);
-      group_scales8(sve + size_t(grp) * f, nv, mv);
+      group_scales8(pend1, n1, m1);
+      group_scales8(pendv, nv, mv);
       if (rescale) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -137,26 +154,12 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
     };
     auto compute = [&](const UpStep<INT8, MT>& st) {
       u32x4_t t[8];
-      if constexpr (GROUPED) {
-        typename W::T b[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) b[r] = st.b1[r] & m1;
-        W::transpose(b, t);
-      } else {
-        W::transpose(st.b1, t);
-      }
+      block_transpose<INT8, GROUPED>(st.b1, m1, t);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc1[mt][c] = mfma16x16x32(st.a[mt], t[c], acc1[mt][c]);
-      if constexpr (GROUPED) {
-        typename W::T b[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) b[r] = st.b2[r] & mv;
-        W::transpose(b, t);
-      } else {
-        W::transpose(st.b2, t);
-      }
+      block_transpose<INT8, GROUPED>(st.b2, mv, t);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -164,23 +167,35 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
     };
 
     // d is a multiple of 64: two 32-deep steps per iteration, the next step's loads in flight during compute.
-    // group boundaries (GROUPED) are multiples of 64 rows, so they fall on iteration starts.
     UpStep<INT8, MT> sa, sb;
-    int gnext = 0;  // GROUPED: first row of the next group
-    load(sa, 0);
-    for (int k0 = 0; k0 < d; k0 += 64) {
-      if (GROUPED && k0 == gnext) {
-        enter_group(k0 / sl.gsize, k0 != 0);
-        gnext += sl.gsize;
+    auto steps = [&](int klo, int khi) {
+      for (int k0 = klo; k0 < khi; k0 += 64) {
+        load(sb, k0 + 32);
+        compute(sa);
+        if (k0 + 64 < d) load(sa, k0 + 64);
+        compute(sb);
       }
-      load(sb, k0 + 32);
-      compute(sa);
-      if (k0 + 64 < d) load(sa, k0 + 64);
-      compute(sb);
+    };
+    load(sa, 0);
+    if constexpr (GROUPED) {
+      // group boundaries are multiples of 64 rows: each group is a whole number of iterations
+      const int ng = d / sl.gsize;
+      pend1 = load_raw8(s1e);
+      pendv = load_raw8(sve);
+      for (int gi = 0; gi < ng; ++gi) {
+        enter_group(gi > 0);
+        if (gi + 1 < ng) {
+          pend1 = load_raw8(s1e + size_t(gi + 1) * f);
+          pendv = load_raw8(sve + size_t(gi + 1) * f);
+        }
+        steps(gi * sl.gsize, (gi + 1) * sl.gsize);
+      }
+    } else {
+      steps(0, d);
     }
 
     float sc1[8], scv[8];
-    if (GROUPED) {
+    if (GROUPED) {  // the accumulators are in units of the last group's scale
 #pragma unroll
       for (int c = 0; c < 8; ++c) { sc1[c] = cur1[c]; scv[c] = curv[c]; }
     } else if (INT8) {
@@ -261,11 +276,14 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
       for (int mt = 0; mt < MT; ++mt)
         st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
     };
-    float cur[8];  // GROUPED: the current group's scales (zero replaced by one)
-    u32x2_t msk;   // GROUPED: byte mask of the columns with a non-zero scale in the current group
-    auto enter_group = [&](int grp, bool rescale) {
+    // GROUPED: the current group's scales (zero replaced by one), the byte mask of its columns with a non-zero
+    // scale, and the raw scales of the next group (loaded a group ahead)
+    float cur[8];
+    u32x2_t msk;
+    u32x4_t pend;
+    auto enter_group = [&](bool rescale) {
       float ns[8];
-      group_scales8(s2e + size_t(grp) * d, ns, msk);
+      group_scales8(pend, ns, msk);
       if (rescale) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -279,14 +297,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
     };
     auto compute = [&](const DownStep<INT8, MT>& st) {
       u32x4_t t[8];
-      if constexpr (GROUPED) {
-        typename W::T b[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) b[r] = st.b[r] & msk;
-        W::transpose(b, t);
-      } else {
-        W::transpose(st.b, t);
-      }
+      block_transpose<INT8, GROUPED>(st.b, msk, t);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -295,22 +306,30 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 
     DownStep<INT8, MT> sa, sb;
     const int kend = kbeg + kchunk;  // kchunk is a multiple of 64
-    int gnext = kbeg;                // GROUPED: the chunk starts inside group kbeg / gsize
-    load(sa, kbeg);
-    for (int k0 = kbeg; k0 < kend; k0 += 64) {
-      if (GROUPED && k0 == gnext) {
-        const int grp = k0 / sl.gsize;
-        enter_group(grp, k0 != kbeg);
-        gnext = (grp + 1) * sl.gsize;
+    auto steps = [&](int klo, int khi) {
+      for (int k0 = klo; k0 < khi; k0 += 64) {
+        load(sb, k0 + 32);
+        compute(sa);
+        if (k0 + 64 < kend) load(sa, k0 + 64);
+        compute(sb);
       }
-      load(sb, k0 + 32);
-      compute(sa);
-      if (k0 + 64 < kend) load(sa, k0 + 64);
-      compute(sb);
+    };
+    load(sa, kbeg);
+    if constexpr (GROUPED) {
+      // the chunk [kbeg, kend) meets groups g0 .. g1 (boundaries are multiples of 64 rows)
+      const int g0 = kbeg / sl.gsize, g1 = (kend - 1) / sl.gsize;
+      pend = load_raw8(s2e + size_t(g0) * d);
+      for (int gi = g0; gi <= g1; ++gi) {
+        enter_group(gi > g0);
+        if (gi < g1) pend = load_raw8(s2e + size_t(gi + 1) * d);
+        steps(max(kbeg, gi * sl.gsize), min(kend, (gi + 1) * sl.gsize));
+      }
+    } else {
+      steps(kbeg, kend);
     }
 
     float sc[8];
-    if (GROUPED) {
+    if (GROUPED) {  // the accumulators are in units of the chunk's last group's scale
 #pragma unroll
       for (int c = 0; c < 8; ++c) sc[c] = cur[c];
     } else if (INT8) {
