@@ -26,8 +26,9 @@ Readings where the pages leave a step open (each is also listed in the design no
     renormalised over the two ([moe] returns top_k of the full softmax and multiplies by it).
   * Selection is by descending logit with the lower expert index first on equal logits (softmax is strictly
     increasing, so this equals selecting on the probabilities, without ties created by rounding them).
-  * Weights are stored [E, in, out]: W1, Wv are [E, d, f], W2 is [E, f, d]; int8 scales are [Es, G, out] with
-    Es = E (per expert) or 1 (shared) and G contiguous groups along the in axis (G = 1: per output channel).
+  * Weights are stored [E, in, out]: W1, Wv are [E, d, f], W2 is [E, f, d] (the checkpoint's JAX layout), or, on
+    request, [E, out, in] (the PyTorch layout [card] converts to); int8 scales are [Es, G, out] with Es = E (per
+    expert) or 1 (shared) and G contiguous groups along the in axis (G = 1: per output channel).
   * In the bf16 and int8 layers the intermediate h = GELU(a) ⊙ b is rounded once to bf16 (round to nearest
     even, directly from float64) before the down projection; the fp32 layer keeps h unrounded.
   * The optional per-expert router bias is added to the logits before the softmax.
@@ -45,8 +46,8 @@ import torch
 F32, BF16, W8 = 0, 1, 2
 
 __all__ = [
-    "F32", "BF16", "W8", "as_f64", "bf16_round", "gelu", "route", "expert_ffn", "dequant", "expert_scales",
-    "forward", "rmsnorm", "block_forward",
+    "F32", "BF16", "W8", "IN_OUT", "OUT_IN", "as_f64", "bf16_round", "gelu", "route", "expert_ffn", "dequant",
+    "expert_scales", "stored_in_out", "forward", "rmsnorm", "block_forward",
 ]
 
 
@@ -149,19 +150,35 @@ def expert_scales(s, e: int) -> np.ndarray:
     return s[e if s.shape[0] > 1 else 0]
 
 
-def _expert_weights(inp: dict, dtype: int, e: int):
+IN_OUT, OUT_IN = "in_out", "out_in"
+
+
+def stored_in_out(w, layout: str):
+    """Expert e's weight as [in, out] from its stored form: [in, out] as in the checkpoint (JAX), or [out, in] as
+    after [card]'s conversion to the PyTorch convention (then it is the transpose)."""
+    if layout == IN_OUT:
+        return w
+    if layout == OUT_IN:
+        return np.asarray(w).T
+    raise ValueError(layout)
+
+
+def _expert_weights(inp: dict, dtype: int, e: int, layout: str = IN_OUT):
+    w = {n: stored_in_out(inp[n][e], layout) for n in ("w1", "wv", "w2")}
     if dtype == F32:
-        return tuple(as_f64(inp[n][e], "f32") for n in ("w1", "wv", "w2"))
+        return tuple(as_f64(w[n], "f32") for n in ("w1", "wv", "w2"))
     if dtype == BF16:
-        return tuple(as_f64(inp[n][e], "bf16") for n in ("w1", "wv", "w2"))
+        return tuple(as_f64(w[n], "bf16") for n in ("w1", "wv", "w2"))
     if dtype == W8:
-        return tuple(dequant(inp[n][e], expert_scales(inp[sn], e)) for n, sn in (("w1", "s1"), ("wv", "sv"),
-                                                                                  ("w2", "s2")))
+        return tuple(dequant(w[n], expert_scales(inp[sn], e)) for n, sn in (("w1", "s1"), ("wv", "sv"), ("w2", "s2")))
     raise ValueError(dtype)
 
 
-def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False) -> dict:
+def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False, layout: str = IN_OUT) -> dict:
     """The whole layer: routing on every token, expert FFNs and combine on ``rows`` (all rows if None).
+
+    layout: how the expert weights are stored, IN_OUT (W1, Wv [E, d, f], W2 [E, f, d]) or OUT_IN (W1, Wv
+    [E, f, d], W2 [E, d, f]); int8 scales are [Es, G, out] either way.
 
     inp: dict of numpy arrays as produced by ``synth.make_inputs`` (x, router_w, w1, wv, w2, s1, sv, s2,
     router_bias).  Returns float64 tensors: out [len(rows), d]; idx [T, k]; p [T, k]; counts [E]; logits; probs;
@@ -181,7 +198,7 @@ def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False
     n = rows.numel()
     sel = idx[rows]  # [n, k]
     out = torch.zeros((n, d), dtype=torch.float64)
-    f = inp["w1"].shape[2]
+    f = inp["w1"].shape[2] if layout == IN_OUT else inp["w1"].shape[1]
     hs = torch.zeros((n, k, f), dtype=torch.float64) if return_h else None
     ys = torch.zeros((n, k, d), dtype=torch.float64) if return_h else None
     round_h = dtype != F32
@@ -190,7 +207,7 @@ def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False
         hit = (sel == e).nonzero()  # (row position, slot j) pairs choosing expert e
         if hit.numel() == 0:
             continue
-        w1, wv, w2 = _expert_weights(inp, dtype, e)
+        w1, wv, w2 = _expert_weights(inp, dtype, e, layout)
         h, y = expert_ffn(x[rows[hit[:, 0]]], w1, wv, w2, round_h)
         del w1, wv, w2
         ys_all[hit[:, 0], hit[:, 1]] = y
@@ -213,7 +230,8 @@ def rmsnorm(v: torch.Tensor, scale: torch.Tensor, eps: float) -> torch.Tensor:
     return v / torch.sqrt((v * v).mean(dim=-1, keepdim=True) + eps) * scale
 
 
-def block_forward(inp: dict, dtype: int, pre_scale, post_scale, eps: float, rows=None, k: int = 2) -> dict:
+def block_forward(inp: dict, dtype: int, pre_scale, post_scale, eps: float, rows=None, k: int = 2,
+                  layout: str = IN_OUT) -> dict:
     """The MoE part of a Grok-1 layer with its two norms and the residual:
     out = x + RMSNorm_post(MoE(RMSNorm_pre(x))).
 
@@ -233,7 +251,7 @@ def block_forward(inp: dict, dtype: int, pre_scale, post_scale, eps: float, rows
         xn_stored = _to_bf16_bits(bf16_round(xn))
     inner = dict(inp)
     inner["x"] = xn_stored
-    r = forward(inner, dtype, rows=rows, k=k)
+    r = forward(inner, dtype, rows=rows, k=k, layout=layout)
     rows_t = r["rows"]
     moe = r["out"]
     r["moe_out"] = moe

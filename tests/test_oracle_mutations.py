@@ -1,11 +1,13 @@
 """Plant plausible mistakes in the oracle (on the CPU, via monkeypatch) and check that a pin catches each one."""
 import math
 
+import numpy as np
 import pytest
 import torch
 
 import oracle
 import oracle.grok_moe_oracle as om
+import synth
 from tests import test_oracle_pins as pins
 
 
@@ -171,3 +173,19 @@ def test_grouped_scale_mistakes_are_caught(bad, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught >= 1
+
+
+def _reshaped_not_transposed(w, layout):
+    """Planted mistake: the [out, in] storage reshaped to [in, out] instead of transposed."""
+    w = np.asarray(w)
+    return w if layout == om.IN_OUT else w.reshape(w.shape[::-1])
+
+
+def test_out_in_layout_mistake_is_caught(monkeypatch):
+    from tests import test_oracle_layout_pins as lp
+    monkeypatch.setattr(om, "stored_in_out", _reshaped_not_transposed)
+    monkeypatch.setattr(oracle, "stored_in_out", _reshaped_not_transposed)
+    with pytest.raises(AssertionError):
+        lp.test_selection_matrices_closed_form()
+    with pytest.raises(AssertionError):
+        lp.test_transposed_storage_is_the_same_layer(synth.BF16, 1, 1)
