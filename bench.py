@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--block", action="store_true",
                     help="time the MoE block (pre-MoE RMSNorm, MoE, post-MoE RMSNorm, residual) instead of the layer")
+    ap.add_argument("--weight-layout", choices=["in_out", "out_in"], default="in_out",
+                    help="expert weights stored [E, in, out] (checkpoint) or [E, out, in] (converted); same values")
     ap.add_argument("--library-gemm", action="store_true",
                     help="only time torch.matmul (hipBLASLt) bf16 on the prefill's per-expert GEMM shapes, for context")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -64,8 +66,13 @@ def parse():
 class Layer:
     """Device-resident inputs and preallocated buffers of one workload, and the timed step."""
 
-    def __init__(self, gm, w, inp, dv, norms=None):
+    def __init__(self, gm, w, inp, dv, norms=None, weight_layout="in_out", transpose=True):
         import torch
+        self.outin = weight_layout == "out_in"
+        if self.outin and transpose:  # the same weights stored [E, out, in] (transposed on the device, untimed)
+            dv = dict(dv)
+            for n in ("w1", "wv", "w2"):
+                dv[n] = dv[n].transpose(1, 2).contiguous()
         self.gm, self.w, self.inp, self.dv = gm, w, inp, dv
         self.norms = norms  # (pre_scale, post_scale, eps) device tensors for the block form
         T, d, f, E = w.T, w.d, w.f, w.E
@@ -113,7 +120,12 @@ class Layer:
         st |= L.grok_moe_bin(P(self.idx), T, E, 2, P(self.counts), P(self.offsets), P(self.perm), P(self.inv), s)
         if timed:
             ev[1].record()
-        if self.grouped is None:
+        es, g1, g2 = self.grouped if self.grouped is not None else (E, 1, 1)
+        if self.outin:
+            st |= L.grok_moe_expert_up_ex(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), 1, es, g1,
+                                          P(self.counts), P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h),
+                                          s)
+        elif self.grouped is None:
             st |= L.grok_moe_expert_up(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), P(self.counts),
                                        P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
         else:
@@ -122,7 +134,10 @@ class Layer:
                                                   P(self.perm), T, d, f, E, 2, P(self.h), s)
         if timed:
             ev[2].record()
-        if self.grouped is None:
+        if self.outin:
+            st |= L.grok_moe_expert_down_ex(P(self.h), P(dv["w2"]), P(self.s2), 1, es, g2, P(self.counts),
+                                            P(self.offsets), T, d, f, E, 2, dt, self.S, P(self.y), s)
+        elif self.grouped is None:
             st |= L.grok_moe_expert_down(P(self.h), P(dv["w2"]), P(self.s2), P(self.counts), P(self.offsets), T, d,
                                          f, E, 2, dt, self.S, P(self.y), s)
         else:
@@ -295,24 +310,26 @@ def main():
         else:
             conv = lambda v: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
         norms = (conv(ns["pre_scale"]), conv(ns["post_scale"]), ns["eps"])
-    layer = Layer(gm, w, inp, dv, norms)
+    layer = Layer(gm, w, inp, dv, norms, a.weight_layout)
     wall, kms = layer.run_with_kernel_times(a.steps, a.warmup)
     ms = wall * 1e3 / a.steps
     nh = n_hit(layer)
     T = w.T
+    tname = w.name + ("_out_in" if a.weight_layout == "out_in" else "")  # the expert kernels' workload
+    wname = tname + ("_block" if a.block else "")
     res = {"metric": METRIC, "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": {0: "f32", 1: "bf16", 2: "bf16 x int8-weight"}[w.dtype], "data": "synthetic",
-           "config": {"workload": w.name + ("_block" if a.block else ""), "T": T, "d_model": w.d, "d_ff": w.f,
+           "config": {"workload": wname, "T": T, "d_model": w.d, "d_ff": w.f,
                       "experts": w.E, "top_k": 2, "experts_hit": nh, "down_splits": layer.S,
-                      "rmsnorm_residual": bool(a.block)}}
+                      "rmsnorm_residual": bool(a.block), "weight_layout": a.weight_layout}}
     kernels = {"expert_up_ms": kms[0], "expert_down_ms": kms[1], "route_bin_ms": kms[2], "combine_ms": kms[3]}
     if w.T <= 64:  # weight-streaming regime: HBM-bound, the up-projection (W1 and Wv) is the dominant kernel
         ub = up_bytes(w, nh, T)
         ach = ub / (kms[0] * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "up_stream_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": load_traffic(w.name, "up"), "algorithmic_bytes": ub}
+                           "traffic": load_traffic(tname, "up"), "algorithmic_bytes": ub}
         db = down_bytes(w, nh, T, layer.S)
         kernels["expert_down_GBps"] = db / (kms[1] * 1e-3) / 1e9
         kernels["layer_GBps"] = (ub + db) / (ms * 1e-3) / 1e9
@@ -321,7 +338,7 @@ def main():
         ach = fl / (kms[0] * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": "tiled_dma_kernel<2>" if w.dtype == 1 else "tiled_reg_kernel<2>", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
-                           "traffic": load_traffic(w.name, "up"), "algorithmic_flops": fl}
+                           "traffic": load_traffic(tname, "up"), "algorithmic_flops": fl}
         kernels["layer_TFLOPs"] = 3 * fl / 2 / (ms * 1e-3) / 1e12
     res["kernels"] = kernels
     log(f"{w.name}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down {kms[1]:.3f} ms")
@@ -329,19 +346,20 @@ def main():
     if not a.no_prefill and w.name == "decode_bf16" and not a.block:
         pw = synth.WORKLOADS["prefill_bf16"]
         pinp = synth.make_inputs(pw, weights=wts)
-        pdv = dict(dv)
+        pdv = dict(layer.dv)  # the decode layer's weights, already in the chosen layout
         pdv["x"] = dev_inputs({**pinp, "w1": None, "wv": None, "w2": None}, synth.BF16)["x"]
-        pl = Layer(gm, pw, pinp, pdv)
+        pl = Layer(gm, pw, pinp, pdv, None, a.weight_layout, transpose=False)
+        pname = pw.name + ("_out_in" if a.weight_layout == "out_in" else "")
         pwall, pk = pl.run_with_kernel_times(a.prefill_steps, 2)
         pms = pwall * 1e3 / a.prefill_steps
         fl = up_flops(pw, pw.T)
-        res["prefill"] = {"workload": pw.name, "T": pw.T, "value": pw.T / (pms / 1e3), "unit": "tokens/s",
+        res["prefill"] = {"workload": pname, "T": pw.T, "value": pw.T / (pms / 1e3), "unit": "tokens/s",
                           "ms_per_step": pms, "steps": a.prefill_steps,
                           "layer_TFLOPs": 3 * fl / 2 / (pms * 1e-3) / 1e12,
                           "roofline": {"bound": "mfma", "kernel": "tiled_dma_kernel<2>",
                                        "achieved": fl / (pk[0] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": fl / (pk[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                                       "traffic": load_traffic(pw.name, "up"), "algorithmic_flops": fl},
+                                       "traffic": load_traffic(pname, "up"), "algorithmic_flops": fl},
                           "kernels": {"expert_up_ms": pk[0], "expert_down_ms": pk[1], "route_bin_ms": pk[2],
                                       "combine_ms": pk[3],
                                       "expert_down_TFLOPs": fl / 2 / (pk[1] * 1e-3) / 1e12}}

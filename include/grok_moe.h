@@ -187,6 +187,35 @@ int grok_moe_expert_down_w8_grouped(const void* h, const void* w2, const void* s
                                     int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T,
                                     int64_t d, int64_t f, int E, int k, int splits, float* y, void* stream);
 
+/* ---- Weight storage [E, out, in], and the general forms of the layer and of its two expert steps ----------------
+ * Page "Grok-1-BF16", section "Conversion Details": the checkpoint stores weights in JAX's [in, out] convention
+ * and the conversion transposes them to PyTorch's [out, in].  weight_layout selects which one W1, Wv, W2 use:
+ *   GROK_MOE_IN_OUT: W1, Wv [E, d, f], W2 [E, f, d] (the layout of every other entry point);
+ *   GROK_MOE_OUT_IN: W1, Wv [E, f, d], W2 [E, d, f].
+ * Either way int8 scales are [scale_experts, groups, out] (out = f for W1/Wv, d for W2), grouped along the input
+ * axis as described above; scale_experts and the group counts are ignored unless dtype is GROK_MOE_W8.  An unknown
+ * weight_layout returns GROK_MOE_EINVAL.  The result is bit-identical to the [in, out] form on the same weights:
+ * the kernels multiply the same operands in the same order. */
+typedef enum { GROK_MOE_IN_OUT = 0, GROK_MOE_OUT_IN = 1 } grok_moe_layout;
+
+/* The whole layer; otherwise as grok_moe_forward. */
+int grok_moe_forward_ex(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                        const void* s1, const void* sv, const void* s2, int weight_layout, int scale_experts,
+                        int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                        float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                        int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step: the fused up-projection; otherwise as grok_moe_expert_up. */
+int grok_moe_expert_up_ex(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                          int weight_layout, int scale_experts, int groups_up, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k,
+                          int dtype, void* h, void* stream);
+
+/* Step: the down-projection; otherwise as grok_moe_expert_down. */
+int grok_moe_expert_down_ex(const void* h, const void* w2, const void* s2, int weight_layout, int scale_experts,
+                            int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T, int64_t d,
+                            int64_t f, int E, int k, int dtype, int splits, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "F32", "BF16", "W8", "LIB_PATH", "lib", "forward", "route", "bin_tokens", "expert_up", "expert_down",
     "combine", "workspace_size", "down_splits", "strerror", "dtype_of", "GrokMoeError", "block_forward",
-    "block_workspace_size", "route_norm", "combine_norm",
+    "block_workspace_size", "route_norm", "combine_norm", "IN_OUT", "OUT_IN", "scale_layout",
 ]
 
 F32, BF16, W8 = 0, 1, 2
@@ -51,7 +51,23 @@ _SIGS = {
                                       + [_i64, _i64, _i64, _int, _int, _c_void_p, _c_void_p]),
     "grok_moe_expert_down_w8_grouped": (_int, [_c_void_p] * 3 + [_int, _int] + [_c_void_p] * 2
                                         + [_i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p]),
+    "grok_moe_forward_ex": (_int, [_c_void_p] * 8 + [_int, _int, _int, _int, _i64, _i64, _i64, _int, _int, _int]
+                            + [_c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]),
+    "grok_moe_expert_up_ex": (_int, [_c_void_p] * 5 + [_int, _int, _int] + [_c_void_p] * 3
+                              + [_i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p]),
+    "grok_moe_expert_down_ex": (_int, [_c_void_p] * 3 + [_int, _int, _int] + [_c_void_p] * 2
+                                + [_i64, _i64, _i64, _int, _int, _int, _int, _c_void_p, _c_void_p]),
 }
+
+# weight storage: [E, in, out] (the checkpoint's JAX layout) or [E, out, in] (the converted PyTorch layout)
+IN_OUT, OUT_IN = "in_out", "out_in"
+_LAYOUT = {IN_OUT: 0, OUT_IN: 1}
+
+
+def _layout_code(weight_layout: str) -> int:
+    if weight_layout not in _LAYOUT:
+        raise GrokMoeError(f"weight_layout must be {IN_OUT!r} or {OUT_IN!r}, not {weight_layout!r}")
+    return _LAYOUT[weight_layout]
 
 _lib = None
 
@@ -122,10 +138,16 @@ def down_splits(T: int, d: int, f: int, E: int = 8, k: int = 2, dtype: int = BF1
     return int(lib().grok_moe_down_splits(T, d, f, E, k, dtype))
 
 
-def _layer_shapes(x, router_w, w1, wv, w2):
+def _layer_shapes(x, router_w, w1, wv, w2, weight_layout=IN_OUT):
     T, d = x.shape
-    E, d2, f = w1.shape
-    if router_w.shape != (E, d) or d2 != d or wv.shape != (E, d, f) or w2.shape != (E, f, d):
+    if _layout_code(weight_layout) == 0:
+        E, d2, f = w1.shape
+        up, down = (E, d, f), (E, f, d)
+    else:
+        E, f, d2 = w1.shape
+        up, down = (E, f, d), (E, d, f)
+    if (router_w.shape != (E, d) or d2 != d or tuple(w1.shape) != up or tuple(wv.shape) != up
+            or tuple(w2.shape) != down):
         raise GrokMoeError(f"inconsistent shapes x{tuple(x.shape)} router_w{tuple(router_w.shape)} "
                            f"w1{tuple(w1.shape)} wv{tuple(wv.shape)} w2{tuple(w2.shape)}")
     return T, d, f, E
@@ -155,11 +177,14 @@ def _grouped(scales, E, d, f):
     return l1[0], l1[1], l2[1]
 
 
-def forward(x, router_w, w1, wv, w2, scales=None, router_bias=None, return_routing=False, workspace=None):
+def forward(x, router_w, w1, wv, w2, scales=None, router_bias=None, return_routing=False, workspace=None,
+            weight_layout=IN_OUT):
     """The whole layer.  Returns out [T, d] fp32, or (out, topk_idx [T,2] int32, topk_p [T,2] fp32,
     expert_counts [E] int32) if return_routing.  scales = (s1, sv, s2) for int8 weights, each [Es, G, out] or
-    [Es, out] bf16 (Es = E or 1 shared; G groups along the input axis)."""
-    T, d, f, E = _layer_shapes(x, router_w, w1, wv, w2)
+    [Es, out] bf16 (Es = E or 1 shared; G groups along the input axis).  weight_layout: IN_OUT (W1, Wv [E, d, f],
+    W2 [E, f, d]) or OUT_IN (W1, Wv [E, f, d], W2 [E, d, f])."""
+    T, d, f, E = _layer_shapes(x, router_w, w1, wv, w2, weight_layout)
+    lay = _layout_code(weight_layout)
     dt = dtype_of(x, w1)
     for t, n in ((x, "x"), (router_w, "router_w"), (w1, "w1"), (wv, "wv"), (w2, "w2")):
         _need(t, n)
@@ -180,7 +205,13 @@ def forward(x, router_w, w1, wv, w2, scales=None, router_bias=None, return_routi
     need = workspace_size(T, d, f, E, 2, dt)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    if grouped is None:
+    if lay != 0:
+        es, g1, g2 = grouped if grouped is not None else (E, 1, 1)
+        st = lib().grok_moe_forward_ex(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), lay, es,
+                                       g1, g2, T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
+                                       _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+        _check(st, "grok_moe_forward_ex")
+    elif grouped is None:
         st = lib().grok_moe_forward(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
                                     T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
                                     _p(workspace), workspace.numel() * workspace.element_size(), _stream())
@@ -224,10 +255,11 @@ def bin_tokens(topk_idx, E: int):
     return counts, offsets, perm, inv
 
 
-def expert_up(x, w1, wv, counts, offsets, perm, scales=None, h=None):
+def expert_up(x, w1, wv, counts, offsets, perm, scales=None, h=None, weight_layout=IN_OUT):
     """Fused up-projection step: h [2T, f] (bf16, or fp32 for an fp32 layer) in slot order."""
     T, d = x.shape
-    E, _, f = w1.shape
+    lcode = _layout_code(weight_layout)
+    E, f = (w1.shape[0], w1.shape[2]) if lcode == 0 else (w1.shape[0], w1.shape[1])
     dt = dtype_of(x, w1)
     s1 = sv = None
     lay = (E, 1)
@@ -238,7 +270,11 @@ def expert_up(x, w1, wv, counts, offsets, perm, scales=None, h=None):
             raise GrokMoeError("s1 and sv need the same layout")
     if h is None:
         h = torch.empty((2 * T, f), dtype=torch.float32 if dt == F32 else torch.bfloat16, device=x.device)
-    if lay == (E, 1):
+    if lcode != 0:
+        _check(lib().grok_moe_expert_up_ex(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), lcode, *lay, _p(counts),
+                                           _p(offsets), _p(perm), T, d, f, E, 2, dt, _p(h), _stream()),
+               "grok_moe_expert_up_ex")
+    elif lay == (E, 1):
         _check(lib().grok_moe_expert_up(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), _p(counts), _p(offsets), _p(perm),
                                         T, d, f, E, 2, dt, _p(h), _stream()), "grok_moe_expert_up")
     else:
@@ -248,15 +284,19 @@ def expert_up(x, w1, wv, counts, offsets, perm, scales=None, h=None):
     return h
 
 
-def expert_down(h, w2, counts, offsets, T: int, x_dtype, s2=None, y=None):
+def expert_down(h, w2, counts, offsets, T: int, x_dtype, s2=None, y=None, weight_layout=IN_OUT):
     """Down-projection step: y [S, 2T, d] fp32 partial sums (S = down_splits)."""
-    E, f, d = w2.shape
+    lcode = _layout_code(weight_layout)
+    E, f, d = w2.shape if lcode == 0 else (w2.shape[0], w2.shape[2], w2.shape[1])
     dt = F32 if w2.dtype == torch.float32 else (W8 if w2.dtype == torch.int8 else BF16)
     S = down_splits(T, d, f, E, 2, dt)
     if y is None:
         y = torch.empty((S, 2 * T, d), dtype=torch.float32, device=h.device)
     lay = scale_layout(s2, E, d, "s2") if dt == W8 else (E, 1)
-    if lay == (E, 1):
+    if lcode != 0:
+        _check(lib().grok_moe_expert_down_ex(_p(h), _p(w2), _p(s2), lcode, *lay, _p(counts), _p(offsets), T, d, f, E,
+                                             2, dt, S, _p(y), _stream()), "grok_moe_expert_down_ex")
+    elif lay == (E, 1):
         _check(lib().grok_moe_expert_down(_p(h), _p(w2), _p(s2), _p(counts), _p(offsets), T, d, f, E, 2, dt, S,
                                           _p(y), _stream()), "grok_moe_expert_down")
     else:

@@ -76,12 +76,18 @@ int check_scales(int dtype, const void* s1, const void* sv, const void* s2) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? GROK_MOE_OK : GROK_MOE_EHIP; }
 
-// int8 scale tensors [scale_experts, groups, out]; the default layout is per expert with one group.
+// Weight storage ([E, in, out] or [E, out, in]) and int8 scale tensors [scale_experts, groups, out]; the default
+// is [E, in, out] with per-expert scales of one group.
 struct ScaleSpec {
   int experts;  // 1 (shared by all experts) or E
   int g_up;     // groups along d of W1 / Wv
   int g_down;   // groups along f of W2
+  bool outin = false;  // weights stored [E, out, in]
 };
+
+inline bool ok_layout(int weight_layout) {
+  return weight_layout == GROK_MOE_IN_OUT || weight_layout == GROK_MOE_OUT_IN;
+}
 
 int check_groups(const ScaleSpec& sp, int64_t d, int64_t f, int E) {
   if ((sp.experts != 1 && sp.experts != E) || sp.g_up < 1 || sp.g_down < 1) return GROK_MOE_EINVAL;
@@ -103,32 +109,32 @@ hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, 
                  int64_t f, int E, int dtype, void* h, hipStream_t s) {
   if (dtype == GROK_MOE_F32)
     return gm::launch_up_f32(static_cast<const float*>(x), static_cast<const float*>(w1),
-                             static_cast<const float*>(wv), counts, offsets, perm, int(d), int(f), E, int(p.slots),
-                             static_cast<float*>(h), s);
+                             static_cast<const float*>(wv), sp.outin, counts, offsets, perm, int(d), int(f), E,
+                             int(p.slots), static_cast<float*>(h), s);
   const bool i8 = dtype == GROK_MOE_W8;
   if (p.stream)
     return gm::launch_up_stream(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
-                                static_cast<const uint16_t*>(sv), up_layout(sp, d, f), counts, offsets, perm, int(d),
-                                int(f), E, i8, p.mt, static_cast<uint16_t*>(h), s);
+                                static_cast<const uint16_t*>(sv), up_layout(sp, d, f), sp.outin, counts, offsets,
+                                perm, int(d), int(f), E, i8, p.mt, static_cast<uint16_t*>(h), s);
   return gm::launch_up_tiled(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
-                             static_cast<const uint16_t*>(sv), up_layout(sp, d, f), counts, offsets, perm, int(d),
-                             int(f), E, int(p.slots), i8, static_cast<uint16_t*>(h), s);
+                             static_cast<const uint16_t*>(sv), up_layout(sp, d, f), sp.outin, counts, offsets, perm,
+                             int(d), int(f), E, int(p.slots), i8, static_cast<uint16_t*>(h), s);
 }
 
 hipError_t do_down(const void* h, const void* w2, const void* s2, const ScaleSpec& sp, const int32_t* counts,
                    const int32_t* offsets, const Plan& p, int64_t d, int64_t f, int E, int dtype, float* y,
                    hipStream_t s) {
   if (dtype == GROK_MOE_F32)
-    return gm::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2), counts, offsets, int(d),
-                               int(f), E, int(p.slots), y, s);
+    return gm::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2), sp.outin, counts,
+                               offsets, int(d), int(f), E, int(p.slots), y, s);
   const bool i8 = dtype == GROK_MOE_W8;
   if (p.stream)
     return gm::launch_down_stream(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),
-                                  down_layout(sp, d, f), counts, offsets, int(d), int(f), E, int(p.slots), p.splits,
-                                  i8, p.mt, y, s);
+                                  down_layout(sp, d, f), sp.outin, counts, offsets, int(d), int(f), E, int(p.slots),
+                                  p.splits, i8, p.mt, y, s);
   return gm::launch_down_tiled(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),
-                               down_layout(sp, d, f), counts, offsets, int(d), int(f), E, int(p.slots), p.splits, i8,
-                               y, s);
+                               down_layout(sp, d, f), sp.outin, counts, offsets, int(d), int(f), E, int(p.slots),
+                               p.splits, i8, y, s);
 }
 
 // The whole layer (grok_moe_forward and its grouped-scale form); arguments validated by the caller.
@@ -187,19 +193,36 @@ int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtyp
   return make_plan(T, d, f, E, dtype).splits;
 }
 
-int grok_moe_forward(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
-                     const void* s1, const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k,
-                     int dtype, float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+int grok_moe_forward_ex(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                        const void* s1, const void* sv, const void* s2, int weight_layout, int scale_experts,
+                        int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                        float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                        int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
+  if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
+  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
+  if (dtype == GROK_MOE_W8) {
+    sp.experts = scale_experts;
+    sp.g_up = groups_up;
+    sp.g_down = groups_down;
+    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
+  }
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(w2) || !ok_ptr(out))
     return GROK_MOE_EINVAL;
   if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
   if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
-  return run_layer(x, router_w, w1, wv, w2, s1, sv, s2, ScaleSpec{E, 1, 1}, T, d, f, E, dtype, out, router_bias,
-                   topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
+  return run_layer(x, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, dtype, out, router_bias, topk_idx, topk_p,
+                   expert_counts, workspace, workspace_bytes, stream);
+}
+
+int grok_moe_forward(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                     const void* s1, const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k,
+                     int dtype, float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  return grok_moe_forward_ex(x, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, E, 1, 1, T, d, f, E, k, dtype,
+                             out, router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
 }
 
 int grok_moe_forward_w8_grouped(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
@@ -207,17 +230,9 @@ int grok_moe_forward_w8_grouped(const void* x, const void* router_w, const void*
                                 int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, float* out,
                                 const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_shape(T, d, f, E, k, GROK_MOE_W8);
-  if (st != GROK_MOE_OK) return st;
-  const ScaleSpec sp{scale_experts, groups_up, groups_down};
-  if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
-  if (T == 0) return GROK_MOE_OK;
-  if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(w2) || !ok_ptr(out))
-    return GROK_MOE_EINVAL;
-  if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
-  if ((st = check_scales(GROK_MOE_W8, s1, sv, s2)) != GROK_MOE_OK) return st;
-  return run_layer(x, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, GROK_MOE_W8, out, router_bias, topk_idx,
-                   topk_p, expert_counts, workspace, workspace_bytes, stream);
+  return grok_moe_forward_ex(x, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, scale_experts, groups_up,
+                             groups_down, T, d, f, E, k, GROK_MOE_W8, out, router_bias, topk_idx, topk_p,
+                             expert_counts, workspace, workspace_bytes, stream);
 }
 
 int grok_moe_route(const void* x, const void* router_w, const float* router_bias, int64_t T, int64_t d, int E, int k,
@@ -240,64 +255,74 @@ int grok_moe_bin(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* coun
   return hip_status(gm::launch_bin(topk_idx, int(T), E, counts, offsets, perm, inv, static_cast<hipStream_t>(stream)));
 }
 
-int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
-                       const int32_t* counts, const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d,
-                       int64_t f, int E, int k, int dtype, void* h, void* stream) {
+int grok_moe_expert_up_ex(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                          int weight_layout, int scale_experts, int groups_up, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k,
+                          int dtype, void* h, void* stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
+  if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
+  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
+  if (dtype == GROK_MOE_W8) {
+    sp.experts = scale_experts;
+    sp.g_up = groups_up;
+    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
+  }
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(perm) || !ok_ptr(h))
     return GROK_MOE_EINVAL;
   if ((st = check_scales(dtype, s1, sv, dtype == GROK_MOE_W8 ? s1 : nullptr)) != GROK_MOE_OK) return st;
   const Plan p = make_plan(T, d, f, E, dtype);
-  return hip_status(do_up(x, w1, wv, s1, sv, ScaleSpec{E, 1, 1}, counts, offsets, perm, p, d, f, E, dtype, h,
+  return hip_status(do_up(x, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h,
                           static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d,
+                       int64_t f, int E, int k, int dtype, void* h, void* stream) {
+  return grok_moe_expert_up_ex(x, w1, wv, s1, sv, GROK_MOE_IN_OUT, E, 1, counts, offsets, perm, T, d, f, E, k, dtype,
+                               h, stream);
 }
 
 int grok_moe_expert_up_w8_grouped(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
                                   int scale_experts, int groups_up, const int32_t* counts, const int32_t* offsets,
                                   const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k, void* h,
                                   void* stream) {
-  int st = check_shape(T, d, f, E, k, GROK_MOE_W8);
-  if (st != GROK_MOE_OK) return st;
-  const ScaleSpec sp{scale_experts, groups_up, 1};
-  if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
-  if (T == 0) return GROK_MOE_OK;
-  if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(perm) ||
-      !ok_ptr(h) || !ok_ptr(s1) || !ok_ptr(sv))
-    return GROK_MOE_EINVAL;
-  const Plan p = make_plan(T, d, f, E, GROK_MOE_W8);
-  return hip_status(do_up(x, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, GROK_MOE_W8, h,
-                          static_cast<hipStream_t>(stream)));
+  return grok_moe_expert_up_ex(x, w1, wv, s1, sv, GROK_MOE_IN_OUT, scale_experts, groups_up, counts, offsets, perm,
+                               T, d, f, E, k, GROK_MOE_W8, h, stream);
 }
 
-int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const int32_t* counts, const int32_t* offsets,
-                         int64_t T, int64_t d, int64_t f, int E, int k, int dtype, int splits, float* y, void* stream) {
+int grok_moe_expert_down_ex(const void* h, const void* w2, const void* s2, int weight_layout, int scale_experts,
+                            int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T, int64_t d,
+                            int64_t f, int E, int k, int dtype, int splits, float* y, void* stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
+  if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
+  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
+  if (dtype == GROK_MOE_W8) {
+    sp.experts = scale_experts;
+    sp.g_down = groups_down;
+    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
+  }
   const Plan p = make_plan(T, d, f, E, dtype);
   if (splits != p.splits) return GROK_MOE_EINVAL;
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(h) || !ok_ptr(w2) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(y)) return GROK_MOE_EINVAL;
   if (dtype == GROK_MOE_W8 ? !ok_ptr(s2) : s2 != nullptr) return GROK_MOE_EINVAL;
-  return hip_status(do_down(h, w2, s2, ScaleSpec{E, 1, 1}, counts, offsets, p, d, f, E, dtype, y,
-                            static_cast<hipStream_t>(stream)));
+  return hip_status(do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, dtype, y, static_cast<hipStream_t>(stream)));
+}
+
+int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const int32_t* counts, const int32_t* offsets,
+                         int64_t T, int64_t d, int64_t f, int E, int k, int dtype, int splits, float* y, void* stream) {
+  return grok_moe_expert_down_ex(h, w2, s2, GROK_MOE_IN_OUT, E, 1, counts, offsets, T, d, f, E, k, dtype, splits, y,
+                                 stream);
 }
 
 int grok_moe_expert_down_w8_grouped(const void* h, const void* w2, const void* s2, int scale_experts,
                                     int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T,
                                     int64_t d, int64_t f, int E, int k, int splits, float* y, void* stream) {
-  int st = check_shape(T, d, f, E, k, GROK_MOE_W8);
-  if (st != GROK_MOE_OK) return st;
-  const ScaleSpec sp{scale_experts, 1, groups_down};
-  if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
-  const Plan p = make_plan(T, d, f, E, GROK_MOE_W8);
-  if (splits != p.splits) return GROK_MOE_EINVAL;
-  if (T == 0) return GROK_MOE_OK;
-  if (!ok_ptr(h) || !ok_ptr(w2) || !ok_ptr(s2) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(y))
-    return GROK_MOE_EINVAL;
-  return hip_status(do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, GROK_MOE_W8, y,
-                            static_cast<hipStream_t>(stream)));
+  return grok_moe_expert_down_ex(h, w2, s2, GROK_MOE_IN_OUT, scale_experts, groups_down, counts, offsets, T, d, f, E,
+                                 k, GROK_MOE_W8, splits, y, stream);
 }
 
 int grok_moe_combine(const float* y, int splits, const float* topk_p, const int32_t* inv, int64_t T, int64_t d, int k,

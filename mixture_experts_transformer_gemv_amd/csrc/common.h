@@ -83,7 +83,19 @@ __device__ __forceinline__ void transpose8x8_i8_to_bf16(const u32x2_t r[8], u32x
   }
 }
 
-template <typename T>
-__device__ __forceinline__ T ldg(const T* p) { return *p; }
+// 8 int8 values (byte i of the pair = element i) -> 8 bf16, exactly, two per dword (element 2q in the low half
+// of dword q).
+__device__ __forceinline__ u32x4_t i8x8_to_bf16(const u32x2_t& v) {
+  u32x4_t t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = v[q >> 1];
+    const int b0 = 2 * (q & 1);
+    const float f0 = float(int32_t(w << (24 - 8 * b0)) >> 24);
+    const float f1 = float(int32_t(w << (16 - 8 * b0)) >> 24);
+    t[q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+  return t;
+}
 
 }  // namespace gm

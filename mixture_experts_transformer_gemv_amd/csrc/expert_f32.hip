@@ -5,7 +5,9 @@
 //
 // Grouped over the expert-sorted slots like the bf16 kernels: a workgroup of 256 threads computes a 64-row x
 // 64-column tile (per matrix; NMAT = 2 computes the same columns of W1 and Wv), 4 x 4 outputs per thread,
-// with 16-deep K steps staged through LDS.
+// with 16-deep K steps staged through LDS.  Weights stored [E, in, out] are copied row by row; weights stored
+// [E, out, in] (OUTIN) are read as 4 consecutive k of one column per thread and transposed into the same
+// [k][column] LDS tile.
 #include "common.h"
 #include "launch.h"
 
@@ -15,7 +17,7 @@ namespace {
 constexpr int FBM = 64, FBN = 64, FBK = 16;
 }
 
-template <int NMAT>
+template <int NMAT, bool OUTIN>
 __global__ __launch_bounds__(256) void f32_tiled_kernel(const float* __restrict__ A, const float* __restrict__ B0,
                                                         const float* __restrict__ B1,
                                                         const int32_t* __restrict__ counts,
@@ -34,9 +36,10 @@ __global__ __launch_bounds__(256) void f32_tiled_kernel(const float* __restrict_
   const int arr = min(ar, rows - 1);
   const size_t arow = (NMAT == 2) ? size_t(perm[row0 + arr]) : size_t(row0 + arr);
   const float* a_src = A + arow * K + ak;
-  // B piece: k row tid/16, columns 4 (tid%16) .. +3
-  const int bk = tid >> 4, bn = 4 * (tid & 15);
-  const size_t b_off = size_t(e) * K * N + size_t(bk) * N + nbase + bn;
+  // B piece: [in, out]: k row tid/16, columns 4 (tid%16) .. +3; [out, in]: column tid/4, k 4 (tid%4) .. +3
+  const int bk = OUTIN ? 4 * (tid & 3) : tid >> 4, bn = OUTIN ? tid >> 2 : 4 * (tid & 15);
+  const size_t b_off = OUTIN ? size_t(e) * K * N + size_t(nbase + bn) * K + bk
+                             : size_t(e) * K * N + size_t(bk) * N + nbase + bn;
 
   float acc[NMAT][4][4];
 #pragma unroll
@@ -50,10 +53,19 @@ __global__ __launch_bounds__(256) void f32_tiled_kernel(const float* __restrict_
     const f32x4_t av = *reinterpret_cast<const f32x4_t*>(a_src + k0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) As[ak + i][ar] = av[i];
-    *reinterpret_cast<f32x4_t*>(&Bs[0][bk][bn]) = *reinterpret_cast<const f32x4_t*>(B0 + b_off + size_t(k0) * N);
-    if (NMAT == 2)
-      *reinterpret_cast<f32x4_t*>(&Bs[NMAT - 1][bk][bn]) =
-          *reinterpret_cast<const f32x4_t*>(B1 + b_off + size_t(k0) * N);
+    if (OUTIN) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>((m ? B1 : B0) + b_off + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Bs[m][bk + i][bn] = bv[i];
+      }
+    } else {
+      *reinterpret_cast<f32x4_t*>(&Bs[0][bk][bn]) = *reinterpret_cast<const f32x4_t*>(B0 + b_off + size_t(k0) * N);
+      if (NMAT == 2)
+        *reinterpret_cast<f32x4_t*>(&Bs[NMAT - 1][bk][bn]) =
+            *reinterpret_cast<const f32x4_t*>(B1 + b_off + size_t(k0) * N);
+    }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < FBK; ++kk) {
@@ -86,18 +98,20 @@ __global__ __launch_bounds__(256) void f32_tiled_kernel(const float* __restrict_
   }
 }
 
-hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, const int32_t* counts,
+hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, bool outin, const int32_t* counts,
                          const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, float* h,
                          hipStream_t s) {
   const dim3 grid(slots / FBM + E, f / FBN), block(256);
-  f32_tiled_kernel<2><<<grid, block, 0, s>>>(x, w1, wv, counts, offsets, perm, d, f, E, h);
+  if (outin) f32_tiled_kernel<2, true><<<grid, block, 0, s>>>(x, w1, wv, counts, offsets, perm, d, f, E, h);
+  else f32_tiled_kernel<2, false><<<grid, block, 0, s>>>(x, w1, wv, counts, offsets, perm, d, f, E, h);
   return hipGetLastError();
 }
 
-hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* counts, const int32_t* offsets, int d,
-                           int f, int E, int slots, float* y, hipStream_t s) {
+hipError_t launch_down_f32(const float* h, const float* w2, bool outin, const int32_t* counts,
+                           const int32_t* offsets, int d, int f, int E, int slots, float* y, hipStream_t s) {
   const dim3 grid(slots / FBM + E, d / FBN), block(256);
-  f32_tiled_kernel<1><<<grid, block, 0, s>>>(h, w2, nullptr, counts, offsets, nullptr, f, d, E, y);
+  if (outin) f32_tiled_kernel<1, true><<<grid, block, 0, s>>>(h, w2, nullptr, counts, offsets, nullptr, f, d, E, y);
+  else f32_tiled_kernel<1, false><<<grid, block, 0, s>>>(h, w2, nullptr, counts, offsets, nullptr, f, d, E, y);
   return hipGetLastError();
 }
 

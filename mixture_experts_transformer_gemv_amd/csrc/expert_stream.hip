@@ -12,6 +12,11 @@
 // Lane l covers columns n0 + 8 (l & 15) .. +7 and k rows 8 (l >> 4) .. +7 of each 32-deep step, so a wave
 // owns 128 columns; the four 16-lane groups read four different row blocks of 256 contiguous bytes.
 //
+// Weights stored [E, out, in] (OUTIN; the PyTorch layout of "Grok-1-BF16", section "Conversion Details") need no
+// transpose: each of the lane's 8 columns is a row of the stored matrix, whose 8 consecutive k are one 16-byte
+// (int8: 8-byte) load, already the MFMA operand (int8 converted to bf16).  For one column the four 16-lane
+// groups read 64 contiguous bytes of the row; the next 32-deep step reads the next 64.
+//
 // Up-projection: one wave per 128 columns of both W1 and Wv over the whole d axis (GELU needs the full sum);
 // h = bf16(GELU(a) * b) is written for the valid token rows.  Down-projection: one wave per 128 columns of W2
 // over one of S chunks of the f axis; fp32 partial sums go to y[S, slots, d] and are added by the combine.
@@ -69,10 +74,26 @@ __device__ __forceinline__ void group_scales8(const u32x4_t& raw, float o[8], u3
   }
 }
 
-// Transpose of a weight block, its int8 columns first masked (byte mask m) if MASKED.
-template <bool INT8, bool MASKED>
-__device__ __forceinline__ void block_transpose(const typename WRow<INT8>::T r[8], const u32x2_t& m, u32x4_t t[8]) {
-  if constexpr (MASKED) {
+// The lane's weight block as 8 MFMA operands t[c] (8 consecutive k of column c), its int8 columns masked by
+// the byte mask m (byte c for column c) if MASKED.  [in, out] storage: r[i] is row i (8 columns) and is
+// transposed; [out, in] storage (OUTIN): r[c] is column c (8 k) and is only converted.
+template <bool INT8, bool MASKED, bool OUTIN>
+__device__ __forceinline__ void block_operands(const typename WRow<INT8>::T r[8], const u32x2_t& m, u32x4_t t[8]) {
+  if constexpr (OUTIN) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (INT8) {
+        u32x2_t v = r[c];
+        if constexpr (MASKED) {
+          const uint32_t keep = ((m[c >> 2] >> (8 * (c & 3))) & 0xffu) ? ~0u : 0u;
+          v &= u32x2_t{keep, keep};
+        }
+        t[c] = i8x8_to_bf16(v);
+      } else {
+        t[c] = r[c];
+      }
+    }
+  } else if constexpr (MASKED) {
     typename WRow<INT8>::T b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) b[i] = r[i] & m;
@@ -82,7 +103,7 @@ __device__ __forceinline__ void block_transpose(const typename WRow<INT8>::T r[8
   }
 }
 
-template <bool INT8, int MT, bool GROUPED>
+template <bool INT8, int MT, bool GROUPED, bool OUTIN>
 __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restrict__ x, const void* __restrict__ w1,
                                                         const void* __restrict__ wv, const uint16_t* __restrict__ s1,
                                                         const uint16_t* __restrict__ sv, ScaleLayout sl,
@@ -102,7 +123,8 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
   if (n0 >= f) return;  // no workgroup barrier in this kernel
   const int col = n0 + 8 * c16;
   const size_t ebase = size_t(e) * d * f;
-  const size_t lane_base = ebase + size_t(8 * g) * f + col;  // row 8g of each 32-deep step, column col
+  // [in, out]: row 8g of each 32-deep step, column col; [out, in]: row col, k 8g of each step
+  const size_t lane_base = OUTIN ? ebase + size_t(col) * d + 8 * g : ebase + size_t(8 * g) * f + col;
   const uint16_t* s1e = INT8 ? s1 + size_t(e) * sl.estride + col : nullptr;  // group 0's scales of the lane
   const uint16_t* sve = INT8 ? sv + size_t(e) * sl.estride + col : nullptr;
 
@@ -122,11 +144,12 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
       for (int c = 0; c < 8; ++c) { acc1[mt][c] = f32x4_t{0, 0, 0, 0}; acc2[mt][c] = f32x4_t{0, 0, 0, 0}; }
 
     auto load = [&](UpStep<INT8, MT>& st, int k0) {
-      const size_t rb = lane_base + size_t(k0) * f;
+      const size_t rb = lane_base + (OUTIN ? size_t(k0) : size_t(k0) * f);
+      const size_t rs = OUTIN ? size_t(d) : size_t(f);  // between the 8 rows (columns for OUTIN) of the block
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        st.b1[r] = W::load(w1, rb + size_t(r) * f);
-        st.b2[r] = W::load(wv, rb + size_t(r) * f);
+        st.b1[r] = W::load(w1, rb + size_t(r) * rs);
+        st.b2[r] = W::load(wv, rb + size_t(r) * rs);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -154,12 +177,12 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
     };
     auto compute = [&](const UpStep<INT8, MT>& st) {
       u32x4_t t[8];
-      block_transpose<INT8, GROUPED>(st.b1, m1, t);
+      block_operands<INT8, GROUPED, OUTIN>(st.b1, m1, t);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc1[mt][c] = mfma16x16x32(st.a[mt], t[c], acc1[mt][c]);
-      block_transpose<INT8, GROUPED>(st.b2, mv, t);
+      block_operands<INT8, GROUPED, OUTIN>(st.b2, mv, t);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -231,7 +254,7 @@ struct DownStep {
   u32x4_t a[MT];
 };
 
-template <bool INT8, int MT, bool GROUPED>
+template <bool INT8, int MT, bool GROUPED, bool OUTIN>
 __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __restrict__ h, const void* __restrict__ w2,
                                                           const uint16_t* __restrict__ s2, ScaleLayout sl,
                                                           const int32_t* __restrict__ counts,
@@ -250,7 +273,9 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
   const int col = n0 + 8 * c16;
   const int kchunk = f / S;
   const int kbeg = blockIdx.y * kchunk;
-  const size_t lane_base = size_t(e) * f * d + size_t(8 * g) * d + col;
+  // [in, out]: row 8g of each 32-deep step, column col; [out, in]: row col, k 8g of each step
+  const size_t ebase = size_t(e) * f * d;
+  const size_t lane_base = OUTIN ? ebase + size_t(col) * f + 8 * g : ebase + size_t(8 * g) * d + col;
   const uint16_t* s2e = INT8 ? s2 + size_t(e) * sl.estride + col : nullptr;  // group 0's scales of the lane
 
   for (int mb = 0; mb < n_e; mb += 16 * MT) {
@@ -269,9 +294,10 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
       for (int c = 0; c < 8; ++c) acc[mt][c] = f32x4_t{0, 0, 0, 0};
 
     auto load = [&](DownStep<INT8, MT>& st, int k0) {
-      const size_t rb = lane_base + size_t(k0) * d;
+      const size_t rb = lane_base + (OUTIN ? size_t(k0) : size_t(k0) * d);
+      const size_t rs = OUTIN ? size_t(f) : size_t(d);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) st.b[r] = W::load(w2, rb + size_t(r) * d);
+      for (int r = 0; r < 8; ++r) st.b[r] = W::load(w2, rb + size_t(r) * rs);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
@@ -297,7 +323,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
     };
     auto compute = [&](const DownStep<INT8, MT>& st) {
       u32x4_t t[8];
-      block_transpose<INT8, GROUPED>(st.b, msk, t);
+      block_operands<INT8, GROUPED, OUTIN>(st.b, msk, t);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -358,38 +384,39 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 }
 
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                            const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
-                            const int32_t* perm, int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s) {
+                            const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, bool int8, int mt,
+                            uint16_t* h, hipStream_t s) {
   const dim3 grid((f + 511) / 512, E), block(256);
   const bool grouped = int8 && sl.gsize < d;
-#define GM_UP(I8, MT, GR) up_stream_kernel<I8, MT, GR><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, \
-                                                                          perm, d, f, h)
-  if (grouped) {
-    if (mt == 1) GM_UP(true, 1, true); else GM_UP(true, 2, true);
-  } else if (int8) {
-    if (mt == 1) GM_UP(true, 1, false); else GM_UP(true, 2, false);
-  } else {
-    if (mt == 1) GM_UP(false, 1, false); else GM_UP(false, 2, false);
-  }
+#define GM_UP(I8, MT, GR, OI) up_stream_kernel<I8, MT, GR, OI><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, \
+                                                                                  offsets, perm, d, f, h)
+#define GM_UP_MT(I8, GR, OI) do { if (mt == 1) GM_UP(I8, 1, GR, OI); else GM_UP(I8, 2, GR, OI); } while (0)
+#define GM_UP_L(I8, GR) do { if (outin) GM_UP_MT(I8, GR, true); else GM_UP_MT(I8, GR, false); } while (0)
+  if (grouped) GM_UP_L(true, true);
+  else if (int8) GM_UP_L(true, false);
+  else GM_UP_L(false, false);
+#undef GM_UP_L
+#undef GM_UP_MT
 #undef GM_UP
   return hipGetLastError();
 }
 
-hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl, bool outin,
                               const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                               bool int8, int mt, float* y, hipStream_t s) {
   const dim3 grid((d + 511) / 512, S, E), block(256);
   const int64_t stride = int64_t(slots) * d;
   const bool grouped = int8 && sl.gsize < f;
-#define GM_DOWN(I8, MT, GR) down_stream_kernel<I8, MT, GR><<<grid, block, 0, s>>>(h, w2, s2, sl, counts, offsets, d, \
-                                                                              f, S, stride, y)
-  if (grouped) {
-    if (mt == 1) GM_DOWN(true, 1, true); else GM_DOWN(true, 2, true);
-  } else if (int8) {
-    if (mt == 1) GM_DOWN(true, 1, false); else GM_DOWN(true, 2, false);
-  } else {
-    if (mt == 1) GM_DOWN(false, 1, false); else GM_DOWN(false, 2, false);
-  }
+#define GM_DOWN(I8, MT, GR, OI) down_stream_kernel<I8, MT, GR, OI><<<grid, block, 0, s>>>(h, w2, s2, sl, counts, \
+                                                                                      offsets, d, f, S, stride, y)
+#define GM_DOWN_MT(I8, GR, OI) do { if (mt == 1) GM_DOWN(I8, 1, GR, OI); else GM_DOWN(I8, 2, GR, OI); } while (0)
+#define GM_DOWN_L(I8, GR) do { if (outin) GM_DOWN_MT(I8, GR, true); else GM_DOWN_MT(I8, GR, false); } while (0)
+  if (grouped) GM_DOWN_L(true, true);
+  else if (int8) GM_DOWN_L(true, false);
+  else GM_DOWN_L(false, false);
+#undef GM_DOWN_L
+#undef GM_DOWN_MT
 #undef GM_DOWN
   return hipGetLastError();
 }

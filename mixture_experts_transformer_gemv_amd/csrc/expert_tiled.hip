@@ -14,7 +14,9 @@
 // s[g-1]/s[g], the epilogue multiplies by the last group's scale; a zero scale is replaced by one and the
 // column's int8 values of that group are masked to zero while they are converted.  bf16 weights take the
 // direct-to-LDS kernel of expert_tiled_dma.hip instead.  The GROUPED form uses 128-row tiles (64 x 128 per
-// wave) so that the accumulators leave registers for the rescaling.
+// wave) so that the accumulators leave registers for the rescaling.  Weights stored [E, out, in] (OUTIN) are
+// loaded as 8 consecutive k of each of the thread's 8 columns (eight lanes read 64 contiguous bytes of a row)
+// and only converted, not transposed, before the same LDS stores.
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -46,7 +48,7 @@ template <> struct BRow<true> {
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1).  B0/B1: weights [E, K, N].
 // out: h bf16 [slots, N] (NMAT = 2) or y f32 [slots, N] (NMAT = 1).
-template <int NMAT, bool INT8, bool GROUPED>
+template <int NMAT, bool INT8, bool GROUPED, bool OUTIN>
 __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restrict__ A, const void* __restrict__ B0,
                                                     const void* __restrict__ B1, const uint16_t* __restrict__ sc0,
                                                     const uint16_t* __restrict__ sc1, ScaleLayout sl,
@@ -84,7 +86,9 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
   const int mat = (NMAT == 2) ? (wave >> 1) : 0;
   const int gcol = nbase + ((NMAT == 2) ? (wave & 1) * 64 : wave * 64) + nb * 8;
   const void* bmat = (NMAT == 2 && mat == 1) ? B1 : B0;
-  const size_t b_base = size_t(e) * K * N + size_t(8 * kb) * N + gcol;
+  // [in, out]: rows 8 kb .. +7 of the K step, 8 columns; [out, in]: column rows gcol .. +7, k 8 kb .. +7
+  const size_t b_base = OUTIN ? size_t(e) * K * N + size_t(gcol) * K + 8 * kb
+                              : size_t(e) * K * N + size_t(8 * kb) * N + gcol;
   const int b_lds_row = wave * 64 + nb * 8;  // first of the 8 LDS rows (columns) this thread writes
 
   // GROUPED: scales of the 8 columns of this thread's B block (group 0), and the byte mask of those with a
@@ -107,18 +111,31 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) rb[r] = W::load(bmat, b_base + size_t(k0 + r) * N);
+    for (int r = 0; r < 8; ++r)
+      rb[r] = OUTIN ? W::load(bmat, b_base + size_t(r) * K + k0) : W::load(bmat, b_base + size_t(k0 + r) * N);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NA; ++i)
       *reinterpret_cast<u32x4_t*>(&As[buf][((tid >> 3) + 32 * i) * LDK + 8 * (tid & 7)]) = ra[i];
     u32x4_t t[8];
-    if constexpr (GROUPED) {
+    if constexpr (OUTIN) {  // rb[c] is column c: mask whole columns, convert without transposing
 #pragma unroll
-      for (int r = 0; r < 8; ++r) rb[r] &= bmask;
+      for (int c = 0; c < 8; ++c) {
+        u32x2_t v = rb[c];
+        if constexpr (GROUPED) {
+          const uint32_t keep = ((bmask[c >> 2] >> (8 * (c & 3))) & 0xffu) ? ~0u : 0u;
+          v &= u32x2_t{keep, keep};
+        }
+        t[c] = i8x8_to_bf16(v);
+      }
+    } else {
+      if constexpr (GROUPED) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) rb[r] &= bmask;
+      }
+      W::transpose(rb, t);
     }
-    W::transpose(rb, t);
 #pragma unroll
     for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4_t*>(&Bs[buf][(b_lds_row + c) * LDK + 8 * kb]) = t[c];
   };
@@ -238,32 +255,31 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
 }
 
 hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                           const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
-                           const int32_t* perm, int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s) {
-  if (!int8) return launch_up_tiled_dma(x, w1, wv, counts, offsets, perm, d, f, E, slots, h, s);
-  if (sl.gsize < d) {
-    const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2), 128)), block(256);
-    tiled_reg_kernel<2, true, true><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, E, h);
-  } else {
-    const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
-    tiled_reg_kernel<2, true, false><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, E, h);
-  }
+                           const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
+                           const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, bool int8,
+                           uint16_t* h, hipStream_t s) {
+  if (!int8) return launch_up_tiled_dma(x, w1, wv, outin, counts, offsets, perm, d, f, E, slots, h, s);
+  const bool grouped = sl.gsize < d;
+  const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2), grouped ? 128 : BM)), block(256);
+#define GM_UPT(GR, OI) tiled_reg_kernel<2, true, GR, OI><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, \
+                                                                             perm, d, f, E, h)
+  if (grouped) { if (outin) GM_UPT(true, true); else GM_UPT(true, false); }
+  else { if (outin) GM_UPT(false, true); else GM_UPT(false, false); }
+#undef GM_UPT
   return hipGetLastError();
 }
 
-hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl, bool outin,
                              const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                              bool int8, float* y, hipStream_t s) {
-  if (!int8) return launch_down_tiled_dma(h, w2, counts, offsets, d, f, E, slots, S, y, s);
-  if (sl.gsize < f) {
-    const dim3 grid(tile::grid_tiles(slots, E, d / BNT, 128)), block(256);
-    tiled_reg_kernel<1, true, true><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, offsets, nullptr,
-                                                           f, d, E, y);
-  } else {
-    const dim3 grid(tile::grid_tiles(slots, E, d / BNT)), block(256);
-    tiled_reg_kernel<1, true, false><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, offsets,
-                                                            nullptr, f, d, E, y);
-  }
+  if (!int8) return launch_down_tiled_dma(h, w2, outin, counts, offsets, d, f, E, slots, S, y, s);
+  const bool grouped = sl.gsize < f;
+  const dim3 grid(tile::grid_tiles(slots, E, d / BNT, grouped ? 128 : BM)), block(256);
+#define GM_DNT(GR, OI) tiled_reg_kernel<1, true, GR, OI><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, \
+                                                                             offsets, nullptr, f, d, E, y)
+  if (grouped) { if (outin) GM_DNT(true, true); else GM_DNT(true, false); }
+  else { if (outin) GM_DNT(false, true); else GM_DNT(false, false); }
+#undef GM_DNT
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@
 // so their MFMA fragments (8 consecutive k of one column per lane) come from two ds_read_b64_tr_b16: within each
 // 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane 4 r + j / 4 (r = 0..3), i.e. 4
 // consecutive k of one column when four lanes address four consecutive k rows.
+// Weights stored [E, out, in] (OUTIN) are K-contiguous like A: their tile is copied and read exactly as the A
+// tile ([256 weight rows][32 k], same swizzle, 16-byte fragment reads, no transpose reads).
 // Schedule: one workgroup barrier per K step, between its two 16-deep halves; every MFMA is followed by at most
 // one LDS fragment read or one copy (pinned with sched_barrier), so the copies (half of step kt+3 after the
 // barrier, the other half in the next half-step) and the fragments of the next half-step are issued in the
@@ -73,8 +75,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16.  B0/B1: bf16 weights
-// [E, K, N] (B1 only for NMAT = 2).  out: h bf16 [slots, N] (NMAT = 2) or y f32 [slots, N] (NMAT = 1).
-template <int NMAT>
+// [E, K, N], or [E, N, K] if OUTIN (B1 only for NMAT = 2).  out: h bf16 [slots, N] (NMAT = 2) or y f32 [slots, N]
+// (NMAT = 1).
+template <int NMAT, bool OUTIN>
 __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B0,
                                                         const uint16_t* __restrict__ B1,
@@ -116,11 +119,26 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   const uint32_t b_voff = uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
   const uint32_t a_dst = lds0 + uint32_t(64 * wave) * (BK * 2);
   const uint32_t b_dst = lds0 + A_STAGE + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * 256;
+  // OUTIN: the weight tile is [256 weight rows][32 k] like A; wave w copies tile rows 64 w .. +63 (NMAT = 2: rows
+  // 0..127 are W1 rows nbase.., 128..255 the same Wv rows; NMAT = 1: W2 rows nbase..), piece i rows 16 i + lane/4
+  const uint16_t* bt_base = bmat + size_t(e) * K * N;
+  uint32_t bt_voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * wave + 16 * i + (lane >> 2);
+    const int wrow = nbase + ((NMAT == 2) ? (r & 127) : r);
+    bt_voff[i] = (uint32_t(wrow) * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u;
+  }
+  const uint32_t bt_dst = lds0 + A_STAGE + uint32_t(64 * wave) * (BK * 2);
   // piece n of the copies of K step kt into ring slot stage (n < 4: A piece n; else B piece n - 4)
   auto copy_piece = [&](int stage, int kt, int n) {
     const uint32_t so = uint32_t(stage) * STAGE;
     if (n < 4) g2lds16(A + size_t(kbase + kt * BK), a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
-    else g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - 4)) * N, b_voff, b_dst + so + uint32_t(4 * (n - 4)) * 256);
+    else if (OUTIN)
+      g2lds16(bt_base + size_t(kbase + kt * BK), bt_voff[n - 4], bt_dst + so + uint32_t(16 * (n - 4)) * (BK * 2));
+    else
+      g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - 4)) * N, b_voff,
+              b_dst + so + uint32_t(4 * (n - 4)) * 256);
   };
 
   // ---- fragments.  Waves 2 x 2: wave rows wm*128 .. +127, 4 column sub-tiles of 32.
@@ -150,12 +168,26 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
         b_off[j][ks][h] = A_STAGE + bsub * B_SUB + k * 256 + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
       }
   }
+  // OUTIN: weight fragment j is the 16-byte read of tile row (its column) with A's swizzle
+  int bt_off[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r = ((NMAT == 2) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + (lane & 31);
+      bt_off[j][ks] = A_STAGE + r * (BK * 2) + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
+    }
   // fragment piece p of half-step ks from ring slot st, in the order the MFMAs consume them:
-  // A0, B0 (two halves), B1, B2, B3, A1, A2, A3
+  // A0, B0 (two halves), B1, B2, B3, A1, A2, A3 (OUTIN: A0, B0, B1, B2, B3, A1, A2, A3, one read each)
+  constexpr int NPIECE = OUTIN ? 8 : 12;
   u32x4_t fa[2][4], fb[2][4];
   u32x2_t bh[2][4][2];
   auto read_piece = [&](int buf, const lds_u8* st, int ks, int p) {
-    if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
+    if (OUTIN) {
+      if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
+      else if (p <= 4) fb[buf][p - 1] = *(const __attribute__((address_space(3))) u32x4_t*)(st + bt_off[p - 1][ks]);
+      else fa[buf][p - 4] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[p - 4][ks]);
+    } else if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
     else if (p <= 8) {
       const int j = (p - 1) >> 1, h = (p - 1) & 1;
       bh[buf][j][h] = lds_tr16(st + b_off[j][ks][h]);
@@ -165,6 +197,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     }
   };
   auto join_b = [&](int buf) {
+    if (OUTIN) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[buf][j] = u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
   };
@@ -191,7 +224,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   wait_vm<8 * (NSTAGE - 3) + 4>();  // step 0 landed (step 1 and half of step 2 may be in flight)
   lds_barrier();
 #pragma unroll
-  for (int p = 0; p < 12; ++p) read_piece(0, lds, 0, p);
+  for (int p = 0; p < NPIECE; ++p) read_piece(0, lds, 0, p);
   join_b(0);
   for (int kt = 0; kt < KT; ++kt) {
     const lds_u8* st = lds + (kt % NSTAGE) * STAGE;
@@ -200,7 +233,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
-      if (m < 12) read_piece(1, st, 1, m);
+      if (m < NPIECE) read_piece(1, st, 1, m);
       if (m >= 12) copy_piece(pstage, pk, m - 8);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -213,7 +246,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
       if (m < 4) copy_piece(cstage, ck, m);
-      if (m < 12) read_piece(0, nst, 0, m);
+      if (m < NPIECE) read_piece(0, nst, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(0);
@@ -252,20 +285,27 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   }
 }
 
-hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const int32_t* counts,
+hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, bool outin, const int32_t* counts,
                                const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
                                uint16_t* h, hipStream_t s) {
   const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
-  tiled_dma_kernel<2><<<grid, block, 0, s>>>(x, static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(wv),
-                                             counts, offsets, perm, d, f, E, h, 0);
+  const uint16_t* b0 = static_cast<const uint16_t*>(w1);
+  const uint16_t* b1 = static_cast<const uint16_t*>(wv);
+  if (outin) tiled_dma_kernel<2, true><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, d, f, E, h, 0);
+  else tiled_dma_kernel<2, false><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, d, f, E, h, 0);
   return hipGetLastError();
 }
 
-hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const int32_t* counts, const int32_t* offsets,
-                                 int d, int f, int E, int slots, int S, float* y, hipStream_t s) {
+hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, bool outin, const int32_t* counts,
+                                 const int32_t* offsets, int d, int f, int E, int slots, int S, float* y,
+                                 hipStream_t s) {
   const dim3 grid(tile::grid_tiles(slots, E, d / BNT), S), block(256);
-  tiled_dma_kernel<1><<<grid, block, 0, s>>>(h, static_cast<const uint16_t*>(w2), nullptr, counts, offsets, nullptr,
-                                             f, d, E, y, int64_t(slots) * d);
+  const uint16_t* b0 = static_cast<const uint16_t*>(w2);
+  const int64_t stride = int64_t(slots) * d;
+  if (outin)
+    tiled_dma_kernel<1, true><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, f, d, E, y, stride);
+  else
+    tiled_dma_kernel<1, false><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, f, d, E, y, stride);
   return hipGetLastError();
 }
 

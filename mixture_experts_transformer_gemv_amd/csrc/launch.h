@@ -36,35 +36,39 @@ hipError_t launch_combine(const float* y, int S, const float* p, const int32_t* 
 
 // Streaming (few tokens per expert) expert kernels: weights go HBM -> registers -> MFMA, no LDS tiling.
 // mt = number of 16-row MFMA tiles held per pass (1 or 2).
+// outin: weights stored [E, out, in] instead of [E, in, out].
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                            const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
-                            const int32_t* perm, int d, int f, int E, bool int8, int mt, uint16_t* h, hipStream_t s);
-hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+                            const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, bool int8, int mt,
+                            uint16_t* h, hipStream_t s);
+hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl, bool outin,
                               const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                               bool int8, int mt, float* y, hipStream_t s);
 
 // LDS-tiled grouped GEMMs (many tokens per expert); int8 weights use register-staged tiles, bf16 weights the
 // direct-to-LDS kernels below.
 hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
-                           const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
-                           const int32_t* perm, int d, int f, int E, int slots, bool int8, uint16_t* h, hipStream_t s);
-hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
+                           const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
+                           const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, bool int8,
+                           uint16_t* h, hipStream_t s);
+hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl, bool outin,
                              const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                              bool int8, float* y, hipStream_t s);
 
-// The bf16 forms of the tiled kernels: direct global -> LDS copies, LDS transpose reads.
-hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const int32_t* counts,
+// The bf16 forms of the tiled kernels: direct global -> LDS copies ([in, out] weights: LDS transpose reads).
+hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, bool outin, const int32_t* counts,
                                const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
                                uint16_t* h, hipStream_t s);
-hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const int32_t* counts, const int32_t* offsets,
-                                 int d, int f, int E, int slots, int S, float* y, hipStream_t s);
+hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, bool outin, const int32_t* counts,
+                                 const int32_t* offsets, int d, int f, int E, int slots, int S, float* y,
+                                 hipStream_t s);
 
 // fp32 layer (VALU, LDS tiles).
-hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, const int32_t* counts,
+hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, bool outin, const int32_t* counts,
                          const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, float* h,
                          hipStream_t s);
-hipError_t launch_down_f32(const float* h, const float* w2, const int32_t* counts, const int32_t* offsets, int d,
-                           int f, int E, int slots, float* y, hipStream_t s);
+hipError_t launch_down_f32(const float* h, const float* w2, bool outin, const int32_t* counts,
+                           const int32_t* offsets, int d, int f, int E, int slots, float* y, hipStream_t s);
 
 // Tile scheduling shared by the grouped kernels: the m-th row tile (of height bm) over all experts in
 // ascending expert order.  Returns false if m is past the last tile.  counts has E entries.
