@@ -17,6 +17,7 @@ struct Plan {
   int64_t slots;
   bool stream;  // streaming kernels (else LDS-tiled grouped GEMM or the fp32 kernels)
   int mt;       // 16-row MFMA tiles per pass of the streaming kernels
+  int mt_oi;    // the same for the [out, in] streaming kernels (1, 2 or 4)
   int splits;   // partial sums of the down-projection
   size_t o_idx, o_p, o_counts, o_offsets, o_perm, o_inv, o_h, o_y, total;
   size_t o_xn, total_block;  // the block form adds the normed input [T, d]
@@ -49,6 +50,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
   p.slots = 2 * T;
   p.stream = dtype != GROK_MOE_F32 && T <= kStreamMaxTokens;
   p.mt = T <= 16 ? 1 : 2;
+  p.mt_oi = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
   p.splits = down_splits(T, f, dtype);
   size_t o = 0;
   p.o_idx = o; o = align256(o + size_t(p.slots) * 4);
@@ -112,6 +114,10 @@ hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, 
                              static_cast<const float*>(wv), sp.outin, counts, offsets, perm, int(d), int(f), E,
                              int(p.slots), static_cast<float*>(h), s);
   const bool i8 = dtype == GROK_MOE_W8;
+  if (p.stream && sp.outin && gm::oi_stream_fits(int(d), i8, up_layout(sp, d, f), int(d)))
+    return gm::launch_up_stream_oi(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
+                                   static_cast<const uint16_t*>(sv), up_layout(sp, d, f), counts, offsets, perm,
+                                   int(d), int(f), E, i8, p.mt_oi, static_cast<uint16_t*>(h), s);
   if (p.stream)
     return gm::launch_up_stream(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
                                 static_cast<const uint16_t*>(sv), up_layout(sp, d, f), sp.outin, counts, offsets,
@@ -128,6 +134,10 @@ hipError_t do_down(const void* h, const void* w2, const void* s2, const ScaleSpe
     return gm::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2), sp.outin, counts,
                                offsets, int(d), int(f), E, int(p.slots), y, s);
   const bool i8 = dtype == GROK_MOE_W8;
+  if (p.stream && sp.outin && gm::oi_stream_fits(int(f / p.splits), i8, down_layout(sp, d, f), int(f)))
+    return gm::launch_down_stream_oi(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),
+                                     down_layout(sp, d, f), counts, offsets, int(d), int(f), E, int(p.slots),
+                                     p.splits, i8, p.mt_oi, y, s);
   if (p.stream)
     return gm::launch_down_stream(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),
                                   down_layout(sp, d, f), sp.outin, counts, offsets, int(d), int(f), E, int(p.slots),

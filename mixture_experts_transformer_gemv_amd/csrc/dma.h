@@ -1,0 +1,42 @@
+// Direct global -> LDS copies and the waits around them, shared by the kernels that stage tiles in LDS (gfx950).
+#pragma once
+
+#include "common.h"
+
+// The copies are issued from inline assembly (they only set M0, no destination register).
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace gm {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global -> LDS copy of one wave: lane i reads base + voff (bytes; base wave-uniform) and writes LDS
+// bytes [dst + 16 i, dst + 16 i + 16) (dst wave-uniform).  Inline assembly so that the compiler does not wait for
+// every copy in flight before each LDS read (it cannot tell the ring stages apart); completion is awaited with
+// an explicit vmcnt before the stage barrier.  No destination register; no "memory" clobber (the barrier
+// sequence orders the LDS accesses).
+__device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(dst) : "m0");
+}
+
+// LDS transpose read: within each 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane
+// 4 r + j / 4 (r = 0..3).
+__device__ __forceinline__ u32x2_t lds_tr16(const lds_u8* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p)));
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding (copies complete in issue order).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N));
+}
+
+// Workgroup barrier ordering LDS accesses only (a __syncthreads would also wait for all copies in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace gm

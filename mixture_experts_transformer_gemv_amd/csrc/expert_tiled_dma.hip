@@ -23,11 +23,9 @@
 // added by the combine) so that its smaller number of tiles still fills the chip.  Up-projection epilogue: the GELU product
 // tile is staged in the idle ring and written as 16-byte row pieces.
 #include "common.h"
+#include "dma.h"
 #include "launch.h"
 #include "tiles.h"
-
-// The copies are issued from inline assembly (they only set M0, no destination register).
-#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace gm {
 
@@ -39,39 +37,6 @@ constexpr int NSTAGE = 4;               // ring depth
 constexpr int A_STAGE = BM * BK * 2;    // bytes: [256 rows][32 k]
 constexpr int B_SUB = BK * 128 * 2;     // bytes: one [32 k][128 columns] weight sub-tile
 constexpr int STAGE = A_STAGE + 2 * B_SUB;
-}
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
-// 16-byte global -> LDS copy of one wave: lane i reads base + voff (bytes; base wave-uniform) and writes LDS
-// bytes [dst + 16 i, dst + 16 i + 16) (dst wave-uniform).  Inline assembly so that the compiler does not wait for
-// every copy in flight before each LDS read (it cannot tell the ring stages apart); completion is awaited with
-// an explicit vmcnt before the stage barrier.  No destination register; no "memory" clobber (the barrier
-// sequence orders the LDS accesses).
-__device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(dst) : "m0");
-}
-
-// LDS transpose read (see the header comment).
-__device__ __forceinline__ u32x2_t lds_tr16(const lds_u8* p) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p)));
-}
-
-template <int N> __device__ __forceinline__ void wait_vm() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)");
-  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)");
-  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)");
-  else static_assert(N < 0, "unsupported wait count");
-}
-
-// Workgroup barrier ordering LDS accesses only (a __syncthreads would also wait for all copies in flight).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16.  B0/B1: bf16 weights
