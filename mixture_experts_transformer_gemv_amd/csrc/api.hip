@@ -17,7 +17,7 @@ struct Plan {
   int64_t slots;
   bool stream;  // streaming kernels (else LDS-tiled grouped GEMM or the fp32 kernels)
   int mt;       // 16-row MFMA tiles per pass of the streaming kernels
-  int mt_oi;    // the same for the [out, in] streaming kernels (1, 2 or 4)
+  int mt_oi;    // the same for the [out, in] streaming kernels
   int splits;   // partial sums of the down-projection
   size_t o_idx, o_p, o_counts, o_offsets, o_perm, o_inv, o_h, o_y, total;
   size_t o_xn, total_block;  // the block form adds the normed input [T, d]
@@ -50,7 +50,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
   p.slots = 2 * T;
   p.stream = dtype != GROK_MOE_F32 && T <= kStreamMaxTokens;
   p.mt = T <= 16 ? 1 : 2;
-  p.mt_oi = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+  p.mt_oi = T <= 16 ? 1 : 2;  // (4 tiles measured slower at T = 64: the token tile outgrows the weight tile)
   p.splits = down_splits(T, f, dtype);
   size_t o = 0;
   p.o_idx = o; o = align256(o + size_t(p.slots) * 4);

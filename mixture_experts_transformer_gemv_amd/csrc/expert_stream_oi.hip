@@ -275,11 +275,8 @@ static void launch_oi_mt(int mt, dim3 grid, hipStream_t s, const uint16_t* A, co
   if (mt == 1)
     oi_stream_kernel<NMAT, INT8, GROUPED, 1><<<grid, block, 0, s>>>(A, W0, W1, sc0, sc1, sl, counts, offsets, perm,
                                                                     K, N, Kc, spw, out, split_stride);
-  else if (mt == 2)
-    oi_stream_kernel<NMAT, INT8, GROUPED, 2><<<grid, block, 0, s>>>(A, W0, W1, sc0, sc1, sl, counts, offsets, perm,
-                                                                    K, N, Kc, spw, out, split_stride);
   else
-    oi_stream_kernel<NMAT, INT8, GROUPED, 4><<<grid, block, 0, s>>>(A, W0, W1, sc0, sc1, sl, counts, offsets, perm,
+    oi_stream_kernel<NMAT, INT8, GROUPED, 2><<<grid, block, 0, s>>>(A, W0, W1, sc0, sc1, sl, counts, offsets, perm,
                                                                     K, N, Kc, spw, out, split_stride);
 }
 

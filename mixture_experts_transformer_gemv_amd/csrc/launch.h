@@ -46,7 +46,7 @@ hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t*
                               bool int8, int mt, float* y, hipStream_t s);
 
 // Streaming kernels for weights stored [E, out, in]: weight rows staged in LDS by direct copies of 256-byte
-// pieces.  mt = 16-row token tiles per pass (1, 2 or 4).  Usable when oi_stream_fits(K chunk, ...).
+// pieces.  mt = 16-row token tiles per pass (1 or 2).  Usable when oi_stream_fits(K chunk, ...).
 bool oi_stream_fits(int Kc, bool int8, ScaleLayout sl, int K);
 hipError_t launch_up_stream_oi(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                                const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
