@@ -216,6 +216,14 @@ int grok_moe_expert_down_ex(const void* h, const void* w2, const void* s2, int w
                             int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T, int64_t d,
                             int64_t f, int E, int k, int dtype, int splits, float* y, void* stream);
 
+/* The MoE block (as grok_moe_block_forward) with the weight layout and int8 scale layout of grok_moe_forward_ex. */
+int grok_moe_block_forward_ex(const void* x, const void* pre_scale, const void* post_scale, double eps,
+                              const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
+                              const void* sv, const void* s2, int weight_layout, int scale_experts, int groups_up,
+                              int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype, float* out,
+                              const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,9 @@ _SIGS = {
                               + [_i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p]),
     "grok_moe_expert_down_ex": (_int, [_c_void_p] * 3 + [_int, _int, _int] + [_c_void_p] * 2
                                 + [_i64, _i64, _i64, _int, _int, _int, _int, _c_void_p, _c_void_p]),
+    "grok_moe_block_forward_ex": (_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_double] + [_c_void_p] * 7
+                                  + [_int, _int, _int, _int, _i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 6
+                                  + [ctypes.c_size_t, _c_void_p]),
 }
 
 # weight storage: [E, in, out] (the checkpoint's JAX layout) or [E, out, in] (the converted PyTorch layout)
@@ -320,18 +323,24 @@ def block_workspace_size(T: int, d: int, f: int, E: int = 8, k: int = 2, dtype: 
 
 
 def block_forward(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, scales=None, router_bias=None,
-                  return_routing=False, workspace=None):
+                  return_routing=False, workspace=None, weight_layout=IN_OUT):
     """The MoE part of a Grok-1 layer with its norms and residual: out = x + RMSNorm(MoE(RMSNorm(x; pre_scale));
-    post_scale), fp32 [T, d].  pre_scale, post_scale: [d] in the activation type of x."""
-    T, d, f, E = _layer_shapes(x, router_w, w1, wv, w2)
+    post_scale), fp32 [T, d].  pre_scale, post_scale: [d] in the activation type of x.  Weights, scales and
+    weight_layout as for forward()."""
+    T, d, f, E = _layer_shapes(x, router_w, w1, wv, w2, weight_layout)
+    lay = _layout_code(weight_layout)
     dt = dtype_of(x, w1)
     for t, n in ((x, "x"), (router_w, "router_w"), (w1, "w1"), (wv, "wv"), (w2, "w2")):
         _need(t, n)
     _need(pre_scale, "pre_scale", x.dtype, (d,))
     _need(post_scale, "post_scale", x.dtype, (d,))
     s1 = sv = s2 = None
+    grouped = None
     if dt == W8:
+        if scales is None:
+            raise GrokMoeError("int8 weights need scales (s1, sv, s2)")
         s1, sv, s2 = scales
+        grouped = _grouped(scales, E, d, f)
     dev = x.device
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
     idx = torch.empty((T, 2), dtype=torch.int32, device=dev) if return_routing else None
@@ -340,11 +349,19 @@ def block_forward(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, scales=No
     need = block_workspace_size(T, d, f, E, 2, dt)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    st = lib().grok_moe_block_forward(_p(x), _p(pre_scale), _p(post_scale), float(eps), _p(router_w), _p(w1),
-                                      _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), T, d, f, E, 2, dt, _p(out),
-                                      _p(router_bias), _p(idx), _p(pr), _p(cnt), _p(workspace),
-                                      workspace.numel() * workspace.element_size(), _stream())
-    _check(st, "grok_moe_block_forward")
+    if lay == 0 and grouped is None:
+        st = lib().grok_moe_block_forward(_p(x), _p(pre_scale), _p(post_scale), float(eps), _p(router_w), _p(w1),
+                                          _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), T, d, f, E, 2, dt, _p(out),
+                                          _p(router_bias), _p(idx), _p(pr), _p(cnt), _p(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream())
+        _check(st, "grok_moe_block_forward")
+    else:
+        es, g1, g2 = grouped if grouped is not None else (E, 1, 1)
+        st = lib().grok_moe_block_forward_ex(_p(x), _p(pre_scale), _p(post_scale), float(eps), _p(router_w), _p(w1),
+                                             _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), lay, es, g1, g2, T, d, f, E, 2,
+                                             dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt), _p(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream())
+        _check(st, "grok_moe_block_forward_ex")
     if return_routing:
         return out, idx, pr, cnt
     return out

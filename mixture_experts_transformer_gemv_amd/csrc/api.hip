@@ -377,14 +377,22 @@ int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const
                                             post_scale, eps, out, static_cast<hipStream_t>(stream)));
 }
 
-int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,
-                           const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
-                           const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
-                           float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                           int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+int grok_moe_block_forward_ex(const void* x, const void* pre_scale, const void* post_scale, double eps,
+                              const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
+                              const void* sv, const void* s2, int weight_layout, int scale_experts, int groups_up,
+                              int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype, float* out,
+                              const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
-  if (!(eps >= 0.0)) return GROK_MOE_EINVAL;
+  if (!(eps >= 0.0) || !ok_layout(weight_layout)) return GROK_MOE_EINVAL;
+  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
+  if (dtype == GROK_MOE_W8) {
+    sp.experts = scale_experts;
+    sp.g_up = groups_up;
+    sp.g_down = groups_down;
+    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
+  }
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(pre_scale) || !ok_ptr(post_scale) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) ||
       !ok_ptr(w2) || !ok_ptr(out))
@@ -410,15 +418,24 @@ int grok_moe_block_forward(const void* x, const void* pre_scale, const void* pos
   hipError_t e = gm::launch_router_norm(x, pre_scale, eps, router_w, router_bias, int(T), int(d), E,
                                         dtype != GROK_MOE_F32, xn, idx, pr, s);
   if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
-  if (e == hipSuccess)
-    e = do_up(xn, w1, wv, s1, sv, ScaleSpec{E, 1, 1}, counts, offsets, perm, p, d, f, E, dtype, h, s);
-  if (e == hipSuccess) e = do_down(h, w2, s2, ScaleSpec{E, 1, 1}, counts, offsets, p, d, f, E, dtype, y, s);
+  if (e == hipSuccess) e = do_up(xn, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h, s);
+  if (e == hipSuccess) e = do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, dtype, y, s);
   if (e == hipSuccess)
     e = gm::launch_combine_norm(y, p.splits, pr, inv, int(T), int(d), x, dtype != GROK_MOE_F32, post_scale, eps, out,
                                 s);
   if (e == hipSuccess && expert_counts)
     e = hipMemcpyAsync(expert_counts, counts, size_t(E) * 4, hipMemcpyDeviceToDevice, s);
   return hip_status(e);
+}
+
+int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,
+                           const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
+                           const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                           float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                           int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  return grok_moe_block_forward_ex(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, E,
+                                   1, 1, T, d, f, E, k, dtype, out, router_bias, topk_idx, topk_p, expert_counts,
+                                   workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

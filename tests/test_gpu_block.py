@@ -105,3 +105,29 @@ def test_block_grok_decode(gm):
     say("[setup] drawing Grok-1-shape bf16 weights")
     w = synth.WORKLOADS["decode_bf16"]
     check_block(gm, w)
+
+
+@pytest.mark.parametrize("dtype,T,g", [(BF16, 24, 1), (W8, 40, 4), (W8, 300, 2)])
+def test_block_out_in_and_grouped(gm, dtype, T, g):
+    """The block with [out, in] weights (and grouped int8 scales): bit-identical to the [in, out] block on the same
+    weights, and against the oracle reading the [out, in] storage."""
+    w = synth.Workload(f"blk_oi_T{T}", T=T, d=512, f=1024, E=8, dtype=dtype, groups_up=g, groups_down=g)
+    say(f"[case] block out_in {w.name} dtype={synth.DTYPE_NAMES[dtype]} groups={g}")
+    inp = synth.make_inputs(w)
+    dv = dev_inputs(inp, dtype)
+    ns = synth.make_norm_scales(w)
+    g_pre, g_post = _scales_dev(ns, dtype)
+    ref = gm.block_forward(dv["x"], g_pre, g_post, ns["eps"], dv["router_w"], dv["w1"], dv["wv"], dv["w2"],
+                           scales=dv["scales"])
+    tr = lambda t: t.transpose(1, 2).contiguous()
+    out = gm.block_forward(dv["x"], g_pre, g_post, ns["eps"], dv["router_w"], tr(dv["w1"]), tr(dv["wv"]),
+                           tr(dv["w2"]), scales=dv["scales"], weight_layout=gm.OUT_IN)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    tin = dict(inp)
+    for n in ("w1", "wv", "w2"):
+        tin[n] = np.ascontiguousarray(np.swapaxes(inp[n], 1, 2))
+    want = oracle.block_forward(tin, dtype, ns["pre_scale"], ns["post_scale"], ns["eps"], layout=oracle.OUT_IN)
+    err = rel_err(out.cpu().numpy(), want["out"].numpy())
+    say(f"[result] block out_in {w.name}: max_err/rms={err:.3e}")
+    assert err <= TOL[dtype]
