@@ -14,8 +14,12 @@
 // so their MFMA fragments (8 consecutive k of one column per lane) come from two ds_read_b64_tr_b16: within each
 // 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane 4 r + j / 4 (r = 0..3), i.e. 4
 // consecutive k of one column when four lanes address four consecutive k rows.
-// Weights stored [E, out, in] (OUTIN) are K-contiguous like A: their tile is copied and read exactly as the A
-// tile ([256 weight rows][32 k], same swizzle, 16-byte fragment reads, no transpose reads).
+// Weights stored [E, out, in] (OUTIN) are K-contiguous like A, so their fragments are plain 16-byte reads; but
+// copying them per 32-k step would fetch 64-byte row pieces, half of each 128-byte line at a time (measured: twice
+// the HBM traffic and 64-byte row pieces read ~15% slower).  So their tile is copied per pair of K steps,
+// [256 weight rows][64 k] with 128-byte rows (16-byte chunk c of row r in slot c ^ ((r >> 1) & 7)), into one of
+// three pair slots beside a 4-deep ring of A stages (4 x 16 KB + 3 x 32 KB = 160 KB); a pair's copies are issued
+// during the two steps three and two steps ahead of it, so the per-step copy count and waits are unchanged.
 // Schedule: one workgroup barrier per K step, between its two 16-deep halves; every MFMA is followed by at most
 // one LDS fragment read or one copy (pinned with sched_barrier), so the copies (half of step kt+3 after the
 // barrier, the other half in the next half-step) and the fragments of the next half-step are issued in the
@@ -37,6 +41,8 @@ constexpr int NSTAGE = 4;               // ring depth
 constexpr int A_STAGE = BM * BK * 2;    // bytes: [256 rows][32 k]
 constexpr int B_SUB = BK * 128 * 2;     // bytes: one [32 k][128 columns] weight sub-tile
 constexpr int STAGE = A_STAGE + 2 * B_SUB;
+constexpr int B_PAIR = BM * 2 * BK * 2;  // bytes: [256 weight rows][64 k] ([out, in] weights)
+constexpr int NPAIR = 3;                // pair slots
 }
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16.  B0/B1: bf16 weights
@@ -54,7 +60,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   int e, row0, rows, ntile;
   if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole WG
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  constexpr int LDS_BYTES = OUTIN ? NSTAGE * A_STAGE + NPAIR * B_PAIR : NSTAGE * STAGE;
+  constexpr int A_STRIDE = OUTIN ? A_STAGE : STAGE;  // between ring slots of A
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   lds_u8* lds = (lds_u8*)(smem);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
@@ -84,26 +92,34 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   const uint32_t b_voff = uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
   const uint32_t a_dst = lds0 + uint32_t(64 * wave) * (BK * 2);
   const uint32_t b_dst = lds0 + A_STAGE + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * 256;
-  // OUTIN: the weight tile is [256 weight rows][32 k] like A; wave w copies tile rows 64 w .. +63 (NMAT = 2: rows
-  // 0..127 are W1 rows nbase.., 128..255 the same Wv rows; NMAT = 1: W2 rows nbase..), piece i rows 16 i + lane/4
+  // OUTIN: the weight tile of K-step pair q is [256 weight rows][64 k] (NMAT = 2: rows 0..127 are W1 rows
+  // nbase.., 128..255 the same Wv rows; NMAT = 1: W2 rows nbase..); wave w copies tile rows 64 w .. +63, copy c
+  // (0..7) rows 8 c + lane/8, lane's slot (lane & 7) of the 128-byte row holding chunk (lane & 7) ^ ((row >> 1) & 7)
   const uint16_t* bt_base = bmat + size_t(e) * K * N;
-  uint32_t bt_voff[4];
+  uint32_t bp_voff[OUTIN ? 8 : 1];
+  if constexpr (OUTIN) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 64 * wave + 16 * i + (lane >> 2);
-    const int wrow = nbase + ((NMAT == 2) ? (r & 127) : r);
-    bt_voff[i] = (uint32_t(wrow) * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u;
+    for (int c = 0; c < 8; ++c) {
+      const int r = 64 * wave + 8 * c + (lane >> 3);
+      const int wrow = nbase + ((NMAT == 2) ? (r & 127) : r);
+      bp_voff[c] = (uint32_t(wrow) * uint32_t(K) + 8u * uint32_t((lane & 7) ^ ((r >> 1) & 7))) * 2u;
+    }
   }
-  const uint32_t bt_dst = lds0 + A_STAGE + uint32_t(64 * wave) * (BK * 2);
-  // piece n of the copies of K step kt into ring slot stage (n < 4: A piece n; else B piece n - 4)
+  const uint32_t bp_dst = lds0 + NSTAGE * A_STAGE + uint32_t(64 * wave) * 128;
+  // piece n of the copies of K step kt into ring slot stage (n < 4: A piece n; else B piece n - 4, [in, out])
   auto copy_piece = [&](int stage, int kt, int n) {
-    const uint32_t so = uint32_t(stage) * STAGE;
-    if (n < 4) g2lds16(A + size_t(kbase + kt * BK), a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
-    else if (OUTIN)
-      g2lds16(bt_base + size_t(kbase + kt * BK), bt_voff[n - 4], bt_dst + so + uint32_t(16 * (n - 4)) * (BK * 2));
+    const uint32_t so = uint32_t(stage) * A_STRIDE;
+    if (n < 4)
+      g2lds16(A + size_t(kbase + kt * BK), a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
     else
       g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - 4)) * N, b_voff,
               b_dst + so + uint32_t(4 * (n - 4)) * 256);
+  };
+  // OUTIN: copy c of K-step pair q into pair slot q % 3 (past the end: the last pair again, into a free slot)
+  auto copy_pair = [&](int q, int c) {
+    const int qd = min(q, (Ks / BK) / 2 - 1);
+    g2lds16(bt_base + size_t(kbase + qd * 2 * BK), bp_voff[c],
+            bp_dst + uint32_t((q % NPAIR) * B_PAIR) + uint32_t(c * 1024));
   };
 
   // ---- fragments.  Waves 2 x 2: wave rows wm*128 .. +127, 4 column sub-tiles of 32.
@@ -133,24 +149,29 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
         b_off[j][ks][h] = A_STAGE + bsub * B_SUB + k * 256 + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
       }
   }
-  // OUTIN: weight fragment j is the 16-byte read of tile row (its column) with A's swizzle
-  int bt_off[4][2];
+  // OUTIN: weight fragment j of half-step ks of the pair's step p2 (0, 1) is the 16-byte read of tile row (its
+  // column), k chunk 4 p2 + 2 ks + (lane >> 5) of the 128-byte row
+  int bt_off[4][2][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int r = ((NMAT == 2) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + (lane & 31);
-      bt_off[j][ks] = A_STAGE + r * (BK * 2) + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
-    }
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const int r = ((NMAT == 2) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + (lane & 31);
+        bt_off[j][ks][p2] = r * 128 + 16 * ((4 * p2 + 2 * ks + (lane >> 5)) ^ ((r >> 1) & 7));
+      }
   // fragment piece p of half-step ks from ring slot st, in the order the MFMAs consume them:
   // A0, B0 (two halves), B1, B2, B3, A1, A2, A3 (OUTIN: A0, B0, B1, B2, B3, A1, A2, A3, one read each)
   constexpr int NPIECE = OUTIN ? 8 : 12;
   u32x4_t fa[2][4], fb[2][4];
   u32x2_t bh[2][4][2];
-  auto read_piece = [&](int buf, const lds_u8* st, int ks, int p) {
+  // st: the step's A slot (and, [in, out], its weight sub-tiles); sb, p2: OUTIN pair slot and step within it
+  auto read_piece = [&](int buf, const lds_u8* st, const lds_u8* sb, int p2, int ks, int p) {
     if (OUTIN) {
       if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
-      else if (p <= 4) fb[buf][p - 1] = *(const __attribute__((address_space(3))) u32x4_t*)(st + bt_off[p - 1][ks]);
+      else if (p <= 4)
+        fb[buf][p - 1] = *(const __attribute__((address_space(3))) u32x4_t*)(sb + bt_off[p - 1][ks][p2]);
       else fa[buf][p - 4] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[p - 4][ks]);
     } else if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
     else if (p <= 8) {
@@ -180,38 +201,62 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   // multiplies buffer 1 while the copies of step kt+3 are issued and half-step 0 of step kt+1 is read.  Each MFMA
   // is followed by at most one copy or one LDS read, in a fixed order.  Copies past the last step re-read the last
   // step into a ring slot that is never read again, so every step issues 8 copies and the wait count is constant.
+  // OUTIN: the weight copies of pair q are issued in the B slots of steps 2 q - 3 and 2 q - 2 (4 each), so that
+  // step kt issues copies 4 ((kt + 1) % 2) .. +3 of pair (kt + 3) / 2; the prologue issues pair 0 and the first
+  // half of pair 1.
   const int KT = Ks / BK;
+  const lds_u8* bpairs = lds + NSTAGE * A_STAGE;
+  if constexpr (OUTIN) {
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
+    for (int n = 0; n < 4; ++n) copy_piece(0, 0, n);
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
-      if (s < NSTAGE - 2 || n < 4) copy_piece(s, min(s, KT - 1), n);
-  wait_vm<8 * (NSTAGE - 3) + 4>();  // step 0 landed (step 1 and half of step 2 may be in flight)
+    for (int c = 0; c < 8; ++c) copy_pair(0, c);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) copy_piece(1, min(1, KT - 1), n);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) copy_pair(1, c);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) copy_piece(2, min(2, KT - 1), n);
+    wait_vm<12>();  // step 0 (A and pair 0) landed
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        if (s < NSTAGE - 2 || n < 4) copy_piece(s, min(s, KT - 1), n);
+    wait_vm<8 * (NSTAGE - 3) + 4>();  // step 0 landed (step 1 and half of step 2 may be in flight)
+  }
   lds_barrier();
 #pragma unroll
-  for (int p = 0; p < NPIECE; ++p) read_piece(0, lds, 0, p);
+  for (int p = 0; p < NPIECE; ++p) read_piece(0, lds, bpairs, 0, 0, p);
   join_b(0);
   for (int kt = 0; kt < KT; ++kt) {
-    const lds_u8* st = lds + (kt % NSTAGE) * STAGE;
-    // second half of the copies of step kt+2 (its first half was issued after the barrier of step kt-1)
+    const lds_u8* st = lds + (kt % NSTAGE) * A_STRIDE;
+    const lds_u8* sb = bpairs + ((kt >> 1) % NPAIR) * B_PAIR;
+    // second half of the copies of step kt+2 (its first half was issued after the barrier of step kt-1); OUTIN:
+    // four copies of pair (kt + 3) / 2
     const int pstage = (kt + NSTAGE - 2) % NSTAGE, pk = min(kt + NSTAGE - 2, KT - 1);
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
-      if (m < NPIECE) read_piece(1, st, 1, m);
-      if (m >= 12) copy_piece(pstage, pk, m - 8);
+      if (m < NPIECE) read_piece(1, st, sb, kt & 1, 1, m);
+      if (m >= 12) {
+        if (OUTIN) copy_pair((kt + 3) >> 1, 4 * ((kt + 1) & 1) + (m - 12));
+        else copy_piece(pstage, pk, m - 8);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(1);
     wait_vm<8 * (NSTAGE - 3)>();  // step kt+1 landed (steps kt+2 .. may be in flight)
     lds_barrier();                       // ... for every wave; every wave finished reading step kt-1
     const int cstage = (kt + NSTAGE - 1) % NSTAGE, ck = min(kt + NSTAGE - 1, KT - 1);
-    const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * STAGE;
+    const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * A_STRIDE;
+    const lds_u8* nsb = bpairs + (((kt + 1) >> 1) % NPAIR) * B_PAIR;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
       if (m < 4) copy_piece(cstage, ck, m);
-      if (m < NPIECE) read_piece(0, nst, 0, m);
+      if (m < NPIECE) read_piece(0, nst, nsb, (kt + 1) & 1, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(0);
