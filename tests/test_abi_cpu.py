@@ -51,7 +51,7 @@ def test_workspace_size_and_splits(L):
     assert gm.workspace_size(8, 6100, 32768) == 0        # d not a multiple of 256
     ws_dec = gm.workspace_size(8, 6144, 32768)
     assert ws_dec >= 16 * 32768 * 2 + 16 * 6144 * 4 * gm.down_splits(8, 6144, 32768)
-    assert gm.down_splits(8, 6144, 32768) == 16
+    assert gm.down_splits(8, 6144, 32768) == 8
     assert gm.down_splits(8192, 6144, 32768) == 2   # LDS-tiled bf16 path splits K in two
     assert gm.down_splits(8192, 6144, 32768, 8, 2, gm.W8) == 1
     assert gm.down_splits(64, 128, 512, 8, 2, gm.F32) == 1
