@@ -1,7 +1,10 @@
 #!/usr/bin/env python3
 """Throughput of the Grok-1 MoE FFN layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16|prefill_bf16|int8_w8|skew_bf16|tiny_f32]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload decode_bf16|prefill_bf16|int8_w8|int8_w8_g8|skew_bf16|tiny_f32]
+                    [--weight-layout in_out|out_in] [--block] [--no-prefill] [--no-cpu-baseline]
+    python bench.py --library-gemm      (torch.mm / hipBLASLt on the prefill's per-expert shapes, for context)
 
 A step is one pass of the whole layer (router, binning, fused up-projection with GELU product, down-projection,
 combine) over one batch of seeded synthetic tokens, with weights and inputs already resident in HBM.  The step
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Grok-1 MoE layer tokens/s (T=8 decode, T=8192 prefill); % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_VALU_TFLOPS = 157.3       # MI355X fp32 vector ALU (published)
 
 
 def log(msg):
@@ -324,7 +328,13 @@ def main():
                       "experts": w.E, "top_k": 2, "experts_hit": nh, "down_splits": layer.S,
                       "rmsnorm_residual": bool(a.block), "weight_layout": a.weight_layout}}
     kernels = {"expert_up_ms": kms[0], "expert_down_ms": kms[1], "route_bin_ms": kms[2], "combine_ms": kms[3]}
-    if w.T <= 64:  # weight-streaming regime: HBM-bound, the up-projection (W1 and Wv) is the dominant kernel
+    if w.dtype == 0:  # the fp32 layer: vector-ALU kernels (tiny shapes: launch latency in practice)
+        fl = up_flops(w, T)
+        ach = fl / (kms[0] * 1e-3) / 1e12
+        res["roofline"] = {"bound": "alu", "kernel": "f32_tiled_kernel<2>", "achieved": ach,
+                           "peak": FP32_VALU_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP32_VALU_TFLOPS,
+                           "traffic": None, "algorithmic_flops": fl}
+    elif w.T <= 64:  # weight-streaming regime: HBM-bound, the up-projection (W1 and Wv) is the dominant kernel
         ub = up_bytes(w, nh, T)
         ach = ub / (kms[0] * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "up_stream_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
@@ -336,7 +346,8 @@ def main():
     else:
         fl = up_flops(w, T)
         ach = fl / (kms[0] * 1e-3) / 1e12
-        res["roofline"] = {"bound": "mfma", "kernel": "tiled_dma_kernel<2>" if w.dtype == 1 else "tiled_reg_kernel<2>", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+        kname = "tiled_dma_kernel<2>" if w.dtype == 1 else "tiled_reg_kernel<2>"
+        res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
                            "traffic": load_traffic(tname, "up"), "algorithmic_flops": fl}
         kernels["layer_TFLOPs"] = 3 * fl / 2 / (ms * 1e-3) / 1e12

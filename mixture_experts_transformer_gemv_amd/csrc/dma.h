@@ -23,7 +23,8 @@ __device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, uint32_
 // LDS transpose read: within each 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane
 // 4 r + j / 4 (r = 0..3).
 __device__ __forceinline__ u32x2_t lds_tr16(const lds_u8* p) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p)));
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p)));
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding (copies complete in issue order).

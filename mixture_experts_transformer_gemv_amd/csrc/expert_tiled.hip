@@ -30,25 +30,14 @@ constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements)
 }
 
-template <bool INT8> struct BRow;
-template <> struct BRow<false> {
-  typedef u32x4_t T;
-  static __device__ __forceinline__ T load(const void* base, size_t i) {
-    return *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + i);
-  }
-  static __device__ __forceinline__ void transpose(const T r[8], u32x4_t t[8]) { transpose8x8_bf16(r, t); }
-};
-template <> struct BRow<true> {
-  typedef u32x2_t T;
-  static __device__ __forceinline__ T load(const void* base, size_t i) {
-    return *reinterpret_cast<const u32x2_t*>(static_cast<const int8_t*>(base) + i);
-  }
-  static __device__ __forceinline__ void transpose(const T r[8], u32x4_t t[8]) { transpose8x8_i8_to_bf16(r, t); }
-};
+// Row piece of an int8 weight block: 8 bytes = 8 columns (or, [out, in], 8 k of one column).
+__device__ __forceinline__ u32x2_t load_i8x8(const void* base, size_t i) {
+  return *reinterpret_cast<const u32x2_t*>(static_cast<const int8_t*>(base) + i);
+}
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1).  B0/B1: weights [E, K, N].
 // out: h bf16 [slots, N] (NMAT = 2) or y f32 [slots, N] (NMAT = 1).
-template <int NMAT, bool INT8, bool GROUPED, bool OUTIN>
+template <int NMAT, bool GROUPED, bool OUTIN>
 __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restrict__ A, const void* __restrict__ B0,
                                                     const void* __restrict__ B1, const uint16_t* __restrict__ sc0,
                                                     const uint16_t* __restrict__ sc1, ScaleLayout sl,
@@ -56,8 +45,6 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
                                                     const int32_t* __restrict__ offsets,
                                                     const int32_t* __restrict__ perm, int K, int N, int E,
                                                     void* __restrict__ out) {
-  static_assert(INT8 || !GROUPED, "grouped scales belong to int8 weights");
-  typedef BRow<INT8> W;
   constexpr int BNM = BNT / NMAT;       // columns per matrix
   constexpr int TBM = GROUPED ? 128 : BM;  // rows per tile
   constexpr int MI = TBM / 64;          // 32-row MFMA blocks per wave
@@ -93,7 +80,7 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
 
   // GROUPED: scales of the 8 columns of this thread's B block (group 0), and the byte mask of those with a
   // non-zero scale in the group of the K step held in rb
-  const uint16_t* bscale = INT8 ? ((NMAT == 2 && mat == 1) ? sc1 : sc0) + size_t(e) * sl.estride + gcol : nullptr;
+  const uint16_t* bscale = ((NMAT == 2 && mat == 1) ? sc1 : sc0) + size_t(e) * sl.estride + gcol;
   u32x2_t bmask = {~0u, ~0u};
   auto set_bmask = [&](int grp) {
     const u32x4_t w = *reinterpret_cast<const u32x4_t*>(bscale + size_t(grp) * N);
@@ -106,13 +93,13 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
   };
 
   u32x4_t ra[NA];
-  typename W::T rb[8];
+  u32x2_t rb[8];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      rb[r] = OUTIN ? W::load(bmat, b_base + size_t(r) * K + k0) : W::load(bmat, b_base + size_t(k0 + r) * N);
+      rb[r] = OUTIN ? load_i8x8(bmat, b_base + size_t(r) * K + k0) : load_i8x8(bmat, b_base + size_t(k0 + r) * N);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -134,7 +121,7 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
 #pragma unroll
         for (int r = 0; r < 8; ++r) rb[r] &= bmask;
       }
-      W::transpose(rb, t);
+      transpose8x8_i8_to_bf16(rb, t);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4_t*>(&Bs[buf][(b_lds_row + c) * LDK + 8 * kb]) = t[c];
@@ -243,15 +230,14 @@ __global__ __launch_bounds__(256) void tiled_reg_kernel(const uint16_t* __restri
     __syncthreads();
   }
 
-  if constexpr (INT8) {  // the scale of the last group (GROUPED) or of the only one, then the plain epilogue
+  // the scale of the last group (GROUPED) or of the only one, then the plain epilogue
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sj = GROUPED ? cur[j] : bf16f(jscale[j][0]);
+  for (int j = 0; j < 4; ++j) {
+    const float sj = GROUPED ? cur[j] : bf16f(jscale[j][0]);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) acc[i][j] *= sj;
-    }
+    for (int i = 0; i < MI; ++i) acc[i][j] *= sj;
   }
-  tile::store_tile<NMAT, false, MI>(acc, wm, wn, lane, e, row0, rows, nbase, N, nullptr, nullptr, out);
+  tile::store_tile<NMAT, MI>(acc, wm, wn, lane, row0, rows, nbase, N, out);
 }
 
 hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
@@ -261,7 +247,7 @@ hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, co
   if (!int8) return launch_up_tiled_dma(x, w1, wv, outin, counts, offsets, perm, d, f, E, slots, h, s);
   const bool grouped = sl.gsize < d;
   const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2), grouped ? 128 : BM)), block(256);
-#define GM_UPT(GR, OI) tiled_reg_kernel<2, true, GR, OI><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, \
+#define GM_UPT(GR, OI) tiled_reg_kernel<2, GR, OI><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, \
                                                                              perm, d, f, E, h)
   if (grouped) { if (outin) GM_UPT(true, true); else GM_UPT(true, false); }
   else { if (outin) GM_UPT(false, true); else GM_UPT(false, false); }
@@ -275,7 +261,7 @@ hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* 
   if (!int8) return launch_down_tiled_dma(h, w2, outin, counts, offsets, d, f, E, slots, S, y, s);
   const bool grouped = sl.gsize < f;
   const dim3 grid(tile::grid_tiles(slots, E, d / BNT, grouped ? 128 : BM)), block(256);
-#define GM_DNT(GR, OI) tiled_reg_kernel<1, true, GR, OI><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, \
+#define GM_DNT(GR, OI) tiled_reg_kernel<1, GR, OI><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, \
                                                                              offsets, nullptr, f, d, E, y)
   if (grouped) { if (outin) GM_DNT(true, true); else GM_DNT(true, false); }
   else { if (outin) GM_DNT(false, true); else GM_DNT(false, false); }

@@ -24,8 +24,8 @@
 // one LDS fragment read or one copy (pinned with sched_barrier), so the copies (half of step kt+3 after the
 // barrier, the other half in the next half-step) and the fragments of the next half-step are issued in the
 // shadow of the 32-cycle MFMAs.  The down-projection may split K over gridDim.y workgroups (fp32 partial sums,
-// added by the combine) so that its smaller number of tiles still fills the chip.  Up-projection epilogue: the GELU product
-// tile is staged in the idle ring and written as 16-byte row pieces.
+// added by the combine) so that its smaller number of tiles still fills the chip.  Up-projection epilogue: the
+// GELU product tile is staged in the idle ring and written as 16-byte row pieces.
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
                                                         void* __restrict__ out, int64_t split_stride) {
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   int e, row0, rows, ntile;
-  if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile)) return;  // whole WG
+  if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile))
+    return;  // whole workgroup
 
   constexpr int LDS_BYTES = OUTIN ? NSTAGE * A_STAGE + NPAIR * B_PAIR : NSTAGE * STAGE;
   constexpr int A_STRIDE = OUTIN ? A_STAGE : STAGE;  // between ring slots of A
@@ -88,7 +89,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   // 256-byte row holds column chunk (lane & 15) ^ (4 (k & 3)).
   const int sub = wave >> 1;
   const uint16_t* bmat = (NMAT == 2 && sub == 1) ? B1 : B0;
-  const uint16_t* b_base = bmat + size_t(e) * K * N + size_t(16 * (wave & 1)) * N + nbase + ((NMAT == 1) ? 128 * sub : 0);
+  const uint16_t* b_base =
+      bmat + size_t(e) * K * N + size_t(16 * (wave & 1)) * N + nbase + ((NMAT == 1) ? 128 * sub : 0);
   const uint32_t b_voff = uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
   const uint32_t a_dst = lds0 + uint32_t(64 * wave) * (BK * 2);
   const uint32_t b_dst = lds0 + A_STAGE + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * 256;
@@ -185,7 +187,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   auto join_b = [&](int buf) {
     if (OUTIN) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[buf][j] = u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
+    for (int j = 0; j < 4; ++j)
+      fb[buf][j] = u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
   };
 
   f32x16_t acc[4][4];
@@ -290,8 +293,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
             *(const __attribute__((address_space(3))) u32x4_t*)(ht + r * 128 + c8);
     }
   } else {
-    tile::store_tile<NMAT, false>(acc, wm, wn, lane, e, row0, rows, nbase, N, nullptr, nullptr,
-                                  static_cast<float*>(out) + blockIdx.y * split_stride);
+    tile::store_tile<NMAT>(acc, wm, wn, lane, row0, rows, nbase, N,
+                           static_cast<float*>(out) + blockIdx.y * split_stride);
   }
 }
 

@@ -7,8 +7,9 @@
 // One workgroup of 4 waves per token (enough waves in flight even for a decode step of 8 tokens).  Each lane
 // accumulates its strided share of the d products in fp64: a product of two bf16 (or two fp32) values is exact
 // in fp64, so the only rounding is fp64 summation.  A fixed butterfly reduction inside each wave and a fixed
-// order across the 4 waves make the result deterministic.  Selection uses the fp64 logits (descending, lower expert index on
-// equal logits), which is the same order as the probabilities since softmax is strictly increasing.
+// order across the 4 waves make the result deterministic.  Selection uses the fp64 logits (descending, lower
+// expert index on equal logits), which is the same order as the probabilities since softmax is strictly
+// increasing.
 #include "common.h"
 #include "launch.h"
 
@@ -107,7 +108,8 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
   uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
   u += 0xFFFFFFFFFFFull + ((u >> 45) & 1ull);  // half of 2^45, minus one, plus the kept LSB
   u &= ~((1ull << 45) - 1ull);
-  return static_cast<uint16_t>(__float_as_uint(static_cast<float>(__longlong_as_double(static_cast<long long>(u)))) >> 16);
+  const float f = static_cast<float>(__longlong_as_double(static_cast<long long>(u)));  // exact: 8 significant bits
+  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
 }
 
 // Router with the pre-MoE RMSNorm in front ("Grok-1-BF16", section "Architecture": four norms per layer, one

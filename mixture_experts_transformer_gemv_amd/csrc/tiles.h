@@ -1,8 +1,7 @@
 // Tile scheduling and epilogue shared by the two LDS-tiled grouped-GEMM kernels (gfx950).
 //
 // Expert FFN, page "A functional bridge between openai/grok and xai-org/grok-1" (architecture diagram):
-// y = (GELU(x W1) (*) (x Wv)) W2; int8 weights times per-(expert, output channel) bf16 scales, page
-// "Grok-1-BF16", section "Conversion Details".
+// y = (GELU(x W1) (*) (x Wv)) W2.
 //
 // A workgroup of 4 waves computes a 256-row x 256-column output tile of the expert-sorted assignment slots:
 //   * up-projection (NMAT = 2): 128 columns of W1 and the same 128 columns of Wv; h = bf16(GELU(a) * b);
@@ -67,29 +66,25 @@ static inline unsigned grid_tiles(int slots, int E, int NT, int bm = BM) {
 }
 
 // Epilogue.  acc[i][j] (i < MI row blocks of 32): wave (wm, wn) rows wm*32*MI + 32 i .., column sub-tile j
-// (NMAT = 2: j = 0,1 are W1 columns wn*64 + 32 j, j = 2,3 the same Wv columns; NMAT = 1: columns wn*128 + 32 j).  Lane holds column
-// (lane & 31) of each sub-tile, rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5) of each 32-row block.
-template <int NMAT, bool INT8, int MI = 4>
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[MI][4], int wm, int wn, int lane, int e, int row0,
-                                           int rows, int nbase, int N, const uint16_t* sc0, const uint16_t* sc1,
-                                           void* out) {
+// (NMAT = 2: j = 0,1 are W1 columns wn*64 + 32 j, j = 2,3 the same Wv columns; NMAT = 1: columns wn*128 + 32 j).
+// Lane holds column (lane & 31) of each sub-tile, rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5) of each 32-row block.
+// NMAT = 2 writes h = bf16(GELU(a) * b) to h [slots, N]; NMAT = 1 writes the fp32 accumulators to y [slots, N].
+// Any scale has been applied to acc already.
+template <int NMAT, int MI = 4>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[MI][4], int wm, int wn, int lane, int row0, int rows,
+                                           int nbase, int N, void* out) {
   const int lr = lane & 31, rhalf = 4 * (lane >> 5);
   if (NMAT == 2) {
     uint16_t* h = static_cast<uint16_t*>(out);
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
       const int n = nbase + wn * 64 + jn * 32 + lr;
-      float s_a = 1.0f, s_b = 1.0f;
-      if (INT8) { s_a = bf16f(sc0[size_t(e) * N + n]); s_b = bf16f(sc1[size_t(e) * N + n]); }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * 32 * MI + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
-          if (r < rows) {
-            const float a = acc[i][jn][v] * s_a, b = acc[i][2 + jn][v] * s_b;
-            h[size_t(row0 + r) * N + n] = uint16_t(f2bf(gelu_erf(a) * b));
-          }
+          if (r < rows) h[size_t(row0 + r) * N + n] = uint16_t(f2bf(gelu_erf(acc[i][jn][v]) * acc[i][2 + jn][v]));
         }
       }
     }
@@ -98,13 +93,12 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[MI][4], int wm,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = nbase + wn * 128 + j * 32 + lr;
-      const float s = INT8 ? bf16f(sc0[size_t(e) * N + n]) : 1.0f;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * 32 * MI + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
-          if (r < rows) y[size_t(row0 + r) * N + n] = INT8 ? acc[i][j][v] * s : acc[i][j][v];
+          if (r < rows) y[size_t(row0 + r) * N + n] = acc[i][j][v];
         }
       }
     }
