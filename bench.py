@@ -50,7 +50,7 @@ def source_hash(files) -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-prefill", action="store_true", help="skip the companion T=8192 prefill measurement")
@@ -177,6 +177,9 @@ class Layer:
         wall = time.perf_counter() - t0
         k = np.array([[e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]), e[0].elapsed_time(e[1]),
                        e[3].elapsed_time(e[4])] for e in evs])
+        per_step = np.array([e[0].elapsed_time(e[4]) for e in evs])  # first to last event of each step, ms
+        self.step_stats = {"median": float(np.median(per_step)), "min": float(per_step.min()),
+                           "p90": float(np.percentile(per_step, 90)), "n": int(steps)}
         return wall, k.mean(axis=0)  # ms: up, down, route+bin, combine
 
 
@@ -222,19 +225,32 @@ def load_traffic(workload: str, kernel: str):
 
 def cpu_baseline(w, inp, oracle, synth, block=False):
     """The oracle as it stands, on a bounded sample of the workload (routing for all tokens, expert path on a few
-    rows), timed on this host's cores."""
+    rows), timed on this host's cores; and the same for one row on a single thread."""
     import torch
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if block:
+            ns = synth.make_norm_scales(w)
+            oracle.block_forward(inp, w.dtype, ns["pre_scale"], ns["post_scale"], ns["eps"], rows=rows)
+        else:
+            oracle.forward(inp, w.dtype, rows=rows)
+        return time.perf_counter() - t0
+
     rows = synth.sampled_rows(w.T, 2 if w.T <= 64 else 4)
-    t0 = time.perf_counter()
-    if block:
-        ns = synth.make_norm_scales(w)
-        oracle.block_forward(inp, w.dtype, ns["pre_scale"], ns["post_scale"], ns["eps"], rows=rows)
-    else:
-        oracle.forward(inp, w.dtype, rows=rows)
-    dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"{len(rows)} of {w.T} token rows of {w.name} through the float64 oracle (routing on all "
-                      f"{w.T} tokens, both selected experts per row), {dt:.1f} s"}
+    threads = torch.get_num_threads()
+    dt = run(rows)
+    res = {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(rows)} of {w.T} token rows of {w.name} through the float64 oracle (routing on all "
+                     f"{w.T} tokens, both selected experts per row), {dt:.1f} s"}
+    torch.set_num_threads(1)
+    try:
+        dt1 = run(rows[:1])
+    finally:
+        torch.set_num_threads(threads)
+    res["single_thread"] = {"value": 1 / dt1, "unit": "tokens/s", "cores": 1,
+                            "sample": f"1 token row of {w.name} (routing on all {w.T} tokens), {dt1:.1f} s"}
+    return res
 
 
 def library_gemm(steps, warmup):
@@ -352,6 +368,7 @@ def main():
                            "traffic": load_traffic(tname, "up"), "algorithmic_flops": fl}
         kernels["layer_TFLOPs"] = 3 * fl / 2 / (ms * 1e-3) / 1e12
     res["kernels"] = kernels
+    res["step_ms"] = layer.step_stats  # per step, first to last event on the stream: median, min, p90
     log(f"{w.name}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down {kms[1]:.3f} ms")
 
     if not a.no_prefill and w.name == "decode_bf16" and not a.block:
@@ -373,7 +390,8 @@ def main():
                                        "traffic": load_traffic(pname, "up"), "algorithmic_flops": fl},
                           "kernels": {"expert_up_ms": pk[0], "expert_down_ms": pk[1], "route_bin_ms": pk[2],
                                       "combine_ms": pk[3],
-                                      "expert_down_TFLOPs": fl / 2 / (pk[1] * 1e-3) / 1e12}}
+                                      "expert_down_TFLOPs": fl / 2 / (pk[1] * 1e-3) / 1e12},
+                          "step_ms": pl.step_stats}
         log(f"prefill: {pms:.3f} ms/step, {res['prefill']['value']:.0f} tokens/s")
         del pl, pdv
         torch.cuda.empty_cache()
