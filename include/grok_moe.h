@@ -24,9 +24,14 @@
  *     distinct workspaces may run concurrently.
  *   - Weight layout is [E, in, out]: W1 and Wv are [E, d, f], W2 is [E, f, d].  Scales (int8 only) are
  *     [E, 1, f] for W1 and Wv and [E, 1, d] for W2: one bf16 scale per (expert, output channel).
- *   - Supported shapes: k == 2, 2 <= E <= 64.  bf16 and int8 layers need d and f to be multiples of 256;
- *     the fp32 layer needs multiples of 64.  T may be any value >= 0 (T == 0 enqueues nothing).
+ *   - Supported shapes: k == 2, 2 <= E <= 64, d * f < 2^31.  bf16 and int8 layers need d and f to be multiples
+ *     of 256; the fp32 layer needs multiples of 64.  T may be any value in [0, 2^24] (T == 0 enqueues nothing).
  *     Other shapes return GROK_MOE_EUNSUPPORTED; they are never padded silently.
+ *   - Passes: the bf16 layer runs at most P = min((2^31 - 1) / (2 d), (2^31 - 1) / (4 f)) tokens per pass (its
+ *     tiled kernels address x and h with 32-bit offsets; P = 16383 at d = 6144, f = 32768).  The whole-layer
+ *     entry points split a larger T into ceil(T / P) passes of near-equal size over consecutive tokens, each
+ *     routed, binned and computed on its own (tokens are independent; expert_counts are summed); the step
+ *     entry points grok_moe_expert_up* / grok_moe_expert_down* take at most P tokens (else EUNSUPPORTED).
  */
 #ifndef GROK_MOE_H
 #define GROK_MOE_H
@@ -48,7 +53,8 @@ typedef enum { GROK_MOE_F32 = 0, GROK_MOE_BF16 = 1, GROK_MOE_W8 = 2 } grok_moe_d
 enum {
   GROK_MOE_OK = 0,
   GROK_MOE_EINVAL = -1,       /* NULL or misaligned pointer, negative size, unknown dtype */
-  GROK_MOE_EUNSUPPORTED = -2, /* valid but unsupported shape (k != 2, E outside [2,64], d/f granularity) */
+  GROK_MOE_EUNSUPPORTED = -2, /* valid but unsupported shape (k != 2, E outside [2,64], d/f granularity or
+                                 size, more than one pass of tokens in an expert step) */
   GROK_MOE_EWORKSPACE = -3,   /* workspace smaller than grok_moe_workspace_size() */
   GROK_MOE_EHIP = -4          /* a HIP launch failed */
 };
@@ -57,7 +63,8 @@ enum {
 const char* grok_moe_strerror(int status);
 
 /* Bytes of device workspace grok_moe_forward() needs for this shape (0 if the shape is invalid or T == 0).
- * The workspace holds routing results, the token permutation, h [k*T, f] and the partial expert outputs. */
+ * The workspace holds routing results, the token permutation, h [k*T, f] and the partial expert outputs of
+ * one pass (T tokens, or the larger pass size if T needs several passes). */
 size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
 
 /* The whole layer: router -> token binning -> fused up-projection with GELU product -> down-projection ->
@@ -107,7 +114,8 @@ int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void
                        const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                        int64_t T, int64_t d, int64_t f, int E, int k, int dtype, void* h, void* stream);
 
-/* Number of partial sums grok_moe_expert_down() splits the f axis into for this shape (>= 1). */
+/* Number of partial sums grok_moe_expert_down() splits the f axis into for this shape (>= 1; for a T of
+ * several passes, that of the first pass). */
 int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
 
 /* Down-projection: y[p, s] = sum over the p-th chunk of f of h[s] . W2[e] (* s2[e]), fp32, for every slot s

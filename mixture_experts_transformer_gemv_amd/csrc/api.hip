@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/grok_moe.h"
 #include "launch.h"
 
@@ -32,7 +34,29 @@ int check_shape(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
   if (T > kMaxTokens || d > (int64_t(1) << 20) || f > (int64_t(1) << 20)) return GROK_MOE_EUNSUPPORTED;
   const int64_t g = dtype == GROK_MOE_F32 ? 64 : 256;
   if (d % g != 0 || f % g != 0) return GROK_MOE_EUNSUPPORTED;
+  if (d * f >= (int64_t(1) << 31)) return GROK_MOE_EUNSUPPORTED;  // one expert matrix < 2^32 bytes (32-bit offsets)
   return GROK_MOE_OK;
+}
+
+// Tokens of one pass of the layer.  The LDS-tiled bf16 kernels address x [T, d] and h [2 T, f] with 32-bit byte
+// offsets below 2^31; longer batches run as several passes over consecutive token ranges (the layer treats
+// tokens independently; only the expert counts are summed).
+int64_t max_pass_tokens(int64_t d, int64_t f, int dtype) {
+  if (dtype != GROK_MOE_BF16) return kMaxTokens;
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  return std::max<int64_t>(kStreamMaxTokens + 1, std::min(lim / (2 * d), lim / (4 * f)));
+}
+
+// T tokens as n passes of near-equal size: the first `rem` passes take base + 1 tokens, the others base.
+struct Passes {
+  int64_t n, base, rem;
+  int64_t start(int64_t i) const { return i * base + std::min(i, rem); }
+  int64_t size(int64_t i) const { return base + (i < rem ? 1 : 0); }
+};
+Passes passes(int64_t T, int64_t d, int64_t f, int dtype) {
+  const int64_t m = max_pass_tokens(d, f, dtype);
+  const int64_t n = std::max<int64_t>(1, (T + m - 1) / m);
+  return Passes{n, T / n, T % n};
 }
 
 int down_splits(int64_t T, int64_t f, int dtype) {
@@ -147,17 +171,27 @@ hipError_t do_down(const void* h, const void* w2, const void* s2, const ScaleSpe
                                p.splits, i8, y, s);
 }
 
-// The whole layer (grok_moe_forward and its grouped-scale form); arguments validated by the caller.
-int run_layer(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
-              const void* sv, const void* s2, const ScaleSpec& sp, int64_t T, int64_t d, int64_t f, int E, int dtype,
-              float* out, const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
-              void* workspace, size_t workspace_bytes, void* stream) {
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
-  const Plan p = make_plan(T, d, f, E, dtype);
-  if (workspace_bytes < p.total) return GROK_MOE_EWORKSPACE;
+// Workspace of the whole layer: the larger of the two pass sizes (block: with the normed input).
+size_t workspace_need(int64_t T, int64_t d, int64_t f, int E, int dtype, bool block) {
+  const Passes ps = passes(T, d, f, dtype);
+  size_t need = 0;
+  for (int64_t n : {ps.base + (ps.rem ? 1 : 0), ps.base}) {
+    if (n <= 0) continue;
+    const Plan p = make_plan(n, d, f, E, dtype);
+    need = std::max(need, block ? p.total_block : p.total);
+  }
+  return need;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+// One pass of the layer over T tokens, its workspace at ws; the block form if pre_scale is given.  The counts of
+// the pass are written to expert_counts, or added to it if add_counts.
+hipError_t run_pass(const void* x, const void* pre_scale, const void* post_scale, double eps, const void* router_w,
+                    const void* w1, const void* wv, const void* w2, const void* s1, const void* sv, const void* s2,
+                    const ScaleSpec& sp, int64_t T, int64_t d, int64_t f, int E, int dtype, float* out,
+                    const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
+                    bool add_counts, char* ws, hipStream_t s) {
+  const Plan p = make_plan(T, d, f, E, dtype);
+  const bool bf = dtype != GROK_MOE_F32, block = pre_scale != nullptr;
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + p.o_idx);
   float* pr = topk_p ? topk_p : reinterpret_cast<float*>(ws + p.o_p);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + p.o_counts);
@@ -166,14 +200,40 @@ int run_layer(const void* x, const void* router_w, const void* w1, const void* w
   int32_t* inv = reinterpret_cast<int32_t*>(ws + p.o_inv);
   void* h = ws + p.o_h;
   float* y = reinterpret_cast<float*>(ws + p.o_y);
+  const void* xe = block ? ws + p.o_xn : x;  // the experts' input
 
-  hipError_t e = gm::launch_router(x, router_w, router_bias, int(T), int(d), E, dtype != GROK_MOE_F32, idx, pr, s);
+  hipError_t e = block ? gm::launch_router_norm(x, pre_scale, eps, router_w, router_bias, int(T), int(d), E, bf,
+                                                ws + p.o_xn, idx, pr, s)
+                       : gm::launch_router(x, router_w, router_bias, int(T), int(d), E, bf, idx, pr, s);
   if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
-  if (e == hipSuccess) e = do_up(x, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h, s);
+  if (e == hipSuccess) e = do_up(xe, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h, s);
   if (e == hipSuccess) e = do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, dtype, y, s);
-  if (e == hipSuccess) e = gm::launch_combine(y, p.splits, pr, inv, int(T), int(d), out, s);
-  if (e == hipSuccess && expert_counts)
-    e = hipMemcpyAsync(expert_counts, counts, size_t(E) * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = block ? gm::launch_combine_norm(y, p.splits, pr, inv, int(T), int(d), x, bf, post_scale, eps, out, s)
+              : gm::launch_combine(y, p.splits, pr, inv, int(T), int(d), out, s);
+  if (e == hipSuccess && expert_counts) e = gm::launch_counts_out(expert_counts, counts, E, add_counts, s);
+  return e;
+}
+
+// The whole layer (grok_moe_forward, grok_moe_block_forward and their forms) as passes over consecutive token
+// ranges; arguments validated by the caller.
+int run_layer(const void* x, const void* pre_scale, const void* post_scale, double eps, const void* router_w,
+              const void* w1, const void* wv, const void* w2, const void* s1, const void* sv, const void* s2,
+              const ScaleSpec& sp, int64_t T, int64_t d, int64_t f, int E, int dtype, float* out,
+              const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
+  if (workspace_bytes < workspace_need(T, d, f, E, dtype, pre_scale != nullptr)) return GROK_MOE_EWORKSPACE;
+  const Passes ps = passes(T, d, f, dtype);
+  const size_t xrow = size_t(d) * (dtype == GROK_MOE_F32 ? 4 : 2);  // bytes per token of x
+  hipError_t e = hipSuccess;
+  for (int64_t i = 0; i < ps.n && e == hipSuccess; ++i) {
+    const int64_t t0 = ps.start(i);
+    e = run_pass(static_cast<const char*>(x) + t0 * xrow, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv,
+                 s2, sp, ps.size(i), d, f, E, dtype, out + t0 * d, router_bias,
+                 topk_idx ? topk_idx + 2 * t0 : nullptr, topk_p ? topk_p + 2 * t0 : nullptr, expert_counts, i > 0,
+                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  }
   return hip_status(e);
 }
 
@@ -186,7 +246,8 @@ const char* grok_moe_strerror(int status) {
     case GROK_MOE_OK: return "ok";
     case GROK_MOE_EINVAL: return "invalid argument (NULL or misaligned pointer, negative size or unknown dtype)";
     case GROK_MOE_EUNSUPPORTED: return "unsupported shape (needs k == 2, 2 <= E <= 64, d and f multiples of 256 "
-                                       "for bf16/int8 or of 64 for fp32)";
+                                       "for bf16/int8 or of 64 for fp32, d * f < 2^31; the expert step entry "
+                                       "points take at most one pass of tokens)";
     case GROK_MOE_EWORKSPACE: return "workspace too small";
     case GROK_MOE_EHIP: return "HIP kernel launch failed";
     default: return "unknown status";
@@ -195,12 +256,12 @@ const char* grok_moe_strerror(int status) {
 
 size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
   if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK || T == 0) return 0;
-  return make_plan(T, d, f, E, dtype).total;
+  return workspace_need(T, d, f, E, dtype, false);
 }
 
 int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
   if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK) return 1;
-  return make_plan(T, d, f, E, dtype).splits;
+  return make_plan(passes(T, d, f, dtype).size(0), d, f, E, dtype).splits;
 }
 
 int grok_moe_forward_ex(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
@@ -223,8 +284,8 @@ int grok_moe_forward_ex(const void* x, const void* router_w, const void* w1, con
     return GROK_MOE_EINVAL;
   if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
   if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
-  return run_layer(x, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, dtype, out, router_bias, topk_idx, topk_p,
-                   expert_counts, workspace, workspace_bytes, stream);
+  return run_layer(x, nullptr, nullptr, 0.0, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, dtype, out,
+                   router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
 }
 
 int grok_moe_forward(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
@@ -271,6 +332,7 @@ int grok_moe_expert_up_ex(const void* x, const void* w1, const void* wv, const v
                           int dtype, void* h, void* stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
+  if (T > max_pass_tokens(d, f, dtype)) return GROK_MOE_EUNSUPPORTED;  // one pass only (32-bit offsets)
   if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
   ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
   if (dtype == GROK_MOE_W8) {
@@ -307,6 +369,7 @@ int grok_moe_expert_down_ex(const void* h, const void* w2, const void* s2, int w
                             int64_t f, int E, int k, int dtype, int splits, float* y, void* stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
+  if (T > max_pass_tokens(d, f, dtype)) return GROK_MOE_EUNSUPPORTED;  // one pass only (32-bit offsets)
   if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
   ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
   if (dtype == GROK_MOE_W8) {
@@ -346,7 +409,7 @@ int grok_moe_combine(const float* y, int splits, const float* topk_p, const int3
 
 size_t grok_moe_block_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
   if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK || T == 0) return 0;
-  return make_plan(T, d, f, E, dtype).total_block;
+  return workspace_need(T, d, f, E, dtype, true);
 }
 
 int grok_moe_route_norm(const void* x, const void* pre_scale, double eps, const void* router_w,
@@ -399,33 +462,8 @@ int grok_moe_block_forward_ex(const void* x, const void* pre_scale, const void* 
     return GROK_MOE_EINVAL;
   if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
   if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
-  const Plan p = make_plan(T, d, f, E, dtype);
-  if (workspace_bytes < p.total_block) return GROK_MOE_EWORKSPACE;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + p.o_idx);
-  float* pr = topk_p ? topk_p : reinterpret_cast<float*>(ws + p.o_p);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.o_counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + p.o_offsets);
-  int32_t* perm = reinterpret_cast<int32_t*>(ws + p.o_perm);
-  int32_t* inv = reinterpret_cast<int32_t*>(ws + p.o_inv);
-  void* h = ws + p.o_h;
-  float* y = reinterpret_cast<float*>(ws + p.o_y);
-  void* xn = ws + p.o_xn;
-
-  hipError_t e = gm::launch_router_norm(x, pre_scale, eps, router_w, router_bias, int(T), int(d), E,
-                                        dtype != GROK_MOE_F32, xn, idx, pr, s);
-  if (e == hipSuccess) e = gm::launch_bin(idx, int(T), E, counts, offsets, perm, inv, s);
-  if (e == hipSuccess) e = do_up(xn, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h, s);
-  if (e == hipSuccess) e = do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, dtype, y, s);
-  if (e == hipSuccess)
-    e = gm::launch_combine_norm(y, p.splits, pr, inv, int(T), int(d), x, dtype != GROK_MOE_F32, post_scale, eps, out,
-                                s);
-  if (e == hipSuccess && expert_counts)
-    e = hipMemcpyAsync(expert_counts, counts, size_t(E) * 4, hipMemcpyDeviceToDevice, s);
-  return hip_status(e);
+  return run_layer(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, dtype, out,
+                   router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
 }
 
 int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,

@@ -80,4 +80,16 @@ hipError_t launch_bin(const int32_t* idx, int T, int E, int32_t* counts, int32_t
   return hipGetLastError();
 }
 
+// Per-expert counts of one pass written (add = 0) or added (add = 1) to the caller's array, E <= 64.
+__global__ __launch_bounds__(64) void counts_out_kernel(int32_t* __restrict__ dst, const int32_t* __restrict__ src,
+                                                        int E, int add) {
+  const int e = threadIdx.x;
+  if (e < E) dst[e] = add ? dst[e] + src[e] : src[e];
+}
+
+hipError_t launch_counts_out(int32_t* dst, const int32_t* src, int E, bool add, hipStream_t s) {
+  counts_out_kernel<<<1, 64, 0, s>>>(dst, src, E, add ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace gm

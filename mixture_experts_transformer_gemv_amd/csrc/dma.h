@@ -20,6 +20,21 @@ __device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, uint32_
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(dst) : "m0");
 }
 
+// Descriptor of a raw (unstrided) buffer of `bytes` bytes at `base` for the copies below: a lane whose offset
+// is at or past `bytes` reads zeros and touches no memory.  Word 3 selects 32-bit data (required for the range
+// check of untyped loads).
+__device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{uint32_t(a), uint32_t(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// 16-byte buffer -> LDS copy of one wave: lane i reads buffer bytes [soff + voff, +16) (zeros if voff is out of
+// range; soff wave-uniform) and writes LDS bytes [dst + 16 i, dst + 16 i + 16).  Same waiting rules as g2lds16.
+__device__ __forceinline__ void b2lds16(const u32x4_t& rsrc, uint32_t soff, uint32_t voff, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               : : "v"(voff), "s"(rsrc), "s"(soff), "s"(dst) : "m0");
+}
+
 // LDS transpose read: within each 16-lane group, lane j receives element j % 4 of the 8 bytes addressed by lane
 // 4 r + j / 4 (r = 0..3).
 __device__ __forceinline__ u32x2_t lds_tr16(const lds_u8* p) {

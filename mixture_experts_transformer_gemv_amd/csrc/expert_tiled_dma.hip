@@ -45,17 +45,18 @@ constexpr int B_PAIR = BM * 2 * BK * 2;  // bytes: [256 weight rows][64 k] ([out
 constexpr int NPAIR = 3;                // pair slots
 }
 
-// A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16.  B0/B1: bf16 weights
-// [E, K, N], or [E, N, K] if OUTIN (B1 only for NMAT = 2).  out: h bf16 [slots, N] (NMAT = 2) or y f32 [slots, N]
-// (NMAT = 1).
+// A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16, a_bytes bytes in all (< 2^31).
+// B0/B1: bf16 weights [E, K, N], or [E, N, K] if OUTIN (B1 only for NMAT = 2).  out: h bf16 [slots, N] (NMAT = 2)
+// or y f32 [slots, N] (NMAT = 1).
 template <int NMAT, bool OUTIN>
 __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B0,
                                                         const uint16_t* __restrict__ B1,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ perm, int K, int N, int E,
-                                                        void* __restrict__ out, int64_t split_stride) {
+                                                        const int32_t* __restrict__ perm, uint32_t a_bytes, int K,
+                                                        int N, int E, void* __restrict__ out,
+                                                        int64_t split_stride) {
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   int e, row0, rows, ntile;
   if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile))
@@ -75,14 +76,20 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   const int kbase = blockIdx.y * Ks;
 
   // ---- copies.  A: wave w, piece i copies rows 64 w + 16 i + lane/4; lane's slot (lane & 3) of the 64-byte row
-  // holds k chunk (lane & 3) ^ ((row >> 2) & 3).  Byte offsets from A (32 bits: x and h are < 4 GiB).
+  // holds k chunk (lane & 3) ^ ((row >> 2) & 3).  Byte offsets from A (32 bits).  Rows past the expert's end (the
+  // tail tile) get an out-of-range offset, so their copies write zeros: those rows are never stored, and
+  // multiplying zeros takes markedly less power than multiplying data.
+  const u32x4_t a_rsrc = buffer_rsrc(A, a_bytes);
   uint32_t a_voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 64 * wave + 16 * i + (lane >> 2);
-    const int rr = min(r, rows - 1);  // rows past the expert's end repeat a valid row; never stored
-    const uint32_t arow = (NMAT == 2) ? uint32_t(perm[row0 + rr]) : uint32_t(row0 + rr);
-    a_voff[i] = (arow * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u;
+    if (r < rows) {
+      const uint32_t arow = (NMAT == 2) ? uint32_t(perm[row0 + r]) : uint32_t(row0 + r);
+      a_voff[i] = (arow * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u;
+    } else {
+      a_voff[i] = 0x80000000u;
+    }
   }
   // B: weight sub-tile sub = wave >> 1 (NMAT = 2: W1 / Wv columns nbase..+127; NMAT = 1: W2 columns
   // nbase + 128 sub ..+127); piece i copies k rows 16 (wave & 1) + 4 i + lane/16, lane's slot (lane & 15) of the
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   auto copy_piece = [&](int stage, int kt, int n) {
     const uint32_t so = uint32_t(stage) * A_STRIDE;
     if (n < 4)
-      g2lds16(A + size_t(kbase + kt * BK), a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
+      b2lds16(a_rsrc, uint32_t(kbase + kt * BK) * 2u, a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
     else
       g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - 4)) * N, b_voff,
               b_dst + so + uint32_t(4 * (n - 4)) * 256);
@@ -209,6 +216,17 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   // half of pair 1.
   const int KT = Ks / BK;
   const lds_u8* bpairs = lds + NSTAGE * A_STAGE;
+  // zeros in the A slots of rows past the expert's end, in every ring stage (written by this lane only; the
+  // out-of-range copies leave them zero)
+  if (rows < BM) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (a_voff[i] == 0x80000000u)
+#pragma unroll
+        for (int st = 0; st < NSTAGE; ++st)
+          *(__attribute__((address_space(3))) u32x4_t*)(lds + (a_dst - lds0) + st * A_STRIDE + 16 * i * (BK * 2) +
+                                                        16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+  }
   if constexpr (OUTIN) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) copy_piece(0, 0, n);
@@ -304,8 +322,11 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
   const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
   const uint16_t* b0 = static_cast<const uint16_t*>(w1);
   const uint16_t* b1 = static_cast<const uint16_t*>(wv);
-  if (outin) tiled_dma_kernel<2, true><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, d, f, E, h, 0);
-  else tiled_dma_kernel<2, false><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, d, f, E, h, 0);
+  const size_t xbytes = size_t(slots / 2) * d * 2;  // x: [slots / 2 tokens, d] (two slots per token)
+  if (xbytes >= (size_t(1) << 31) || size_t(2) * slots * f >= (size_t(1) << 31)) return hipErrorInvalidValue;
+  const uint32_t xb = uint32_t(xbytes);
+  if (outin) tiled_dma_kernel<2, true><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, xb, d, f, E, h, 0);
+  else tiled_dma_kernel<2, false><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, xb, d, f, E, h, 0);
   return hipGetLastError();
 }
 
@@ -315,10 +336,15 @@ hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, bool outin, 
   const dim3 grid(tile::grid_tiles(slots, E, d / BNT), S), block(256);
   const uint16_t* b0 = static_cast<const uint16_t*>(w2);
   const int64_t stride = int64_t(slots) * d;
+  const size_t hbytes = size_t(slots) * f * 2;  // h: [slots, f]
+  if (hbytes >= (size_t(1) << 31)) return hipErrorInvalidValue;
+  const uint32_t hb = uint32_t(hbytes);
   if (outin)
-    tiled_dma_kernel<1, true><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, f, d, E, y, stride);
+    tiled_dma_kernel<1, true><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, hb, f, d, E, y,
+                                                     stride);
   else
-    tiled_dma_kernel<1, false><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, f, d, E, y, stride);
+    tiled_dma_kernel<1, false><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, hb, f, d, E, y,
+                                                      stride);
   return hipGetLastError();
 }
 

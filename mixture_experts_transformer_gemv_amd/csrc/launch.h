@@ -29,6 +29,7 @@ hipError_t launch_combine_norm(const float* y, int S, const float* p, const int3
 // Histogram + scan + stable permutation of the k = 2 assignments per token (one workgroup).
 hipError_t launch_bin(const int32_t* idx, int T, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                       int32_t* inv, hipStream_t s);
+hipError_t launch_counts_out(int32_t* dst, const int32_t* src, int E, bool add, hipStream_t s);
 
 // Combine: out[t] = sum_j p[t,j] * sum_s y[s, inv[t,j]].
 hipError_t launch_combine(const float* y, int S, const float* p, const int32_t* inv, int T, int d, float* out,

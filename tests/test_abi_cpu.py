@@ -60,6 +60,35 @@ def test_workspace_size_and_splits(L):
     assert gm.workspace_size(64, 128, 512, 8, 2, gm.F32) >= 128 * 512 * 4 + 128 * 128 * 4
 
 
+def test_long_batches_run_in_passes(L):
+    """bf16 at d = 6144, f = 32768 runs at most 16383 tokens per pass (32-bit offsets into x and h); a longer
+    batch is split into near-equal passes, and the workspace is that of the larger pass."""
+    import mixture_experts_transformer_gemv_amd as gm
+    d, f = 6144, 32768
+    assert gm.workspace_size(16383, d, f) > gm.workspace_size(16382, d, f)      # one pass
+    assert gm.workspace_size(16384, d, f) == gm.workspace_size(8192, d, f)      # two passes of 8192
+    assert gm.workspace_size(16385, d, f) == gm.workspace_size(8193, d, f)      # 8193 + 8192
+    assert gm.workspace_size(50000, d, f) == gm.workspace_size(12500, d, f)     # four passes
+    assert gm.block_workspace_size(20000, d, f) == gm.block_workspace_size(10000, d, f)
+    assert gm.down_splits(20000, d, f) == 2
+    # int8 and fp32 layers address with 64-bit offsets: one pass
+    assert gm.workspace_size(20000, d, f, 8, 2, gm.W8) > gm.workspace_size(10000, d, f, 8, 2, gm.W8)
+    # the limit comes from h [2 T, f] (and from x [T, d] when d is large)
+    assert gm.workspace_size(2047, 256, 1 << 18) > gm.workspace_size(2046, 256, 1 << 18)  # P = 2047: one pass
+    assert gm.workspace_size(2048, 256, 1 << 18) == gm.workspace_size(1024, 256, 1 << 18)
+    assert gm.workspace_size(2100, 256, 1 << 18) == gm.workspace_size(1050, 256, 1 << 18)
+    assert gm.workspace_size(1100, 1 << 20, 256) == gm.workspace_size(550, 1 << 20, 256)  # P = 1023
+    # one expert matrix must stay below 2^32 bytes
+    assert gm.workspace_size(8, 1 << 20, 1 << 11) == 0
+    # the expert steps take one pass at most (rejected on the host, before any pointer is read)
+    fake = ctypes.c_void_p(0x100000)
+    assert L.grok_moe_expert_up(fake, fake, fake, None, None, fake, fake, fake, 16384, d, f, 8, 2, 1, fake,
+                                None) == -2
+    assert L.grok_moe_expert_up(fake, fake, fake, None, None, fake, fake, None, 16383, d, f, 8, 2, 1, fake,
+                                None) == -1
+    assert L.grok_moe_expert_down(fake, fake, None, fake, fake, 16384, d, f, 8, 2, 1, 2, fake, None) == -2
+
+
 def _fwd(L, **kw):
     fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
     a = dict(x=fake, router_w=fake, w1=fake, wv=fake, w2=fake, s1=None, sv=None, s2=None, T=8, d=256, f=512, E=8,
