@@ -251,7 +251,10 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
   for (int p = 0; p < NPIECE; ++p) read_piece(0, lds, bpairs, 0, 0, p);
   join_b(0);
-  for (int kt = 0; kt < KT; ++kt) {
+  // One K step; P is the step's parity (kt & 1), a compile-time constant so that the [out, in] forms index their
+  // pair-slot offset arrays with constants (a runtime index turns each into a chain of selects).
+  auto kstep = [&](int kt, auto parity) {
+    constexpr int P = decltype(parity)::value;
     const lds_u8* st = lds + (kt % NSTAGE) * A_STRIDE;
     const lds_u8* sb = bpairs + ((kt >> 1) % NPAIR) * B_PAIR;
     // second half of the copies of step kt+2 (its first half was issued after the barrier of step kt-1); OUTIN:
@@ -260,9 +263,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
-      if (m < NPIECE) read_piece(1, st, sb, kt & 1, 1, m);
+      if (m < NPIECE) read_piece(1, st, sb, P, 1, m);
       if (m >= 12) {
-        if (OUTIN) copy_pair((kt + 3) >> 1, 4 * ((kt + 1) & 1) + (m - 12));
+        if (OUTIN) copy_pair((kt + 3) >> 1, 4 * (1 - P) + (m - 12));
         else copy_piece(pstage, pk, m - 8);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -277,10 +280,18 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
       if (m < 4) copy_piece(cstage, ck, m);
-      if (m < NPIECE) read_piece(0, nst, nsb, (kt + 1) & 1, 0, m);
+      if (m < NPIECE) read_piece(0, nst, nsb, 1 - P, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(0);
+  };
+  if constexpr (OUTIN) {
+    for (int kt = 0; kt < KT; kt += 2) {  // KT is even: K steps come in pairs
+      kstep(kt, std::integral_constant<int, 0>{});
+      kstep(kt + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int kt = 0; kt < KT; ++kt) kstep(kt, std::integral_constant<int, 0>{});  // parity unused
   }
   asm volatile("s_waitcnt vmcnt(0)");
 
