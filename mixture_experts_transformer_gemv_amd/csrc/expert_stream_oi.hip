@@ -44,7 +44,11 @@ struct OiCfg {
   static constexpr int WROWS_PER_COPY = 1024 / ROWB;           // 4 or 8
   static constexpr int ABYTES = MT * 16 * OI_AROW;             // token tile per stage
   static constexpr int STAGE = NMAT * WTILE + ABYTES;
-  static constexpr int NSTG = (OI_LDS / STAGE) < 4 ? (OI_LDS / STAGE) : 4;
+  // ring depth: at most 4 stages; two workgroups per CU (80 KB each) where that leaves at least 3 stages, else
+  // one workgroup with up to 144 KB (measured on MI355X: two resident rings keep more copies in flight; 3 stages
+  // for 24 KB int8 up-projection stages: up-projection with grouped scales 0.65 -> 0.56 ms at T = 64)
+  static constexpr int NSTG2 = (80 * 1024 / STAGE) < 4 ? (80 * 1024 / STAGE) : 4;
+  static constexpr int NSTG = NSTG2 >= 3 ? NSTG2 : ((OI_LDS / STAGE) < 4 ? (OI_LDS / STAGE) : 4);
   static constexpr int A_PER_WAVE = ABYTES / 1024 / 4;         // = MT
   static constexpr int CPW = NMAT * W_PER_WAVE + A_PER_WAVE;   // copies per wave per stage
   static_assert(NSTG >= 2, "stage ring does not fit");
