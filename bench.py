@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-prefill", action="store_true", help="skip the companion T=8192 prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=10, help="timed prefill steps (0: no prefill, as --no-prefill)")
     ap.add_argument("--block", action="store_true",
                     help="time the MoE block (pre-MoE RMSNorm, MoE, post-MoE RMSNorm, residual) instead of the layer")
     ap.add_argument("--weight-layout", choices=["in_out", "out_in"], default="in_out",
@@ -64,7 +64,10 @@ def parse():
                     help="only time torch.matmul (hipBLASLt) bf16 on the prefill's per-expert GEMM shapes, for context")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.steps < 1 or a.warmup < 0 or a.prefill_steps < 0:
+        ap.error("--steps must be >= 1; --warmup and --prefill-steps >= 0")
+    return a
 
 
 class Layer:
@@ -371,7 +374,7 @@ def main():
     res["step_ms"] = layer.step_stats  # per step, first to last event on the stream: median, min, p90
     log(f"{w.name}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down {kms[1]:.3f} ms")
 
-    if not a.no_prefill and w.name == "decode_bf16" and not a.block:
+    if not a.no_prefill and a.prefill_steps > 0 and w.name == "decode_bf16" and not a.block:
         pw = synth.WORKLOADS["prefill_bf16"]
         pinp = synth.make_inputs(pw, weights=wts)
         pdv = dict(layer.dv)  # the decode layer's weights, already in the chosen layout

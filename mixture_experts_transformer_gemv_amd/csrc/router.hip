@@ -4,12 +4,14 @@
 // logits come from a Dense gate with one output per expert, the gates are the softmax of the logits (no noise
 // at inference), and top_k with k = 2 returns the two largest gates with their indices.
 //
-// One workgroup of 4 waves per token (enough waves in flight even for a decode step of 8 tokens).  Each lane
-// accumulates its strided share of the d products in fp64: a product of two bf16 (or two fp32) values is exact
-// in fp64, so the only rounding is fp64 summation.  A fixed butterfly reduction inside each wave and a fixed
-// order across the 4 waves make the result deterministic.  Selection uses the fp64 logits (descending, lower
-// expert index on equal logits), which is the same order as the probabilities since softmax is strictly
-// increasing.
+// One workgroup per token.  For a small batch (a decode step) the workgroup has one thread per 8-element chunk
+// of d (up to 1024 threads), so every load of the token is issued at once and the kernel pays one memory latency;
+// for a large batch it has 4 waves, each thread striding over d.  Each thread accumulates its products in fp64:
+// a product of two bf16 (or two fp32) values is exact in fp64, so the only rounding is fp64 summation.  A fixed
+// butterfly inside each wave and a fixed order across the waves make the result deterministic.  Selection runs
+// on one wave with one lane per expert: the fp64 logits in descending order, the lower expert index first on
+// equal logits (the same order as the probabilities, since softmax is strictly increasing), and the softmax
+// denominator summed by a butterfly (every lane obtains the same sum).
 #include "common.h"
 #include "launch.h"
 
@@ -32,51 +34,87 @@ template <> struct Vec8<false> {
   }
 };
 
-// Selection from the per-wave partial logits: softmax over all E (fp64), the two largest logits with the lower
-// expert index first on equal logits.
-template <int EMAX>
-__device__ __forceinline__ void select_top2(const double (&part)[4][EMAX], const float* bias, int E, int t,
-                                            int32_t* idx, float* p) {
-  double l[EMAX];
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e)
-    l[e] = (e < E) ? ((part[0][e] + part[1][e]) + (part[2][e] + part[3][e])) + (bias ? double(bias[e]) : 0.0) : 0.0;
-  int e1 = 0;
-#pragma unroll
-  for (int e = 1; e < EMAX; ++e)
-    if (e < E && l[e] > l[e1]) e1 = e;
-  int e2 = -1;
-  double l2 = 0.0, l1 = l[0];
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < E && e != e1 && (e2 < 0 || l[e] > l2)) { e2 = e; l2 = l[e]; }
-    if (e == e1) l1 = l[e];
-  }
-  double s = 0.0;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e)
-    if (e < E) s += exp(l[e] - l1);
-  idx[2 * t] = e1;
-  idx[2 * t + 1] = e2;
-  p[2 * t] = float(1.0 / s);
-  p[2 * t + 1] = float(exp(l2 - l1) / s);
+constexpr int kRouterMaxWaves = 16;
+constexpr int kRouterWideTokens = 256;  // batches up to this many tokens use the wide workgroups
+
+// (value, index) order of the top-k: larger value first, lower index first on equal values.
+__device__ __forceinline__ bool ranks_before(double a, int ia, double b, int ib) {
+  return a > b || (a == b && ia < ib);
 }
 
+// The largest (value, index) pair over the wave, the same in every lane.
+__device__ __forceinline__ void wave_top(double& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(i, off, 64);
+    if (ranks_before(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+}
+
+// Selection from the per-wave partial logits part[w][e] (w < nw), called by one whole wave: lane e holds expert
+// e's logit (partials summed in ascending w, then the bias), the two largest logits with the lower expert index
+// first on equal logits, and their softmax probabilities over all E.  Lane 0 writes the results of token t.
+template <int EMAX>
+__device__ __forceinline__ void select_top2(const double (*part)[EMAX], int nw, const float* bias, int E, int t,
+                                            int lane, int32_t* idx, float* p) {
+  const bool valid = lane < E;
+  double l = 0.0;
+  if (valid) {
+    l = part[0][lane];
+    for (int w = 1; w < nw; ++w) l += part[w][lane];
+    if (bias) l += double(bias[lane]);
+  }
+  double v1 = valid ? l : -__DBL_MAX__;
+  int e1 = valid ? lane : 64 + lane;
+  wave_top(v1, e1);
+  double v2 = (valid && lane != e1) ? l : -__DBL_MAX__;
+  int e2 = (valid && lane != e1) ? lane : 64 + lane;
+  wave_top(v2, e2);
+  double ex = valid ? exp(l - v1) : 0.0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ex += __shfl_xor(ex, off, 64);
+  if (lane == 0) {
+    idx[2 * t] = e1;
+    idx[2 * t + 1] = e2;
+    p[2 * t] = float(1.0 / ex);
+    p[2 * t + 1] = float(exp(v2 - v1) / ex);
+  }
+}
+
+// Per-wave butterfly of the per-thread partial logits, then the selection by wave 0.
+template <int EMAX>
+__device__ __forceinline__ void reduce_select(double (&acc)[EMAX], double (*part)[EMAX], const float* bias, int E,
+                                              int t, int32_t* idx, float* p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
+  }
+  __syncthreads();
+  if (wave == 0) select_top2<EMAX>(part, nw, bias, E, t, lane, idx, p);
+}
+
+// Up to 1024 threads for E <= 16 experts; 256 (registers for 32 or 64 fp64 partial logits) beyond.
+template <int EMAX> constexpr int router_max_threads() { return EMAX <= 16 ? 1024 : 256; }
+
 template <bool BF16, int EMAX>
-__global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict__ x, const void* __restrict__ rw,
-                                                          const float* __restrict__ bias, int T, int d, int E,
-                                                          int32_t* __restrict__ idx, float* __restrict__ p) {
-  // One workgroup (4 waves) per token; wave w accumulates the k in its quarter of d, lane-strided by 8.
-  __shared__ double part[4][EMAX];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(router_max_threads<EMAX>()) void router_topk_kernel(const void* __restrict__ x, const void* __restrict__ rw,
+                                                           const float* __restrict__ bias, int T, int d, int E,
+                                                           int32_t* __restrict__ idx, float* __restrict__ p) {
+  // One workgroup per token; thread i accumulates the 8-element chunks 8 i, 8 (i + blockDim), ... of d.
+  __shared__ double part[kRouterMaxWaves][EMAX];
   const int t = blockIdx.x;
   double acc[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) acc[e] = 0.0;
   const int64_t xrow = int64_t(t) * d;
-  const int q = d >> 2;  // d is a multiple of 64, so each quarter is a multiple of 16
-  const int kend = (wave + 1) * q;
-  for (int k0 = wave * q + lane * 8; k0 < kend; k0 += 512) {
+  for (int k0 = 8 * threadIdx.x; k0 < d; k0 += 8 * blockDim.x) {
     float xv[8];
     Vec8<BF16>::load(x, xrow + k0, xv);
 #pragma unroll
@@ -89,17 +127,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
       }
     }
   }
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc[e] += __shfl_xor(acc[e], off, 64);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) select_top2<EMAX>(part, bias, E, t, idx, p);
+  reduce_select<EMAX>(acc, part, bias, E, t, idx, p);
 }
 
 // float64 -> bf16 bit pattern with a single round-to-nearest-even step (bf16 keeps 8 significant bits, so 45
@@ -123,7 +151,7 @@ __global__ __launch_bounds__(256) void router_norm_kernel(const void* __restrict
                                                           const float* __restrict__ bias, int T, int d, int E,
                                                           void* __restrict__ xn, int32_t* __restrict__ idx,
                                                           float* __restrict__ p) {
-  __shared__ double part[4][EMAX];
+  __shared__ double part[kRouterMaxWaves][EMAX];
   __shared__ double ssq[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x;
@@ -184,23 +212,15 @@ __global__ __launch_bounds__(256) void router_norm_kernel(const void* __restrict
       }
     }
   }
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc[e] += __shfl_xor(acc[e], off, 64);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) select_top2<EMAX>(part, bias, E, t, idx, p);
+  reduce_select<EMAX>(acc, part, bias, E, t, idx, p);
 }
 
 template <bool BF16>
 static hipError_t launch_router_t(const void* x, const void* rw, const float* bias, int T, int d, int E, int32_t* idx,
                                   float* p, hipStream_t s) {
-  const dim3 grid(T), block(256);
+  // small batches: one thread per 8-element chunk of d (all loads in flight at once); large: 4 waves per token
+  const int wide = (d / 8 + 63) / 64 * 64 < 1024 ? (d / 8 + 63) / 64 * 64 : 1024;
+  const dim3 grid(T), block(T <= kRouterWideTokens && E <= 16 ? wide : 256);
   if (E <= 8) router_topk_kernel<BF16, 8><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
   else if (E <= 16) router_topk_kernel<BF16, 16><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
   else if (E <= 32) router_topk_kernel<BF16, 32><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
