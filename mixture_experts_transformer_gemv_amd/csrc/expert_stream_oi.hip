@@ -44,11 +44,14 @@ struct OiCfg {
   static constexpr int WROWS_PER_COPY = 1024 / ROWB;           // 4 or 8
   static constexpr int ABYTES = MT * 16 * OI_AROW;             // token tile per stage
   static constexpr int STAGE = NMAT * WTILE + ABYTES;
-  // ring depth: at most 4 stages; two workgroups per CU (80 KB each) where that leaves at least 3 stages, else
-  // one workgroup with up to 144 KB (measured on MI355X: two resident rings keep more copies in flight; 3 stages
-  // for 24 KB int8 up-projection stages: up-projection with grouped scales 0.65 -> 0.56 ms at T = 64)
+  // ring depth (measured on MI355X).  Up-projection: at most 4 stages; two workgroups per CU (80 KB each) where
+  // that leaves at least 3 stages, else one workgroup with up to 144 KB (two resident rings keep more copies in
+  // flight: int8 with grouped scales 0.65 -> 0.56 ms at T = 64).  Down-projection: 2 stages, so that 3-4
+  // workgroups share a CU and the whole grid (one workgroup per 64 columns and expert, every chunk of f) runs
+  // in one round (bf16 T = 8: 0.578 -> 0.549 ms against 4 stages over 6 rounds).
   static constexpr int NSTG2 = (80 * 1024 / STAGE) < 4 ? (80 * 1024 / STAGE) : 4;
-  static constexpr int NSTG = NSTG2 >= 3 ? NSTG2 : ((OI_LDS / STAGE) < 4 ? (OI_LDS / STAGE) : 4);
+  static constexpr int NSTG =
+      NMAT == 1 ? 2 : (NSTG2 >= 3 ? NSTG2 : ((OI_LDS / STAGE) < 4 ? (OI_LDS / STAGE) : 4));
   static constexpr int A_PER_WAVE = ABYTES / 1024 / 4;         // = MT
   static constexpr int CPW = NMAT * W_PER_WAVE + A_PER_WAVE;   // copies per wave per stage
   static_assert(NSTG >= 2, "stage ring does not fit");
@@ -302,7 +305,7 @@ hipError_t launch_up_stream_oi(const uint16_t* x, const void* w1, const void* wv
 hipError_t launch_down_stream_oi(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl,
                                  const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots,
                                  int S, bool int8, int mt, float* y, hipStream_t s) {
-  const int spw = S >= 4 ? S / 4 : 1;  // chunks per workgroup: 4 workgroup rows over the S chunks
+  const int spw = S;  // chunks per workgroup: all of them (partial sums still stored per chunk)
   const dim3 grid(d / OI_COLS, S / spw, E);
   const int64_t stride = int64_t(slots) * d;
   const bool grouped = int8 && sl.gsize < f;
