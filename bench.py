@@ -356,7 +356,8 @@ def main():
     elif w.T <= 64:  # weight-streaming regime: HBM-bound, the up-projection (W1 and Wv) is the dominant kernel
         ub = up_bytes(w, nh, T)
         ach = ub / (kms[0] * 1e-3) / 1e9
-        res["roofline"] = {"bound": "hbm", "kernel": "up_stream_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
+        kname = "oi_stream_kernel<2>" if a.weight_layout == "out_in" else "up_stream_kernel"
+        res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                            "traffic": load_traffic(tname, "up"), "algorithmic_bytes": ub}
         db = down_bytes(w, nh, T, layer.S)
@@ -365,7 +366,8 @@ def main():
     else:
         fl = up_flops(w, T)
         ach = fl / (kms[0] * 1e-3) / 1e12
-        kname = "tiled_dma_kernel<2>" if w.dtype == 1 else "tiled_reg_kernel<2>"
+        oi = "true" if a.weight_layout == "out_in" else "false"
+        kname = f"tiled_dma_kernel<2, {oi}>" if w.dtype == 1 else f"tiled_reg_kernel<2, false, {oi}>"
         res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
                            "traffic": load_traffic(tname, "up"), "algorithmic_flops": fl}
@@ -387,7 +389,8 @@ def main():
         res["prefill"] = {"workload": pname, "T": pw.T, "value": pw.T / (pms / 1e3), "unit": "tokens/s",
                           "ms_per_step": pms, "steps": a.prefill_steps,
                           "layer_TFLOPs": 3 * fl / 2 / (pms * 1e-3) / 1e12,
-                          "roofline": {"bound": "mfma", "kernel": "tiled_dma_kernel<2>",
+                          "roofline": {"bound": "mfma",
+                                       "kernel": f"tiled_dma_kernel<2, {str(a.weight_layout == 'out_in').lower()}>",
                                        "achieved": fl / (pk[0] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": fl / (pk[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                                        "traffic": load_traffic(pname, "up"), "algorithmic_flops": fl},
