@@ -42,6 +42,13 @@ __device__ __forceinline__ u32x2_t lds_tr16(const lds_u8* p) {
       u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p)));
 }
 
+// LDS 8-bit transpose read: within each 16-lane group, lane j receives byte j % 8 of the 8 bytes addressed by
+// lane 2 r + j / 8 (r = 0..7), byte r of the result from lane 2 r + j / 8.
+__device__ __forceinline__ u32x2_t lds_tr8(const lds_u8* p) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p)));
+}
+
 // Wait until at most N vector memory operations of this wave are outstanding (copies complete in issue order).
 template <int N> __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");

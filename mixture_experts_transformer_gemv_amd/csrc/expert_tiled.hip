@@ -244,8 +244,10 @@ hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, co
                            const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, bool int8,
                            uint16_t* h, hipStream_t s) {
-  if (!int8) return launch_up_tiled_dma(x, w1, wv, outin, counts, offsets, perm, d, f, E, slots, h, s);
   const bool grouped = sl.gsize < d;
+  if (!int8 || (!grouped && !outin))  // bf16, and int8 with one scale group from [in, out] storage: direct copies
+    return launch_up_tiled_dma(x, w1, wv, s1, sv, sl.estride, int8, outin, counts, offsets, perm, d, f, E, slots,
+                               h, s);
   const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2), grouped ? 128 : BM)), block(256);
 #define GM_UPT(GR, OI) tiled_reg_kernel<2, GR, OI><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, \
                                                                              perm, d, f, E, h)
@@ -258,8 +260,9 @@ hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, co
 hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl, bool outin,
                              const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                              bool int8, float* y, hipStream_t s) {
-  if (!int8) return launch_down_tiled_dma(h, w2, outin, counts, offsets, d, f, E, slots, S, y, s);
   const bool grouped = sl.gsize < f;
+  if (!int8 || (!grouped && !outin))
+    return launch_down_tiled_dma(h, w2, s2, sl.estride, int8, outin, counts, offsets, d, f, E, slots, S, y, s);
   const dim3 grid(tile::grid_tiles(slots, E, d / BNT, grouped ? 128 : BM)), block(256);
 #define GM_DNT(GR, OI) tiled_reg_kernel<1, GR, OI><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, \
                                                                              offsets, nullptr, f, d, E, y)

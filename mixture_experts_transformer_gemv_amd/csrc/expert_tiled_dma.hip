@@ -39,25 +39,32 @@ using tile::BNT;
 constexpr int BK = 32;                  // K per ring stage
 constexpr int NSTAGE = 4;               // ring depth
 constexpr int A_STAGE = BM * BK * 2;    // bytes: [256 rows][32 k]
-constexpr int B_SUB = BK * 128 * 2;     // bytes: one [32 k][128 columns] weight sub-tile
-constexpr int STAGE = A_STAGE + 2 * B_SUB;
+template <bool INT8> constexpr int b_sub() { return BK * 128 * (INT8 ? 1 : 2); }  // bytes: [32 k][128 col]
 constexpr int B_PAIR = BM * 2 * BK * 2;  // bytes: [256 weight rows][64 k] ([out, in] weights)
 constexpr int NPAIR = 3;                // pair slots
 }
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16, a_bytes bytes in all (< 2^31).
-// B0/B1: bf16 weights [E, K, N], or [E, N, K] if OUTIN (B1 only for NMAT = 2).  out: h bf16 [slots, N] (NMAT = 2)
+// B0/B1: weights [E, K, N] (bf16, or int8 if INT8), or bf16 [E, N, K] if OUTIN (B1 only for NMAT = 2).  INT8:
+// per-column bf16 scales s0 (of B0), s1 (of B1) at expert stride s_estride.  out: h bf16 [slots, N] (NMAT = 2)
 // or y f32 [slots, N] (NMAT = 1).
-template <int NMAT, bool OUTIN>
-__global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restrict__ A,
-                                                        const uint16_t* __restrict__ B0,
-                                                        const uint16_t* __restrict__ B1,
+template <int NMAT, bool OUTIN, bool INT8>
+__global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restrict__ A, const void* __restrict__ B0,
+                                                        const void* __restrict__ B1,
+                                                        const uint16_t* __restrict__ s0,
+                                                        const uint16_t* __restrict__ s1, int64_t s_estride,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ perm, uint32_t a_bytes, int K,
                                                         int N, int E, void* __restrict__ out,
                                                         int64_t split_stride) {
+  static_assert(!(OUTIN && INT8), "int8 weights are tiled from [E, K, N] storage");
   constexpr int BNM = BNT / NMAT;  // columns per matrix
+  constexpr int B_SUB = b_sub<INT8>();
+  constexpr int STAGE = A_STAGE + 2 * B_SUB;
+  constexpr int WB = INT8 ? 1 : 2;             // bytes per weight
+  constexpr int BCOPIES = INT8 ? 2 : 4;        // 1 KB weight copies per wave and K step ([in, out])
+  constexpr int CPS = 4 + BCOPIES;             // copies per wave and K step ([out, in]: 4 + 4)
   int e, row0, rows, ntile;
   if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile))
     return;  // whole workgroup
@@ -92,15 +99,20 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     }
   }
   // B: weight sub-tile sub = wave >> 1 (NMAT = 2: W1 / Wv columns nbase..+127; NMAT = 1: W2 columns
-  // nbase + 128 sub ..+127); piece i copies k rows 16 (wave & 1) + 4 i + lane/16, lane's slot (lane & 15) of the
-  // 256-byte row holds column chunk (lane & 15) ^ (4 (k & 3)).
+  // nbase + 128 sub ..+127).  bf16: piece i copies k rows 16 (wave & 1) + 4 i + lane/16, lane's slot (lane & 15)
+  // of the 256-byte row holds column chunk (lane & 15) ^ (4 (k & 3)).  int8: piece i copies k rows
+  // 16 (wave & 1) + 8 i + lane/8, lane's slot (lane & 7) of the 128-byte row holds 16-column chunk
+  // (lane & 7) ^ (2 ((k >> 1) & 3)) (the transpose reads below then touch distinct banks).
   const int sub = wave >> 1;
-  const uint16_t* bmat = (NMAT == 2 && sub == 1) ? B1 : B0;
-  const uint16_t* b_base =
-      bmat + size_t(e) * K * N + size_t(16 * (wave & 1)) * N + nbase + ((NMAT == 1) ? 128 * sub : 0);
-  const uint32_t b_voff = uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
+  const uint16_t* bmat = static_cast<const uint16_t*>((NMAT == 2 && sub == 1) ? B1 : B0);  // int8: bytes
+  const size_t b_elem = size_t(e) * K * N + size_t(16 * (wave & 1)) * N + nbase + ((NMAT == 1) ? 128 * sub : 0);
+  const uint16_t* b_base = bmat + b_elem;                                              // bf16
+  const uint8_t* b_base8 = reinterpret_cast<const uint8_t*>(bmat) + b_elem;           // int8
+  const uint32_t b_voff =
+      INT8 ? uint32_t((lane >> 3) * N + 16 * ((lane & 7) ^ (2 * ((lane >> 4) & 3))))
+           : uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
   const uint32_t a_dst = lds0 + uint32_t(64 * wave) * (BK * 2);
-  const uint32_t b_dst = lds0 + A_STAGE + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * 256;
+  const uint32_t b_dst = lds0 + A_STAGE + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * (128 * WB);
   // OUTIN: the weight tile of K-step pair q is [256 weight rows][64 k] (NMAT = 2: rows 0..127 are W1 rows
   // nbase.., 128..255 the same Wv rows; NMAT = 1: W2 rows nbase..); wave w copies tile rows 64 w .. +63, copy c
   // (0..7) rows 8 c + lane/8, lane's slot (lane & 7) of the 128-byte row holding chunk (lane & 7) ^ ((row >> 1) & 7)
@@ -120,7 +132,10 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     const uint32_t so = uint32_t(stage) * A_STRIDE;
     if (n < 4)
       b2lds16(a_rsrc, uint32_t(kbase + kt * BK) * 2u, a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
-    else
+    else if (INT8)  // 8 weight rows of 128 bytes per piece
+      g2lds16(b_base8 + size_t(kbase + kt * BK) * N + size_t(8 * (n - 4)) * N, b_voff,
+              b_dst + so + uint32_t(8 * (n - 4)) * 128);
+    else  // 4 weight rows of 256 bytes per piece
       g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - 4)) * N, b_voff,
               b_dst + so + uint32_t(4 * (n - 4)) * 256);
   };
@@ -158,6 +173,23 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
         b_off[j][ks][h] = A_STAGE + bsub * B_SUB + k * 256 + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
       }
   }
+  // INT8: one 8-bit transpose read per fragment (ds_read_b64_tr_b8: within each 16-lane group, lane j receives
+  // byte j % 8 of the 8 bytes addressed by lane 2 r + j / 8, r = 0..7).  Lane 2 r + q of group G addresses k row
+  // 16 ks + 8 (G >> 1) + r and columns col8 .. +7, col8 = (sub-tile column base) + 16 (G & 1) + 8 q, so lane j
+  // receives k rows 16 ks + 8 (G >> 1) .. +7 of column (sub-tile column base) + 16 (G & 1) + j: its MFMA operand.
+  int b8_off[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int bsub = (NMAT == 2) ? (j >> 1) : wn;
+    const int lc = (NMAT == 2) ? (wn * 64 + (j & 1) * 32) : (j * 32);
+    const int G = lane >> 4, s = lane & 15;
+    const int col8 = lc + 16 * (G & 1) + 8 * (s & 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k = 16 * ks + 8 * (G >> 1) + (s >> 1);
+      b8_off[j][ks] = A_STAGE + bsub * B_SUB + k * 128 + 16 * ((col8 >> 4) ^ (2 * ((k >> 1) & 3))) + (col8 & 15);
+    }
+  }
   // OUTIN: weight fragment j of half-step ks of the pair's step p2 (0, 1) is the 16-byte read of tile row (its
   // column), k chunk 4 p2 + 2 ks + (lane >> 5) of the 128-byte row
   int bt_off[4][2][2];
@@ -171,16 +203,21 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
         bt_off[j][ks][p2] = r * 128 + 16 * ((4 * p2 + 2 * ks + (lane >> 5)) ^ ((r >> 1) & 7));
       }
   // fragment piece p of half-step ks from ring slot st, in the order the MFMAs consume them:
-  // A0, B0 (two halves), B1, B2, B3, A1, A2, A3 (OUTIN: A0, B0, B1, B2, B3, A1, A2, A3, one read each)
-  constexpr int NPIECE = OUTIN ? 8 : 12;
+  // A0, B0 (two halves), B1, B2, B3, A1, A2, A3 (OUTIN, INT8: A0, B0, B1, B2, B3, A1, A2, A3, one read each)
+  constexpr int NPIECE = (OUTIN || INT8) ? 8 : 12;
   u32x4_t fa[2][4], fb[2][4];
   u32x2_t bh[2][4][2];
+  u32x2_t b8[2][4];
   // st: the step's A slot (and, [in, out], its weight sub-tiles); sb, p2: OUTIN pair slot and step within it
   auto read_piece = [&](int buf, const lds_u8* st, const lds_u8* sb, int p2, int ks, int p) {
     if (OUTIN) {
       if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
       else if (p <= 4)
         fb[buf][p - 1] = *(const __attribute__((address_space(3))) u32x4_t*)(sb + bt_off[p - 1][ks][p2]);
+      else fa[buf][p - 4] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[p - 4][ks]);
+    } else if (INT8) {
+      if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
+      else if (p <= 4) b8[buf][p - 1] = lds_tr8(st + b8_off[p - 1][ks]);
       else fa[buf][p - 4] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[p - 4][ks]);
     } else if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
     else if (p <= 8) {
@@ -195,7 +232,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     if (OUTIN) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      fb[buf][j] = u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
+      fb[buf][j] = INT8 ? i8x8_to_bf16(b8[buf][j])  // exact: |q| <= 127 has 8 significant bits
+                        : u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
   };
 
   f32x16_t acc[4][4];
@@ -210,7 +248,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   // half-step 1 are read; then the wave waits for its copies of step kt+1 and joins the barrier; half-step 1
   // multiplies buffer 1 while the copies of step kt+3 are issued and half-step 0 of step kt+1 is read.  Each MFMA
   // is followed by at most one copy or one LDS read, in a fixed order.  Copies past the last step re-read the last
-  // step into a ring slot that is never read again, so every step issues 8 copies and the wait count is constant.
+  // step into a ring slot that is never read again, so every step issues CPS copies and the wait count is constant.
   // OUTIN: the weight copies of pair q are issued in the B slots of steps 2 q - 3 and 2 q - 2 (4 each), so that
   // step kt issues copies 4 ((kt + 1) % 2) .. +3 of pair (kt + 3) / 2; the prologue issues pair 0 and the first
   // half of pair 1.
@@ -243,9 +281,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
+      for (int n = 0; n < CPS; ++n)
         if (s < NSTAGE - 2 || n < 4) copy_piece(s, min(s, KT - 1), n);
-    wait_vm<8 * (NSTAGE - 3) + 4>();  // step 0 landed (step 1 and half of step 2 may be in flight)
+    wait_vm<CPS * (NSTAGE - 3) + 4>();  // step 0 landed (step 1 and half of step 2 may be in flight)
   }
   lds_barrier();
 #pragma unroll
@@ -266,12 +304,12 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
       if (m < NPIECE) read_piece(1, st, sb, P, 1, m);
       if (m >= 12) {
         if (OUTIN) copy_pair((kt + 3) >> 1, 4 * (1 - P) + (m - 12));
-        else copy_piece(pstage, pk, m - 8);
+        else if (m - 8 < CPS) copy_piece(pstage, pk, m - 8);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(1);
-    wait_vm<8 * (NSTAGE - 3)>();  // step kt+1 landed (steps kt+2 .. may be in flight)
+    wait_vm<CPS * (NSTAGE - 3)>();  // step kt+1 landed (steps kt+2 .. may be in flight)
     lds_barrier();                       // ... for every wave; every wave finished reading step kt-1
     const int cstage = (kt + NSTAGE - 1) % NSTAGE, ck = min(kt + NSTAGE - 1, KT - 1);
     const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * A_STRIDE;
@@ -303,12 +341,17 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
       const int c = wn * 64 + jn * 32 + lr;
+      // int8: the column's scales multiply the fp32 accumulators before the GELU product
+      const float sa = INT8 ? bf16f(s0[e * s_estride + nbase + c]) : 1.0f;
+      const float sb = INT8 ? bf16f(s1[e * s_estride + nbase + c]) : 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
-          ht[r * 128 + c] = uint16_t(f2bf(gelu_erf(acc[i][jn][v]) * acc[i][2 + jn][v]));
+          const float a = INT8 ? acc[i][jn][v] * sa : acc[i][jn][v];
+          const float b = INT8 ? acc[i][2 + jn][v] * sb : acc[i][2 + jn][v];
+          ht[r * 128 + c] = uint16_t(f2bf(gelu_erf(a) * b));
         }
     }
     lds_barrier();
@@ -322,40 +365,55 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
             *(const __attribute__((address_space(3))) u32x4_t*)(ht + r * 128 + c8);
     }
   } else {
+    if constexpr (INT8) {  // the column's scale multiplies the fp32 accumulators
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = bf16f(s0[e * s_estride + nbase + wn * 128 + j * 32 + (lane & 31)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] *= sc;
+      }
+    }
     tile::store_tile<NMAT>(acc, wm, wn, lane, row0, rows, nbase, N,
                            static_cast<float*>(out) + blockIdx.y * split_stride);
   }
 }
 
-hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, bool outin, const int32_t* counts,
+hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
+                               const uint16_t* sv, int64_t s_estride, bool int8, bool outin, const int32_t* counts,
                                const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
                                uint16_t* h, hipStream_t s) {
   const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
-  const uint16_t* b0 = static_cast<const uint16_t*>(w1);
-  const uint16_t* b1 = static_cast<const uint16_t*>(wv);
   const size_t xbytes = size_t(slots / 2) * d * 2;  // x: [slots / 2 tokens, d] (two slots per token)
   if (xbytes >= (size_t(1) << 31) || size_t(2) * slots * f >= (size_t(1) << 31)) return hipErrorInvalidValue;
+  if (int8 && outin) return hipErrorInvalidValue;
   const uint32_t xb = uint32_t(xbytes);
-  if (outin) tiled_dma_kernel<2, true><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, xb, d, f, E, h, 0);
-  else tiled_dma_kernel<2, false><<<grid, block, 0, s>>>(x, b0, b1, counts, offsets, perm, xb, d, f, E, h, 0);
+#define GM_UPD(OI, I8) tiled_dma_kernel<2, OI, I8><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, \
+                                                                           offsets, perm, xb, d, f, E, h, 0)
+  if (int8) GM_UPD(false, true);
+  else if (outin) GM_UPD(true, false);
+  else GM_UPD(false, false);
+#undef GM_UPD
   return hipGetLastError();
 }
 
-hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, bool outin, const int32_t* counts,
-                                 const int32_t* offsets, int d, int f, int E, int slots, int S, float* y,
-                                 hipStream_t s) {
+hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const uint16_t* s2, int64_t s_estride, bool int8,
+                                 bool outin, const int32_t* counts, const int32_t* offsets, int d, int f, int E,
+                                 int slots, int S, float* y, hipStream_t s) {
   const dim3 grid(tile::grid_tiles(slots, E, d / BNT), S), block(256);
-  const uint16_t* b0 = static_cast<const uint16_t*>(w2);
   const int64_t stride = int64_t(slots) * d;
   const size_t hbytes = size_t(slots) * f * 2;  // h: [slots, f]
   if (hbytes >= (size_t(1) << 31)) return hipErrorInvalidValue;
+  if (int8 && outin) return hipErrorInvalidValue;
   const uint32_t hb = uint32_t(hbytes);
-  if (outin)
-    tiled_dma_kernel<1, true><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, hb, f, d, E, y,
-                                                     stride);
-  else
-    tiled_dma_kernel<1, false><<<grid, block, 0, s>>>(h, b0, nullptr, counts, offsets, nullptr, hb, f, d, E, y,
-                                                      stride);
+#define GM_DND(OI, I8) tiled_dma_kernel<1, OI, I8><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, s_estride, \
+                                                                           counts, offsets, nullptr, hb, f, d, E, y, \
+                                                                           stride)
+  if (int8) GM_DND(false, true);
+  else if (outin) GM_DND(true, false);
+  else GM_DND(false, false);
+#undef GM_DND
   return hipGetLastError();
 }
 

@@ -57,8 +57,9 @@ hipError_t launch_down_stream_oi(const uint16_t* h, const void* w2, const uint16
                                  const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots,
                                  int S, bool int8, int mt, float* y, hipStream_t s);
 
-// LDS-tiled grouped GEMMs (many tokens per expert); int8 weights use register-staged tiles, bf16 weights the
-// direct-to-LDS kernels below.
+// LDS-tiled grouped GEMMs (many tokens per expert): the direct-to-LDS kernels below for bf16 weights and for int8
+// weights with one scale group in [in, out] storage; register-staged tiles for int8 with grouped scales or in
+// [out, in] storage.
 hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                            const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, bool int8,
@@ -67,13 +68,15 @@ hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* 
                              const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                              bool int8, float* y, hipStream_t s);
 
-// The bf16 forms of the tiled kernels: direct global -> LDS copies ([in, out] weights: LDS transpose reads).
-hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, bool outin, const int32_t* counts,
+// Direct global -> LDS copies, LDS transpose reads for [in, out] weights (bf16, or int8 with per-column scales
+// [Es, 1, N] at expert stride s_estride).
+hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
+                               const uint16_t* sv, int64_t s_estride, bool int8, bool outin, const int32_t* counts,
                                const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
                                uint16_t* h, hipStream_t s);
-hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, bool outin, const int32_t* counts,
-                                 const int32_t* offsets, int d, int f, int E, int slots, int S, float* y,
-                                 hipStream_t s);
+hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const uint16_t* s2, int64_t s_estride, bool int8,
+                                 bool outin, const int32_t* counts, const int32_t* offsets, int d, int f, int E,
+                                 int slots, int S, float* y, hipStream_t s);
 
 // fp32 layer (VALU, LDS tiles).
 hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, bool outin, const int32_t* counts,
