@@ -3,6 +3,8 @@
 Bar: routing indices, per-expert counts, the permutation and its inverse bit-exact; the layer output within
 max|gpu - oracle| <= 1e-2 rms(oracle) for bf16 and int8 layers and 1e-4 rms(oracle) for the fp32 layer.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -285,8 +287,34 @@ def test_grok_skew_bf16_sampled(gm, grok_bf16):
     assert c[0] > 0.4 * c.sum() and c[5] > 0.2 * c.sum()
 
 
-def test_grok_int8(gm):
+@pytest.fixture(scope="module")
+def grok_int8():
     say("[setup] drawing Grok-1-shape int8 weights (4.83 GB)")
     w = synth.WORKLOADS["int8_w8"]
-    inp = synth.make_inputs(w)
-    check_layer(gm, w, inp=inp)
+    wts = synth.make_weights(w)
+    dvw = dev_inputs({**wts, "x": np.zeros((1, w.d), np.uint16), "router_bias": None}, W8)
+    say("[setup] done")
+    yield wts, dvw
+    del dvw
+    torch.cuda.empty_cache()
+
+
+def _grok_int8_case(gm, grok_int8, T, sampled):
+    w = dataclasses.replace(synth.WORKLOADS["int8_w8"], T=T, name=f"int8_w8_T{T}", sampled_rows=sampled)
+    wts, dvw = grok_int8
+    inp = synth.make_inputs(w, weights=wts)
+    dv = dict(dvw)
+    dv["x"] = dev_inputs({"x": inp["x"], "router_w": inp["router_w"], "w1": None, "wv": None, "w2": None,
+                          "s1": None, "sv": None, "s2": None, "router_bias": None}, W8)["x"]
+    rows = None if sampled is None else synth.sampled_rows(T, sampled)
+    return check_layer(gm, w, inp=inp, rows=rows, dv=dv)
+
+
+def test_grok_int8(gm, grok_int8):
+    """The int8 workload (T = 64, weight-streaming kernels), every row."""
+    _grok_int8_case(gm, grok_int8, 64, None)
+
+
+def test_grok_int8_prefill_sampled(gm, grok_int8):
+    """int8 weights at prefill size (T = 8192: the direct-to-LDS int8 tile kernels), 64 seeded rows."""
+    _grok_int8_case(gm, grok_int8, 8192, 64)
