@@ -62,7 +62,14 @@ Passes passes(int64_t T, int64_t d, int64_t f, int dtype) {
 int down_splits(int64_t T, int64_t f, int dtype) {
   // LDS-tiled bf16 down-projection: K split in two, so that its tiles fill the chip in more, shorter rounds
   if (dtype == GROK_MOE_BF16 && T > kStreamMaxTokens) return 2;
-  if (dtype == GROK_MOE_F32 || T > kStreamMaxTokens) return 1;
+  // fp32 layer: a small batch gives few tiles, each a long chain of 16-deep K steps: for T <= 256 split K into
+  // up to 8 parts of at least 128 k (partial sums added by the combine)
+  if (dtype == GROK_MOE_F32) {
+    int s = 1;
+    while (T <= 256 && s < 8 && f / (2 * s) >= 128 && (f / (2 * s)) % 16 == 0) s *= 2;
+    return s;
+  }
+  if (T > kStreamMaxTokens) return 1;
   // chunks of at least 2048 rows of W2 (a multiple of 64), at most 8 chunks (measured against 4, 16 and 32)
   int s = 1;
   while (s < 8 && (f / (2 * s)) % 64 == 0 && f / (2 * s) >= 2048) s *= 2;
@@ -156,7 +163,7 @@ hipError_t do_down(const void* h, const void* w2, const void* s2, const ScaleSpe
                    hipStream_t s) {
   if (dtype == GROK_MOE_F32)
     return gm::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2), sp.outin, counts,
-                               offsets, int(d), int(f), E, int(p.slots), y, s);
+                               offsets, int(d), int(f), E, int(p.slots), p.splits, y, s);
   const bool i8 = dtype == GROK_MOE_W8;
   if (p.stream && sp.outin && gm::oi_stream_fits(int(f / p.splits), i8, down_layout(sp, d, f), int(f)))
     return gm::launch_down_stream_oi(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),

@@ -23,13 +23,16 @@ __global__ __launch_bounds__(256) void f32_tiled_kernel(const float* __restrict_
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ perm, int K, int N, int E,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, int64_t split_stride) {
   int e, row0, rows;
   if (!find_row_tile(counts, offsets, E, FBM, blockIdx.x, &e, &row0, &rows)) return;
   __shared__ float As[FBK][FBM + 4];
   __shared__ float Bs[NMAT][FBK][FBN + 4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int nbase = blockIdx.y * FBN;
+  // split blockIdx.z of gridDim.z covers k in [kbase, kbase + Ks) (NMAT = 1: partial sums, added by the combine)
+  const int Ks = K / gridDim.z, kbase = blockIdx.z * Ks;
+  out += blockIdx.z * split_stride;
 
   // A piece: row tid/4, k 4 (tid%4) .. +3
   const int ar = tid >> 2, ak = 4 * (tid & 3);
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void f32_tiled_kernel(const float* __restrict_
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[m][i][j] = 0.0f;
 
-  for (int k0 = 0; k0 < K; k0 += FBK) {
+  for (int k0 = kbase; k0 < kbase + Ks; k0 += FBK) {
     const f32x4_t av = *reinterpret_cast<const f32x4_t*>(a_src + k0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) As[ak + i][ar] = av[i];
@@ -102,16 +105,20 @@ hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, bool 
                          const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, float* h,
                          hipStream_t s) {
   const dim3 grid(slots / FBM + E, f / FBN), block(256);
-  if (outin) f32_tiled_kernel<2, true><<<grid, block, 0, s>>>(x, w1, wv, counts, offsets, perm, d, f, E, h);
-  else f32_tiled_kernel<2, false><<<grid, block, 0, s>>>(x, w1, wv, counts, offsets, perm, d, f, E, h);
+  if (outin) f32_tiled_kernel<2, true><<<grid, block, 0, s>>>(x, w1, wv, counts, offsets, perm, d, f, E, h, 0);
+  else f32_tiled_kernel<2, false><<<grid, block, 0, s>>>(x, w1, wv, counts, offsets, perm, d, f, E, h, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_down_f32(const float* h, const float* w2, bool outin, const int32_t* counts,
-                           const int32_t* offsets, int d, int f, int E, int slots, float* y, hipStream_t s) {
-  const dim3 grid(slots / FBM + E, d / FBN), block(256);
-  if (outin) f32_tiled_kernel<1, true><<<grid, block, 0, s>>>(h, w2, nullptr, counts, offsets, nullptr, f, d, E, y);
-  else f32_tiled_kernel<1, false><<<grid, block, 0, s>>>(h, w2, nullptr, counts, offsets, nullptr, f, d, E, y);
+                           const int32_t* offsets, int d, int f, int E, int slots, int S, float* y, hipStream_t s) {
+  if (S < 1 || f % (S * FBK) != 0) return hipErrorInvalidValue;
+  const dim3 grid(slots / FBM + E, d / FBN, S), block(256);
+  const int64_t stride = int64_t(slots) * d;
+  if (outin)
+    f32_tiled_kernel<1, true><<<grid, block, 0, s>>>(h, w2, nullptr, counts, offsets, nullptr, f, d, E, y, stride);
+  else
+    f32_tiled_kernel<1, false><<<grid, block, 0, s>>>(h, w2, nullptr, counts, offsets, nullptr, f, d, E, y, stride);
   return hipGetLastError();
 }
 

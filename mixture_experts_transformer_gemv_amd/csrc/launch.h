@@ -83,7 +83,7 @@ hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, bool 
                          const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, float* h,
                          hipStream_t s);
 hipError_t launch_down_f32(const float* h, const float* w2, bool outin, const int32_t* counts,
-                           const int32_t* offsets, int d, int f, int E, int slots, float* y, hipStream_t s);
+                           const int32_t* offsets, int d, int f, int E, int slots, int S, float* y, hipStream_t s);
 
 // Tile scheduling shared by the grouped kernels: the m-th row tile (of height bm) over all experts in
 // ascending expert order.  Returns false if m is past the last tile.  counts has E entries.

@@ -54,7 +54,8 @@ def test_workspace_size_and_splits(L):
     assert gm.down_splits(8, 6144, 32768) == 8
     assert gm.down_splits(8192, 6144, 32768) == 2   # LDS-tiled bf16 path splits K in two
     assert gm.down_splits(8192, 6144, 32768, 8, 2, gm.W8) == 1
-    assert gm.down_splits(64, 128, 512, 8, 2, gm.F32) == 1
+    assert gm.down_splits(64, 128, 512, 8, 2, gm.F32) == 4   # small fp32 batch: K split in parts of 128
+    assert gm.down_splits(300, 128, 512, 8, 2, gm.F32) == 1
     ws_pre = gm.workspace_size(8192, 6144, 32768)
     assert ws_pre >= 16384 * 32768 * 2 + 16384 * 6144 * 4
     assert gm.workspace_size(64, 128, 512, 8, 2, gm.F32) >= 128 * 512 * 4 + 128 * 128 * 4
