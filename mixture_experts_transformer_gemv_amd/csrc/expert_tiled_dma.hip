@@ -48,31 +48,37 @@ constexpr int NPAIR = 3;                // pair slots
 // B0/B1: weights [E, K, N] (bf16, or int8 if INT8), or bf16 [E, N, K] if OUTIN (B1 only for NMAT = 2).  INT8:
 // per-column bf16 scales s0 (of B0), s1 (of B1) at expert stride s_estride.  out: h bf16 [slots, N] (NMAT = 2)
 // or y f32 [slots, N] (NMAT = 1).
-template <int NMAT, bool OUTIN, bool INT8>
-__global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restrict__ A, const void* __restrict__ B0,
+// LDS bytes of one tile body
+template <int NMAT, bool OUTIN, bool INT8, int TBM>
+constexpr int tile_lds_bytes() {
+  return OUTIN ? NSTAGE * TBM * BK * 2 + NPAIR * B_PAIR : NSTAGE * (TBM * BK * 2 + 2 * b_sub<INT8>());
+}
+
+// One output tile: expert e, assignment rows row0 .. row0 + rows - 1 (rows <= TBM), column tile ntile; lds holds
+// tile_lds_bytes() bytes.
+template <int NMAT, bool OUTIN, bool INT8, int TBM>
+__device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, const void* __restrict__ B0,
                                                         const void* __restrict__ B1,
                                                         const uint16_t* __restrict__ s0,
                                                         const uint16_t* __restrict__ s1, int64_t s_estride,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ perm, uint32_t a_bytes, int K,
-                                                        int N, int E, void* __restrict__ out,
-                                                        int64_t split_stride) {
+                                                        int N, void* __restrict__ out, int64_t split_stride, int e,
+                                                        int row0, int rows, int ntile, lds_u8* lds) {
   static_assert(!(OUTIN && INT8), "int8 weights are tiled from [E, K, N] storage");
+  static_assert(TBM == 256 || TBM == 128, "tiles of 256 or 128 rows");
   constexpr int BNM = BNT / NMAT;  // columns per matrix
+  constexpr int MI = TBM / 64;     // row blocks of 32 per wave (waves 2 x 2: TBM / 2 rows each)
+  constexpr int AP = TBM / 64;     // 1 KB activation copies per wave and K step
+  constexpr int NMF = 4 * MI;      // MFMAs per wave and half-step
+  constexpr int A_STG = TBM * BK * 2;  // bytes: [TBM rows][32 k]
   constexpr int B_SUB = b_sub<INT8>();
-  constexpr int STAGE = A_STAGE + 2 * B_SUB;
+  constexpr int STAGE = A_STG + 2 * B_SUB;
   constexpr int WB = INT8 ? 1 : 2;             // bytes per weight
   constexpr int BCOPIES = INT8 ? 2 : 4;        // 1 KB weight copies per wave and K step ([in, out])
-  constexpr int CPS = 4 + BCOPIES;             // copies per wave and K step ([out, in]: 4 + 4)
-  int e, row0, rows, ntile;
-  if (!tile::map_tile<tile::Group<NMAT>::N>(counts, offsets, E, N / BNM, blockIdx.x, &e, &row0, &rows, &ntile))
-    return;  // whole workgroup
-
-  constexpr int LDS_BYTES = OUTIN ? NSTAGE * A_STAGE + NPAIR * B_PAIR : NSTAGE * STAGE;
-  constexpr int A_STRIDE = OUTIN ? A_STAGE : STAGE;  // between ring slots of A
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-  lds_u8* lds = (lds_u8*)(smem);
+  constexpr int CPS = AP + BCOPIES;            // copies per wave and K step ([out, in]: AP + 4)
+  constexpr int A_STRIDE = OUTIN ? A_STG : STAGE;  // between ring slots of A
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -82,15 +88,15 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   const int Ks = K / gridDim.y;
   const int kbase = blockIdx.y * Ks;
 
-  // ---- copies.  A: wave w, piece i copies rows 64 w + 16 i + lane/4; lane's slot (lane & 3) of the 64-byte row
+  // ---- copies.  A: wave w, piece i copies rows (TBM/4) w + 16 i + lane/4; lane's slot (lane & 3) of the 64-byte row
   // holds k chunk (lane & 3) ^ ((row >> 2) & 3).  Byte offsets from A (32 bits).  Rows past the expert's end (the
   // tail tile) get an out-of-range offset, so their copies write zeros: those rows are never stored, and
   // multiplying zeros takes markedly less power than multiplying data.
   const u32x4_t a_rsrc = buffer_rsrc(A, a_bytes);
-  uint32_t a_voff[4];
+  uint32_t a_voff[AP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 64 * wave + 16 * i + (lane >> 2);
+  for (int i = 0; i < AP; ++i) {
+    const int r = (TBM / 4) * wave + 16 * i + (lane >> 2);
     if (r < rows) {
       const uint32_t arow = (NMAT == 2) ? uint32_t(perm[row0 + r]) : uint32_t(row0 + r);
       a_voff[i] = (arow * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u;
@@ -111,8 +117,8 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   const uint32_t b_voff =
       INT8 ? uint32_t((lane >> 3) * N + 16 * ((lane & 7) ^ (2 * ((lane >> 4) & 3))))
            : uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
-  const uint32_t a_dst = lds0 + uint32_t(64 * wave) * (BK * 2);
-  const uint32_t b_dst = lds0 + A_STAGE + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * (128 * WB);
+  const uint32_t a_dst = lds0 + uint32_t((TBM / 4) * wave) * (BK * 2);
+  const uint32_t b_dst = lds0 + A_STG + uint32_t(sub) * B_SUB + uint32_t(16 * (wave & 1)) * (128 * WB);
   // OUTIN: the weight tile of K-step pair q is [256 weight rows][64 k] (NMAT = 2: rows 0..127 are W1 rows
   // nbase.., 128..255 the same Wv rows; NMAT = 1: W2 rows nbase..); wave w copies tile rows 64 w .. +63, copy c
   // (0..7) rows 8 c + lane/8, lane's slot (lane & 7) of the 128-byte row holding chunk (lane & 7) ^ ((row >> 1) & 7)
@@ -126,18 +132,18 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
       bp_voff[c] = (uint32_t(wrow) * uint32_t(K) + 8u * uint32_t((lane & 7) ^ ((r >> 1) & 7))) * 2u;
     }
   }
-  const uint32_t bp_dst = lds0 + NSTAGE * A_STAGE + uint32_t(64 * wave) * 128;
-  // piece n of the copies of K step kt into ring slot stage (n < 4: A piece n; else B piece n - 4, [in, out])
+  const uint32_t bp_dst = lds0 + NSTAGE * A_STG + uint32_t(64 * wave) * 128;
+  // piece n of the copies of K step kt into ring slot stage (n < AP: A piece n; else B piece n - AP, [in, out])
   auto copy_piece = [&](int stage, int kt, int n) {
     const uint32_t so = uint32_t(stage) * A_STRIDE;
-    if (n < 4)
+    if (n < AP)
       b2lds16(a_rsrc, uint32_t(kbase + kt * BK) * 2u, a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
     else if (INT8)  // 8 weight rows of 128 bytes per piece
-      g2lds16(b_base8 + size_t(kbase + kt * BK) * N + size_t(8 * (n - 4)) * N, b_voff,
-              b_dst + so + uint32_t(8 * (n - 4)) * 128);
+      g2lds16(b_base8 + size_t(kbase + kt * BK) * N + size_t(8 * (n - AP)) * N, b_voff,
+              b_dst + so + uint32_t(8 * (n - AP)) * 128);
     else  // 4 weight rows of 256 bytes per piece
-      g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - 4)) * N, b_voff,
-              b_dst + so + uint32_t(4 * (n - 4)) * 256);
+      g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - AP)) * N, b_voff,
+              b_dst + so + uint32_t(4 * (n - AP)) * 256);
   };
   // OUTIN: copy c of K-step pair q into pair slot q % 3 (past the end: the last pair again, into a free slot)
   auto copy_pair = [&](int q, int c) {
@@ -146,14 +152,14 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
             bp_dst + uint32_t((q % NPAIR) * B_PAIR) + uint32_t(c * 1024));
   };
 
-  // ---- fragments.  Waves 2 x 2: wave rows wm*128 .. +127, 4 column sub-tiles of 32.
+  // ---- fragments.  Waves 2 x 2: wave rows wm*TBM/2 .. +TBM/2-1 (MI blocks of 32), 4 column sub-tiles of 32.
   const int wm = wave >> 1, wn = wave & 1;
-  int a_off[4][2];  // A row wm*128 + 32 i + (lane & 31), k chunk 2 ks + (lane >> 5)
+  int a_off[MI][2];  // A row wm*TBM/2 + 32 i + (lane & 31), k chunk 2 ks + (lane >> 5)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int r = wm * 128 + 32 * i + (lane & 31);
+      const int r = wm * (TBM / 2) + 32 * i + (lane & 31);
       a_off[i][ks] = r * (BK * 2) + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
     }
   // B halves h: lane addresses k row 16 ks + 8 g + 4 h + (s >> 2) and columns col .. +3 of its sub-tile, where
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = 16 * ks + 8 * (G >> 1) + 4 * h + (s >> 2);
-        b_off[j][ks][h] = A_STAGE + bsub * B_SUB + k * 256 + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
+        b_off[j][ks][h] = A_STG + bsub * B_SUB + k * 256 + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
       }
   }
   // INT8: one 8-bit transpose read per fragment (ds_read_b64_tr_b8: within each 16-lane group, lane j receives
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int k = 16 * ks + 8 * (G >> 1) + (s >> 1);
-      b8_off[j][ks] = A_STAGE + bsub * B_SUB + k * 128 + 16 * ((col8 >> 4) ^ (2 * ((k >> 1) & 3))) + (col8 & 15);
+      b8_off[j][ks] = A_STG + bsub * B_SUB + k * 128 + 16 * ((col8 >> 4) ^ (2 * ((k >> 1) & 3))) + (col8 & 15);
     }
   }
   // OUTIN: weight fragment j of half-step ks of the pair's step p2 (0, 1) is the 16-byte read of tile row (its
@@ -204,8 +210,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
       }
   // fragment piece p of half-step ks from ring slot st, in the order the MFMAs consume them:
   // A0, B0 (two halves), B1, B2, B3, A1, A2, A3 (OUTIN, INT8: A0, B0, B1, B2, B3, A1, A2, A3, one read each)
-  constexpr int NPIECE = (OUTIN || INT8) ? 8 : 12;
-  u32x4_t fa[2][4], fb[2][4];
+  constexpr int NPIECE = (OUTIN || INT8) ? 4 + MI : 8 + MI;
+  constexpr int NSLOT = NMF > NPIECE ? NMF : NPIECE;  // instruction slots per half-step (one MFMA each, if any)
+  u32x4_t fa[2][MI], fb[2][4];
   u32x2_t bh[2][4][2];
   u32x2_t b8[2][4];
   // st: the step's A slot (and, [in, out], its weight sub-tiles); sb, p2: OUTIN pair slot and step within it
@@ -236,9 +243,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
                         : u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -253,12 +260,12 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   // step kt issues copies 4 ((kt + 1) % 2) .. +3 of pair (kt + 3) / 2; the prologue issues pair 0 and the first
   // half of pair 1.
   const int KT = Ks / BK;
-  const lds_u8* bpairs = lds + NSTAGE * A_STAGE;
+  const lds_u8* bpairs = lds + NSTAGE * A_STG;
   // zeros in the A slots of rows past the expert's end, in every ring stage (written by this lane only; the
   // out-of-range copies leave them zero)
-  if (rows < BM) {
+  if (rows < TBM) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < AP; ++i)
       if (a_voff[i] == 0x80000000u)
 #pragma unroll
         for (int st = 0; st < NSTAGE; ++st)
@@ -267,23 +274,23 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   }
   if constexpr (OUTIN) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) copy_piece(0, 0, n);
+    for (int n = 0; n < AP; ++n) copy_piece(0, 0, n);
 #pragma unroll
     for (int c = 0; c < 8; ++c) copy_pair(0, c);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) copy_piece(1, min(1, KT - 1), n);
+    for (int n = 0; n < AP; ++n) copy_piece(1, min(1, KT - 1), n);
 #pragma unroll
     for (int c = 0; c < 4; ++c) copy_pair(1, c);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) copy_piece(2, min(2, KT - 1), n);
-    wait_vm<12>();  // step 0 (A and pair 0) landed
+    for (int n = 0; n < AP; ++n) copy_piece(2, min(2, KT - 1), n);
+    wait_vm<2 * AP + 4>();  // step 0 (A and pair 0) landed
   } else {
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
 #pragma unroll
       for (int n = 0; n < CPS; ++n)
-        if (s < NSTAGE - 2 || n < 4) copy_piece(s, min(s, KT - 1), n);
-    wait_vm<CPS * (NSTAGE - 3) + 4>();  // step 0 landed (step 1 and half of step 2 may be in flight)
+        if (s < NSTAGE - 2 || n < AP) copy_piece(s, min(s, KT - 1), n);
+    wait_vm<CPS * (NSTAGE - 3) + AP>();  // step 0 landed (step 1 and half of step 2 may be in flight)
   }
   lds_barrier();
 #pragma unroll
@@ -299,12 +306,13 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     // four copies of pair (kt + 3) / 2
     const int pstage = (kt + NSTAGE - 2) % NSTAGE, pk = min(kt + NSTAGE - 2, KT - 1);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
+    for (int m = 0; m < NSLOT; ++m) {
+      if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
       if (m < NPIECE) read_piece(1, st, sb, P, 1, m);
-      if (m >= 12) {
-        if (OUTIN) copy_pair((kt + 3) >> 1, 4 * (1 - P) + (m - 12));
-        else if (m - 8 < CPS) copy_piece(pstage, pk, m - 8);
+      const int cb = m - (NSLOT - 4);  // the last 4 slots issue the weight copies
+      if (cb >= 0) {
+        if (OUTIN) copy_pair((kt + 3) >> 1, 4 * (1 - P) + cb);
+        else if (cb < BCOPIES) copy_piece(pstage, pk, AP + cb);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -315,9 +323,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * A_STRIDE;
     const lds_u8* nsb = bpairs + (((kt + 1) >> 1) % NPAIR) * B_PAIR;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
-      if (m < 4) copy_piece(cstage, ck, m);
+    for (int m = 0; m < NSLOT; ++m) {
+      if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
+      if (m < AP) copy_piece(cstage, ck, m);
       if (m < NPIECE) read_piece(0, nst, nsb, 1 - P, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   asm volatile("s_waitcnt vmcnt(0)");
 
   if constexpr (NMAT == 2) {
-    // h tile [256 rows][128 columns] bf16 staged in the (now idle) ring, then written as 16-byte row pieces
+    // h tile [TBM rows][128 columns] bf16 staged in the (now idle) ring, then written as 16-byte row pieces
     lds_barrier();
     __attribute__((address_space(3))) uint16_t* ht = (__attribute__((address_space(3))) uint16_t*)(lds);
     const int lr = lane & 31, rhalf = 4 * (lane >> 5);
@@ -345,10 +353,10 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
       const float sa = INT8 ? bf16f(s0[e * s_estride + nbase + c]) : 1.0f;
       const float sb = INT8 ? bf16f(s1[e * s_estride + nbase + c]) : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
+          const int r = wm * (TBM / 2) + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
           const float a = INT8 ? acc[i][jn][v] * sa : acc[i][jn][v];
           const float b = INT8 ? acc[i][2 + jn][v] * sb : acc[i][2 + jn][v];
           ht[r * 128 + c] = uint16_t(f2bf(gelu_erf(a) * b));
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
     lds_barrier();
     uint16_t* h = static_cast<uint16_t*>(out);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < TBM / 16; ++q) {
       const int chunk = q * 256 + tid;          // 16-byte chunk: row chunk / 16, columns 8 (chunk % 16) ..
       const int r = chunk >> 4, c8 = (chunk & 15) * 8;
       if (r < rows)
@@ -370,27 +378,58 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
       for (int j = 0; j < 4; ++j) {
         const float sc = bf16f(s0[e * s_estride + nbase + wn * 128 + j * 32 + (lane & 31)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[i][j][v] *= sc;
       }
     }
-    tile::store_tile<NMAT>(acc, wm, wn, lane, row0, rows, nbase, N,
+    tile::store_tile<NMAT, MI>(acc, wm, wn, lane, row0, rows, nbase, N,
                            static_cast<float*>(out) + blockIdx.y * split_stride);
   }
 }
+
+// The grouped GEMM: workgroup blockIdx.x takes the tile map_tile gives it among the row tiles R of TBM rows, in the
+// XCD-aware order.
+template <int NMAT, bool OUTIN, bool INT8, int TBM, tile::Rows R>
+__global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restrict__ A, const void* __restrict__ B0,
+                                                        const void* __restrict__ B1,
+                                                        const uint16_t* __restrict__ s0,
+                                                        const uint16_t* __restrict__ s1, int64_t s_estride,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ perm, uint32_t a_bytes, int K,
+                                                        int N, int E, void* __restrict__ out,
+                                                        int64_t split_stride) {
+  int e, row0, rows, ntile;
+  if (!tile::map_tile<tile::Group<NMAT>::N, TBM, R>(counts, offsets, E, N / (BNT / NMAT), blockIdx.x, &e, &row0,
+                                                    &rows, &ntile))
+    return;  // whole workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<NMAT, OUTIN, INT8, TBM>()];
+  tiled_dma_tile<NMAT, OUTIN, INT8, TBM>(A, B0, B1, s0, s1, s_estride, counts, offsets, perm, a_bytes, K, N, out,
+                                         split_stride, e, row0, rows, ntile, (lds_u8*)(smem));
+}
+
+// An expert's rows as 256-row tiles; with at least tile::kSplitFull full tiles, a last tile of at most 128 rows
+// goes to a second launch as a 128-row tile (half the MFMA work on its padding).
+static unsigned tail_tiles(int E, int NT) { return (unsigned(E) * unsigned(NT) + 7u) & ~7u; }
 
 hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                                const uint16_t* sv, int64_t s_estride, bool int8, bool outin, const int32_t* counts,
                                const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
                                uint16_t* h, hipStream_t s) {
-  const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2))), block(256);
+  const int NT = f / (BNT / 2);
+  const dim3 grid(tile::grid_tiles(slots, E, NT)), grid_t(tail_tiles(E, NT)), block(256);
   const size_t xbytes = size_t(slots / 2) * d * 2;  // x: [slots / 2 tokens, d] (two slots per token)
   if (xbytes >= (size_t(1) << 31) || size_t(2) * slots * f >= (size_t(1) << 31)) return hipErrorInvalidValue;
   if (int8 && outin) return hipErrorInvalidValue;
   const uint32_t xb = uint32_t(xbytes);
-#define GM_UPD(OI, I8) tiled_dma_kernel<2, OI, I8><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, \
-                                                                           offsets, perm, xb, d, f, E, h, 0)
+#define GM_UPD(OI, I8)                                                                                           \
+  do {                                                                                                         \
+    tiled_dma_kernel<2, OI, I8, 256, tile::Rows::Main><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, s_estride,       \
+                                                                               counts, offsets, perm, xb, d, f, E, h, 0); \
+    tiled_dma_kernel<2, OI, I8, 128, tile::Rows::Tail><<<grid_t, block, 0, s>>>(x, w1, wv, s1, sv, s_estride,     \
+                                                                                counts, offsets, perm, xb, d, f, E, h, 0); \
+  } while (0)
   if (int8) GM_UPD(false, true);
   else if (outin) GM_UPD(true, false);
   else GM_UPD(false, false);
@@ -401,15 +440,22 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
 hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const uint16_t* s2, int64_t s_estride, bool int8,
                                  bool outin, const int32_t* counts, const int32_t* offsets, int d, int f, int E,
                                  int slots, int S, float* y, hipStream_t s) {
-  const dim3 grid(tile::grid_tiles(slots, E, d / BNT), S), block(256);
+  const int NT = d / BNT;
+  const dim3 grid(tile::grid_tiles(slots, E, NT), S), grid_t(tail_tiles(E, NT), S), block(256);
   const int64_t stride = int64_t(slots) * d;
   const size_t hbytes = size_t(slots) * f * 2;  // h: [slots, f]
   if (hbytes >= (size_t(1) << 31)) return hipErrorInvalidValue;
   if (int8 && outin) return hipErrorInvalidValue;
   const uint32_t hb = uint32_t(hbytes);
-#define GM_DND(OI, I8) tiled_dma_kernel<1, OI, I8><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, s_estride, \
-                                                                           counts, offsets, nullptr, hb, f, d, E, y, \
-                                                                           stride)
+#define GM_DND(OI, I8)                                                                                           \
+  do {                                                                                                         \
+    tiled_dma_kernel<1, OI, I8, 256, tile::Rows::Main><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr,        \
+                                                                               s_estride, counts, offsets, nullptr, \
+                                                                               hb, f, d, E, y, stride);           \
+    tiled_dma_kernel<1, OI, I8, 128, tile::Rows::Tail><<<grid_t, block, 0, s>>>(h, w2, nullptr, s2, nullptr,      \
+                                                                                s_estride, counts, offsets, nullptr, \
+                                                                                hb, f, d, E, y, stride);          \
+  } while (0)
   if (int8) GM_DND(false, true);
   else if (outin) GM_DND(true, false);
   else GM_DND(false, false);

@@ -22,16 +22,46 @@ constexpr int BNT = 256;  // output columns per tile (all matrices)
 // T = 8192) do not fit, so it favours row reuse (8).  Measured on MI355X.
 template <int NMAT> struct Group { static constexpr int N = NMAT == 2 ? 4 : 8; };
 
-// Map workgroup p to (expert, first row slot, valid rows, column tile) for row tiles of TBM rows; false if p has
-// no tile.
+// Which row tiles of an expert with n assignment slots a launch covers:
+//   All:  ceil(n / TBM) tiles of TBM rows (the last one partly filled);
+//   Main: 256-row tiles, except a last tile of at most 128 rows when the expert has at least kSplitFull full tiles;
+//   Tail: that last tile alone, as one 128-row tile.
+// Main and Tail together cover every row once.  A tail split off this way costs half the MFMA work of a 256-row
+// tile, but runs in a later launch and reads the expert's weight columns again, so only experts with many full
+// tiles (which read them many times anyway) give up their tail (measured on MI355X).
+enum class Rows { All, Main, Tail };
+constexpr int kSplitFull = 4;
+
+template <Rows R, int TBM>
+__device__ __forceinline__ int row_tiles(int n) {
+  const bool split = n / 256 >= kSplitFull && n % 256 != 0 && n % 256 <= 128;
+  if constexpr (R == Rows::All) return (n + TBM - 1) / TBM;
+  else if constexpr (R == Rows::Main) return (n + 255) / 256 - (split ? 1 : 0);
+  else return split ? 1 : 0;
+}
+
+// first row (relative to the expert's first slot) and valid rows of row tile m
+template <Rows R, int TBM>
+__device__ __forceinline__ void tile_rows(int n, int m, int* r0, int* rows) {
+  if constexpr (R == Rows::Tail) {
+    *r0 = n - n % 256;
+    *rows = n % 256;
+  } else {
+    *r0 = m * TBM;
+    *rows = min(TBM, n - m * TBM);
+  }
+}
+
+// Map workgroup p to (expert, first row slot, valid rows, column tile) for the row tiles R of TBM rows; false if p
+// has no tile.
 // Workgroup p runs on XCD p % 8 (round-robin dispatch).  Each XCD gets a contiguous range of tiles, ordered
 // expert -> group of NGROUP column tiles -> row tile -> column tile, so the ~32 tiles resident on one XCD share
 // their A rows (NGROUP ways) and their weight columns (32 / NGROUP ways) in that XCD's L2.
-template <int NGROUP, int TBM = BM>
+template <int NGROUP, int TBM = BM, Rows R = Rows::All>
 __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* offsets, int E, int NT, int p,
                                          int* e_out, int* row0_out, int* rows_out, int* nt_out) {
   int total = 0;
-  for (int e = 0; e < E; ++e) total += (counts[e] + TBM - 1) / TBM;
+  for (int e = 0; e < E; ++e) total += row_tiles<R, TBM>(counts[e]);
   total *= NT;
   const int chunk = (total + 7) >> 3;
   const int q = p >> 3;
@@ -40,7 +70,7 @@ __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* o
   if (L >= total) return false;
   for (int e = 0; e < E; ++e) {
     const int n = counts[e];
-    const int mt = (n + TBM - 1) / TBM;
+    const int mt = row_tiles<R, TBM>(n);
     const int te = mt * NT;
     if (L < te) {
       const int ng = L / (mt * NGROUP);
@@ -49,8 +79,10 @@ __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* o
       const int m = rem / gsz;
       *nt_out = ng * NGROUP + (rem - m * gsz);
       *e_out = e;
-      *row0_out = offsets[e] + m * TBM;
-      *rows_out = min(TBM, n - m * TBM);
+      int r0, rows;
+      tile_rows<R, TBM>(n, m, &r0, &rows);
+      *row0_out = offsets[e] + r0;
+      *rows_out = rows;
       return true;
     }
     L -= te;

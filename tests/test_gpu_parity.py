@@ -190,6 +190,23 @@ def test_layer_all_tokens_to_two_experts(gm):
         assert ref["counts"].tolist() == [T, T, 0, 0, 0, 0, 0, 0]
 
 
+def test_layer_short_last_tiles(gm):
+    """router_w = 0 puts all T tokens on experts 0 and 1.  T = 1100 and 1152 give each of them 4 full 256-row
+    tiles and a last tile of 76 / 128 rows, which the tiled kernels run as a separate 128-row tile; T = 1153 leaves
+    a 129-row last tile inside the 256-row launch.  Both weight types, and the [out, in] layout."""
+    from tests.test_gpu_layout import check_layout
+    for T, dtype in ((1100, BF16), (1152, BF16), (1153, BF16), (1100, W8)):
+        w = synth.Workload(f"tail_T{T}_{dtype}", T=T, d=256, f=512, dtype=dtype, w_std=0.1)
+        inp = synth.make_inputs(w)
+        inp["router_w"] = np.zeros_like(inp["router_w"])
+        _, ref = check_layer(gm, w, inp=inp)
+        assert ref["counts"].tolist() == [T, T, 0, 0, 0, 0, 0, 0]
+    w = synth.Workload("oi_tail_T1100", T=1100, d=256, f=512, w_std=0.1)
+    inp = synth.make_inputs(w)
+    inp["router_w"] = np.zeros_like(inp["router_w"])
+    check_layout(gm, w, inp=inp)
+
+
 def test_steps_compose_to_forward(gm):
     """grok_moe_forward equals the five step entry points called in order (bit-identical)."""
     for w in (synth.Workload("c1", T=8, d=256, f=4096, w_std=0.1), synth.Workload("c2", T=300, d=256, f=512),
