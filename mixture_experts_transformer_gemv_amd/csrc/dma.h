@@ -20,6 +20,13 @@ __device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, uint32_
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(dst) : "m0");
 }
 
+// As g2lds16, with the nontemporal hint: the lines pass through the caches with low retention.  For data read
+// once per launch (weights streamed by the few-token kernels), where it leaves the caches to the rest and reads
+// HBM faster (measured on MI355X: 6.3 -> 6.8 TB/s for the weight streams).
+__device__ __forceinline__ void g2lds16_nt(const void* base, uint32_t voff, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(base), "s"(dst) : "m0");
+}
+
 // Descriptor of a raw (unstrided) buffer of `bytes` bytes at `base` for the copies below: a lane whose offset
 // is at or past `bytes` reads zeros and touches no memory.  Word 3 selects 32-bit data (required for the range
 // check of untyped loads).

@@ -32,18 +32,19 @@
 
 namespace gm {
 
+// Weight rows are read once per launch: nontemporal loads (low cache retention) stream them faster from HBM.
 template <bool INT8> struct WRow;
 template <> struct WRow<false> {  // bf16: 16 bytes = 8 columns
   typedef u32x4_t T;
   static __device__ __forceinline__ T load(const void* base, size_t i) {
-    return *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + i);
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + i));
   }
   static __device__ __forceinline__ void transpose(const T r[8], u32x4_t t[8]) { transpose8x8_bf16(r, t); }
 };
 template <> struct WRow<true> {  // int8: 8 bytes = 8 columns
   typedef u32x2_t T;
   static __device__ __forceinline__ T load(const void* base, size_t i) {
-    return *reinterpret_cast<const u32x2_t*>(static_cast<const int8_t*>(base) + i);
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(static_cast<const int8_t*>(base) + i));
   }
   static __device__ __forceinline__ void transpose(const T r[8], u32x4_t t[8]) { transpose8x8_i8_to_bf16(r, t); }
 };

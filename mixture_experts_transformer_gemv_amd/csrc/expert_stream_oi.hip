@@ -13,6 +13,7 @@
 // 8-byte) LDS reads.  16-byte chunk c of tile row r sits in slot c ^ (r & 15) (256-byte rows) or c ^ ((r >> 1) & 7)
 // (128-byte rows), chosen on the global side, so both the copies and the operand reads are free of bank
 // conflicts.
+// The weight copies carry the nontemporal hint: each weight byte is read once per launch.
 //
 // A workgroup of 4 waves owns 64 output columns (16 per wave) of W1 and Wv (up) or of W2 (down: spw consecutive
 // chunks of the f axis, a partial sum stored per chunk, so that one ring streams several chunks) for all token
@@ -138,11 +139,11 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
       const int k0 = kbeg + s * OI_KS;
 #pragma unroll
       for (int i = 0; i < C::W_PER_WAVE; ++i)
-        g2lds16(wb0 + size_t(k0) * ESZ, w_voff[i], so + uint32_t((16 * wave + C::WROWS_PER_COPY * i) * C::ROWB));
+        g2lds16_nt(wb0 + size_t(k0) * ESZ, w_voff[i], so + uint32_t((16 * wave + C::WROWS_PER_COPY * i) * C::ROWB));
       if (NMAT == 2) {
 #pragma unroll
         for (int i = 0; i < C::W_PER_WAVE; ++i)
-          g2lds16(wb1 + size_t(k0) * ESZ, w_voff[i],
+          g2lds16_nt(wb1 + size_t(k0) * ESZ, w_voff[i],
                   so + uint32_t(C::WTILE + (16 * wave + C::WROWS_PER_COPY * i) * C::ROWB));
       }
 #pragma unroll

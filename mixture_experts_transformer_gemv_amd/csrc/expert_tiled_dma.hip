@@ -79,6 +79,13 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   constexpr int BCOPIES = INT8 ? 2 : 4;        // 1 KB weight copies per wave and K step ([in, out])
   constexpr int CPS = AP + BCOPIES;            // copies per wave and K step ([out, in]: AP + 4)
   constexpr int A_STRIDE = OUTIN ? A_STG : STAGE;  // between ring slots of A
+  // 128-row tiles run one per expert and column tile in their launch, so each weight byte is read once there:
+  // nontemporal copies (the 256-row tiles share weight columns through the caches and keep the default policy).
+  constexpr bool B_NT = TBM == 128;
+  auto copy_b = [](const void* base, uint32_t voff, uint32_t dst) {
+    if constexpr (B_NT) g2lds16_nt(base, voff, dst);
+    else g2lds16(base, voff, dst);
+  };
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -139,16 +146,16 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     if (n < AP)
       b2lds16(a_rsrc, uint32_t(kbase + kt * BK) * 2u, a_voff[n], a_dst + so + uint32_t(16 * n) * (BK * 2));
     else if (INT8)  // 8 weight rows of 128 bytes per piece
-      g2lds16(b_base8 + size_t(kbase + kt * BK) * N + size_t(8 * (n - AP)) * N, b_voff,
+      copy_b(b_base8 + size_t(kbase + kt * BK) * N + size_t(8 * (n - AP)) * N, b_voff,
               b_dst + so + uint32_t(8 * (n - AP)) * 128);
     else  // 4 weight rows of 256 bytes per piece
-      g2lds16(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - AP)) * N, b_voff,
+      copy_b(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - AP)) * N, b_voff,
               b_dst + so + uint32_t(4 * (n - AP)) * 256);
   };
   // OUTIN: copy c of K-step pair q into pair slot q % 3 (past the end: the last pair again, into a free slot)
   auto copy_pair = [&](int q, int c) {
     const int qd = min(q, (Ks / BK) / 2 - 1);
-    g2lds16(bt_base + size_t(kbase + qd * 2 * BK), bp_voff[c],
+    copy_b(bt_base + size_t(kbase + qd * 2 * BK), bp_voff[c],
             bp_dst + uint32_t((q % NPAIR) * B_PAIR) + uint32_t(c * 1024));
   };
 
@@ -409,8 +416,9 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
                                          split_stride, e, row0, rows, ntile, (lds_u8*)(smem));
 }
 
-// An expert's rows as 256-row tiles; with at least tile::kSplitFull full tiles, a last tile of at most 128 rows
-// goes to a second launch as a 128-row tile (half the MFMA work on its padding).
+// Two launches: the 256-row tiles (tile::Rows::Main), then at most one 128-row tile per expert and column tile
+// (tile::Rows::Tail: an expert with at most 128 slots, or the short last tile of a large expert).  The device
+// decides from the counts; a workgroup without a tile exits at once.
 static unsigned tail_tiles(int E, int NT) { return (unsigned(E) * unsigned(NT) + 7u) & ~7u; }
 
 hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,

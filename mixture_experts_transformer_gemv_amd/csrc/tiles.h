@@ -24,26 +24,30 @@ template <int NMAT> struct Group { static constexpr int N = NMAT == 2 ? 4 : 8; }
 
 // Which row tiles of an expert with n assignment slots a launch covers:
 //   All:  ceil(n / TBM) tiles of TBM rows (the last one partly filled);
-//   Main: 256-row tiles, except a last tile of at most 128 rows when the expert has at least kSplitFull full tiles;
-//   Tail: that last tile alone, as one 128-row tile.
-// Main and Tail together cover every row once.  A tail split off this way costs half the MFMA work of a 256-row
-// tile, but runs in a later launch and reads the expert's weight columns again, so only experts with many full
-// tiles (which read them many times anyway) give up their tail (measured on MI355X).
+//   Main: 256-row tiles of the experts with more than 128 slots, except a last tile of at most 128 rows when the
+//         expert has at least kSplitFull full tiles;
+//   Tail: one 128-row tile per expert: the whole expert if it has at most 128 slots, else that split-off last tile.
+// Main and Tail together cover every row once.  A 128-row tile costs half the MFMA work of a 256-row one, which
+// decides small experts (all of them for batches of a few hundred tokens, where the padding of 256-row tiles
+// dominated).  A tail split off a large expert runs in a later launch and reads the expert's weight columns
+// again, without the row sharing of the 256-row launch, so only experts with many full tiles (which read them
+// many times anyway) give up their tail (measured on MI355X).
 enum class Rows { All, Main, Tail };
 constexpr int kSplitFull = 4;
 
 template <Rows R, int TBM>
 __device__ __forceinline__ int row_tiles(int n) {
+  const bool small = n > 0 && n <= 128;
   const bool split = n / 256 >= kSplitFull && n % 256 != 0 && n % 256 <= 128;
   if constexpr (R == Rows::All) return (n + TBM - 1) / TBM;
-  else if constexpr (R == Rows::Main) return (n + 255) / 256 - (split ? 1 : 0);
-  else return split ? 1 : 0;
+  else if constexpr (R == Rows::Main) return small ? 0 : (n + 255) / 256 - (split ? 1 : 0);
+  else return (small || split) ? 1 : 0;
 }
 
 // first row (relative to the expert's first slot) and valid rows of row tile m
 template <Rows R, int TBM>
 __device__ __forceinline__ void tile_rows(int n, int m, int* r0, int* rows) {
-  if constexpr (R == Rows::Tail) {
+  if constexpr (R == Rows::Tail) {  // n <= 128, or the last n % 256 <= 128 slots
     *r0 = n - n % 256;
     *rows = n % 256;
   } else {

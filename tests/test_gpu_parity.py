@@ -273,7 +273,7 @@ def grok_bf16():
 
 
 def _grok_case(gm, grok_bf16, name):
-    w = synth.WORKLOADS[name]
+    w = synth.WORKLOADS[name] if isinstance(name, str) else name
     wts, dvw = grok_bf16
     inp = synth.make_inputs(w, weights=wts)
     dv = dict(dvw)
@@ -304,6 +304,19 @@ def test_grok_skew_bf16_sampled(gm, grok_bf16):
     assert c[0] > 0.4 * c.sum() and c[5] > 0.2 * c.sum()
 
 
+@pytest.mark.parametrize("T", [72, 256, 600])
+def test_grok_mid_batch_bf16_sampled(gm, grok_bf16, T):
+    """Batches of a few hundred tokens at Grok-1 shape: experts with at most 128 slots run as 128-row tiles with
+    nontemporal weight copies (all of them at T = 72 and 256), larger ones as 256-row tiles (T = 600)."""
+    w = dataclasses.replace(synth.WORKLOADS["prefill_bf16"], T=T, name=f"mid_bf16_T{T}", sampled_rows=64)
+    (out, ref), _ = _grok_case(gm, grok_bf16, w)
+    c = ref["counts"].numpy()
+    if T <= 256:
+        assert c.max() <= 128
+    else:
+        assert c.min() <= 128 < c.max()
+
+
 @pytest.fixture(scope="module")
 def grok_int8():
     say("[setup] drawing Grok-1-shape int8 weights (4.83 GB)")
@@ -330,6 +343,11 @@ def _grok_int8_case(gm, grok_int8, T, sampled):
 def test_grok_int8(gm, grok_int8):
     """The int8 workload (T = 64, weight-streaming kernels), every row."""
     _grok_int8_case(gm, grok_int8, 64, None)
+
+
+def test_grok_int8_mid_batch_sampled(gm, grok_int8):
+    """int8 weights at T = 128: every expert in the 128-row tiles, 64 seeded rows."""
+    _grok_int8_case(gm, grok_int8, 128, 64)
 
 
 def test_grok_int8_prefill_sampled(gm, grok_int8):
