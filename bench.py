@@ -369,7 +369,7 @@ def main():
         oi = "true" if a.weight_layout == "out_in" else "false"
         grouped = w.groups_up > 1 or w.groups_down > 1
         if w.dtype == 1 or (not grouped and oi == "false"):  # 256-row tiles, then 128-row last tiles
-            kname = f"tiled_dma_kernel<2, {oi}, {'true' if w.dtype == 2 else 'false'}, 256|128>"
+            kname = f"tiled_dma_kernel<2, {oi}, {'true' if w.dtype == 2 else 'false'}, 256> + tiled_dma_small_kernel"
         else:
             kname = f"tiled_reg_kernel<2, {'true' if grouped else 'false'}, {oi}>"
         res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
@@ -394,7 +394,7 @@ def main():
                           "ms_per_step": pms, "steps": a.prefill_steps,
                           "layer_TFLOPs": 3 * fl / 2 / (pms * 1e-3) / 1e12,
                           "roofline": {"bound": "mfma",
-                                       "kernel": f"tiled_dma_kernel<2, {str(a.weight_layout == 'out_in').lower()}, false, 256|128>",
+                                       "kernel": f"tiled_dma_kernel<2, {str(a.weight_layout == 'out_in').lower()}, false, 256> + tiled_dma_small_kernel",
                                        "achieved": fl / (pk[0] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": fl / (pk[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                                        "traffic": load_traffic(pname, "up"), "algorithmic_flops": fl},

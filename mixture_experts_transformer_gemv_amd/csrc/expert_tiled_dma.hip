@@ -67,7 +67,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
                                                         int N, void* __restrict__ out, int64_t split_stride, int e,
                                                         int row0, int rows, int ntile, lds_u8* lds) {
   static_assert(!(OUTIN && INT8), "int8 weights are tiled from [E, K, N] storage");
-  static_assert(TBM == 256 || TBM == 128, "tiles of 256 or 128 rows");
+  static_assert(TBM == 256 || TBM == 192 || TBM == 128, "tiles of 256, 192 or 128 rows");
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   constexpr int MI = TBM / 64;     // row blocks of 32 per wave (waves 2 x 2: TBM / 2 rows each)
   constexpr int AP = TBM / 64;     // 1 KB activation copies per wave and K step
@@ -396,7 +396,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
 }
 
 // The grouped GEMM: workgroup blockIdx.x takes the tile map_tile gives it among the row tiles R of TBM rows, in the
-// XCD-aware order.
+// XCD-aware order.  The up-projection (NMAT = 2) gives the experts that 192-row tiles pad less to those.
 template <int NMAT, bool OUTIN, bool INT8, int TBM, tile::Rows R>
 __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restrict__ A, const void* __restrict__ B0,
                                                         const void* __restrict__ B1,
@@ -408,25 +408,59 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
                                                         int N, int E, void* __restrict__ out,
                                                         int64_t split_stride) {
   int e, row0, rows, ntile;
-  if (!tile::map_tile<tile::Group<NMAT>::N, TBM, R>(counts, offsets, E, N / (BNT / NMAT), blockIdx.x, &e, &row0,
-                                                    &rows, &ntile))
+  if (!tile::map_tile<tile::Group<NMAT>::N, TBM, R, NMAT == 2>(counts, offsets, E, N / (BNT / NMAT), blockIdx.x,
+                                                               &e, &row0, &rows, &ntile))
     return;  // whole workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<NMAT, OUTIN, INT8, TBM>()];
   tiled_dma_tile<NMAT, OUTIN, INT8, TBM>(A, B0, B1, s0, s1, s_estride, counts, offsets, perm, a_bytes, K, N, out,
                                          split_stride, e, row0, rows, ntile, (lds_u8*)(smem));
 }
 
-// Two launches: the 256-row tiles (tile::Rows::Main), then at most one 128-row tile per expert and column tile
-// (tile::Rows::Tail: an expert with at most 128 slots, or the short last tile of a large expert).  The device
-// decides from the counts; a workgroup without a tile exits at once.
+// The up-projection's second launch: the 192-row tiles (tile::Rows::Mid) and the 128-row tiles (tile::Rows::Tail)
+// in one grid, each workgroup running the body of its tile's height (one launch fewer than a launch per height:
+// an empty launch of the upper-bound grid costs ~70 us at prefill size, measured on MI355X).
+template <bool OUTIN, bool INT8>
+__global__ __launch_bounds__(256) void tiled_dma_small_kernel(const uint16_t* __restrict__ A,
+                                                              const void* __restrict__ B0,
+                                                              const void* __restrict__ B1,
+                                                              const uint16_t* __restrict__ s0,
+                                                              const uint16_t* __restrict__ s1, int64_t s_estride,
+                                                              const int32_t* __restrict__ counts,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ perm, uint32_t a_bytes,
+                                                              int K, int N, int E, void* __restrict__ out) {
+  bool mid;
+  int e, row0, rows, ntile;
+  if (!tile::map_small_tile<tile::Group<2>::N>(counts, offsets, E, N / (BNT / 2), blockIdx.x, &mid, &e, &row0, &rows,
+                                               &ntile))
+    return;  // whole workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<2, OUTIN, INT8, 192>()];
+  if (mid)
+    tiled_dma_tile<2, OUTIN, INT8, 192>(A, B0, B1, s0, s1, s_estride, counts, offsets, perm, a_bytes, K, N, out, 0,
+                                        e, row0, rows, ntile, (lds_u8*)(smem));
+  else
+    tiled_dma_tile<2, OUTIN, INT8, 128>(A, B0, B1, s0, s1, s_estride, counts, offsets, perm, a_bytes, K, N, out, 0,
+                                        e, row0, rows, ntile, (lds_u8*)(smem));
+}
+
+// Launches: the 256-row tiles (tile::Rows::Main); then, for the up-projection, the 192-row tiles of experts with up
+// to tile::kMidMax slots that they pad less (tile::Rows::Mid) together with at most one 128-row tile per expert and
+// column tile (tile::Rows::Tail: an expert with at most 128 slots, or the short last tile of a large expert); for
+// the down-projection the 128-row tiles alone.  The device decides from the counts; the grids are upper bounds and
+// a workgroup without a tile exits at once.
 static unsigned tail_tiles(int E, int NT) { return (unsigned(E) * unsigned(NT) + 7u) & ~7u; }
+static unsigned small_tiles(int slots, int E, int NT) {
+  const unsigned per_expert = unsigned(tile::kMidMax / 192), bound = unsigned(slots / 192 + E);
+  const unsigned b1 = (per_expert * unsigned(E) < bound ? per_expert * unsigned(E) : bound) * unsigned(NT);
+  return 8u * ((b1 + 7u) / 8u) + tail_tiles(E, NT);
+}
 
 hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                                const uint16_t* sv, int64_t s_estride, bool int8, bool outin, const int32_t* counts,
                                const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
                                uint16_t* h, hipStream_t s) {
   const int NT = f / (BNT / 2);
-  const dim3 grid(tile::grid_tiles(slots, E, NT)), grid_t(tail_tiles(E, NT)), block(256);
+  const dim3 grid(tile::grid_tiles(slots, E, NT)), grid_s(small_tiles(slots, E, NT)), block(256);
   const size_t xbytes = size_t(slots / 2) * d * 2;  // x: [slots / 2 tokens, d] (two slots per token)
   if (xbytes >= (size_t(1) << 31) || size_t(2) * slots * f >= (size_t(1) << 31)) return hipErrorInvalidValue;
   if (int8 && outin) return hipErrorInvalidValue;
@@ -435,8 +469,8 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
   do {                                                                                                         \
     tiled_dma_kernel<2, OI, I8, 256, tile::Rows::Main><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, s_estride,       \
                                                                                counts, offsets, perm, xb, d, f, E, h, 0); \
-    tiled_dma_kernel<2, OI, I8, 128, tile::Rows::Tail><<<grid_t, block, 0, s>>>(x, w1, wv, s1, sv, s_estride,     \
-                                                                                counts, offsets, perm, xb, d, f, E, h, 0); \
+    tiled_dma_small_kernel<OI, I8><<<grid_s, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, offsets, perm,  \
+                                                             xb, d, f, E, h);                                   \
   } while (0)
   if (int8) GM_UPD(false, true);
   else if (outin) GM_UPD(true, false);

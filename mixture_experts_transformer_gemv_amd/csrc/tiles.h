@@ -24,23 +24,33 @@ template <int NMAT> struct Group { static constexpr int N = NMAT == 2 ? 4 : 8; }
 
 // Which row tiles of an expert with n assignment slots a launch covers:
 //   All:  ceil(n / TBM) tiles of TBM rows (the last one partly filled);
-//   Main: 256-row tiles of the experts with more than 128 slots, except a last tile of at most 128 rows when the
-//         expert has at least kSplitFull full tiles;
+//   Main: 256-row tiles of the other experts (below), except a last tile of at most 128 rows when the expert has
+//         at least kSplitFull full tiles;
+//   Mid:  192-row tiles of the experts with 128 < n <= kMidMax slots that 192-row tiles pad less than 256-row ones
+//         (n in (128, 192], (256, 384] or (512, 576]), if MID (else those experts stay in Main);
 //   Tail: one 128-row tile per expert: the whole expert if it has at most 128 slots, else that split-off last tile.
-// Main and Tail together cover every row once.  A 128-row tile costs half the MFMA work of a 256-row one, which
-// decides small experts (all of them for batches of a few hundred tokens, where the padding of 256-row tiles
-// dominated).  A tail split off a large expert runs in a later launch and reads the expert's weight columns
-// again, without the row sharing of the 256-row launch, so only experts with many full tiles (which read them
-// many times anyway) give up their tail (measured on MI355X).
-enum class Rows { All, Main, Tail };
+// Main, Mid and Tail together cover every row once.  Smaller tiles spend less MFMA work on padding rows, which
+// decides small experts (batches of a few hundred tokens, the small experts of skewed routing).  A tail split off a
+// large expert runs in a later launch and reads the expert's weight columns again, without the row sharing of the
+// 256-row launch, so only experts with many full tiles (which read them many times anyway) give up their tail
+// (measured on MI355X).  The down-projection runs without Mid: its launches hold few rounds of tiles, and the
+// partly idle last round of one more launch cost more than the 192-row tiles saved (measured on MI355X).
+enum class Rows { All, Main, Mid, Tail };
 constexpr int kSplitFull = 4;
+constexpr int kMidMax = 576;
 
-template <Rows R, int TBM>
+__device__ __forceinline__ bool mid_expert(int n) {
+  return n > 128 && n <= kMidMax && (n + 191) / 192 * 192 < (n + 255) / 256 * 256;
+}
+
+template <Rows R, int TBM, bool MID = true>
 __device__ __forceinline__ int row_tiles(int n) {
   const bool small = n > 0 && n <= 128;
+  const bool mid = MID && mid_expert(n);
   const bool split = n / 256 >= kSplitFull && n % 256 != 0 && n % 256 <= 128;
   if constexpr (R == Rows::All) return (n + TBM - 1) / TBM;
-  else if constexpr (R == Rows::Main) return small ? 0 : (n + 255) / 256 - (split ? 1 : 0);
+  else if constexpr (R == Rows::Main) return (small || mid) ? 0 : (n + 255) / 256 - (split ? 1 : 0);
+  else if constexpr (R == Rows::Mid) return mid ? (n + 191) / 192 : 0;
   else return (small || split) ? 1 : 0;
 }
 
@@ -56,25 +66,14 @@ __device__ __forceinline__ void tile_rows(int n, int m, int* r0, int* rows) {
   }
 }
 
-// Map workgroup p to (expert, first row slot, valid rows, column tile) for the row tiles R of TBM rows; false if p
-// has no tile.
-// Workgroup p runs on XCD p % 8 (round-robin dispatch).  Each XCD gets a contiguous range of tiles, ordered
-// expert -> group of NGROUP column tiles -> row tile -> column tile, so the ~32 tiles resident on one XCD share
-// their A rows (NGROUP ways) and their weight columns (32 / NGROUP ways) in that XCD's L2.
-template <int NGROUP, int TBM = BM, Rows R = Rows::All>
-__device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* offsets, int E, int NT, int p,
-                                         int* e_out, int* row0_out, int* rows_out, int* nt_out) {
-  int total = 0;
-  for (int e = 0; e < E; ++e) total += row_tiles<R, TBM>(counts[e]);
-  total *= NT;
-  const int chunk = (total + 7) >> 3;
-  const int q = p >> 3;
-  if (q >= chunk) return false;
-  int L = (p & 7) * chunk + q;
-  if (L >= total) return false;
+// Tile L (in the order below) among the row tiles R of TBM rows: (expert, first row slot, valid rows, column tile).
+// Order: expert -> group of NGROUP column tiles -> row tile -> column tile.
+template <int NGROUP, Rows R, int TBM, bool MID>
+__device__ __forceinline__ bool locate(const int32_t* counts, const int32_t* offsets, int E, int NT, int L,
+                                       int* e_out, int* row0_out, int* rows_out, int* nt_out) {
   for (int e = 0; e < E; ++e) {
     const int n = counts[e];
-    const int mt = row_tiles<R, TBM>(n);
+    const int mt = row_tiles<R, TBM, MID>(n);
     const int te = mt * NT;
     if (L < te) {
       const int ng = L / (mt * NGROUP);
@@ -92,6 +91,53 @@ __device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* o
     L -= te;
   }
   return false;
+}
+
+// Map workgroup p to (expert, first row slot, valid rows, column tile) for the row tiles R of TBM rows; false if p
+// has no tile.
+// Workgroup p runs on XCD p % 8 (round-robin dispatch).  Each XCD gets a contiguous range of tiles in the order of
+// locate(), so the ~32 tiles resident on one XCD share their A rows (NGROUP ways) and their weight columns
+// (32 / NGROUP ways) in that XCD's L2.
+template <int NGROUP, int TBM = BM, Rows R = Rows::All, bool MID = true>
+__device__ __forceinline__ bool map_tile(const int32_t* counts, const int32_t* offsets, int E, int NT, int p,
+                                         int* e_out, int* row0_out, int* rows_out, int* nt_out) {
+  int total = 0;
+  for (int e = 0; e < E; ++e) total += row_tiles<R, TBM, MID>(counts[e]);
+  total *= NT;
+  const int chunk = (total + 7) >> 3;
+  const int q = p >> 3;
+  if (q >= chunk) return false;
+  const int L = (p & 7) * chunk + q;
+  if (L >= total) return false;
+  return locate<NGROUP, R, TBM, MID>(counts, offsets, E, NT, L, e_out, row0_out, rows_out, nt_out);
+}
+
+// Map workgroup p of one launch over the Mid (192-row) and Tail (128-row) tiles: each XCD takes its contiguous
+// eighth of the Mid tiles first, then of the Tail tiles.  *mid tells which.  Host grid: 8 (ceil(B1 / 8) +
+// ceil(B2 / 8)) workgroups for upper bounds B1, B2 of the two tile counts.
+template <int NGROUP>
+__device__ __forceinline__ bool map_small_tile(const int32_t* counts, const int32_t* offsets, int E, int NT, int p,
+                                               bool* mid, int* e_out, int* row0_out, int* rows_out, int* nt_out) {
+  int t1 = 0, t2 = 0;
+  for (int e = 0; e < E; ++e) {
+    t1 += row_tiles<Rows::Mid, 192>(counts[e]);
+    t2 += row_tiles<Rows::Tail, 128>(counts[e]);
+  }
+  t1 *= NT;
+  t2 *= NT;
+  const int x = p & 7, c1 = (t1 + 7) >> 3, c2 = (t2 + 7) >> 3;
+  int q = p >> 3;
+  *mid = q < c1;
+  if (*mid) {
+    const int L = x * c1 + q;
+    return L < t1 && locate<NGROUP, Rows::Mid, 192, true>(counts, offsets, E, NT, L, e_out, row0_out, rows_out,
+                                                           nt_out);
+  }
+  q -= c1;
+  if (q >= c2) return false;
+  const int L = x * c2 + q;
+  return L < t2 && locate<NGROUP, Rows::Tail, 128, true>(counts, offsets, E, NT, L, e_out, row0_out, rows_out,
+                                                          nt_out);
 }
 
 // Upper bound of the number of tiles, rounded to a multiple of 8 (the grid); the exact count depends on the

@@ -190,21 +190,25 @@ def test_layer_all_tokens_to_two_experts(gm):
         assert ref["counts"].tolist() == [T, T, 0, 0, 0, 0, 0, 0]
 
 
-def test_layer_short_last_tiles(gm):
-    """router_w = 0 puts all T tokens on experts 0 and 1.  T = 1100 and 1152 give each of them 4 full 256-row
-    tiles and a last tile of 76 / 128 rows, which the tiled kernels run as a separate 128-row tile; T = 1153 leaves
-    a 129-row last tile inside the 256-row launch.  Both weight types, and the [out, in] layout."""
+def test_layer_tile_heights(gm):
+    """router_w = 0 puts all T tokens on experts 0 and 1, so each has exactly T slots.  The tiled kernels pick the
+    tile height from the count: T = 150, 315, 384 and 550 run as 1, 2, 2 and 3 tiles of 192 rows; T = 1100 and 1152
+    as 4 full 256-row tiles plus a last tile of 76 / 128 rows run as a 128-row tile; T = 1153 keeps its 129-row last
+    tile in the 256-row launch.  Both weight types, and the [out, in] layout."""
     from tests.test_gpu_layout import check_layout
-    for T, dtype in ((1100, BF16), (1152, BF16), (1153, BF16), (1100, W8)):
-        w = synth.Workload(f"tail_T{T}_{dtype}", T=T, d=256, f=512, dtype=dtype, w_std=0.1)
+    cases = [(150, BF16), (315, BF16), (384, BF16), (550, BF16), (1100, BF16), (1152, BF16), (1153, BF16),
+             (315, W8), (1100, W8)]
+    for T, dtype in cases:
+        w = synth.Workload(f"tiles_T{T}_{dtype}", T=T, d=256, f=512, dtype=dtype, w_std=0.1)
         inp = synth.make_inputs(w)
         inp["router_w"] = np.zeros_like(inp["router_w"])
         _, ref = check_layer(gm, w, inp=inp)
         assert ref["counts"].tolist() == [T, T, 0, 0, 0, 0, 0, 0]
-    w = synth.Workload("oi_tail_T1100", T=1100, d=256, f=512, w_std=0.1)
-    inp = synth.make_inputs(w)
-    inp["router_w"] = np.zeros_like(inp["router_w"])
-    check_layout(gm, w, inp=inp)
+    for T in (315, 1100):
+        w = synth.Workload(f"oi_tiles_T{T}", T=T, d=256, f=512, w_std=0.1)
+        inp = synth.make_inputs(w)
+        inp["router_w"] = np.zeros_like(inp["router_w"])
+        check_layout(gm, w, inp=inp)
 
 
 def test_steps_compose_to_forward(gm):
@@ -307,7 +311,8 @@ def test_grok_skew_bf16_sampled(gm, grok_bf16):
 @pytest.mark.parametrize("T", [72, 256, 600])
 def test_grok_mid_batch_bf16_sampled(gm, grok_bf16, T):
     """Batches of a few hundred tokens at Grok-1 shape: experts with at most 128 slots run as 128-row tiles with
-    nontemporal weight copies (all of them at T = 72 and 256), larger ones as 256-row tiles (T = 600)."""
+    nontemporal weight copies (all of them at T = 72 and 256); at T = 600 one expert does, the others (149-160
+    slots) run as 192-row tiles."""
     w = dataclasses.replace(synth.WORKLOADS["prefill_bf16"], T=T, name=f"mid_bf16_T{T}", sampled_rows=64)
     (out, ref), _ = _grok_case(gm, grok_bf16, w)
     c = ref["counts"].numpy()
