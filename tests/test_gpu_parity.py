@@ -63,7 +63,9 @@ def check_layer(gm, w: synth.Workload, inp=None, rows=None, name=None, dv=None):
 
 @pytest.mark.parametrize("T,d,E,dtype,bias", [
     (1, 256, 8, BF16, False), (77, 512, 8, BF16, True), (1000, 256, 8, BF16, False), (50, 256, 16, BF16, False),
-    (30, 256, 64, BF16, True), (64, 128, 8, F32, False), (129, 192, 8, F32, True), (20, 6144, 8, BF16, False)])
+    (30, 256, 64, BF16, True), (64, 128, 8, F32, False), (129, 192, 8, F32, True), (20, 6144, 8, BF16, False),
+    # batches above 256 tokens with up to 8 experts: 8 tokens per workgroup, ragged last workgroup
+    (1003, 256, 8, BF16, True), (300, 512, 4, F32, True), (777, 6144, 8, BF16, False), (260, 256, 2, BF16, False)])
 def test_router_step(gm, T, d, E, dtype, bias):
     say(f"[case] router T={T} d={d} E={E} dtype={dtype} bias={bias}")
     w = synth.Workload("r", T=T, d=d, f=256, E=E, dtype=dtype)
@@ -80,15 +82,16 @@ def test_router_step(gm, T, d, E, dtype, bias):
     assert np.allclose(p.cpu().numpy(), ref["p"].numpy(), rtol=1e-6, atol=0)
 
 
-def test_router_ties_take_lower_index(gm):
-    x = torch.randn(40, 256, device="cuda").to(torch.bfloat16)
+@pytest.mark.parametrize("T", [40, 603])
+def test_router_ties_take_lower_index(gm, T):
+    x = torch.randn(T, 256, device="cuda").to(torch.bfloat16)
     rw = torch.zeros(8, 256, device="cuda", dtype=torch.bfloat16)
     bias = torch.tensor([0, 0, 1, 1, 1, 0, 0, 0], dtype=torch.float32, device="cuda")
     idx, p = gm.route(x, rw, bias)
     assert (idx.cpu() == torch.tensor([2, 3], dtype=torch.int32)).all()
     idx0, p0 = gm.route(x, rw, None)
     assert (idx0.cpu() == torch.tensor([0, 1], dtype=torch.int32)).all()
-    assert torch.allclose(p0.cpu(), torch.full((40, 2), 0.125))
+    assert torch.allclose(p0.cpu(), torch.full((T, 2), 0.125))
 
 
 def _random_assignments(T, E, rng):
