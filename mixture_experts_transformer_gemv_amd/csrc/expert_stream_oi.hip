@@ -47,12 +47,14 @@ struct OiCfg {
   static constexpr int STAGE = NMAT * WTILE + ABYTES;
   // ring depth (measured on MI355X).  Up-projection: at most 4 stages; two workgroups per CU (80 KB each) where
   // that leaves at least 3 stages, else one workgroup with up to 144 KB (two resident rings keep more copies in
-  // flight: int8 with grouped scales 0.65 -> 0.56 ms at T = 64).  Down-projection: 2 stages, so that 3-4
+  // flight: int8 with grouped scales 0.65 -> 0.56 ms at T = 64), 3 stages for one 16-row tile (bf16 T = 8:
+  // 0.953 -> 0.945 ms against 4; 2 stages on two workgroups per CU: 0.953).  Down-projection: 2 stages, so that 3-4
   // workgroups share a CU and the whole grid (one workgroup per 64 columns and expert, every chunk of f) runs
   // in one round (bf16 T = 8: 0.578 -> 0.549 ms against 4 stages over 6 rounds).
   static constexpr int NSTG2 = (80 * 1024 / STAGE) < 4 ? (80 * 1024 / STAGE) : 4;
+  static constexpr int NSTG1 = MT == 1 ? 3 : 4;  // one workgroup per CU
   static constexpr int NSTG =
-      NMAT == 1 ? 2 : (NSTG2 >= 3 ? NSTG2 : ((OI_LDS / STAGE) < 4 ? (OI_LDS / STAGE) : 4));
+      NMAT == 1 ? 2 : (NSTG2 >= 3 ? NSTG2 : ((OI_LDS / STAGE) < NSTG1 ? (OI_LDS / STAGE) : NSTG1));
   static constexpr int A_PER_WAVE = ABYTES / 1024 / 4;         // = MT
   static constexpr int CPW = NMAT * W_PER_WAVE + A_PER_WAVE;   // copies per wave per stage
   static_assert(NSTG >= 2, "stage ring does not fit");
