@@ -26,6 +26,10 @@
 // shadow of the 32-cycle MFMAs.  The down-projection may split K over gridDim.y workgroups (fp32 partial sums,
 // added by the combine) so that its smaller number of tiles still fills the chip.  Up-projection epilogue: the
 // GELU product tile is staged in the idle ring and written as 16-byte row pieces.
+// Tile heights: the body is compiled for 256, 192 and 128 rows (4, 3 or 2 row blocks of 32 per wave; every copy,
+// fragment and epilogue loop scales with the height).  The 256-row tiles run in one launch; small experts and the
+// short last tiles of large ones run in a second launch (tiles.h gives the rules), whose 128-row tiles read each
+// weight byte once and copy it with the nontemporal hint.
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
