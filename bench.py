@@ -357,7 +357,8 @@ def main():
         res["roofline"] = {"bound": "alu", "kernel": "f32_tiled_kernel<2>", "achieved": ach,
                            "peak": FP32_VALU_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP32_VALU_TFLOPS,
                            "traffic": None, "algorithmic_flops": fl}
-    elif w.T <= 64:  # weight-streaming regime: HBM-bound, the up-projection (W1 and Wv) is the dominant kernel
+    elif w.T <= (128 if w.dtype == synth.W8 else 96):  # weight-streaming kernels: HBM-bound, the up-projection
+        # (W1 and Wv) is the dominant kernel
         ub = up_bytes(w, nh, T)
         ach = ub / (kms[0] * 1e-3) / 1e9
         kname = "oi_stream_kernel<2>" if a.weight_layout == "out_in" else "up_stream_kernel"

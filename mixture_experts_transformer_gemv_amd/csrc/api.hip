@@ -13,7 +13,16 @@
 namespace {
 
 constexpr int64_t kMaxTokens = int64_t(1) << 24;
-constexpr int kStreamMaxTokens = 64;  // at most this many tokens: few rows per expert -> weight streaming kernels
+// At most this many tokens: few rows per expert -> weight-streaming kernels (16 or 32 rows per pass over the
+// weights), else the LDS-tiled kernels.  Measured on MI355X at the Grok-1 shape: bf16 streams win up to T = 96
+// (T = 96: 1.50 against 1.64 ms per layer) and lose at T = 128 (two passes for most experts: 2.46 against 1.66);
+// int8 tiles spend their MFMA time on padding rows at small T, and the int8 streams win up to T = 128 (grouped
+// scales, T = 128: 1.51 against 2.08 ms; one scale group: even at T = 128, slower from T = 160).
+constexpr int kStreamMaxTokensBf16 = 96;
+constexpr int kStreamMaxTokensInt8 = 128;
+int stream_max_tokens(int dtype) {
+  return dtype == GROK_MOE_W8 ? kStreamMaxTokensInt8 : kStreamMaxTokensBf16;
+}
 
 struct Plan {
   int64_t slots;
@@ -44,7 +53,7 @@ int check_shape(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
 int64_t max_pass_tokens(int64_t d, int64_t f, int dtype) {
   if (dtype != GROK_MOE_BF16) return kMaxTokens;
   const int64_t lim = (int64_t(1) << 31) - 1;
-  return std::max<int64_t>(kStreamMaxTokens + 1, std::min(lim / (2 * d), lim / (4 * f)));
+  return std::max<int64_t>(kStreamMaxTokensBf16 + 1, std::min(lim / (2 * d), lim / (4 * f)));
 }
 
 // T tokens as n passes of near-equal size: the first `rem` passes take base + 1 tokens, the others base.
@@ -61,7 +70,7 @@ Passes passes(int64_t T, int64_t d, int64_t f, int dtype) {
 
 int down_splits(int64_t T, int64_t f, int dtype) {
   // LDS-tiled bf16 down-projection: K split in two, so that its tiles fill the chip in more, shorter rounds
-  if (dtype == GROK_MOE_BF16 && T > kStreamMaxTokens) return 2;
+  if (dtype == GROK_MOE_BF16 && T > stream_max_tokens(dtype)) return 2;
   // fp32 layer: a small batch gives few tiles, each a long chain of 16-deep K steps: for T <= 256 split K into
   // up to 8 parts of at least 128 k (partial sums added by the combine)
   if (dtype == GROK_MOE_F32) {
@@ -69,7 +78,7 @@ int down_splits(int64_t T, int64_t f, int dtype) {
     while (T <= 256 && s < 8 && f / (2 * s) >= 128 && (f / (2 * s)) % 16 == 0) s *= 2;
     return s;
   }
-  if (T > kStreamMaxTokens) return 1;
+  if (T > stream_max_tokens(dtype)) return 1;
   // chunks of at least 2048 rows of W2 (a multiple of 64), at most 8 chunks (measured against 4, 16 and 32)
   int s = 1;
   while (s < 8 && (f / (2 * s)) % 64 == 0 && f / (2 * s) >= 2048) s *= 2;
@@ -79,7 +88,7 @@ int down_splits(int64_t T, int64_t f, int dtype) {
 Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
   Plan p;
   p.slots = 2 * T;
-  p.stream = dtype != GROK_MOE_F32 && T <= kStreamMaxTokens;
+  p.stream = dtype != GROK_MOE_F32 && T <= stream_max_tokens(dtype);
   p.mt = T <= 16 ? 1 : 2;
   p.mt_oi = T <= 16 ? 1 : 2;  // (4 tiles measured slower at T = 64: the token tile outgrows the weight tile)
   p.splits = down_splits(T, f, dtype);

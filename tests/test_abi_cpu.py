@@ -54,6 +54,9 @@ def test_workspace_size_and_splits(L):
     assert gm.down_splits(8, 6144, 32768) == 8
     assert gm.down_splits(8192, 6144, 32768) == 2   # LDS-tiled bf16 path splits K in two
     assert gm.down_splits(8192, 6144, 32768, 8, 2, gm.W8) == 1
+    # the streaming kernels take bf16 batches up to 96 tokens and int8 batches up to 128
+    assert gm.down_splits(96, 6144, 32768) == 8 and gm.down_splits(97, 6144, 32768) == 2
+    assert gm.down_splits(128, 6144, 32768, 8, 2, gm.W8) == 8 and gm.down_splits(129, 6144, 32768, 8, 2, gm.W8) == 1
     assert gm.down_splits(64, 128, 512, 8, 2, gm.F32) == 4   # small fp32 batch: K split in parts of 128
     assert gm.down_splits(300, 128, 512, 8, 2, gm.F32) == 1
     ws_pre = gm.workspace_size(8192, 6144, 32768)

@@ -31,12 +31,13 @@ def _w(name, T, d, f, E=8, g1=1, g2=1, es=None, seed=0):
 
 
 CASES = [
-    # streaming kernels (T <= 64): one and two 16-row tiles per pass, 64-row groups, chunks of the down
+    # streaming kernels (int8: T <= 128): one and two 16-row tiles per pass, 64-row groups, chunks of the down
     # projection that start inside a group (f = 8192 in 4 chunks of 2048, groups of 4096)
     _w("g_T10_gs64", 10, 512, 1024, g1=8, g2=16),
     _w("g_T40", 40, 512, 2048, g1=2, g2=4),
     _w("g_T40_midchunk", 40, 256, 8192, g1=4, g2=2),
     _w("g_T64_shared", 64, 512, 1024, g1=2, g2=4, es=1),
+    _w("g_T128", 128, 512, 1024, g1=4, g2=8),          # the largest int8 streaming batch: several passes
     # LDS-tiled kernels: 128-row tiles, several tiles and ragged tails, E = 4, group counts 3 and 6
     _w("g_T300", 300, 512, 1024, g1=4, g2=8),
     _w("g_T700_E4", 700, 768, 1536, E=4, g1=3, g2=6),

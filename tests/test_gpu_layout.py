@@ -67,9 +67,11 @@ def _w(name, T, d, f, E=8, dtype=BF16, g1=1, g2=1, es=None):
 CASES = [
     _w("oi_bf16_T10", 10, 512, 1024),                      # streaming, one 16-row tile per pass
     _w("oi_bf16_T40", 40, 256, 8192),                      # streaming, two tiles, 4 down chunks
+    _w("oi_bf16_T96", 96, 512, 1024),                      # streaming, several passes (largest bf16 batch)
     _w("oi_bf16_T300", 300, 512, 1024),                    # direct-to-LDS tiles, down K split in 2
     _w("oi_bf16_T700_E4", 700, 768, 1536, E=4),
     _w("oi_w8_T40", 40, 512, 2048, dtype=W8),              # int8 streaming
+    _w("oi_w8_T128", 128, 512, 1024, dtype=W8),            # int8 streaming, several passes
     _w("oi_w8_T300", 300, 512, 1024, dtype=W8),            # int8 register-staged tiles
     _w("oi_w8g_T40", 40, 512, 2048, dtype=W8, g1=4, g2=4),  # grouped scales, streaming
     _w("oi_w8g_T300_shared", 300, 512, 1024, dtype=W8, g1=2, g2=8, es=1),  # grouped + shared, tiles

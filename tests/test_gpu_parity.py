@@ -146,7 +146,7 @@ def test_up_step_matches_oracle_h(gm, T, d, f, dtype):
 # ------------------------------------------------------------------------------------------------ whole layer, small
 
 SMALL = [
-    # streaming kernels (T <= 64), one and two 16-row tiles per pass
+    # streaming kernels (T <= 96 for bf16, <= 128 for int8), one and two 16-row tiles per pass
     synth.Workload("bf16_T1", T=1, d=256, f=512, w_std=0.1),
     synth.Workload("bf16_T8", T=8, d=256, f=512, w_std=0.1),
     synth.Workload("bf16_T13_f768", T=13, d=512, f=768, w_std=0.07),
@@ -154,7 +154,9 @@ SMALL = [
     synth.Workload("bf16_T64_E16", T=64, d=256, f=512, E=16, w_std=0.1),
     synth.Workload("bf16_T8_split2", T=8, d=256, f=4096, w_std=0.1),
     synth.Workload("bf16_T5_split4", T=5, d=512, f=8192, w_std=0.05),
-    # LDS-tiled grouped GEMM (T > 64), ragged row tiles
+    # streaming kernels above 32 rows per expert: several passes over the weights (bf16 T = 65, 96)
+    synth.Workload("bf16_T96", T=96, d=256, f=512, w_std=0.1),
+    # LDS-tiled grouped GEMM (bf16 T > 96), ragged row tiles
     synth.Workload("bf16_T65", T=65, d=256, f=512, w_std=0.1),
     synth.Workload("bf16_T300", T=300, d=512, f=768, w_std=0.07),
     synth.Workload("bf16_T1000_E4", T=1000, d=256, f=512, E=4, w_std=0.1),
@@ -164,7 +166,8 @@ SMALL = [
     synth.Workload("w8_T8", T=8, d=256, f=512, dtype=W8),
     synth.Workload("w8_T64", T=64, d=512, f=1024, dtype=W8),
     synth.Workload("w8_T33_split2", T=33, d=256, f=4096, dtype=W8),
-    synth.Workload("w8_T200", T=200, d=256, f=768, dtype=W8),
+    synth.Workload("w8_T128", T=128, d=256, f=768, dtype=W8),     # int8 streaming, the largest batch
+    synth.Workload("w8_T200", T=200, d=256, f=768, dtype=W8),     # int8 LDS tiles
     # fp32
     synth.Workload("f32_T1", T=1, d=64, f=64, E=2, dtype=F32),
     synth.Workload("f32_T200", T=200, d=192, f=320, dtype=F32),
@@ -313,9 +316,9 @@ def test_grok_skew_bf16_sampled(gm, grok_bf16):
 
 @pytest.mark.parametrize("T", [72, 256, 600])
 def test_grok_mid_batch_bf16_sampled(gm, grok_bf16, T):
-    """Batches of a few hundred tokens at Grok-1 shape: experts with at most 128 slots run as 128-row tiles with
-    nontemporal weight copies (all of them at T = 72 and 256); at T = 600 one expert does, the others (149-160
-    slots) run as 192-row tiles."""
+    """Batches of a few hundred tokens at Grok-1 shape: T = 72 on the streaming kernels (11-23 slots per expert,
+    one pass of 32 rows); at T = 256 every expert has at most 128 slots and runs as 128-row tiles with
+    nontemporal weight copies; at T = 600 one expert does, the others (149-160 slots) run as 192-row tiles."""
     w = dataclasses.replace(synth.WORKLOADS["prefill_bf16"], T=T, name=f"mid_bf16_T{T}", sampled_rows=64)
     (out, ref), _ = _grok_case(gm, grok_bf16, w)
     c = ref["counts"].numpy()
@@ -353,9 +356,11 @@ def test_grok_int8(gm, grok_int8):
     _grok_int8_case(gm, grok_int8, 64, None)
 
 
-def test_grok_int8_mid_batch_sampled(gm, grok_int8):
-    """int8 weights at T = 128: every expert in the 128-row tiles, 64 seeded rows."""
-    _grok_int8_case(gm, grok_int8, 128, 64)
+@pytest.mark.parametrize("T", [128, 192])
+def test_grok_int8_mid_batch_sampled(gm, grok_int8, T):
+    """int8 weights at T = 128 (the largest int8 streaming batch, several passes) and T = 192 (every expert in
+    the 128-row tiles), 64 seeded rows."""
+    _grok_int8_case(gm, grok_int8, T, 64)
 
 
 def test_grok_int8_prefill_sampled(gm, grok_int8):
