@@ -301,7 +301,7 @@ def main():
         library_gemm(a.steps, a.warmup)
         return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is designed but not built "
+        print(json.dumps({"error": "this layer runs on one GPU; multi-GPU sharding is designed but not implemented "
                                    "(tensor-parallel over d_ff with a reduce-scatter of the fp32 output)",
                           "n_gpus": a.gpus}))
         sys.exit(2)
