@@ -6,8 +6,9 @@
 // A workgroup of 4 waves computes a 256-row x 256-column output tile of the expert-sorted assignment slots:
 //   * up-projection (NMAT = 2): 128 columns of W1 and the same 128 columns of Wv; h = bf16(GELU(a) * b);
 //   * down-projection (NMAT = 1): 256 columns of W2; fp32 output.
-// Each wave holds a 128 x 128 accumulator tile as 4 x 4 MFMA 32x32 blocks (256 fp32 per lane).  A kernel may use
-// half-height tiles (128 rows, 64 x 128 per wave) where it needs accumulator registers for other work.
+// Each wave holds a 128 x 128 accumulator tile as 4 x 4 MFMA 32x32 blocks (256 fp32 per lane).  Shorter tiles (192
+// or 128 rows: 96 or 64 x 128 per wave) serve small experts and short last tiles (Rows below), and the
+// register-staged int8 kernel with grouped scales, which needs accumulator registers for its rescaling.
 #pragma once
 
 #include "common.h"
