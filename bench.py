@@ -62,11 +62,13 @@ def parse():
                     help="expert weights stored [E, in, out] (checkpoint) or [E, out, in] (converted); same values")
     ap.add_argument("--library-gemm", action="store_true",
                     help="only time torch.matmul (hipBLASLt) bf16 on the prefill's per-expert GEMM shapes, for context")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload at this many tokens instead of its own T (e.g. int8_w8 at 8192)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     a = ap.parse_args()
-    if a.steps < 1 or a.warmup < 0 or a.prefill_steps < 0:
-        ap.error("--steps must be >= 1; --warmup and --prefill-steps >= 0")
+    if a.steps < 1 or a.warmup < 0 or a.prefill_steps < 0 or a.tokens < 0:
+        ap.error("--steps must be >= 1; --warmup, --prefill-steps and --tokens >= 0")
     return a
 
 
@@ -314,6 +316,9 @@ def main():
     gm.lib()
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[a.workload]
+    if a.tokens:
+        import dataclasses
+        w = dataclasses.replace(w, T=a.tokens, name=f"{w.name}_T{a.tokens}")
     log(f"workload {w.name}: drawing weights")
     t0 = time.perf_counter()
     wts = synth.make_weights(w)
