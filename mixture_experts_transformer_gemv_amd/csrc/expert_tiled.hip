@@ -248,6 +248,9 @@ hipError_t launch_up_tiled(const uint16_t* x, const void* w1, const void* wv, co
   if (!int8 || (!grouped && !outin))  // bf16, and int8 with one scale group from [in, out] storage: direct copies
     return launch_up_tiled_dma(x, w1, wv, s1, sv, sl.estride, int8, outin, counts, offsets, perm, d, f, E, slots,
                                h, s);
+  if (grouped && !outin && tiled_dma_grouped_fits(d, sl.gsize))  // up to 8 scale groups: direct copies too
+    return launch_up_tiled_dma_grouped(x, w1, wv, s1, sv, sl.estride, sl.gsize, counts, offsets, perm, d, f, E,
+                                       slots, h, s);
   const dim3 grid(tile::grid_tiles(slots, E, f / (BNT / 2), grouped ? 128 : BM)), block(256);
 #define GM_UPT(GR, OI) tiled_reg_kernel<2, GR, OI><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, offsets, \
                                                                              perm, d, f, E, h)
@@ -263,6 +266,9 @@ hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* 
   const bool grouped = sl.gsize < f;
   if (!int8 || (!grouped && !outin))
     return launch_down_tiled_dma(h, w2, s2, sl.estride, int8, outin, counts, offsets, d, f, E, slots, S, y, s);
+  if (grouped && !outin && tiled_dma_grouped_fits(f, sl.gsize))
+    return launch_down_tiled_dma_grouped(h, w2, s2, sl.estride, sl.gsize, counts, offsets, d, f, E, slots, S, y,
+                                         s);
   const dim3 grid(tile::grid_tiles(slots, E, d / BNT, grouped ? 128 : BM)), block(256);
 #define GM_DNT(GR, OI) tiled_reg_kernel<1, GR, OI><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, sl, counts, \
                                                                              offsets, nullptr, f, d, E, y)

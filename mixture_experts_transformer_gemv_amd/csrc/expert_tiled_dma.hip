@@ -57,10 +57,16 @@ template <int NMAT, bool OUTIN, bool INT8, int TBM>
 constexpr int tile_lds_bytes() {
   return OUTIN ? NSTAGE * TBM * BK * 2 + NPAIR * B_PAIR : NSTAGE * (TBM * BK * 2 + 2 * b_sub<INT8>());
 }
+// Grouped int8 scales: at most this many groups along K, their scales for the tile's 256 output columns kept as
+// fp32 in LDS beside the ring (GROUPED tiles only).
+constexpr int kDmaMaxGroups = 8;
+constexpr int kScaleTableBytes = kDmaMaxGroups * BNT * 4;
 
 // One output tile: expert e, assignment rows row0 .. row0 + rows - 1 (rows <= TBM), column tile ntile; lds holds
-// tile_lds_bytes() bytes.
-template <int NMAT, bool OUTIN, bool INT8, int TBM>
+// tile_lds_bytes() bytes (plus kScaleTableBytes if GROUPED).  B_NT: nontemporal weight copies (for launches that
+// read each weight byte once).  GROUPED (int8, [in, out], 128-row tiles): int8 scales in groups of gsize rows of
+// K (at most kDmaMaxGroups groups); otherwise one scale per column, or none for bf16.
+template <int NMAT, bool OUTIN, bool INT8, int TBM, bool B_NT = (TBM == 128), bool GROUPED = false>
 __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, const void* __restrict__ B0,
                                                         const void* __restrict__ B1,
                                                         const uint16_t* __restrict__ s0,
@@ -69,9 +75,10 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ perm, uint32_t a_bytes, int K,
                                                         int N, void* __restrict__ out, int64_t split_stride, int e,
-                                                        int row0, int rows, int ntile, lds_u8* lds) {
+                                                        int row0, int rows, int ntile, lds_u8* lds, int gsize = 0) {
   static_assert(!(OUTIN && INT8), "int8 weights are tiled from [E, K, N] storage");
   static_assert(TBM == 256 || TBM == 192 || TBM == 128, "tiles of 256, 192 or 128 rows");
+  static_assert(!GROUPED || (INT8 && !OUTIN && TBM == 128), "grouped scales: int8 [in, out] weights, 128-row tiles");
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   constexpr int MI = TBM / 64;     // row blocks of 32 per wave (waves 2 x 2: TBM / 2 rows each)
   constexpr int AP = TBM / 64;     // 1 KB activation copies per wave and K step
@@ -83,9 +90,8 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   constexpr int BCOPIES = INT8 ? 2 : 4;        // 1 KB weight copies per wave and K step ([in, out])
   constexpr int CPS = AP + BCOPIES;            // copies per wave and K step ([out, in]: AP + 4)
   constexpr int A_STRIDE = OUTIN ? A_STG : STAGE;  // between ring slots of A
-  // 128-row tiles run one per expert and column tile in their launch, so each weight byte is read once there:
-  // nontemporal copies (the 256-row tiles share weight columns through the caches and keep the default policy).
-  constexpr bool B_NT = TBM == 128;
+  // Launches whose tiles read each weight byte once (one 128-row tile per expert and column tile) copy the weights
+  // with the nontemporal hint; tiles that share weight columns through the caches keep the default policy.
   auto copy_b = [](const void* base, uint32_t voff, uint32_t dst) {
     if constexpr (B_NT) g2lds16_nt(base, voff, dst);
     else g2lds16(base, voff, dst);
@@ -246,12 +252,22 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
       fa[buf][i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[i][ks]);
     }
   };
-  auto join_b = [&](int buf) {
+  // keep (GROUPED): bit j clear masks the int8 values of fragment j's column (a zero scale in the step's group)
+  auto join_b = [&](int buf, uint32_t keep) {
     if (OUTIN) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[buf][j] = INT8 ? i8x8_to_bf16(b8[buf][j])  // exact: |q| <= 127 has 8 significant bits
-                        : u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (INT8) {
+        u32x2_t v = b8[buf][j];
+        if constexpr (GROUPED) {
+          const uint32_t m = ((keep >> j) & 1u) ? ~0u : 0u;
+          v &= u32x2_t{m, m};
+        }
+        fb[buf][j] = i8x8_to_bf16(v);  // exact: |q| <= 127 has 8 significant bits
+      } else {
+        fb[buf][j] = u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
+      }
+    }
   };
 
   f32x16_t acc[MI][4];
@@ -261,6 +277,34 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // GROUPED: the accumulators are kept in units of the current group's scale.  The scales of the tile's columns
+  // for every group are staged in an LDS table before the copies start (tile column c: NMAT = 2: W1 columns
+  // 0..127, Wv 128..255; NMAT = 1: W2 columns); the lane's accumulator column of sub-tile j is tcol[j].  Entering
+  // group g multiplies column j by cur[j] / s[g] (zero scales replaced by one, their int8 values masked to zero);
+  // the epilogue multiplies by the last group's scale, so the result is sum_g s[g] * P[g].
+  const int G = GROUPED ? K / gsize : 1;
+  __attribute__((address_space(3))) float* tbl =
+      (__attribute__((address_space(3))) float*)(lds + tile_lds_bytes<NMAT, OUTIN, INT8, TBM>());
+  int tcol[4];
+  float cur[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  uint32_t keep_cur = 0xfu, keep_next = 0xfu;
+  int gnext = 0;  // first K row of the next group
+  auto group_scale = [&](int g, int j) { return tbl[g * BNT + tcol[j]]; };
+  auto group_keep = [&](int g) {
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k |= (group_scale(g, j) != 0.0f ? 1u : 0u) << j;
+    return k;
+  };
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      tcol[j] = NMAT == 2 ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + (lane & 31)) : (wn * 128 + j * 32 + (lane & 31));
+    // thread tid writes tile column tid for every group (ordinary loads, finished before the copies start)
+    const uint16_t* sp = (NMAT == 2 && tid >= 128 ? s1 : s0) + e * s_estride + nbase + (NMAT == 2 ? (tid & 127) : tid);
+    for (int g = 0; g < G; ++g) tbl[g * BNT + tid] = bf16f(sp[size_t(g) * N]);
+  }
 
   // ---- main loop.  Step kt: half-step 0 multiplies fragments buffer 0 while the 12 fragment pieces of
   // half-step 1 are read; then the wave waits for its copies of step kt+1 and joins the barrier; half-step 1
@@ -304,13 +348,41 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     wait_vm<CPS * (NSTAGE - 3) + AP>();  // step 0 landed (step 1 and half of step 2 may be in flight)
   }
   lds_barrier();
+  if constexpr (GROUPED) {  // the group of step 0 (kbase is a multiple of gsize or inside a group)
+    const int g0 = kbase / gsize;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = group_scale(g0, j);
+      cur[j] = v != 0.0f ? v : 1.0f;
+    }
+    keep_cur = group_keep(g0);
+    keep_next = g0 + 1 < G ? group_keep(g0 + 1) : keep_cur;
+    gnext = (g0 + 1) * gsize;
+  }
 #pragma unroll
   for (int p = 0; p < NPIECE; ++p) read_piece(0, lds, bpairs, 0, 0, p);
-  join_b(0);
+  join_b(0, keep_cur);
   // One K step; P is the step's parity (kt & 1), a compile-time constant so that the [out, in] forms index their
   // pair-slot offset arrays with constants (a runtime index turns each into a chain of selects).
   auto kstep = [&](int kt, auto parity) {
     constexpr int P = decltype(parity)::value;
+    if constexpr (GROUPED) {
+      if (kbase + kt * BK == gnext) {  // step kt opens group g: change the accumulators' unit
+        const int g = gnext / gsize;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = group_scale(g, j);
+          const float nv = v != 0.0f ? v : 1.0f;
+          const float r = cur[j] / nv;
+          cur[j] = nv;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) acc[i][j] *= r;
+        }
+        keep_cur = keep_next;
+        keep_next = g + 1 < G ? group_keep(g + 1) : keep_cur;
+        gnext += gsize;
+      }
+    }
     const lds_u8* st = lds + (kt % NSTAGE) * A_STRIDE;
     const lds_u8* sb = bpairs + ((kt >> 1) % NPAIR) * B_PAIR;
     // second half of the copies of step kt+2 (its first half was issued after the barrier of step kt-1); OUTIN:
@@ -327,7 +399,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    join_b(1);
+    join_b(1, keep_cur);
     wait_vm<CPS * (NSTAGE - 3)>();  // step kt+1 landed (steps kt+2 .. may be in flight)
     lds_barrier();                       // ... for every wave; every wave finished reading step kt-1
     const int cstage = (kt + NSTAGE - 1) % NSTAGE, ck = min(kt + NSTAGE - 1, KT - 1);
@@ -340,7 +412,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
       if (m < NPIECE) read_piece(0, nst, nsb, 1 - P, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
-    join_b(0);
+    join_b(0, (GROUPED && kbase + (kt + 1) * BK == gnext) ? keep_next : keep_cur);  // fragments of step kt+1
   };
   if constexpr (OUTIN) {
     for (int kt = 0; kt < KT; kt += 2) {  // KT is even: K steps come in pairs
@@ -361,8 +433,8 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     for (int jn = 0; jn < 2; ++jn) {
       const int c = wn * 64 + jn * 32 + lr;
       // int8: the column's scales multiply the fp32 accumulators before the GELU product
-      const float sa = INT8 ? bf16f(s0[e * s_estride + nbase + c]) : 1.0f;
-      const float sb = INT8 ? bf16f(s1[e * s_estride + nbase + c]) : 1.0f;
+      const float sa = GROUPED ? cur[jn] : (INT8 ? bf16f(s0[e * s_estride + nbase + c]) : 1.0f);
+      const float sb = GROUPED ? cur[2 + jn] : (INT8 ? bf16f(s1[e * s_estride + nbase + c]) : 1.0f);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -387,7 +459,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     if constexpr (INT8) {  // the column's scale multiplies the fp32 accumulators
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sc = bf16f(s0[e * s_estride + nbase + wn * 128 + j * 32 + (lane & 31)]);
+        const float sc = GROUPED ? cur[j] : bf16f(s0[e * s_estride + nbase + wn * 128 + j * 32 + (lane & 31)]);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -445,6 +517,62 @@ __global__ __launch_bounds__(256) void tiled_dma_small_kernel(const uint16_t* __
   else
     tiled_dma_tile<2, OUTIN, INT8, 128>(A, B0, B1, s0, s1, s_estride, counts, offsets, perm, a_bytes, K, N, out, 0,
                                         e, row0, rows, ntile, (lds_u8*)(smem));
+}
+
+// int8 weights ([in, out]) with grouped scales (at most kDmaMaxGroups groups along K): 128-row tiles of every
+// expert in one launch, in the XCD-aware order, so an expert's row tiles share its weight columns in L2 (default
+// copies).  128 rows leave the registers the group rescaling needs (256-row tiles spill there).
+template <int NMAT>
+__global__ __launch_bounds__(256) void tiled_dma_grouped_kernel(const uint16_t* __restrict__ A,
+                                                                const void* __restrict__ B0,
+                                                                const void* __restrict__ B1,
+                                                                const uint16_t* __restrict__ s0,
+                                                                const uint16_t* __restrict__ s1, int64_t s_estride,
+                                                                const int32_t* __restrict__ counts,
+                                                                const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ perm, uint32_t a_bytes,
+                                                                int K, int N, int E, void* __restrict__ out,
+                                                                int64_t split_stride, int gsize) {
+  int e, row0, rows, ntile;
+  if (!tile::map_tile<tile::Group<NMAT>::N, 128, tile::Rows::All>(counts, offsets, E, N / (BNT / NMAT), blockIdx.x,
+                                                                  &e, &row0, &rows, &ntile))
+    return;  // whole workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<NMAT, false, true, 128>() + kScaleTableBytes];
+  tiled_dma_tile<NMAT, false, true, 128, false, true>(A, B0, B1, s0, s1, s_estride, counts, offsets, perm, a_bytes, K,
+                                                      N, out, split_stride, e, row0, rows, ntile, (lds_u8*)(smem),
+                                                      gsize);
+}
+
+bool tiled_dma_grouped_fits(int K, int gsize) {
+  return gsize > 0 && gsize % BK == 0 && K % gsize == 0 && K / gsize <= kDmaMaxGroups;
+}
+
+hipError_t launch_up_tiled_dma_grouped(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
+                                       const uint16_t* sv, int64_t s_estride, int gsize, const int32_t* counts,
+                                       const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
+                                       uint16_t* h, hipStream_t s) {
+  const int NT = f / (BNT / 2);
+  const dim3 grid(tile::grid_tiles(slots, E, NT, 128)), block(256);
+  const size_t xbytes = size_t(slots / 2) * d;  // x: [slots / 2 tokens, d] bf16
+  if (2 * xbytes >= (size_t(1) << 31) || size_t(2) * slots * f >= (size_t(1) << 31) ||
+      !tiled_dma_grouped_fits(d, gsize))
+    return hipErrorInvalidValue;
+  tiled_dma_grouped_kernel<2><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, offsets, perm,
+                                                     uint32_t(2 * xbytes), d, f, E, h, 0, gsize);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_tiled_dma_grouped(const uint16_t* h, const void* w2, const uint16_t* s2, int64_t s_estride,
+                                         int gsize, const int32_t* counts, const int32_t* offsets, int d, int f,
+                                         int E, int slots, int S, float* y, hipStream_t s) {
+  const int NT = d / BNT;
+  const dim3 grid(tile::grid_tiles(slots, E, NT, 128), S), block(256);
+  const size_t hbytes = size_t(slots) * f * 2;  // h: [slots, f]
+  if (hbytes >= (size_t(1) << 31) || !tiled_dma_grouped_fits(f, gsize)) return hipErrorInvalidValue;
+  tiled_dma_grouped_kernel<1><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, s_estride, counts, offsets,
+                                                     nullptr, uint32_t(hbytes), f, d, E, y, int64_t(slots) * d,
+                                                     gsize);
+  return hipGetLastError();
 }
 
 // Launches: the 256-row tiles (tile::Rows::Main); then, for the up-projection, the 192-row tiles of experts with up

@@ -68,6 +68,15 @@ hipError_t launch_down_tiled(const uint16_t* h, const void* w2, const uint16_t* 
                              const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                              bool int8, float* y, hipStream_t s);
 
+// Grouped int8 scales on the direct-to-LDS tiles ([in, out] weights, K / gsize <= 8 groups along K; 128-row tiles).
+bool tiled_dma_grouped_fits(int K, int gsize);
+hipError_t launch_up_tiled_dma_grouped(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
+                                       const uint16_t* sv, int64_t s_estride, int gsize, const int32_t* counts,
+                                       const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots,
+                                       uint16_t* h, hipStream_t s);
+hipError_t launch_down_tiled_dma_grouped(const uint16_t* h, const void* w2, const uint16_t* s2, int64_t s_estride,
+                                         int gsize, const int32_t* counts, const int32_t* offsets, int d, int f,
+                                         int E, int slots, int S, float* y, hipStream_t s);
 // Direct global -> LDS copies, LDS transpose reads for [in, out] weights (bf16, or int8 with per-column scales
 // [Es, 1, N] at expert stride s_estride).
 hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,

@@ -4,6 +4,8 @@ axis) against the oracle, through the C ABI.
 Bar as for the other layers: routing and counts bit-exact, out within 1e-2 rms(oracle).  Where two layouts
 describe the same weights the kernels must agree bit for bit (equal scales in every group change the
 accumulators' unit by exactly 1)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -104,3 +106,10 @@ def test_two_dimensional_per_expert_form_is_the_default(gm):
 def test_grok_int8_group_scales(gm):
     """Grok-1 shape, T = 64, int8 weights with (8, 8, N) scales, every row against the oracle."""
     check_layer(gm, synth.WORKLOADS["int8_w8_g8"])
+
+
+def test_grok_int8_group_scales_prefill_sampled(gm):
+    """Grok-1 shape, T = 2048 (the direct-to-LDS 128-row tiles with grouped scales), int8 weights with (8, 8, N)
+    scales, 64 seeded rows against the oracle."""
+    w = dataclasses.replace(synth.WORKLOADS["int8_w8_g8"], T=2048, name="int8_w8_g8_T2048", sampled_rows=64)
+    check_layer(gm, w, rows=synth.sampled_rows(w.T, 64))
