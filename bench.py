@@ -380,6 +380,8 @@ def main():
         grouped = w.groups_up > 1 or w.groups_down > 1
         if w.dtype == 1 or (not grouped and oi == "false"):  # 256-row tiles, then 128-row last tiles
             kname = f"tiled_dma_kernel<2, {oi}, {'true' if w.dtype == 2 else 'false'}, 256> + tiled_dma_small_kernel"
+        elif grouped and oi == "false" and w.groups_up <= 8:  # grouped scales on the 128-row direct-to-LDS tiles
+            kname = "tiled_dma_grouped_kernel<2>"
         else:
             kname = f"tiled_reg_kernel<2, {'true' if grouped else 'false'}, {oi}>"
         res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
