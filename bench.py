@@ -64,11 +64,14 @@ def parse():
                     help="only time torch.matmul (hipBLASLt) bf16 on the prefill's per-expert GEMM shapes, for context")
     ap.add_argument("--tokens", type=int, default=0,
                     help="run the workload at this many tokens instead of its own T (e.g. int8_w8 at 8192)")
+    ap.add_argument("--d-ff", type=int, default=0,
+                    help="run the workload at this d_ff instead of its own (e.g. 4096: one GPU's share of a layer "
+                         "split over 8 GPUs along d_ff)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     a = ap.parse_args()
-    if a.steps < 1 or a.warmup < 0 or a.prefill_steps < 0 or a.tokens < 0:
-        ap.error("--steps must be >= 1; --warmup, --prefill-steps and --tokens >= 0")
+    if a.steps < 1 or a.warmup < 0 or a.prefill_steps < 0 or a.tokens < 0 or a.d_ff < 0:
+        ap.error("--steps must be >= 1; --warmup, --prefill-steps, --tokens and --d-ff >= 0")
     return a
 
 
@@ -316,9 +319,12 @@ def main():
     gm.lib()
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[a.workload]
-    if a.tokens:
+    if a.tokens or a.d_ff:
         import dataclasses
-        w = dataclasses.replace(w, T=a.tokens, name=f"{w.name}_T{a.tokens}")
+        if a.tokens:
+            w = dataclasses.replace(w, T=a.tokens, name=f"{w.name}_T{a.tokens}")
+        if a.d_ff:
+            w = dataclasses.replace(w, f=a.d_ff, name=f"{w.name}_f{a.d_ff}")
     log(f"workload {w.name}: drawing weights")
     t0 = time.perf_counter()
     wts = synth.make_weights(w)
