@@ -104,7 +104,10 @@ __device__ __forceinline__ void block_operands(const typename WRow<INT8>::T r[8]
   }
 }
 
-template <bool INT8, int MT, bool GROUPED, bool OUTIN>
+// KS = 4 (small f: fewer workgroups than CUs): the 4 waves of a workgroup take the same 128 columns and one
+// quarter of the d axis each; the partial sums meet in LDS and are added in ascending quarter order before the
+// GELU product (the [out, in] kernel adds the same quarters in the same order).
+template <bool INT8, int MT, bool GROUPED, bool OUTIN, int KS = 1>
 __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restrict__ x, const void* __restrict__ w1,
                                                         const void* __restrict__ wv, const uint16_t* __restrict__ s1,
                                                         const uint16_t* __restrict__ sv, ScaleLayout sl,
@@ -113,6 +116,7 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ perm, int d, int f,
                                                         uint16_t* __restrict__ h) {
   static_assert(INT8 || !GROUPED, "grouped scales belong to int8 weights");
+  static_assert(KS == 1 || (KS == 4 && !INT8), "the d axis is split only for bf16 weights");
   typedef WRow<INT8> W;
   const int e = blockIdx.y;
   const int n_e = counts[e];
@@ -120,8 +124,10 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
   const int off = offsets[e];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const int n0 = (blockIdx.x * 4 + wave) * 128;
-  if (n0 >= f) return;  // no workgroup barrier in this kernel
+  const int n0 = KS == 1 ? (blockIdx.x * 4 + wave) * 128 : blockIdx.x * 128;
+  if (n0 >= f) return;  // KS = 1: no workgroup barrier in this kernel; KS = 4: the whole workgroup
+  const int klo = KS == 1 ? 0 : wave * (d / KS), khi = KS == 1 ? d : klo + d / KS;  // this wave's part of d
+  __shared__ f32x4_t red[KS == 1 ? 1 : 3][2][MT][8][64];  // KS = 4: partial sums of waves 1..3
   const int col = n0 + 8 * c16;
   const size_t ebase = size_t(e) * d * f;
   // [in, out]: row 8g of each 32-deep step, column col; [out, in]: row col, k 8g of each step
@@ -192,15 +198,15 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
 
     // d is a multiple of 64: two 32-deep steps per iteration, the next step's loads in flight during compute.
     UpStep<INT8, MT> sa, sb;
-    auto steps = [&](int klo, int khi) {
-      for (int k0 = klo; k0 < khi; k0 += 64) {
+    auto steps = [&](int k_lo, int k_hi) {
+      for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
         load(sb, k0 + 32);
         compute(sa);
-        if (k0 + 64 < d) load(sa, k0 + 64);
+        if (k0 + 64 < khi) load(sa, k0 + 64);
         compute(sb);
       }
     };
-    load(sa, 0);
+    load(sa, klo);
     if constexpr (GROUPED) {
       // group boundaries are multiples of 64 rows: each group is a whole number of iterations
       const int ng = d / sl.gsize;
@@ -215,7 +221,32 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
         steps(gi * sl.gsize, (gi + 1) * sl.gsize);
       }
     } else {
-      steps(0, d);
+      steps(klo, khi);
+    }
+    if constexpr (KS > 1) {  // quarters 1..3 to LDS; wave 0 adds them in order and writes h
+      if (wave > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            red[wave - 1][0][mt][c][lane] = acc1[mt][c];
+            red[wave - 1][1][mt][c][lane] = acc2[mt][c];
+          }
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < KS - 1; ++q)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              acc1[mt][c] += red[q][0][mt][c][lane];
+              acc2[mt][c] += red[q][1][mt][c][lane];
+            }
+      }
+      __syncthreads();  // the next pass may overwrite red
+      if (wave != 0) continue;
     }
 
     float sc1[8], scv[8];
@@ -384,12 +415,30 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
   }
 }
 
+// The up-projection's split of the d axis over the 4 waves of a workgroup (KS = 4) when its grid of one workgroup
+// per 512 columns and expert would leave CUs idle (a layer's share of d_ff on one of several GPUs; measured at
+// f = 4096: 64 workgroups, 3.3 TB/s).  bf16 layers only: an int8 layer with grouped scales sums its groups in
+// order, and one whose groups all have the same scale must give the bits of the per-channel form, so neither int8
+// form splits.  d / 4 a multiple of 128 (the stages of the [out, in] kernel, which splits the same way).
+int up_stream_ksplit(int d, int f, int E, bool int8) {
+  return (!int8 && d % 512 == 0 && ((f + 511) / 512) * E < 256) ? 4 : 1;
+}
+
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                             const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
                             const int32_t* offsets, const int32_t* perm, int d, int f, int E, bool int8, int mt,
                             uint16_t* h, hipStream_t s) {
   const dim3 grid((f + 511) / 512, E), block(256);
   const bool grouped = int8 && sl.gsize < d;
+  if (up_stream_ksplit(d, f, E, int8) == 4) {
+    const dim3 grid4((f + 127) / 128, E);
+#define GM_UP4(MT, OI) up_stream_kernel<false, MT, false, OI, 4><<<grid4, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, \
+                                                                                      offsets, perm, d, f, h)
+    if (outin) { if (mt == 1) GM_UP4(1, true); else GM_UP4(2, true); }
+    else { if (mt == 1) GM_UP4(1, false); else GM_UP4(2, false); }
+#undef GM_UP4
+    return hipGetLastError();
+  }
 #define GM_UP(I8, MT, GR, OI) up_stream_kernel<I8, MT, GR, OI><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, \
                                                                                   offsets, perm, d, f, h)
 #define GM_UP_MT(I8, GR, OI) do { if (mt == 1) GM_UP(I8, 1, GR, OI); else GM_UP(I8, 2, GR, OI); } while (0)

@@ -79,7 +79,9 @@ __device__ __forceinline__ uint32_t lane_scale_bits(const u32x4_t& lo, const u32
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16.  W0/W1: weights [E, N, K]
 // (bf16 or int8).  Scales [Es, G, N] (sl).  out: h bf16 [slots, N] (NMAT = 2) or y f32 [S, slots, N] (NMAT = 1,
 // K split in chunks of Kc, spw consecutive chunks per workgroup row blockIdx.y).
-template <int NMAT, bool INT8, bool GROUPED, int MT>
+// KS = 4 (bf16 up-projection): the sums over the four quarters of K are kept apart and added in ascending quarter
+// order at the end, as the [in, out] kernel with its d axis split over 4 waves adds them.
+template <int NMAT, bool INT8, bool GROUPED, int MT, int KS = 1>
 __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restrict__ A, const void* __restrict__ W0,
                                                         const void* __restrict__ W1, const uint16_t* __restrict__ sc0,
                                                         const uint16_t* __restrict__ sc1, ScaleLayout sl,
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
     };
 
     f32x4_t acc[NMAT][MT];
+    f32x4_t part[KS == 1 ? 1 : KS - 1][NMAT][MT];  // KS = 4: sums of quarters 0 .. 2
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -212,6 +215,20 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
       lds_barrier();                       // ... every wave's; every wave finished reading stage s - 1
       copy_stage((s + C::NSTG - 1) % C::NSTG, min(s + C::NSTG - 1, NS - 1));
       const int k0 = kbeg + s * OI_KS;
+      if constexpr (KS > 1) {
+        if (s > 0 && s % (NS / KS) == 0) {  // stage s opens quarter q: keep the sum of quarter q - 1 apart
+          const int q = s / (NS / KS);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+              for (int qq = 0; qq < KS - 1; ++qq)
+                if (qq == q - 1) part[qq][m][mt] = acc[m][mt];
+              acc[m][mt] = f32x4_t{0, 0, 0, 0};
+            }
+        }
+      }
       if (GROUPED && k0 == gnext) {  // stage s opens group gi
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
@@ -265,6 +282,13 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
     }
     wait_vm<0>();   // the copies past the end
     lds_barrier();  // every wave done with the ring before the next pass refills it
+    if constexpr (KS > 1) {  // ((q0 + q1) + q2) + q3
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[m][mt] = ((part[0][m][mt] + part[1][m][mt]) + part[2][m][mt]) + acc[m][mt];
+    }
     store(NMAT == 1 ? blockIdx.y * spw + spw - 1 : 0);
   }
 }
@@ -296,6 +320,14 @@ hipError_t launch_up_stream_oi(const uint16_t* x, const void* w1, const void* wv
                                hipStream_t s) {
   const dim3 grid(f / OI_COLS, 1, E);  // one chunk: the whole d axis
   const bool grouped = int8 && sl.gsize < d;
+  if (up_stream_ksplit(d, f, E, int8) == 4) {  // the [in, out] kernel splits d: sum the same quarters
+    const dim3 block(256);
+#define GM_OI4(MT) oi_stream_kernel<2, false, false, MT, 4><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, \
+                                                                                  offsets, perm, d, f, d, 1, h, 0)
+    if (mt == 1) GM_OI4(1); else GM_OI4(2);
+#undef GM_OI4
+    return hipGetLastError();
+  }
   if (grouped)
     launch_oi_mt<2, true, true>(mt, grid, s, x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, d, 1, h, 0);
   else if (int8)
