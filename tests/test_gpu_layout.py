@@ -68,6 +68,7 @@ CASES = [
     _w("oi_bf16_T10", 10, 512, 1024),                      # streaming, one 16-row tile per pass
     _w("oi_bf16_T40", 40, 256, 8192),                      # streaming, two tiles, 4 down chunks
     _w("oi_bf16_T96", 96, 512, 1024),                      # streaming, several passes (largest bf16 batch)
+    _w("oi_bf16_T8_share", 8, 6144, 4096),                 # a d_ff share: d split over the waves, both layouts
     _w("oi_bf16_T300", 300, 512, 1024),                    # direct-to-LDS tiles, down K split in 2
     _w("oi_bf16_T700_E4", 700, 768, 1536, E=4),
     _w("oi_w8_T40", 40, 512, 2048, dtype=W8),              # int8 streaming

@@ -154,6 +154,8 @@ SMALL = [
     synth.Workload("bf16_T64_E16", T=64, d=256, f=512, E=16, w_std=0.1),
     synth.Workload("bf16_T8_split2", T=8, d=256, f=4096, w_std=0.1),
     synth.Workload("bf16_T5_split4", T=5, d=512, f=8192, w_std=0.05),
+    # one GPU's d_ff share of a Grok-1 layer (d = 6144, f = 4096): the up-projection splits d over the 4 waves
+    synth.Workload("bf16_T8_d6144_f4096", T=8, d=6144, f=4096, w_std=0.02),
     # streaming kernels above 32 rows per expert: several passes over the weights (bf16 T = 65, 96)
     synth.Workload("bf16_T96", T=96, d=256, f=512, w_std=0.1),
     # LDS-tiled grouped GEMM (bf16 T > 96), ragged row tiles
