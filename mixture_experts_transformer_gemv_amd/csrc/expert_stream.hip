@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ perm, int d, int f,
                                                         uint16_t* __restrict__ h) {
   static_assert(INT8 || !GROUPED, "grouped scales belong to int8 weights");
-  static_assert(KS == 1 || (KS == 4 && !INT8), "the d axis is split only for bf16 weights");
+  static_assert(KS == 1 || KS == 4, "the d axis is whole or split in 4");
   typedef WRow<INT8> W;
   const int e = blockIdx.y;
   const int n_e = counts[e];
@@ -128,6 +128,7 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
   if (n0 >= f) return;  // KS = 1: no workgroup barrier in this kernel; KS = 4: the whole workgroup
   const int klo = KS == 1 ? 0 : wave * (d / KS), khi = KS == 1 ? d : klo + d / KS;  // this wave's part of d
   __shared__ f32x4_t red[KS == 1 ? 1 : 3][2][MT][8][64];  // KS = 4: partial sums of waves 1..3
+  __shared__ float redc[KS > 1 && GROUPED ? 3 : 1][2][8][64];  // ... and their units (grouped scales)
   const int col = n0 + 8 * c16;
   const size_t ebase = size_t(e) * d * f;
   // [in, out]: row 8g of each 32-deep step, column col; [out, in]: row col, k 8g of each step
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
       }
     };
     load(sa, klo);
-    if constexpr (GROUPED) {
+    if constexpr (GROUPED && KS == 1) {
       // group boundaries are multiples of 64 rows: each group is a whole number of iterations
       const int ng = d / sl.gsize;
       pend1 = load_raw8(s1e);
@@ -219,6 +220,18 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
           pendv = load_raw8(sve + size_t(gi + 1) * f);
         }
         steps(gi * sl.gsize, (gi + 1) * sl.gsize);
+      }
+    } else if constexpr (GROUPED) {  // the groups that meet this wave's quarter [klo, khi)
+      const int g0 = klo / sl.gsize, g1 = (khi - 1) / sl.gsize;
+      pend1 = load_raw8(s1e + size_t(g0) * f);
+      pendv = load_raw8(sve + size_t(g0) * f);
+      for (int gi = g0; gi <= g1; ++gi) {
+        enter_group(gi > g0);
+        if (gi < g1) {
+          pend1 = load_raw8(s1e + size_t(gi + 1) * f);
+          pendv = load_raw8(sve + size_t(gi + 1) * f);
+        }
+        steps(max(klo, gi * sl.gsize), min(khi, (gi + 1) * sl.gsize));
       }
     } else {
       steps(klo, khi);
@@ -232,18 +245,50 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
             red[wave - 1][0][mt][c][lane] = acc1[mt][c];
             red[wave - 1][1][mt][c][lane] = acc2[mt][c];
           }
+        if constexpr (GROUPED) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            redc[wave - 1][0][c][lane] = cur1[c];
+            redc[wave - 1][1][c][lane] = curv[c];
+          }
+        }
       }
       __syncthreads();
       if (wave == 0) {
+        if constexpr (GROUPED) {
+          // each quarter's sum is in units of its last group's scale: bring quarters 0..2 to the unit u of
+          // quarter 3, t = fma(q2, c2 / u, fma(q1, c1 / u, q0 * (c0 / u))) + q3, in that unit from here on
 #pragma unroll
-        for (int q = 0; q < KS - 1; ++q)
+          for (int c = 0; c < 8; ++c) {
+            const float u1 = redc[2][0][c][lane], uv = redc[2][1][c][lane];
+            const float r1[3] = {cur1[c] / u1, redc[0][0][c][lane] / u1, redc[1][0][c][lane] / u1};
+            const float rv[3] = {curv[c] / uv, redc[0][1][c][lane] / uv, redc[1][1][c][lane] / uv};
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              acc1[mt][c] += red[q][0][mt][c][lane];
-              acc2[mt][c] += red[q][1][mt][c][lane];
-            }
+              for (int v = 0; v < 4; ++v) {
+                float t1 = acc1[mt][c][v] * r1[0], tv = acc2[mt][c][v] * rv[0];
+                t1 = __builtin_fmaf(red[0][0][mt][c][lane][v], r1[1], t1);
+                tv = __builtin_fmaf(red[0][1][mt][c][lane][v], rv[1], tv);
+                t1 = __builtin_fmaf(red[1][0][mt][c][lane][v], r1[2], t1);
+                tv = __builtin_fmaf(red[1][1][mt][c][lane][v], rv[2], tv);
+                acc1[mt][c][v] = t1 + red[2][0][mt][c][lane][v];
+                acc2[mt][c][v] = tv + red[2][1][mt][c][lane][v];
+              }
+            cur1[c] = u1;
+            curv[c] = uv;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < KS - 1; ++q)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int c = 0; c < 8; ++c) {
+                acc1[mt][c] += red[q][0][mt][c][lane];
+                acc2[mt][c] += red[q][1][mt][c][lane];
+              }
+        }
       }
       __syncthreads();  // the next pass may overwrite red
       if (wave != 0) continue;
@@ -417,11 +462,12 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 
 // The up-projection's split of the d axis over the 4 waves of a workgroup (KS = 4) when its grid of one workgroup
 // per 512 columns and expert would leave CUs idle (a layer's share of d_ff on one of several GPUs; measured at
-// f = 4096: 64 workgroups, 3.3 TB/s).  bf16 layers only: an int8 layer with grouped scales sums its groups in
-// order, and one whose groups all have the same scale must give the bits of the per-channel form, so neither int8
-// form splits.  d / 4 a multiple of 128 (the stages of the [out, in] kernel, which splits the same way).
-int up_stream_ksplit(int d, int f, int E, bool int8) {
-  return (!int8 && d % 512 == 0 && ((f + 511) / 512) * E < 256) ? 4 : 1;
+// f = 4096: 64 workgroups, 3.3 TB/s).  d / 4 a multiple of 128 (the stages of the [out, in] kernel, which splits
+// the same way).  With grouped int8 scales the quarter sums are brought to one unit by exact-order fused
+// multiply-adds whose ratios are 1 when every group has the same scale, so such a layer keeps the bits of the
+// per-channel form.
+int up_stream_ksplit(int d, int f, int E) {
+  return (d % 512 == 0 && ((f + 511) / 512) * E < 256) ? 4 : 1;
 }
 
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
@@ -430,12 +476,17 @@ hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, c
                             uint16_t* h, hipStream_t s) {
   const dim3 grid((f + 511) / 512, E), block(256);
   const bool grouped = int8 && sl.gsize < d;
-  if (up_stream_ksplit(d, f, E, int8) == 4) {
+  if (up_stream_ksplit(d, f, E) == 4) {
     const dim3 grid4((f + 127) / 128, E);
-#define GM_UP4(MT, OI) up_stream_kernel<false, MT, false, OI, 4><<<grid4, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, \
-                                                                                      offsets, perm, d, f, h)
-    if (outin) { if (mt == 1) GM_UP4(1, true); else GM_UP4(2, true); }
-    else { if (mt == 1) GM_UP4(1, false); else GM_UP4(2, false); }
+#define GM_UP4(I8, MT, GR, OI) up_stream_kernel<I8, MT, GR, OI, 4><<<grid4, block, 0, s>>>(x, w1, wv, s1, sv, sl, \
+                                                                                        counts, offsets, perm, d, f, h)
+#define GM_UP4_MT(I8, GR, OI) do { if (mt == 1) GM_UP4(I8, 1, GR, OI); else GM_UP4(I8, 2, GR, OI); } while (0)
+#define GM_UP4_L(I8, GR) do { if (outin) GM_UP4_MT(I8, GR, true); else GM_UP4_MT(I8, GR, false); } while (0)
+    if (grouped) GM_UP4_L(true, true);
+    else if (int8) GM_UP4_L(true, false);
+    else GM_UP4_L(false, false);
+#undef GM_UP4_L
+#undef GM_UP4_MT
 #undef GM_UP4
     return hipGetLastError();
   }

@@ -79,8 +79,9 @@ __device__ __forceinline__ uint32_t lane_scale_bits(const u32x4_t& lo, const u32
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16.  W0/W1: weights [E, N, K]
 // (bf16 or int8).  Scales [Es, G, N] (sl).  out: h bf16 [slots, N] (NMAT = 2) or y f32 [S, slots, N] (NMAT = 1,
 // K split in chunks of Kc, spw consecutive chunks per workgroup row blockIdx.y).
-// KS = 4 (bf16 up-projection): the sums over the four quarters of K are kept apart and added in ascending quarter
-// order at the end, as the [in, out] kernel with its d axis split over 4 waves adds them.
+// KS = 4 (up-projection): the sums over the four quarters of K are kept apart and added in ascending quarter order
+// at the end, as the [in, out] kernel with its d axis split over 4 waves adds them (with grouped scales each
+// quarter's sum is first brought to the unit of the last quarter, by the same fused multiply-adds).
 template <int NMAT, bool INT8, bool GROUPED, int MT, int KS = 1>
 __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restrict__ A, const void* __restrict__ W0,
                                                         const void* __restrict__ W1, const uint16_t* __restrict__ sc0,
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
 
     f32x4_t acc[NMAT][MT];
     f32x4_t part[KS == 1 ? 1 : KS - 1][NMAT][MT];  // KS = 4: sums of quarters 0 .. 2
+    float cpart[KS > 1 && GROUPED ? KS - 1 : 1][NMAT];  // ... and their units (grouped scales)
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -227,6 +229,13 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
                 if (qq == q - 1) part[qq][m][mt] = acc[m][mt];
               acc[m][mt] = f32x4_t{0, 0, 0, 0};
             }
+          if constexpr (GROUPED) {
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+              for (int qq = 0; qq < KS - 1; ++qq)
+                if (qq == q - 1) cpart[qq][m] = cur[m];
+          }
         }
       }
       if (GROUPED && k0 == gnext) {  // stage s opens group gi
@@ -282,7 +291,22 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
     }
     wait_vm<0>();   // the copies past the end
     lds_barrier();  // every wave done with the ring before the next pass refills it
-    if constexpr (KS > 1) {  // ((q0 + q1) + q2) + q3
+    if constexpr (KS > 1 && GROUPED) {  // fma(q2, c2 / u, fma(q1, c1 / u, q0 * (c0 / u))) + q3, u = unit of q3
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const float u = cur[m];
+        const float r[3] = {cpart[0][m] / u, cpart[1][m] / u, cpart[2][m] / u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float t = part[0][m][mt][v] * r[0];
+            t = __builtin_fmaf(part[1][m][mt][v], r[1], t);
+            t = __builtin_fmaf(part[2][m][mt][v], r[2], t);
+            acc[m][mt][v] = t + acc[m][mt][v];
+          }
+      }
+    } else if constexpr (KS > 1) {  // ((q0 + q1) + q2) + q3
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -320,11 +344,15 @@ hipError_t launch_up_stream_oi(const uint16_t* x, const void* w1, const void* wv
                                hipStream_t s) {
   const dim3 grid(f / OI_COLS, 1, E);  // one chunk: the whole d axis
   const bool grouped = int8 && sl.gsize < d;
-  if (up_stream_ksplit(d, f, E, int8) == 4) {  // the [in, out] kernel splits d: sum the same quarters
+  if (up_stream_ksplit(d, f, E) == 4) {  // the [in, out] kernel splits d: sum the same quarters
     const dim3 block(256);
-#define GM_OI4(MT) oi_stream_kernel<2, false, false, MT, 4><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, \
-                                                                                  offsets, perm, d, f, d, 1, h, 0)
-    if (mt == 1) GM_OI4(1); else GM_OI4(2);
+#define GM_OI4(I8, GR, MT) oi_stream_kernel<2, I8, GR, MT, 4><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, sl, counts, \
+                                                                                    offsets, perm, d, f, d, 1, h, 0)
+#define GM_OI4_MT(I8, GR) do { if (mt == 1) GM_OI4(I8, GR, 1); else GM_OI4(I8, GR, 2); } while (0)
+    if (grouped) GM_OI4_MT(true, true);
+    else if (int8) GM_OI4_MT(true, false);
+    else GM_OI4_MT(false, false);
+#undef GM_OI4_MT
 #undef GM_OI4
     return hipGetLastError();
   }

@@ -40,7 +40,7 @@ hipError_t launch_combine(const float* y, int S, const float* p, const int32_t* 
 // outin: weights stored [E, out, in] instead of [E, in, out].
 // 4 if the streaming up-projection splits d over the waves of a workgroup (small f), else 1; the [in, out] and
 // [out, in] streaming kernels split alike.
-int up_stream_ksplit(int d, int f, int E, bool int8);
+int up_stream_ksplit(int d, int f, int E);
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                             const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
                             const int32_t* offsets, const int32_t* perm, int d, int f, int E, bool int8, int mt,

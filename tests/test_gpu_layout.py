@@ -75,6 +75,7 @@ CASES = [
     _w("oi_w8_T128", 128, 512, 1024, dtype=W8),            # int8 streaming, several passes
     _w("oi_w8_T300", 300, 512, 1024, dtype=W8),            # int8 register-staged tiles
     _w("oi_w8g_T40", 40, 512, 2048, dtype=W8, g1=4, g2=4),  # grouped scales, streaming
+    _w("oi_w8g_T40_straddle", 40, 1024, 1024, dtype=W8, g1=2, g2=2),  # quarters of d inside a scale group
     _w("oi_w8g_T300_shared", 300, 512, 1024, dtype=W8, g1=2, g2=8, es=1),  # grouped + shared, tiles
     _w("oi_f32_T64", 64, 128, 512, dtype=F32),
     _w("oi_f32_T200", 200, 192, 320, dtype=F32),
