@@ -79,10 +79,10 @@ int down_splits(int64_t T, int64_t f, int dtype) {
     return s;
   }
   if (T > stream_max_tokens(dtype)) return 1;
-  // chunks of at least 2048 rows of W2 (a multiple of 64), at most 8 chunks (measured against 4, 16 and 32)
-  int s = 1;
-  while (s < 8 && (f / (2 * s)) % 64 == 0 && f / (2 * s) >= 2048) s *= 2;
-  return s;
+  // near-equal chunks of at least 2048 rows of W2 with boundaries on multiples of 128 rows, at most 5 (measured
+  // against 2, 4, 6 and 8 chunks)
+  if (f % 128 != 0) return 1;
+  return int(std::min<int64_t>(5, std::max<int64_t>(1, f / 2048)));
 }
 
 Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
@@ -174,7 +174,7 @@ hipError_t do_down(const void* h, const void* w2, const void* s2, const ScaleSpe
     return gm::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w2), sp.outin, counts,
                                offsets, int(d), int(f), E, int(p.slots), p.splits, y, s);
   const bool i8 = dtype == GROK_MOE_W8;
-  if (p.stream && sp.outin && gm::oi_stream_fits(int(f / p.splits), i8, down_layout(sp, d, f), int(f)))
+  if (p.stream && sp.outin && gm::oi_stream_fits(int(f), i8, down_layout(sp, d, f), int(f)))
     return gm::launch_down_stream_oi(static_cast<const uint16_t*>(h), w2, static_cast<const uint16_t*>(s2),
                                      down_layout(sp, d, f), counts, offsets, int(d), int(f), E, int(p.slots),
                                      p.splits, i8, p.mt_oi, y, s);

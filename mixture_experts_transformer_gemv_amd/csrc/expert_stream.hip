@@ -27,6 +27,7 @@
 // products, and the epilogue multiplies by the last group's scale, so that the result is sum_g s[g] * P[g].
 // A zero scale is replaced by one and that group's int8 values of the column are masked to zero, which gives
 // the same sum.  This costs one rounding per group boundary, far below the bf16 rounding of h.
+#include "chunks.h"
 #include "common.h"
 #include "launch.h"
 
@@ -348,8 +349,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
   const int n0 = (blockIdx.x * 4 + wave) * 128;
   if (n0 >= d) return;
   const int col = n0 + 8 * c16;
-  const int kchunk = f / S;
-  const int kbeg = blockIdx.y * kchunk;
+  const int kbeg = down_chunk_begin(blockIdx.y, f, S), kend = down_chunk_begin(blockIdx.y + 1, f, S);
   // [in, out]: row 8g of each 32-deep step, column col; [out, in]: row col, k 8g of each step
   const size_t ebase = size_t(e) * f * d;
   const size_t lane_base = OUTIN ? ebase + size_t(col) * f + 8 * g : ebase + size_t(8 * g) * d + col;
@@ -408,7 +408,6 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
     };
 
     DownStep<INT8, MT> sa, sb;
-    const int kend = kbeg + kchunk;  // kchunk is a multiple of 64
     auto steps = [&](int klo, int khi) {
       for (int k0 = klo; k0 < khi; k0 += 64) {
         load(sb, k0 + 32);

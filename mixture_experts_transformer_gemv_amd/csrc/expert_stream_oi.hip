@@ -15,8 +15,8 @@
 // conflicts.
 // The weight copies carry the nontemporal hint: each weight byte is read once per launch.
 //
-// A workgroup of 4 waves owns 64 output columns (16 per wave) of W1 and Wv (up) or of W2 (down: spw consecutive
-// chunks of the f axis, a partial sum stored per chunk, so that one ring streams several chunks) for all token
+// A workgroup of 4 waves owns 64 output columns (16 per wave) of W1 and Wv (up) or of W2 (down: all spw chunks of
+// the f axis, a partial sum stored per chunk, so that one ring streams every chunk) for all token
 // rows of its expert (16 MT rows per pass), over a ring of NSTG stages with one workgroup barrier per stage.
 // Each (token, column) accumulates over k in 32-deep steps in ascending order, with the same lane-to-k
 // assignment as the [in, out] kernels, so the results are bit-identical to theirs.
@@ -24,6 +24,7 @@
 // Grouped int8 scales (group boundaries on stage boundaries): the accumulators are kept in units of the current
 // group's scale (rescaled by s[g-1]/s[g] on entering group g, zero scales replaced by one with their columns'
 // values masked); the scales of the wave's 16 columns are read with uniform (scalar) loads one group ahead.
+#include "chunks.h"
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
@@ -78,7 +79,8 @@ __device__ __forceinline__ uint32_t lane_scale_bits(const u32x4_t& lo, const u32
 
 // A: x [*, K] (gathered through perm, NMAT = 2) or h [slots, K] (NMAT = 1), bf16.  W0/W1: weights [E, N, K]
 // (bf16 or int8).  Scales [Es, G, N] (sl).  out: h bf16 [slots, N] (NMAT = 2) or y f32 [S, slots, N] (NMAT = 1,
-// K split in chunks of Kc, spw consecutive chunks per workgroup row blockIdx.y).
+// one workgroup row over all of K, stored as spw partial sums over the chunks of down_chunk_begin).  NMAT = 2: Kc = K,
+// spw = 1.
 // KS = 4 (up-projection): the sums over the four quarters of K are kept apart and added in ascending quarter order
 // at the end, as the [in, out] kernel with its d axis split over 4 waves adds them (with grouped scales each
 // quarter's sum is first brought to the unit of the last quarter, by the same fused multiply-adds).
@@ -98,9 +100,8 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
   if (n_e == 0) return;  // whole workgroup
   const int off = offsets[e];
   const int nbase = blockIdx.x * OI_COLS;
-  const int kbeg = blockIdx.y * spw * Kc;
-  const int SPS = Kc / OI_KS;  // stages per chunk
-  const int NS = spw * SPS;
+  const int kbeg = NMAT == 1 ? 0 : blockIdx.y * Kc;
+  const int NS = (NMAT == 1 ? K : Kc) / OI_KS;  // stages
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NSTG * C::STAGE];
   const lds_u8* lds = (const lds_u8*)(smem);
@@ -208,6 +209,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
         }
     };
 
+    int chunk = 0, cnext = down_chunk_begin(1, K, spw);  // NMAT = 1: the chunk being summed and its end
     // ---- prologue: stages 0 .. NSTG-2 (past the end: the last stage again, into slots never read)
 #pragma unroll
     for (int s = 0; s < C::NSTG - 1; ++s) copy_stage(s, min(s, NS - 1));
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
         }
         ++gi;
         gnext = gi * sl.gsize;
-        if (gnext < kbeg + spw * Kc) fetch_group(gi);
+        if (gnext < kbeg + NS * OI_KS) fetch_group(gi);
       }
       const lds_u8* st = lds + (s % C::NSTG) * C::STAGE;
 #pragma unroll
@@ -283,8 +285,9 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[m][mt] = mfma16x16x32(a[mt], b[m], acc[m][mt]);
       }
-      if (NMAT == 1 && s + 1 < NS && (s + 1) % SPS == 0) {  // end of a chunk that is not the last
-        store(blockIdx.y * spw + (s + 1) / SPS - 1);
+      if (NMAT == 1 && s + 1 < NS && (s + 1) * OI_KS == cnext) {  // end of a chunk that is not the last
+        store(chunk);
+        cnext = down_chunk_begin(++chunk + 1, K, spw);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[0][mt] = f32x4_t{0, 0, 0, 0};
       }
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
         for (int mt = 0; mt < MT; ++mt)
           acc[m][mt] = ((part[0][m][mt] + part[1][m][mt]) + part[2][m][mt]) + acc[m][mt];
     }
-    store(NMAT == 1 ? blockIdx.y * spw + spw - 1 : 0);
+    store(NMAT == 1 ? spw - 1 : 0);
   }
 }
 
@@ -369,10 +372,10 @@ hipError_t launch_down_stream_oi(const uint16_t* h, const void* w2, const uint16
                                  const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots,
                                  int S, bool int8, int mt, float* y, hipStream_t s) {
   const int spw = S;  // chunks per workgroup: all of them (partial sums still stored per chunk)
-  const dim3 grid(d / OI_COLS, S / spw, E);
+  const dim3 grid(d / OI_COLS, 1, E);
   const int64_t stride = int64_t(slots) * d;
   const bool grouped = int8 && sl.gsize < f;
-  const int Kc = f / S;
+  const int Kc = f;
   if (grouped)
     launch_oi_mt<1, true, true>(mt, grid, s, h, w2, nullptr, s2, nullptr, sl, counts, offsets, nullptr, f, d, Kc,
                                 spw, y, stride);

@@ -51,12 +51,14 @@ def test_workspace_size_and_splits(L):
     assert gm.workspace_size(8, 6100, 32768) == 0        # d not a multiple of 256
     ws_dec = gm.workspace_size(8, 6144, 32768)
     assert ws_dec >= 16 * 32768 * 2 + 16 * 6144 * 4 * gm.down_splits(8, 6144, 32768)
-    assert gm.down_splits(8, 6144, 32768) == 8
+    assert gm.down_splits(8, 6144, 32768) == 5
     assert gm.down_splits(8192, 6144, 32768) == 2   # LDS-tiled bf16 path splits K in two
     assert gm.down_splits(8192, 6144, 32768, 8, 2, gm.W8) == 1
     # the streaming kernels take bf16 batches up to 96 tokens and int8 batches up to 128
-    assert gm.down_splits(96, 6144, 32768) == 8 and gm.down_splits(97, 6144, 32768) == 2
-    assert gm.down_splits(128, 6144, 32768, 8, 2, gm.W8) == 8 and gm.down_splits(129, 6144, 32768, 8, 2, gm.W8) == 1
+    assert gm.down_splits(96, 6144, 32768) == 5 and gm.down_splits(97, 6144, 32768) == 2
+    assert gm.down_splits(128, 6144, 32768, 8, 2, gm.W8) == 5 and gm.down_splits(129, 6144, 32768, 8, 2, gm.W8) == 1
+    # streaming chunks: at least 2048 rows each, at most 5, boundaries on multiples of 128 rows
+    assert [gm.down_splits(8, 6144, f) for f in (1024, 4096, 6144, 6400, 8192, 16384, 6208)] == [1, 2, 3, 3, 4, 5, 1]
     assert gm.down_splits(64, 128, 512, 8, 2, gm.F32) == 4   # small fp32 batch: K split in parts of 128
     assert gm.down_splits(300, 128, 512, 8, 2, gm.F32) == 1
     ws_pre = gm.workspace_size(8192, 6144, 32768)

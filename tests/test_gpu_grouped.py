@@ -41,6 +41,7 @@ CASES = [
     _w("g_T64_shared", 64, 512, 1024, g1=2, g2=4, es=1),
     _w("g_T128", 128, 512, 1024, g1=4, g2=8),          # the largest int8 streaming batch: several passes
     _w("g_T40_straddle", 40, 1024, 1024, g1=2, g2=2),  # d split in 4 quarters; a 512-row group spans two
+    _w("g_T40_uneven", 40, 256, 6400, g1=2, g2=5),      # down chunks 2048, 2176, 2176: one ends inside a group
     # LDS-tiled kernels: 128-row tiles, several tiles and ragged tails, E = 4, group counts 3 and 6
     _w("g_T300", 300, 512, 1024, g1=4, g2=8),
     _w("g_T700_E4", 700, 768, 1536, E=4, g1=3, g2=6),

@@ -69,6 +69,7 @@ CASES = [
     _w("oi_bf16_T40", 40, 256, 8192),                      # streaming, two tiles, 4 down chunks
     _w("oi_bf16_T96", 96, 512, 1024),                      # streaming, several passes (largest bf16 batch)
     _w("oi_bf16_T8_share", 8, 6144, 4096),                 # a d_ff share: d split over the waves, both layouts
+    _w("oi_bf16_T24_uneven", 24, 256, 6400),               # down chunks of 2048, 2176 and 2176 rows
     _w("oi_bf16_T300", 300, 512, 1024),                    # direct-to-LDS tiles, down K split in 2
     _w("oi_bf16_T700_E4", 700, 768, 1536, E=4),
     _w("oi_w8_T40", 40, 512, 2048, dtype=W8),              # int8 streaming
@@ -76,6 +77,7 @@ CASES = [
     _w("oi_w8_T300", 300, 512, 1024, dtype=W8),            # int8 register-staged tiles
     _w("oi_w8g_T40", 40, 512, 2048, dtype=W8, g1=4, g2=4),  # grouped scales, streaming
     _w("oi_w8g_T40_straddle", 40, 1024, 1024, dtype=W8, g1=2, g2=2),  # quarters of d inside a scale group
+    _w("oi_w8g_T40_uneven", 40, 256, 6400, dtype=W8, g1=2, g2=5),  # a down chunk ends inside a 1280-row group
     _w("oi_w8g_T300_shared", 300, 512, 1024, dtype=W8, g1=2, g2=8, es=1),  # grouped + shared, tiles
     _w("oi_f32_T64", 64, 128, 512, dtype=F32),
     _w("oi_f32_T200", 200, 192, 320, dtype=F32),
