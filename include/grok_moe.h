@@ -120,7 +120,8 @@ int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtyp
 
 /* Down-projection: y[p, s] = sum over the p-th chunk of f of h[s] . W2[e] (* s2[e]), fp32, for every slot s
  * of expert e.  y is [splits, k*T, d] f32 with splits = grok_moe_down_splits(...) (passed back in `splits`
- * as a check; a different value returns GROK_MOE_EINVAL). */
+ * as a check; a different value returns GROK_MOE_EINVAL).  Only the sum over p is specified; the chunks are
+ * near-equal ranges of f (for the weight-streaming batches, boundaries at multiples of 128 rows). */
 int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const int32_t* counts,
                          const int32_t* offsets, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
                          int splits, float* y, void* stream);
