@@ -34,6 +34,26 @@ template <> struct Vec8<false> {
   }
 };
 
+// acc[e] += sum_i xv[i] * gate[e][k0 + i] (fp64 FMAs in ascending i) for the E experts.  The gate rows are loaded
+// eight experts at a time with no branch between the loads, so that their memory latencies overlap instead of
+// adding up; rows past E - 1 read row E - 1 again into partial logits that the top-2 selection never reads.
+template <bool BF16, int EMAX>
+__device__ __forceinline__ void gate_fma(const void* __restrict__ rw, int d, int E, int k0, const float xv[8],
+                                         double acc[EMAX]) {
+#pragma unroll
+  for (int e0 = 0; e0 < EMAX; e0 += 8) {
+    if (e0 < E) {
+      float wv[8][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Vec8<BF16>::load(rw, int64_t(min(e0 + j, E - 1)) * d + k0, wv[j]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[e0 + j] = __fma_rn(double(xv[i]), double(wv[j][i]), acc[e0 + j]);
+    }
+  }
+}
+
 constexpr int kRouterMaxWaves = 16;
 constexpr int kRouterWideTokens = 256;  // batches up to this many tokens use the wide workgroups
 
@@ -117,15 +137,7 @@ __global__ __launch_bounds__(router_max_threads<EMAX>()) void router_topk_kernel
   for (int k0 = 8 * threadIdx.x; k0 < d; k0 += 8 * blockDim.x) {
     float xv[8];
     Vec8<BF16>::load(x, xrow + k0, xv);
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        float wv[8];
-        Vec8<BF16>::load(rw, int64_t(e) * d + k0, wv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[e] = __fma_rn(double(xv[i]), double(wv[i]), acc[e]);
-      }
-    }
+    gate_fma<BF16, EMAX>(rw, d, E, k0, xv, acc);
   }
   reduce_select<EMAX>(acc, part, bias, E, t, idx, p);
 }
@@ -202,15 +214,7 @@ __global__ __launch_bounds__(256) void router_norm_kernel(const void* __restrict
       *reinterpret_cast<f32x4_t*>(dst) = o0;
       *reinterpret_cast<f32x4_t*>(dst + 4) = o1;
     }
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        float wv[8];
-        Vec8<BF16>::load(rw, int64_t(e) * d + k0, wv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[e] = __fma_rn(double(nv[i]), double(wv[i]), acc[e]);
-      }
-    }
+    gate_fma<BF16, EMAX>(rw, d, E, k0, nv, acc);
   }
   reduce_select<EMAX>(acc, part, bias, E, t, idx, p);
 }
