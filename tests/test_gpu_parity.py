@@ -303,6 +303,16 @@ def test_grok_decode_bf16(gm, grok_bf16):
     assert torch.equal(out, again)
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_grok_decode_few_tokens(gm, grok_bf16, T):
+    """One and three tokens at Grok-1 shape, every row against the oracle: at most 2 T experts are hit, the others
+    are empty (their streaming workgroups return at once), and the down-projection runs in 5 chunks of f."""
+    w = dataclasses.replace(synth.WORKLOADS["decode_bf16"], T=T, name=f"decode_bf16_T{T}")
+    (out, ref), _ = _grok_case(gm, grok_bf16, w)
+    assert int((ref["counts"].numpy() == 0).sum()) >= 8 - 2 * T
+    assert gm.down_splits(T, w.d, w.f) == 5
+
+
 def test_grok_prefill_bf16_sampled(gm, grok_bf16):
     (out, ref), dv = _grok_case(gm, grok_bf16, "prefill_bf16")
     again = _forward(gm, dv)[0]
