@@ -368,6 +368,11 @@ def test_grok_int8(gm, grok_int8):
     _grok_int8_case(gm, grok_int8, 64, None)
 
 
+def test_grok_int8_two_tokens(gm, grok_int8):
+    """int8 weights, T = 2 at Grok-1 shape, every row: at most 4 experts hit, the down-projection in 5 chunks."""
+    _grok_int8_case(gm, grok_int8, 2, None)
+
+
 @pytest.mark.parametrize("T", [128, 192])
 def test_grok_int8_mid_batch_sampled(gm, grok_int8, T):
     """int8 weights at T = 128 (the largest int8 streaming batch, several passes) and T = 192 (every expert in
