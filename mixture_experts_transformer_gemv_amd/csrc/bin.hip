@@ -5,8 +5,9 @@
 // Practice": each token is routed to a subset (two) of the experts.  Grouping the assignments by expert turns
 // the per-token expert calls into one matrix product per expert.
 //
-// One workgroup of 1024 threads (16 waves).  Counts use LDS integer atomics (exact, order-free).  The scatter
-// walks the tokens in chunks of 1024 in ascending order; within a chunk each wave ranks its lanes with a
+// One workgroup of NT threads: 1024 (16 waves), or one wave for at most 64 tokens, where the barriers of 16
+// waves cost more than the work.  Counts use LDS integer atomics (exact, order-free).  The scatter walks the
+// tokens in chunks of NT in ascending order; within a chunk each wave ranks its lanes with a
 // ballot and popcount, and waves are ordered by a scan over per-wave counts, so slots of one expert are in
 // ascending token order.
 #include "common.h"
@@ -14,16 +15,18 @@
 
 namespace gm {
 
-__global__ __launch_bounds__(1024) void bin_tokens_kernel(const int32_t* __restrict__ idx, int T, int E,
+template <int NT>
+__global__ __launch_bounds__(NT) void bin_tokens_kernel(const int32_t* __restrict__ idx, int T, int E,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ int s_cnt[64];
   __shared__ int s_base[64];
-  __shared__ int s_wc[64][16];
+  constexpr int NW = NT / 64;
+  __shared__ int s_wc[64][NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < E) s_cnt[tid] = 0;
   __syncthreads();
-  for (int t = tid; t < T; t += 1024) {
+  for (int t = tid; t < T; t += NT) {
     atomicAdd(&s_cnt[idx[2 * t]], 1);
     atomicAdd(&s_cnt[idx[2 * t + 1]], 1);
   }
@@ -40,7 +43,7 @@ __global__ __launch_bounds__(1024) void bin_tokens_kernel(const int32_t* __restr
   }
   __syncthreads();
   const uint64_t lt = (uint64_t(1) << lane) - 1;
-  for (int c0 = 0; c0 < T; c0 += 1024) {
+  for (int c0 = 0; c0 < T; c0 += NT) {
     const int t = c0 + tid;
     const bool valid = t < T;
     const int e0 = valid ? idx[2 * t] : -1;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(1024) void bin_tokens_kernel(const int32_t* __restr
     __syncthreads();
     if (tid < E) {
       int s = 0;
-      for (int w = 0; w < 16; ++w) s += s_wc[tid][w];
+      for (int w = 0; w < NW; ++w) s += s_wc[tid][w];
       s_base[tid] += s;
     }
     __syncthreads();
@@ -76,7 +79,10 @@ __global__ __launch_bounds__(1024) void bin_tokens_kernel(const int32_t* __restr
 
 hipError_t launch_bin(const int32_t* idx, int T, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                       int32_t* inv, hipStream_t s) {
-  bin_tokens_kernel<<<1, 1024, 0, s>>>(idx, T, E, counts, offsets, perm, inv);
+  if (T <= 64)
+    bin_tokens_kernel<64><<<1, 64, 0, s>>>(idx, T, E, counts, offsets, perm, inv);
+  else
+    bin_tokens_kernel<1024><<<1, 1024, 0, s>>>(idx, T, E, counts, offsets, perm, inv);
   return hipGetLastError();
 }
 
