@@ -174,11 +174,17 @@ def _expert_weights(inp: dict, dtype: int, e: int, layout: str = IN_OUT):
     raise ValueError(dtype)
 
 
-def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False, layout: str = IN_OUT) -> dict:
+def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False, layout: str = IN_OUT,
+            round_h: bool | None = None) -> dict:
     """The whole layer: routing on every token, expert FFNs and combine on ``rows`` (all rows if None).
 
     layout: how the expert weights are stored, IN_OUT (W1, Wv [E, d, f], W2 [E, f, d]) or OUT_IN (W1, Wv
     [E, f, d], W2 [E, d, f]); int8 scales are [Es, G, out] either way.
+
+    round_h: whether h is rounded once to bf16 before the down projection.  None (the default) takes the reading
+    above: rounded in the bf16 and int8 layers, not in the fp32 layer.  False gives the plain float64 definition
+    of the architecture diagram ([bridge]) for any storage type, the reference against which the rounding of h
+    itself is measured.
 
     inp: dict of numpy arrays as produced by ``synth.make_inputs`` (x, router_w, w1, wv, w2, s1, sv, s2,
     router_bias).  Returns float64 tensors: out [len(rows), d]; idx [T, k]; p [T, k]; counts [E]; logits; probs;
@@ -201,7 +207,7 @@ def forward(inp: dict, dtype: int, rows=None, k: int = 2, return_h: bool = False
     f = inp["w1"].shape[2] if layout == IN_OUT else inp["w1"].shape[1]
     hs = torch.zeros((n, k, f), dtype=torch.float64) if return_h else None
     ys = torch.zeros((n, k, d), dtype=torch.float64) if return_h else None
-    round_h = dtype != F32
+    round_h = (dtype != F32) if round_h is None else bool(round_h)
     ys_all = torch.zeros((n, k, d), dtype=torch.float64)
     for e in range(E):
         hit = (sel == e).nonzero()  # (row position, slot j) pairs choosing expert e

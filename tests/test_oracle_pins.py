@@ -422,3 +422,36 @@ def test_grok1_shapes_reproduce_printed_counts(golden_dir):
     for wname in ("decode_bf16", "prefill_bf16", "int8_w8", "skew_bf16"):
         w = synth.WORKLOADS[wname]
         assert (w.d, w.f, w.E) == (d, f, E) == (pr["hidden"], 32768, 8)
+
+
+def test_round_h_switch_is_the_plain_definition():
+    """forward(round_h=False) on a bf16 layer is the unrounded definition (numpy/scipy evaluation of the exact
+    stored values, no rounding anywhere); round_h=True on the same inputs rounds each h value to bf16, which the
+    closed form of test_h_rounding_closed_form pins; the default keeps the rounding for bf16 and int8 and not for
+    fp32."""
+    rng = np.random.default_rng(31)
+    T, d, f, E = 11, 8, 16, 8
+    x, rw, w1, wv, w2 = _rand_layer(rng, T, d, f, E, scale=2.0)
+    bits = synth.f32_to_bf16_bits
+    inp = {"x": bits(x), "router_w": bits(rw), "w1": bits(w1), "wv": bits(wv), "w2": bits(w2),
+           "s1": None, "sv": None, "s2": None, "router_bias": None}
+    val = {n: synth.bf16_bits_to_f32(inp[n]).astype(np.float64) for n in ("x", "router_w", "w1", "wv", "w2")}
+    plain = oracle.forward(inp, BF16, round_h=False)
+    rounded = oracle.forward(inp, BF16, round_h=True)
+    default = oracle.forward(inp, BF16)
+    assert torch.equal(default["out"], rounded["out"])
+    logits = val["x"] @ val["router_w"].T
+    probs = softmax(logits, axis=1)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:2]
+        want = sum(probs[t, e] * _dense_geglu(val["x"][t:t + 1], val["w1"][e], val["wv"][e], val["w2"][e])[0]
+                   for e in order)
+        want_r = sum(probs[t, e] * _dense_geglu(val["x"][t:t + 1], val["w1"][e], val["wv"][e], val["w2"][e],
+                                                round_h=True)[0] for e in order)
+        assert np.allclose(plain["out"][t].numpy(), want, rtol=1e-12, atol=1e-13)
+        assert np.allclose(rounded["out"][t].numpy(), want_r, rtol=1e-12, atol=1e-13)
+    assert not torch.allclose(plain["out"], rounded["out"], rtol=1e-6, atol=0)  # the rounding is visible
+    # fp32 layer: the default does not round, round_h=True does
+    f32 = _f32_inputs(x, rw, w1, wv, w2)
+    assert torch.equal(oracle.forward(f32, F32)["out"], oracle.forward(f32, F32, round_h=False)["out"])
+    assert not torch.equal(oracle.forward(f32, F32)["out"], oracle.forward(f32, F32, round_h=True)["out"])
