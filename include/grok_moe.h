@@ -16,28 +16,31 @@
  * Conventions for every entry point:
  *   - All tensors are row-major and contiguous.  Tensor pointers are DEVICE pointers (HBM of the current HIP
  *     device), 16-byte aligned, owned by the caller, and must stay valid until the enqueued work completes.
- *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call only ENQUEUES work on it and
- *     returns without synchronising; results are visible after the stream reaches that point.
+ *   - `stream` is the hipStream_t the work is enqueued on (NULL = the legacy default stream).  Every call only
+ *     ENQUEUES work and returns without synchronising; results are visible after the stream reaches that point.
  *   - Argument errors are detected on the host before anything is enqueued: the call returns a negative
  *     status, enqueues nothing and writes nothing.  A failed kernel launch returns GROK_MOE_EHIP.
  *   - The library allocates no memory and keeps no mutable global state: calls on different streams with
  *     distinct workspaces may run concurrently.
- *   - Weight layout is [E, in, out]: W1 and Wv are [E, d, f], W2 is [E, f, d].  Scales (int8 only) are
- *     [E, 1, f] for W1 and Wv and [E, 1, d] for W2: one bf16 scale per (expert, output channel).
+ *   - Weight layout, unless an entry point takes a grok_moe_layout: [E, in, out], W1 and Wv [E, d, f], W2 [E, f, d].
+ *     int8 scales, unless an entry point takes a scale layout: [E, 1, f] for W1 and Wv, [E, 1, d] for W2 (one bf16
+ *     scale per expert and output channel).
  *   - Supported shapes: k == 2, 2 <= E <= 64, d * f < 2^31.  bf16 and int8 layers need d and f to be multiples
  *     of 256; the fp32 layer needs multiples of 64.  T may be any value in [0, 2^24] (T == 0 enqueues nothing).
  *     Other shapes return GROK_MOE_EUNSUPPORTED; they are never padded silently.
- *   - Passes: the bf16 layer runs at most P = min((2^31 - 1) / (2 d), (2^31 - 1) / (4 f)) tokens per pass (its
- *     tiled kernels address x and h with 32-bit offsets; P = 16383 at d = 6144, f = 32768).  The whole-layer
- *     entry points split a larger T into ceil(T / P) passes of near-equal size over consecutive tokens, each
- *     routed, binned and computed on its own (tokens are independent; expert_counts are summed); the step
- *     entry points grok_moe_expert_up* / grok_moe_expert_down* take at most P tokens (else EUNSUPPORTED).
+ *   - Passes: the bf16 and int8 layers run at most P = min((2^31 - 1) / (2 d), (2^31 - 1) / (4 f)) tokens per
+ *     pass (their tiled kernels address x and h with 32-bit offsets; P = 16383 at d = 6144, f = 32768).  The
+ *     whole-layer entry points split a larger T into ceil(T / P) passes of near-equal size over consecutive tokens,
+ *     each routed, binned and computed on its own (tokens are independent; expert_counts are summed); the step
+ *     entry points grok_moe_expert_up / grok_moe_expert_down take at most P tokens (else EUNSUPPORTED).
  */
 #ifndef GROK_MOE_H
 #define GROK_MOE_H
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -50,11 +53,19 @@ extern "C" {
  * Accumulation is fp32 in every expert matrix product; the router accumulates in fp64. */
 typedef enum { GROK_MOE_F32 = 0, GROK_MOE_BF16 = 1, GROK_MOE_W8 = 2 } grok_moe_dtype;
 
+/* Storage of the expert weights (page "Grok-1-BF16", section "Conversion Details": the checkpoint stores them in
+ * JAX's [in, out] convention and the conversion transposes them to PyTorch's [out, in]):
+ *   GROK_MOE_IN_OUT: W1, Wv [E, d, f], W2 [E, f, d];
+ *   GROK_MOE_OUT_IN: W1, Wv [E, f, d], W2 [E, d, f].
+ * The result is bit-identical for both on the same weights: the kernels multiply the same operands in the same
+ * order. */
+typedef enum { GROK_MOE_IN_OUT = 0, GROK_MOE_OUT_IN = 1 } grok_moe_layout;
+
 enum {
   GROK_MOE_OK = 0,
-  GROK_MOE_EINVAL = -1,       /* NULL or misaligned pointer, negative size, unknown dtype */
+  GROK_MOE_EINVAL = -1,       /* NULL or misaligned pointer, negative size, unknown dtype or layout */
   GROK_MOE_EUNSUPPORTED = -2, /* valid but unsupported shape (k != 2, E outside [2,64], d/f granularity or
-                                 size, more than one pass of tokens in an expert step) */
+                                 size, more than one pass of tokens in an expert step, scale groups) */
   GROK_MOE_EWORKSPACE = -3,   /* workspace smaller than grok_moe_workspace_size() */
   GROK_MOE_EHIP = -4          /* a HIP launch failed */
 };
@@ -62,13 +73,17 @@ enum {
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* grok_moe_strerror(int status);
 
-/* Bytes of device workspace grok_moe_forward() needs for this shape (0 if the shape is invalid or T == 0).
- * The workspace holds routing results, the token permutation, h [k*T, f] and the partial expert outputs of
- * one pass (T tokens, or the larger pass size if T needs several passes). */
-size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
+/* Bytes of device workspace grok_moe_forward() / grok_moe_forward_ex() need for this shape (0 if the shape is
+ * invalid or T == 0).  The workspace holds routing results, the token permutation, h [k*T, f] and the partial
+ * expert outputs of one pass (T tokens, or the larger pass size if T needs several passes). */
+size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype);
 
-/* The whole layer: router -> token binning -> fused up-projection with GELU product -> down-projection ->
- * gate-weighted combine, all on `stream`.
+/* The whole layer, with the arguments of the layer's statement grok_moe_forward(x, router_w, w1, wv, w2,
+ * [int8 scales], T, d, f, E, k, out) followed by optional outputs: router -> token binning -> fused
+ * up-projection with GELU product -> down-projection -> gate-weighted combine, all on `stream`.
+ * Router: "... (MoE Explained)", section "Expert Routing Details" (softmax over all E, top-2; gates and indices
+ * returned); experts: "A functional bridge ...", architecture diagram; combine: "... (MoE Explained)", section
+ * "How MoE Works in Practice"; int8 form: "Grok-1-BF16", section "Conversion Details".
  *   x          [T, d]     f32 | bf16
  *   router_w   [E, d]     f32 | bf16 (the gate weight, [out, in])
  *   w1, wv     [E, d, f]  f32 | bf16 | int8
@@ -84,11 +99,37 @@ size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, in
  * Results are deterministic: identical inputs give bit-identical outputs (no floating-point atomics). */
 int grok_moe_forward(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
                      const void* s1, const void* sv, const void* s2,
-                     int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
+                     int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype,
                      float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream);
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* ---- The steps of the layer, one entry point each (grok_moe_forward enqueues exactly these). ---------------
+/* ---- int8 scale layouts ---------------------------------------------------------------------------------------
+ * Page "Grok-1-BF16", section "Conversion Details": int8 weights times bf16 scales with grouped broadcasting,
+ * scale shapes (1,N), (8,N), (8,1,N) and (8,8,N).  Where an entry point takes (scale_experts, groups), a scale
+ * tensor is [scale_experts, groups, out]:
+ *   W[e, k, n] = q[e, k, n] * s[scale_experts == 1 ? 0 : e, k / (in / groups), n]
+ * with scale_experts = E (one tensor per expert) or 1 (shared by all experts), and `groups` contiguous groups of
+ * in/groups input rows.  (8,1,N) and (8,N) are scale_experts = 8, groups = 1 (the layout of grok_moe_forward);
+ * (1,N) is scale_experts = 1, groups = 1; (8,8,N) is scale_experts = 8, groups = 8.
+ *   s1, sv  [scale_experts, groups_up, f]   bf16, groups_up divides d and d / groups_up is a multiple of 64
+ *   s2      [scale_experts, groups_down, d] bf16, groups_down divides f and f / groups_down is a multiple of 64
+ * Other group counts return GROK_MOE_EUNSUPPORTED; scale_experts other than 1 or E, or a group count < 1,
+ * GROK_MOE_EINVAL.  A zero scale is allowed (its group contributes nothing).  Accumulation is fp32; with more
+ * than one group the kernels keep each column's accumulator in units of the current group's scale (one fp32
+ * rounding per group boundary), so non-zero scales of one column must not differ by more than ~1e30 in ratio.
+ * scale_experts and the group counts are ignored unless dtype is GROK_MOE_W8. */
+
+/* The whole layer in its general form: as grok_moe_forward, with the weights stored as weight_layout says and
+ * int8 scales of layout [scale_experts, groups_up, f] (s1, sv) and [scale_experts, groups_down, d] (s2).
+ * Workspace: grok_moe_workspace_size(). */
+int grok_moe_forward_ex(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                        const void* s1, const void* sv, const void* s2, grok_moe_layout weight_layout,
+                        int scale_experts, int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E,
+                        int k, grok_moe_dtype dtype, float* out, const float* router_bias, int32_t* topk_idx,
+                        float* topk_p, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* ---- The steps of the layer, one entry point each (grok_moe_forward_ex enqueues exactly these). -------------
  * A "slot" is one (token, selected expert) assignment; there are k*T of them, grouped by expert in ascending
  * expert order and, within an expert, in ascending token order. */
 
@@ -96,40 +137,45 @@ int grok_moe_forward(const void* x, const void* router_w, const void* w1, const 
  * over all E, top-2 with the lower-index tie-break.  x [T,d], router_w [E,d] (f32 if dtype == GROK_MOE_F32,
  * else bf16); router_bias [E] f32 or NULL.  Writes topk_idx [T,k] int32 and topk_p [T,k] f32 (both required). */
 int grok_moe_route(const void* x, const void* router_w, const float* router_bias, int64_t T, int64_t d, int E,
-                   int k, int dtype, int32_t* topk_idx, float* topk_p, void* stream);
+                   int k, grok_moe_dtype dtype, int32_t* topk_idx, float* topk_p, hipStream_t stream);
 
 /* Token binning (the dispatch of each token to its selected experts, "... (MoE Explained)", section
  * "How MoE Works in Practice"): histogram of topk_idx [T,k], exclusive prefix sum, stable permutation.
  * Writes counts [E], offsets [E+1] (offsets[e] = first slot of expert e, offsets[E] = k*T),
  * perm [k*T] (slot -> token) and inv [T,k] ((token, j) -> slot).  topk_idx entries must lie in [0, E). */
 int grok_moe_bin(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,
-                 int32_t* perm, int32_t* inv, void* stream);
+                 int32_t* perm, int32_t* inv, hipStream_t stream);
 
 /* Fused up-projection ("A functional bridge ...", architecture diagram; int8 form per "Grok-1-BF16",
  * section "Conversion Details"): for every slot s of expert e with token t = perm[s],
- *   a = x[t] . W1[e] (* s1[e]),  b = x[t] . Wv[e] (* sv[e]),  h[s] = GELU_erf(a) * b,
+ *   a = x[t] . W1[e] (* s1),  b = x[t] . Wv[e] (* sv),  h[s] = GELU_erf(a) * b,
  * fp32 accumulation; h [k*T, f] is bf16 (rounded once, to nearest even) or f32 for GROK_MOE_F32.
- * counts/offsets/perm are grok_moe_bin's outputs. */
+ * counts/offsets/perm are grok_moe_bin's outputs; weights stored as weight_layout says; s1, sv of layout
+ * [scale_experts, groups_up, f] (int8 only, else NULL). */
 int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
-                       const int32_t* counts, const int32_t* offsets, const int32_t* perm,
-                       int64_t T, int64_t d, int64_t f, int E, int k, int dtype, void* h, void* stream);
+                       grok_moe_layout weight_layout, int scale_experts, int groups_up, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k,
+                       grok_moe_dtype dtype, void* h, hipStream_t stream);
 
 /* Number of partial sums grok_moe_expert_down() splits the f axis into for this shape (>= 1; for a T of
  * several passes, that of the first pass). */
-int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
+int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype);
 
-/* Down-projection: y[p, s] = sum over the p-th chunk of f of h[s] . W2[e] (* s2[e]), fp32, for every slot s
- * of expert e.  y is [splits, k*T, d] f32 with splits = grok_moe_down_splits(...) (passed back in `splits`
- * as a check; a different value returns GROK_MOE_EINVAL).  Only the sum over p is specified; the chunks are
- * near-equal ranges of f (for the weight-streaming batches, boundaries at multiples of 128 rows). */
-int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const int32_t* counts,
-                         const int32_t* offsets, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
-                         int splits, float* y, void* stream);
+/* Down-projection (the third matrix of "A functional bridge ...", architecture diagram):
+ * y[p, s] = sum over the p-th chunk of f of h[s] . W2[e] (* s2), fp32, for every slot s of expert e.
+ * y is [splits, k*T, d] f32 with splits = grok_moe_down_splits(...) (passed back in `splits` as a check; a
+ * different value returns GROK_MOE_EINVAL).  Only the sum over p is specified; the chunks are near-equal ranges
+ * of f (for the weight-streaming batches, boundaries at multiples of 128 rows).  W2 stored as weight_layout says;
+ * s2 of layout [scale_experts, groups_down, d] (int8 only, else NULL). */
+int grok_moe_expert_down(const void* h, const void* w2, const void* s2, grok_moe_layout weight_layout,
+                         int scale_experts, int groups_down, const int32_t* counts, const int32_t* offsets,
+                         int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype, int splits, float* y,
+                         hipStream_t stream);
 
 /* Gate-weighted combine ("... (MoE Explained)", section "How MoE Works in Practice"):
  * out[t] = sum_j topk_p[t,j] * (sum_p y[p, inv[t,j]]), the partials summed in ascending p. out [T,d] f32. */
 int grok_moe_combine(const float* y, int splits, const float* topk_p, const int32_t* inv, int64_t T, int64_t d,
-                     int k, float* out, void* stream);
+                     int k, float* out, hipStream_t stream);
 
 /* ---- The MoE part of a Grok-1 layer with its two norms and the residual ------------------------------------
  * Page "Grok-1-BF16", section "Architecture" (four norms per layer: pre-attention, post-attention, pre-MoE,
@@ -143,95 +189,31 @@ int grok_moe_combine(const float* y, int splits, const float* topk_p, const int3
  * evaluated in float64 and written as fp32. */
 
 /* Workspace of grok_moe_block_forward (the layer's workspace plus xn). */
-size_t grok_moe_block_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype);
+size_t grok_moe_block_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype);
 
-/* The block: same arguments and conventions as grok_moe_forward plus pre_scale, post_scale and eps; out [T,d]
+/* The block: the arguments and conventions of grok_moe_forward_ex plus pre_scale, post_scale and eps; out [T,d]
  * fp32 = x + RMSNorm(MoE(RMSNorm(x; pre_scale)); post_scale).  Routing outputs refer to the normed input. */
 int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,
                            const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
-                           const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
-                           float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                           int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream);
+                           const void* sv, const void* s2, grok_moe_layout weight_layout, int scale_experts,
+                           int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E, int k,
+                           grok_moe_dtype dtype, float* out, const float* router_bias, int32_t* topk_idx,
+                           float* topk_p, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
-/* Step: pre-MoE RMSNorm fused with the router.  Writes xn [T,d] (activation type), topk_idx, topk_p. */
+/* Step: pre-MoE RMSNorm fused with the router (the norm of "Grok-1-BF16", section "Verification", in front of
+ * the router of "... (MoE Explained)", section "Expert Routing Details").  Writes xn [T,d] (activation type),
+ * topk_idx, topk_p. */
 int grok_moe_route_norm(const void* x, const void* pre_scale, double eps, const void* router_w,
-                        const float* router_bias, int64_t T, int64_t d, int E, int k, int dtype, void* xn,
-                        int32_t* topk_idx, float* topk_p, void* stream);
+                        const float* router_bias, int64_t T, int64_t d, int E, int k, grok_moe_dtype dtype, void* xn,
+                        int32_t* topk_idx, float* topk_p, hipStream_t stream);
 
-/* Step: combine fused with the post-MoE RMSNorm and the residual add (x is the block input [T,d]). */
+/* Step: combine fused with the post-MoE RMSNorm and the residual add (x is the block input [T,d]); the combine of
+ * "... (MoE Explained)", section "How MoE Works in Practice", then the post-MoE norm of "Grok-1-BF16", section
+ * "Verification". */
 int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const int32_t* inv, const void* x,
-                          const void* post_scale, double eps, int64_t T, int64_t d, int k, int dtype, float* out,
-                          void* stream);
-
-/* ---- int8 weights with grouped scales -------------------------------------------------------------------------
- * Page "Grok-1-BF16", section "Conversion Details": int8 weights times bf16 scales with grouped broadcasting,
- * scale shapes (1,N), (8,N), (8,1,N) and (8,8,N).  Here a scale tensor is [scale_experts, groups, out]:
- *   W[e, k, n] = q[e, k, n] * s[scale_experts == 1 ? 0 : e, k / (in / groups), n]
- * with scale_experts = E (one tensor per expert) or 1 (shared by all experts), and `groups` contiguous groups of
- * in/groups input rows.  (8,1,N) and (8,N) are scale_experts = 8, groups = 1 (the layout of grok_moe_forward);
- * (1,N) is scale_experts = 1, groups = 1; (8,8,N) is scale_experts = 8, groups = 8.
- *   s1, sv  [scale_experts, groups_up, f]   bf16, groups_up divides d and d / groups_up is a multiple of 64
- *   s2      [scale_experts, groups_down, d] bf16, groups_down divides f and f / groups_down is a multiple of 64
- * Other group counts return GROK_MOE_EUNSUPPORTED; scale_experts other than 1 or E, or a group count < 1,
- * GROK_MOE_EINVAL.  A zero scale is allowed (its group contributes nothing).  Accumulation is fp32; with more
- * than one group the kernels keep each column's accumulator in units of the current group's scale (one fp32
- * rounding per group boundary), so non-zero scales of one column must not differ by more than ~1e30 in ratio.
- * Workspace: grok_moe_workspace_size(..., GROK_MOE_W8); splits: grok_moe_down_splits(..., GROK_MOE_W8). */
-
-/* The whole layer with int8 weights and grouped scales; otherwise as grok_moe_forward with dtype GROK_MOE_W8. */
-int grok_moe_forward_w8_grouped(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
-                                const void* s1, const void* sv, const void* s2, int scale_experts, int groups_up,
-                                int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, float* out,
-                                const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
-                                void* workspace, size_t workspace_bytes, void* stream);
-
-/* Step: the fused up-projection (as grok_moe_expert_up, dtype GROK_MOE_W8) with grouped scales s1, sv. */
-int grok_moe_expert_up_w8_grouped(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
-                                  int scale_experts, int groups_up, const int32_t* counts, const int32_t* offsets,
-                                  const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k, void* h,
-                                  void* stream);
-
-/* Step: the down-projection (as grok_moe_expert_down, dtype GROK_MOE_W8) with grouped scales s2. */
-int grok_moe_expert_down_w8_grouped(const void* h, const void* w2, const void* s2, int scale_experts,
-                                    int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T,
-                                    int64_t d, int64_t f, int E, int k, int splits, float* y, void* stream);
-
-/* ---- Weight storage [E, out, in], and the general forms of the layer and of its two expert steps ----------------
- * Page "Grok-1-BF16", section "Conversion Details": the checkpoint stores weights in JAX's [in, out] convention
- * and the conversion transposes them to PyTorch's [out, in].  weight_layout selects which one W1, Wv, W2 use:
- *   GROK_MOE_IN_OUT: W1, Wv [E, d, f], W2 [E, f, d] (the layout of every other entry point);
- *   GROK_MOE_OUT_IN: W1, Wv [E, f, d], W2 [E, d, f].
- * Either way int8 scales are [scale_experts, groups, out] (out = f for W1/Wv, d for W2), grouped along the input
- * axis as described above; scale_experts and the group counts are ignored unless dtype is GROK_MOE_W8.  An unknown
- * weight_layout returns GROK_MOE_EINVAL.  The result is bit-identical to the [in, out] form on the same weights:
- * the kernels multiply the same operands in the same order. */
-typedef enum { GROK_MOE_IN_OUT = 0, GROK_MOE_OUT_IN = 1 } grok_moe_layout;
-
-/* The whole layer; otherwise as grok_moe_forward. */
-int grok_moe_forward_ex(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
-                        const void* s1, const void* sv, const void* s2, int weight_layout, int scale_experts,
-                        int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
-                        float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                        int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream);
-
-/* Step: the fused up-projection; otherwise as grok_moe_expert_up. */
-int grok_moe_expert_up_ex(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
-                          int weight_layout, int scale_experts, int groups_up, const int32_t* counts,
-                          const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k,
-                          int dtype, void* h, void* stream);
-
-/* Step: the down-projection; otherwise as grok_moe_expert_down. */
-int grok_moe_expert_down_ex(const void* h, const void* w2, const void* s2, int weight_layout, int scale_experts,
-                            int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T, int64_t d,
-                            int64_t f, int E, int k, int dtype, int splits, float* y, void* stream);
-
-/* The MoE block (as grok_moe_block_forward) with the weight layout and int8 scale layout of grok_moe_forward_ex. */
-int grok_moe_block_forward_ex(const void* x, const void* pre_scale, const void* post_scale, double eps,
-                              const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
-                              const void* sv, const void* s2, int weight_layout, int scale_experts, int groups_up,
-                              int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype, float* out,
-                              const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                          const void* post_scale, double eps, int64_t T, int64_t d, int k, grok_moe_dtype dtype,
+                          float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

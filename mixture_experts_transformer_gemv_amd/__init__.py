@@ -31,35 +31,23 @@ _SIGS = {
     "grok_moe_down_splits": (_int, [_i64, _i64, _i64, _int, _int, _int]),
     "grok_moe_forward": (_int, [_c_void_p] * 8 + [_i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 6
                          + [ctypes.c_size_t, _c_void_p]),
+    "grok_moe_forward_ex": (_int, [_c_void_p] * 8 + [_int, _int, _int, _int, _i64, _i64, _i64, _int, _int, _int]
+                            + [_c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]),
     "grok_moe_route": (_int, [_c_void_p] * 3 + [_i64, _i64, _int, _int, _int] + [_c_void_p] * 3),
     "grok_moe_bin": (_int, [_c_void_p, _i64, _int, _int] + [_c_void_p] * 5),
-    "grok_moe_expert_up": (_int, [_c_void_p] * 8 + [_i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 2),
-    "grok_moe_expert_down": (_int, [_c_void_p] * 5 + [_i64, _i64, _i64, _int, _int, _int, _int]
-                             + [_c_void_p] * 2),
+    "grok_moe_expert_up": (_int, [_c_void_p] * 5 + [_int, _int, _int] + [_c_void_p] * 3
+                           + [_i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p]),
+    "grok_moe_expert_down": (_int, [_c_void_p] * 3 + [_int, _int, _int] + [_c_void_p] * 2
+                             + [_i64, _i64, _i64, _int, _int, _int, _int, _c_void_p, _c_void_p]),
     "grok_moe_combine": (_int, [_c_void_p, _int, _c_void_p, _c_void_p, _i64, _i64, _int, _c_void_p, _c_void_p]),
     "grok_moe_block_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _int, _int, _int]),
     "grok_moe_block_forward": (_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_double] + [_c_void_p] * 7
-                               + [_i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 6
+                               + [_int, _int, _int, _int, _i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 6
                                + [ctypes.c_size_t, _c_void_p]),
     "grok_moe_route_norm": (_int, [_c_void_p, _c_void_p, ctypes.c_double, _c_void_p, _c_void_p, _i64, _i64, _int,
                                    _int, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "grok_moe_combine_norm": (_int, [_c_void_p, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, ctypes.c_double,
                                      _i64, _i64, _int, _int, _c_void_p, _c_void_p]),
-    "grok_moe_forward_w8_grouped": (_int, [_c_void_p] * 8 + [_int, _int, _int, _i64, _i64, _i64, _int, _int]
-                                    + [_c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]),
-    "grok_moe_expert_up_w8_grouped": (_int, [_c_void_p] * 5 + [_int, _int] + [_c_void_p] * 3
-                                      + [_i64, _i64, _i64, _int, _int, _c_void_p, _c_void_p]),
-    "grok_moe_expert_down_w8_grouped": (_int, [_c_void_p] * 3 + [_int, _int] + [_c_void_p] * 2
-                                        + [_i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p]),
-    "grok_moe_forward_ex": (_int, [_c_void_p] * 8 + [_int, _int, _int, _int, _i64, _i64, _i64, _int, _int, _int]
-                            + [_c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]),
-    "grok_moe_expert_up_ex": (_int, [_c_void_p] * 5 + [_int, _int, _int] + [_c_void_p] * 3
-                              + [_i64, _i64, _i64, _int, _int, _int, _c_void_p, _c_void_p]),
-    "grok_moe_expert_down_ex": (_int, [_c_void_p] * 3 + [_int, _int, _int] + [_c_void_p] * 2
-                                + [_i64, _i64, _i64, _int, _int, _int, _int, _c_void_p, _c_void_p]),
-    "grok_moe_block_forward_ex": (_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_double] + [_c_void_p] * 7
-                                  + [_int, _int, _int, _int, _i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 6
-                                  + [ctypes.c_size_t, _c_void_p]),
 }
 
 # weight storage: [E, in, out] (the checkpoint's JAX layout) or [E, out, in] (the converted PyTorch layout)
@@ -208,23 +196,18 @@ def forward(x, router_w, w1, wv, w2, scales=None, router_bias=None, return_routi
     need = workspace_size(T, d, f, E, 2, dt)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    if lay != 0:
+    wsb = workspace.numel() * workspace.element_size()
+    if lay == 0 and grouped is None:
+        st = lib().grok_moe_forward(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
+                                    T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
+                                    _p(workspace), wsb, _stream())
+        _check(st, "grok_moe_forward")
+    else:
         es, g1, g2 = grouped if grouped is not None else (E, 1, 1)
         st = lib().grok_moe_forward_ex(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), lay, es,
                                        g1, g2, T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
-                                       _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+                                       _p(workspace), wsb, _stream())
         _check(st, "grok_moe_forward_ex")
-    elif grouped is None:
-        st = lib().grok_moe_forward(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
-                                    T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
-                                    _p(workspace), workspace.numel() * workspace.element_size(), _stream())
-        _check(st, "grok_moe_forward")
-    else:
-        st = lib().grok_moe_forward_w8_grouped(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
-                                               *grouped, T, d, f, E, 2, _p(out), _p(router_bias), _p(idx), _p(pr),
-                                               _p(cnt), _p(workspace), workspace.numel() * workspace.element_size(),
-                                               _stream())
-        _check(st, "grok_moe_forward_w8_grouped")
     if return_routing:
         return out, idx, pr, cnt
     return out
@@ -273,17 +256,8 @@ def expert_up(x, w1, wv, counts, offsets, perm, scales=None, h=None, weight_layo
             raise GrokMoeError("s1 and sv need the same layout")
     if h is None:
         h = torch.empty((2 * T, f), dtype=torch.float32 if dt == F32 else torch.bfloat16, device=x.device)
-    if lcode != 0:
-        _check(lib().grok_moe_expert_up_ex(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), lcode, *lay, _p(counts),
-                                           _p(offsets), _p(perm), T, d, f, E, 2, dt, _p(h), _stream()),
-               "grok_moe_expert_up_ex")
-    elif lay == (E, 1):
-        _check(lib().grok_moe_expert_up(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), _p(counts), _p(offsets), _p(perm),
-                                        T, d, f, E, 2, dt, _p(h), _stream()), "grok_moe_expert_up")
-    else:
-        _check(lib().grok_moe_expert_up_w8_grouped(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), *lay, _p(counts),
-                                                   _p(offsets), _p(perm), T, d, f, E, 2, _p(h), _stream()),
-               "grok_moe_expert_up_w8_grouped")
+    _check(lib().grok_moe_expert_up(_p(x), _p(w1), _p(wv), _p(s1), _p(sv), lcode, *lay, _p(counts), _p(offsets),
+                                    _p(perm), T, d, f, E, 2, dt, _p(h), _stream()), "grok_moe_expert_up")
     return h
 
 
@@ -296,15 +270,8 @@ def expert_down(h, w2, counts, offsets, T: int, x_dtype, s2=None, y=None, weight
     if y is None:
         y = torch.empty((S, 2 * T, d), dtype=torch.float32, device=h.device)
     lay = scale_layout(s2, E, d, "s2") if dt == W8 else (E, 1)
-    if lcode != 0:
-        _check(lib().grok_moe_expert_down_ex(_p(h), _p(w2), _p(s2), lcode, *lay, _p(counts), _p(offsets), T, d, f, E,
-                                             2, dt, S, _p(y), _stream()), "grok_moe_expert_down_ex")
-    elif lay == (E, 1):
-        _check(lib().grok_moe_expert_down(_p(h), _p(w2), _p(s2), _p(counts), _p(offsets), T, d, f, E, 2, dt, S,
-                                          _p(y), _stream()), "grok_moe_expert_down")
-    else:
-        _check(lib().grok_moe_expert_down_w8_grouped(_p(h), _p(w2), _p(s2), *lay, _p(counts), _p(offsets), T, d, f,
-                                                     E, 2, S, _p(y), _stream()), "grok_moe_expert_down_w8_grouped")
+    _check(lib().grok_moe_expert_down(_p(h), _p(w2), _p(s2), lcode, *lay, _p(counts), _p(offsets), T, d, f, E, 2,
+                                      dt, S, _p(y), _stream()), "grok_moe_expert_down")
     return y
 
 
@@ -349,19 +316,12 @@ def block_forward(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, scales=No
     need = block_workspace_size(T, d, f, E, 2, dt)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
-    if lay == 0 and grouped is None:
-        st = lib().grok_moe_block_forward(_p(x), _p(pre_scale), _p(post_scale), float(eps), _p(router_w), _p(w1),
-                                          _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), T, d, f, E, 2, dt, _p(out),
-                                          _p(router_bias), _p(idx), _p(pr), _p(cnt), _p(workspace),
-                                          workspace.numel() * workspace.element_size(), _stream())
-        _check(st, "grok_moe_block_forward")
-    else:
-        es, g1, g2 = grouped if grouped is not None else (E, 1, 1)
-        st = lib().grok_moe_block_forward_ex(_p(x), _p(pre_scale), _p(post_scale), float(eps), _p(router_w), _p(w1),
-                                             _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), lay, es, g1, g2, T, d, f, E, 2,
-                                             dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt), _p(workspace),
-                                             workspace.numel() * workspace.element_size(), _stream())
-        _check(st, "grok_moe_block_forward_ex")
+    es, g1, g2 = grouped if grouped is not None else (E, 1, 1)
+    st = lib().grok_moe_block_forward(_p(x), _p(pre_scale), _p(post_scale), float(eps), _p(router_w), _p(w1),
+                                      _p(wv), _p(w2), _p(s1), _p(sv), _p(s2), lay, es, g1, g2, T, d, f, E, 2, dt,
+                                      _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt), _p(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "grok_moe_block_forward")
     if return_routing:
         return out, idx, pr, cnt
     return out

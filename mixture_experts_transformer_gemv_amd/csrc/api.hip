@@ -47,13 +47,14 @@ int check_shape(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
   return GROK_MOE_OK;
 }
 
-// Tokens of one pass of the layer.  The LDS-tiled bf16 kernels address x [T, d] and h [2 T, f] with 32-bit byte
-// offsets below 2^31; longer batches run as several passes over consecutive token ranges (the layer treats
-// tokens independently; only the expert counts are summed).
+// Tokens of one pass of the layer.  The LDS-tiled kernels of the bf16 and int8 layers (direct-to-LDS copies)
+// address x [T, d] and h [2 T, f], both bf16, with 32-bit byte offsets below 2^31; longer batches run as several
+// passes over consecutive token ranges (the layer treats tokens independently; only the expert counts are
+// summed).  The fp32 kernels address with 64-bit offsets.
 int64_t max_pass_tokens(int64_t d, int64_t f, int dtype) {
-  if (dtype != GROK_MOE_BF16) return kMaxTokens;
+  if (dtype == GROK_MOE_F32) return kMaxTokens;
   const int64_t lim = (int64_t(1) << 31) - 1;
-  return std::max<int64_t>(kStreamMaxTokensBf16 + 1, std::min(lim / (2 * d), lim / (4 * f)));
+  return std::max<int64_t>(stream_max_tokens(dtype) + 1, std::min(lim / (2 * d), lim / (4 * f)));
 }
 
 // T tokens as n passes of near-equal size: the first `rem` passes take base + 1 tokens, the others base.
@@ -237,7 +238,7 @@ int run_layer(const void* x, const void* pre_scale, const void* post_scale, doub
               const void* w1, const void* wv, const void* w2, const void* s1, const void* sv, const void* s2,
               const ScaleSpec& sp, int64_t T, int64_t d, int64_t f, int E, int dtype, float* out,
               const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts, void* workspace,
-              size_t workspace_bytes, void* stream) {
+              size_t workspace_bytes, hipStream_t stream) {
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return GROK_MOE_EINVAL;
   if (workspace_bytes < workspace_need(T, d, f, E, dtype, pre_scale != nullptr)) return GROK_MOE_EWORKSPACE;
   const Passes ps = passes(T, d, f, dtype);
@@ -248,9 +249,47 @@ int run_layer(const void* x, const void* pre_scale, const void* post_scale, doub
     e = run_pass(static_cast<const char*>(x) + t0 * xrow, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv,
                  s2, sp, ps.size(i), d, f, E, dtype, out + t0 * d, router_bias,
                  topk_idx ? topk_idx + 2 * t0 : nullptr, topk_p ? topk_p + 2 * t0 : nullptr, expert_counts, i > 0,
-                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+                 static_cast<char*>(workspace), stream);
   }
   return hip_status(e);
+}
+
+// ---- argument checks shared by the entry points
+
+// Scale spec of an entry point's (weight_layout, scale_experts, groups) arguments; GROK_MOE_OK or a status.
+int make_spec(grok_moe_layout weight_layout, int scale_experts, int groups_up, int groups_down, int64_t d,
+              int64_t f, int E, grok_moe_dtype dtype, ScaleSpec* sp) {
+  if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
+  *sp = ScaleSpec{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
+  if (dtype != GROK_MOE_W8) return GROK_MOE_OK;
+  sp->experts = scale_experts;
+  sp->g_up = groups_up;
+  sp->g_down = groups_down;
+  return check_groups(*sp, d, f, E);
+}
+
+// The whole layer (or the block if pre_scale != NULL): shape, pointer and scale checks, then the passes.
+int layer_entry(const void* x, const void* pre_scale, const void* post_scale, double eps, const void* router_w,
+                const void* w1, const void* wv, const void* w2, const void* s1, const void* sv, const void* s2,
+                grok_moe_layout weight_layout, int scale_experts, int groups_up, int groups_down, int64_t T,
+                int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype, float* out, const float* router_bias,
+                int32_t* topk_idx, float* topk_p, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  int st = check_shape(T, d, f, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  const bool block = pre_scale != nullptr || post_scale != nullptr;
+  if (block && !(eps >= 0.0)) return GROK_MOE_EINVAL;
+  ScaleSpec sp;
+  if ((st = make_spec(weight_layout, scale_experts, groups_up, groups_down, d, f, E, dtype, &sp)) != GROK_MOE_OK)
+    return st;
+  if (T == 0) return GROK_MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(w2) || !ok_ptr(out))
+    return GROK_MOE_EINVAL;
+  if (block && (!ok_ptr(pre_scale) || !ok_ptr(post_scale))) return GROK_MOE_EINVAL;
+  if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
+  if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
+  return run_layer(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, dtype, out,
+                   router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
 }
 
 }  // namespace
@@ -260,7 +299,8 @@ extern "C" {
 const char* grok_moe_strerror(int status) {
   switch (status) {
     case GROK_MOE_OK: return "ok";
-    case GROK_MOE_EINVAL: return "invalid argument (NULL or misaligned pointer, negative size or unknown dtype)";
+    case GROK_MOE_EINVAL: return "invalid argument (NULL or misaligned pointer, negative size, unknown dtype or "
+                                 "layout)";
     case GROK_MOE_EUNSUPPORTED: return "unsupported shape (needs k == 2, 2 <= E <= 64, d and f multiples of 256 "
                                        "for bf16/int8 or of 64 for fp32, d * f < 2^31; the expert step entry "
                                        "points take at most one pass of tokens)";
@@ -270,167 +310,120 @@ const char* grok_moe_strerror(int status) {
   }
 }
 
-size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
+size_t grok_moe_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype) {
   if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK || T == 0) return 0;
   return workspace_need(T, d, f, E, dtype, false);
 }
 
-int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
+int grok_moe_down_splits(int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype) {
   if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK) return 1;
   return make_plan(passes(T, d, f, dtype).size(0), d, f, E, dtype).splits;
 }
 
 int grok_moe_forward_ex(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
-                        const void* s1, const void* sv, const void* s2, int weight_layout, int scale_experts,
-                        int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
-                        float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                        int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_shape(T, d, f, E, k, dtype);
-  if (st != GROK_MOE_OK) return st;
-  if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
-  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
-  if (dtype == GROK_MOE_W8) {
-    sp.experts = scale_experts;
-    sp.g_up = groups_up;
-    sp.g_down = groups_down;
-    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
-  }
-  if (T == 0) return GROK_MOE_OK;
-  if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(w2) || !ok_ptr(out))
-    return GROK_MOE_EINVAL;
-  if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
-  if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
-  return run_layer(x, nullptr, nullptr, 0.0, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, dtype, out,
-                   router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
+                        const void* s1, const void* sv, const void* s2, grok_moe_layout weight_layout,
+                        int scale_experts, int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E,
+                        int k, grok_moe_dtype dtype, float* out, const float* router_bias, int32_t* topk_idx,
+                        float* topk_p, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return layer_entry(x, nullptr, nullptr, 0.0, router_w, w1, wv, w2, s1, sv, s2, weight_layout, scale_experts,
+                     groups_up, groups_down, T, d, f, E, k, dtype, out, router_bias, topk_idx, topk_p, expert_counts,
+                     workspace, workspace_bytes, stream);
 }
 
 int grok_moe_forward(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
                      const void* s1, const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k,
-                     int dtype, float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
-  return grok_moe_forward_ex(x, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, E, 1, 1, T, d, f, E, k, dtype,
-                             out, router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
-}
-
-int grok_moe_forward_w8_grouped(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
-                                const void* s1, const void* sv, const void* s2, int scale_experts, int groups_up,
-                                int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, float* out,
-                                const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  return grok_moe_forward_ex(x, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, scale_experts, groups_up,
-                             groups_down, T, d, f, E, k, GROK_MOE_W8, out, router_bias, topk_idx, topk_p,
-                             expert_counts, workspace, workspace_bytes, stream);
+                     grok_moe_dtype dtype, float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return layer_entry(x, nullptr, nullptr, 0.0, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, E, 1, 1, T, d, f,
+                     E, k, dtype, out, router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes,
+                     stream);
 }
 
 int grok_moe_route(const void* x, const void* router_w, const float* router_bias, int64_t T, int64_t d, int E, int k,
-                   int dtype, int32_t* topk_idx, float* topk_p, void* stream) {
+                   grok_moe_dtype dtype, int32_t* topk_idx, float* topk_p, hipStream_t stream) {
   int st = check_shape(T, d, dtype == GROK_MOE_F32 ? 64 : 256, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(router_w) || !ok_ptr(topk_idx) || !ok_ptr(topk_p) || !ok_opt(router_bias))
     return GROK_MOE_EINVAL;
   return hip_status(gm::launch_router(x, router_w, router_bias, int(T), int(d), E, dtype != GROK_MOE_F32, topk_idx,
-                                      topk_p, static_cast<hipStream_t>(stream)));
+                                      topk_p, stream));
 }
 
 int grok_moe_bin(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
-                 int32_t* inv, void* stream) {
+                 int32_t* inv, hipStream_t stream) {
   if (T < 0) return GROK_MOE_EINVAL;
   if (k != 2 || E < 2 || E > 64 || T > kMaxTokens) return GROK_MOE_EUNSUPPORTED;
   if (!ok_ptr(counts) || !ok_ptr(offsets)) return GROK_MOE_EINVAL;
   if (T > 0 && (!ok_ptr(topk_idx) || !ok_ptr(perm) || !ok_ptr(inv))) return GROK_MOE_EINVAL;
-  return hip_status(gm::launch_bin(topk_idx, int(T), E, counts, offsets, perm, inv, static_cast<hipStream_t>(stream)));
+  return hip_status(gm::launch_bin(topk_idx, int(T), E, counts, offsets, perm, inv, stream));
 }
 
-int grok_moe_expert_up_ex(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
-                          int weight_layout, int scale_experts, int groups_up, const int32_t* counts,
-                          const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k,
-                          int dtype, void* h, void* stream) {
+int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
+                       grok_moe_layout weight_layout, int scale_experts, int groups_up, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k,
+                       grok_moe_dtype dtype, void* h, hipStream_t stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
   if (T > max_pass_tokens(d, f, dtype)) return GROK_MOE_EUNSUPPORTED;  // one pass only (32-bit offsets)
-  if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
-  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
-  if (dtype == GROK_MOE_W8) {
-    sp.experts = scale_experts;
-    sp.g_up = groups_up;
-    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
-  }
+  ScaleSpec sp;
+  if ((st = make_spec(weight_layout, scale_experts, groups_up, 1, d, f, E, dtype, &sp)) != GROK_MOE_OK) return st;
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(w1) || !ok_ptr(wv) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(perm) || !ok_ptr(h))
     return GROK_MOE_EINVAL;
   if ((st = check_scales(dtype, s1, sv, dtype == GROK_MOE_W8 ? s1 : nullptr)) != GROK_MOE_OK) return st;
   const Plan p = make_plan(T, d, f, E, dtype);
-  return hip_status(do_up(x, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h,
-                          static_cast<hipStream_t>(stream)));
+  return hip_status(do_up(x, w1, wv, s1, sv, sp, counts, offsets, perm, p, d, f, E, dtype, h, stream));
 }
 
-int grok_moe_expert_up(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
-                       const int32_t* counts, const int32_t* offsets, const int32_t* perm, int64_t T, int64_t d,
-                       int64_t f, int E, int k, int dtype, void* h, void* stream) {
-  return grok_moe_expert_up_ex(x, w1, wv, s1, sv, GROK_MOE_IN_OUT, E, 1, counts, offsets, perm, T, d, f, E, k, dtype,
-                               h, stream);
-}
-
-int grok_moe_expert_up_w8_grouped(const void* x, const void* w1, const void* wv, const void* s1, const void* sv,
-                                  int scale_experts, int groups_up, const int32_t* counts, const int32_t* offsets,
-                                  const int32_t* perm, int64_t T, int64_t d, int64_t f, int E, int k, void* h,
-                                  void* stream) {
-  return grok_moe_expert_up_ex(x, w1, wv, s1, sv, GROK_MOE_IN_OUT, scale_experts, groups_up, counts, offsets, perm,
-                               T, d, f, E, k, GROK_MOE_W8, h, stream);
-}
-
-int grok_moe_expert_down_ex(const void* h, const void* w2, const void* s2, int weight_layout, int scale_experts,
-                            int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T, int64_t d,
-                            int64_t f, int E, int k, int dtype, int splits, float* y, void* stream) {
+int grok_moe_expert_down(const void* h, const void* w2, const void* s2, grok_moe_layout weight_layout,
+                         int scale_experts, int groups_down, const int32_t* counts, const int32_t* offsets,
+                         int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype, int splits, float* y,
+                         hipStream_t stream) {
   int st = check_shape(T, d, f, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
   if (T > max_pass_tokens(d, f, dtype)) return GROK_MOE_EUNSUPPORTED;  // one pass only (32-bit offsets)
-  if (!ok_layout(weight_layout)) return GROK_MOE_EINVAL;
-  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
-  if (dtype == GROK_MOE_W8) {
-    sp.experts = scale_experts;
-    sp.g_down = groups_down;
-    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
-  }
+  ScaleSpec sp;
+  if ((st = make_spec(weight_layout, scale_experts, 1, groups_down, d, f, E, dtype, &sp)) != GROK_MOE_OK) return st;
   const Plan p = make_plan(T, d, f, E, dtype);
   if (splits != p.splits) return GROK_MOE_EINVAL;
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(h) || !ok_ptr(w2) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(y)) return GROK_MOE_EINVAL;
   if (dtype == GROK_MOE_W8 ? !ok_ptr(s2) : s2 != nullptr) return GROK_MOE_EINVAL;
-  return hip_status(do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, dtype, y, static_cast<hipStream_t>(stream)));
-}
-
-int grok_moe_expert_down(const void* h, const void* w2, const void* s2, const int32_t* counts, const int32_t* offsets,
-                         int64_t T, int64_t d, int64_t f, int E, int k, int dtype, int splits, float* y, void* stream) {
-  return grok_moe_expert_down_ex(h, w2, s2, GROK_MOE_IN_OUT, E, 1, counts, offsets, T, d, f, E, k, dtype, splits, y,
-                                 stream);
-}
-
-int grok_moe_expert_down_w8_grouped(const void* h, const void* w2, const void* s2, int scale_experts,
-                                    int groups_down, const int32_t* counts, const int32_t* offsets, int64_t T,
-                                    int64_t d, int64_t f, int E, int k, int splits, float* y, void* stream) {
-  return grok_moe_expert_down_ex(h, w2, s2, GROK_MOE_IN_OUT, scale_experts, groups_down, counts, offsets, T, d, f, E,
-                                 k, GROK_MOE_W8, splits, y, stream);
+  return hip_status(do_down(h, w2, s2, sp, counts, offsets, p, d, f, E, dtype, y, stream));
 }
 
 int grok_moe_combine(const float* y, int splits, const float* topk_p, const int32_t* inv, int64_t T, int64_t d, int k,
-                     float* out, void* stream) {
+                     float* out, hipStream_t stream) {
   if (T < 0 || d <= 0 || splits < 1 || splits > 64) return GROK_MOE_EINVAL;
   if (k != 2 || T > kMaxTokens || d % 4 != 0) return GROK_MOE_EUNSUPPORTED;
   if (T == 0) return GROK_MOE_OK;
   if (!ok_ptr(y) || !ok_ptr(topk_p) || !ok_ptr(inv) || !ok_ptr(out)) return GROK_MOE_EINVAL;
-  return hip_status(gm::launch_combine(y, splits, topk_p, inv, int(T), int(d), out, static_cast<hipStream_t>(stream)));
+  return hip_status(gm::launch_combine(y, splits, topk_p, inv, int(T), int(d), out, stream));
 }
 
-size_t grok_moe_block_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, int dtype) {
+size_t grok_moe_block_workspace_size(int64_t T, int64_t d, int64_t f, int E, int k, grok_moe_dtype dtype) {
   if (check_shape(T, d, f, E, k, dtype) != GROK_MOE_OK || T == 0) return 0;
   return workspace_need(T, d, f, E, dtype, true);
 }
 
+int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,
+                           const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
+                           const void* sv, const void* s2, grok_moe_layout weight_layout, int scale_experts,
+                           int groups_up, int groups_down, int64_t T, int64_t d, int64_t f, int E, int k,
+                           grok_moe_dtype dtype, float* out, const float* router_bias, int32_t* topk_idx,
+                           float* topk_p, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (pre_scale == nullptr || post_scale == nullptr) return GROK_MOE_EINVAL;
+  return layer_entry(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv, s2, weight_layout, scale_experts,
+                     groups_up, groups_down, T, d, f, E, k, dtype, out, router_bias, topk_idx, topk_p, expert_counts,
+                     workspace, workspace_bytes, stream);
+}
+
 int grok_moe_route_norm(const void* x, const void* pre_scale, double eps, const void* router_w,
-                        const float* router_bias, int64_t T, int64_t d, int E, int k, int dtype, void* xn,
-                        int32_t* topk_idx, float* topk_p, void* stream) {
+                        const float* router_bias, int64_t T, int64_t d, int E, int k, grok_moe_dtype dtype, void* xn,
+                        int32_t* topk_idx, float* topk_p, hipStream_t stream) {
   int st = check_shape(T, d, dtype == GROK_MOE_F32 ? 64 : 256, E, k, dtype);
   if (st != GROK_MOE_OK) return st;
   if (!(eps >= 0.0)) return GROK_MOE_EINVAL;
@@ -439,13 +432,12 @@ int grok_moe_route_norm(const void* x, const void* pre_scale, double eps, const 
       !ok_opt(router_bias))
     return GROK_MOE_EINVAL;
   return hip_status(gm::launch_router_norm(x, pre_scale, eps, router_w, router_bias, int(T), int(d), E,
-                                           dtype != GROK_MOE_F32, xn, topk_idx, topk_p,
-                                           static_cast<hipStream_t>(stream)));
+                                           dtype != GROK_MOE_F32, xn, topk_idx, topk_p, stream));
 }
 
 int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const int32_t* inv, const void* x,
-                          const void* post_scale, double eps, int64_t T, int64_t d, int k, int dtype, float* out,
-                          void* stream) {
+                          const void* post_scale, double eps, int64_t T, int64_t d, int k, grok_moe_dtype dtype,
+                          float* out, hipStream_t stream) {
   if (T < 0 || d <= 0 || splits < 1 || splits > 64 || !(eps >= 0.0)) return GROK_MOE_EINVAL;
   if (dtype != GROK_MOE_F32 && dtype != GROK_MOE_BF16 && dtype != GROK_MOE_W8) return GROK_MOE_EINVAL;
   if (k != 2 || T > kMaxTokens || d % 4 != 0) return GROK_MOE_EUNSUPPORTED;
@@ -453,43 +445,7 @@ int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const
   if (!ok_ptr(y) || !ok_ptr(topk_p) || !ok_ptr(inv) || !ok_ptr(x) || !ok_ptr(post_scale) || !ok_ptr(out))
     return GROK_MOE_EINVAL;
   return hip_status(gm::launch_combine_norm(y, splits, topk_p, inv, int(T), int(d), x, dtype != GROK_MOE_F32,
-                                            post_scale, eps, out, static_cast<hipStream_t>(stream)));
-}
-
-int grok_moe_block_forward_ex(const void* x, const void* pre_scale, const void* post_scale, double eps,
-                              const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
-                              const void* sv, const void* s2, int weight_layout, int scale_experts, int groups_up,
-                              int groups_down, int64_t T, int64_t d, int64_t f, int E, int k, int dtype, float* out,
-                              const float* router_bias, int32_t* topk_idx, float* topk_p, int32_t* expert_counts,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_shape(T, d, f, E, k, dtype);
-  if (st != GROK_MOE_OK) return st;
-  if (!(eps >= 0.0) || !ok_layout(weight_layout)) return GROK_MOE_EINVAL;
-  ScaleSpec sp{E, 1, 1, weight_layout == GROK_MOE_OUT_IN};
-  if (dtype == GROK_MOE_W8) {
-    sp.experts = scale_experts;
-    sp.g_up = groups_up;
-    sp.g_down = groups_down;
-    if ((st = check_groups(sp, d, f, E)) != GROK_MOE_OK) return st;
-  }
-  if (T == 0) return GROK_MOE_OK;
-  if (!ok_ptr(x) || !ok_ptr(pre_scale) || !ok_ptr(post_scale) || !ok_ptr(router_w) || !ok_ptr(w1) || !ok_ptr(wv) ||
-      !ok_ptr(w2) || !ok_ptr(out))
-    return GROK_MOE_EINVAL;
-  if (!ok_opt(router_bias) || !ok_opt(topk_idx) || !ok_opt(topk_p) || !ok_opt(expert_counts)) return GROK_MOE_EINVAL;
-  if ((st = check_scales(dtype, s1, sv, s2)) != GROK_MOE_OK) return st;
-  return run_layer(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv, s2, sp, T, d, f, E, dtype, out,
-                   router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
-}
-
-int grok_moe_block_forward(const void* x, const void* pre_scale, const void* post_scale, double eps,
-                           const void* router_w, const void* w1, const void* wv, const void* w2, const void* s1,
-                           const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E, int k, int dtype,
-                           float* out, const float* router_bias, int32_t* topk_idx, float* topk_p,
-                           int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
-  return grok_moe_block_forward_ex(x, pre_scale, post_scale, eps, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, E,
-                                   1, 1, T, d, f, E, k, dtype, out, router_bias, topk_idx, topk_p, expert_counts,
-                                   workspace, workspace_bytes, stream);
+                                            post_scale, eps, out, stream));
 }
 
 }  // extern "C"

@@ -77,8 +77,13 @@ def test_long_batches_run_in_passes(L):
     assert gm.workspace_size(50000, d, f) == gm.workspace_size(12500, d, f)     # four passes
     assert gm.block_workspace_size(20000, d, f) == gm.block_workspace_size(10000, d, f)
     assert gm.down_splits(20000, d, f) == 2
-    # int8 and fp32 layers address with 64-bit offsets: one pass
-    assert gm.workspace_size(20000, d, f, 8, 2, gm.W8) > gm.workspace_size(10000, d, f, 8, 2, gm.W8)
+    # int8 layers run their tiled kernels on the same 32-bit offsets into x and h: the same passes as bf16
+    assert gm.workspace_size(16383, d, f, 8, 2, gm.W8) > gm.workspace_size(16382, d, f, 8, 2, gm.W8)
+    assert gm.workspace_size(16384, d, f, 8, 2, gm.W8) == gm.workspace_size(8192, d, f, 8, 2, gm.W8)
+    assert gm.workspace_size(20000, d, f, 8, 2, gm.W8) == gm.workspace_size(10000, d, f, 8, 2, gm.W8)
+    assert gm.down_splits(20000, d, f, 8, 2, gm.W8) == 1
+    # the fp32 layer addresses with 64-bit offsets: one pass
+    assert gm.workspace_size(20000, 1024, 1024, 8, 2, gm.F32) > gm.workspace_size(10000, 1024, 1024, 8, 2, gm.F32)
     # the limit comes from h [2 T, f] (and from x [T, d] when d is large)
     assert gm.workspace_size(2047, 256, 1 << 18) > gm.workspace_size(2046, 256, 1 << 18)  # P = 2047: one pass
     assert gm.workspace_size(2048, 256, 1 << 18) == gm.workspace_size(1024, 256, 1 << 18)
@@ -88,11 +93,14 @@ def test_long_batches_run_in_passes(L):
     assert gm.workspace_size(8, 1 << 20, 1 << 11) == 0
     # the expert steps take one pass at most (rejected on the host, before any pointer is read)
     fake = ctypes.c_void_p(0x100000)
-    assert L.grok_moe_expert_up(fake, fake, fake, None, None, fake, fake, fake, 16384, d, f, 8, 2, 1, fake,
-                                None) == -2
-    assert L.grok_moe_expert_up(fake, fake, fake, None, None, fake, fake, None, 16383, d, f, 8, 2, 1, fake,
-                                None) == -1
-    assert L.grok_moe_expert_down(fake, fake, None, fake, fake, 16384, d, f, 8, 2, 1, 2, fake, None) == -2
+    for dt in (1, 2):  # bf16, int8
+        sc = None if dt == 1 else fake
+        assert L.grok_moe_expert_up(fake, fake, fake, sc, sc, 0, 8, 1, fake, fake, fake, 16384, d, f, 8, 2, dt, fake,
+                                    None) == -2
+        assert L.grok_moe_expert_up(fake, fake, fake, sc, sc, 0, 8, 1, fake, fake, None, 16383, d, f, 8, 2, dt, fake,
+                                    None) == -1
+        assert L.grok_moe_expert_down(fake, fake, sc, 0, 8, 1, fake, fake, 16384, d, f, 8, 2, dt, 1 if dt == 2 else 2,
+                                      fake, None) == -2
 
 
 def _fwd(L, **kw):
@@ -131,9 +139,16 @@ def test_step_entry_points_reject_bad_arguments_on_host(L):
     assert L.grok_moe_route(fake, fake, None, 8, 256, 8, 3, 1, fake, fake, None) == -2
     assert L.grok_moe_bin(fake, -1, 8, 2, fake, fake, fake, fake, None) == -1
     assert L.grok_moe_bin(fake, 8, 99, 2, fake, fake, fake, fake, None) == -2
-    assert L.grok_moe_expert_up(fake, fake, fake, None, None, fake, fake, None, 8, 256, 512, 8, 2, 1, fake, None) == -1
+    assert L.grok_moe_expert_up(fake, fake, fake, None, None, 0, 8, 1, fake, fake, None, 8, 256, 512, 8, 2, 1, fake,
+                                None) == -1
+    assert L.grok_moe_expert_up(fake, fake, fake, None, None, 2, 8, 1, fake, fake, fake, 8, 256, 512, 8, 2, 1, fake,
+                                None) == -1  # unknown weight layout
     S = L.grok_moe_down_splits(8, 256, 512, 8, 2, 1)
-    assert L.grok_moe_expert_down(fake, fake, None, fake, fake, 8, 256, 512, 8, 2, 1, S + 1, fake, None) == -1
+    assert L.grok_moe_expert_down(fake, fake, None, 0, 8, 1, fake, fake, 8, 256, 512, 8, 2, 1, S + 1, fake,
+                                  None) == -1
+    assert L.grok_moe_block_forward(fake, None, fake, 1e-5, fake, fake, fake, fake, None, None, None, 0, 8, 1, 1, 8,
+                                    256, 512, 8, 2, 1, fake, None, None, None, None, ctypes.c_void_p(0x200000),
+                                    1 << 30, None) == -1  # no pre-norm scale
     assert L.grok_moe_combine(fake, 0, fake, fake, 8, 256, 2, fake, None) == -1
 
 
@@ -145,13 +160,14 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         gm.lib()
 
 
-def _fwd_g(L, se=8, g1=2, g2=4, **kw):
+def _fwd_g(L, se=8, g1=2, g2=4, layout=0, dtype=2, **kw):
     fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
     a = dict(T=8, d=512, f=1024, E=8, k=2, ws_bytes=0)
     a.update(kw)
-    return L.grok_moe_forward_w8_grouped(fake, fake, fake, fake, fake, fake, fake, fake, se, g1, g2, a["T"], a["d"],
-                                         a["f"], a["E"], a["k"], fake, None, None, None, None,
-                                         ctypes.c_void_p(0x200000), a["ws_bytes"], None)
+    sc = fake if dtype == 2 else None
+    return L.grok_moe_forward_ex(fake, fake, fake, fake, fake, sc, sc, sc, layout, se, g1, g2, a["T"], a["d"],
+                                 a["f"], a["E"], a["k"], dtype, fake, None, None, None, None,
+                                 ctypes.c_void_p(0x200000), a["ws_bytes"], None)
 
 
 def test_grouped_scale_layouts_rejected_on_host(L):
@@ -166,13 +182,51 @@ def test_grouped_scale_layouts_rejected_on_host(L):
     assert _fwd_g(L, g1=8, g2=16) == -3       # 64-row groups are accepted
     assert _fwd_g(L, k=3) == -2
     assert _fwd_g(L, T=0) == 0
+    assert _fwd_g(L, layout=1) == -3          # [out, in] weights
+    assert _fwd_g(L, layout=2) == -1          # unknown layout
+    assert _fwd_g(L, se=3, g1=3, dtype=1) == -3   # scale layout ignored for bf16
     fake = ctypes.c_void_p(0x100000)
-    assert L.grok_moe_expert_up_w8_grouped(fake, fake, fake, fake, fake, 8, 3, fake, fake, fake, 8, 512, 1024, 8, 2,
-                                           fake, None) == -2
-    assert L.grok_moe_expert_up_w8_grouped(fake, fake, fake, None, fake, 8, 2, fake, fake, fake, 8, 512, 1024, 8, 2,
-                                           fake, None) == -1
+    assert L.grok_moe_expert_up(fake, fake, fake, fake, fake, 0, 8, 3, fake, fake, fake, 8, 512, 1024, 8, 2, 2,
+                                fake, None) == -2
+    assert L.grok_moe_expert_up(fake, fake, fake, None, fake, 0, 8, 2, fake, fake, fake, 8, 512, 1024, 8, 2, 2,
+                                fake, None) == -1
     S = L.grok_moe_down_splits(8, 512, 1024, 8, 2, 2)
-    assert L.grok_moe_expert_down_w8_grouped(fake, fake, fake, 2, 4, fake, fake, 8, 512, 1024, 8, 2, S, fake,
-                                             None) == -1
-    assert L.grok_moe_expert_down_w8_grouped(fake, fake, fake, 8, 4, fake, fake, 8, 512, 1024, 8, 2, S + 1, fake,
-                                             None) == -1
+    assert L.grok_moe_expert_down(fake, fake, fake, 0, 2, 4, fake, fake, 8, 512, 1024, 8, 2, 2, S, fake,
+                                  None) == -1
+    assert L.grok_moe_expert_down(fake, fake, fake, 0, 8, 4, fake, fake, 8, 512, 1024, 8, 2, 2, S + 1, fake,
+                                  None) == -1
+
+
+def test_export_count(L):
+    """The boundary stays small: the declared entry points and nothing else."""
+    import subprocess
+    import mixture_experts_transformer_gemv_amd as gm
+    r = subprocess.run(["nm", "-D", "--defined-only", gm.LIB_PATH], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("nm not available")
+    exported = sorted({ln.split()[-1] for ln in r.stdout.splitlines() if " T grok_moe" in ln})
+    assert exported == declared_functions()
+    assert len(exported) <= 16
+
+
+def test_probe_library_exports_its_header():
+    """The measurement probes (include/grok_moe_probe.h) load and export every declared function; argument errors
+    are caught on the host."""
+    import mixture_experts_transformer_gemv_amd as gm
+    from mixture_experts_transformer_gemv_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    P = ctypes.CDLL(build.PROBE_LIB)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "grok_moe_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(grok_moe_probe_[a-z_0-9]+)\s*\(", text)))
+    assert len(names) == 4
+    for n in names:
+        assert hasattr(P, n), n
+    f = P.grok_moe_probe_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(ctypes.c_void_p(0x100008), 64, 4, 0, ctypes.c_void_p(0x200000), None) == -1  # misaligned
+    assert f(ctypes.c_void_p(0x100000), 65, 4, 0, ctypes.c_void_p(0x200000), None) == -1  # not a multiple of 16
+    g = P.grok_moe_probe_clock
+    g.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(0, 100, ctypes.c_void_p(0x200000), None) == -1
+    assert gm.LIB_PATH != build.PROBE_LIB

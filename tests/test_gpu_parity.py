@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from tests._helpers import TOL, dev_inputs, dump, rel_err, say
+from tests._helpers import TOL, dev_inputs, dump, rel_err, rms_rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,9 @@ def _forward(gm, dv):
                       router_bias=dv["router_bias"], return_routing=True)
 
 
-def check_layer(gm, w: synth.Workload, inp=None, rows=None, name=None, dv=None):
+def check_layer(gm, w: synth.Workload, inp=None, rows=None, name=None, dv=None, unrounded=False):
+    """The layer through grok_moe_forward against the oracle on `rows` (all rows if None).  unrounded: also log the
+    error against the oracle without the bf16 rounding of h (the plain float64 definition), which has no bar."""
     name = name or w.name
     say(f"[case] {name}: T={w.T} d={w.d} f={w.f} E={w.E} dtype={synth.DTYPE_NAMES[w.dtype]}")
     inp = inp if inp is not None else synth.make_inputs(w)
@@ -47,8 +49,12 @@ def check_layer(gm, w: synth.Workload, inp=None, rows=None, name=None, dv=None):
     err = rel_err(out_g, ref["out"].numpy())
     perr = float(np.max(np.abs(p_g - ref["p"].numpy()) / ref["p"].numpy()))
     say(f"[result] {name}: idx_exact={ok_idx} counts_exact={ok_cnt} counts={cnt_g.tolist()} "
-        f"max_err/rms={err:.3e} (tol {TOL[w.dtype]:.0e}) p_rel_err={perr:.2e} "
-        f"min_gap_cut={ref['min_gap_cut']:.3e}")
+        f"max_err/rms={err:.3e} rms_err/rms={rms_rel_err(out_g, ref['out'].numpy()):.3e} (tol {TOL[w.dtype]:.0e}) "
+        f"p_rel_err={perr:.2e} min_gap_cut={ref['min_gap_cut']:.3e}")
+    if unrounded and w.dtype != F32:
+        plain = oracle.forward(inp, w.dtype, rows=rows, round_h=False)["out"].numpy()
+        say(f"[result] {name}: against the unrounded definition max_err/rms={rel_err(out_g, plain):.3e} "
+            f"rms_err/rms={rms_rel_err(out_g, plain):.3e}")
     if not (ok_idx and ok_cnt and err <= TOL[w.dtype] and perr < 1e-6):
         dump(name, out=out_g, want=ref["out"].numpy(), idx=idx_g, want_idx=ref["idx"].numpy(), p=p_g,
              want_p=ref["p"].numpy(), counts=cnt_g, rows=rows_t)
@@ -293,7 +299,7 @@ def _grok_case(gm, grok_bf16, name):
                           "router_bias": inp["router_bias"]}, BF16)["x"]
     dv["router_bias"] = None if inp["router_bias"] is None else torch.from_numpy(inp["router_bias"]).cuda()
     rows = None if w.sampled_rows is None else synth.sampled_rows(w.T, w.sampled_rows)
-    return check_layer(gm, w, inp=inp, rows=rows, dv=dv), dv
+    return check_layer(gm, w, inp=inp, rows=rows, dv=dv, unrounded=isinstance(name, str)), dv
 
 
 def test_grok_decode_bf16(gm, grok_bf16):
@@ -360,7 +366,7 @@ def _grok_int8_case(gm, grok_int8, T, sampled):
     dv["x"] = dev_inputs({"x": inp["x"], "router_w": inp["router_w"], "w1": None, "wv": None, "w2": None,
                           "s1": None, "sv": None, "s2": None, "router_bias": None}, W8)["x"]
     rows = None if sampled is None else synth.sampled_rows(T, sampled)
-    return check_layer(gm, w, inp=inp, rows=rows, dv=dv)
+    return check_layer(gm, w, inp=inp, rows=rows, dv=dv, unrounded=T == 64)
 
 
 def test_grok_int8(gm, grok_int8):
