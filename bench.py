@@ -1,23 +1,37 @@
 #!/usr/bin/env python3
-"""Throughput of the Grok-1 MoE FFN layer forward on one MI355X.
+"""Throughput of the Grok-1 MoE FFN layer forward on one MI355X, on every workload of the layer.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs LIST | --configs none]
                     [--workload decode_bf16|prefill_bf16|int8_w8|int8_w8_g8|skew_bf16|tiny_f32]
-                    [--weight-layout in_out|out_in] [--block] [--no-prefill] [--no-cpu-baseline]
+                    [--weight-layout in_out|out_in] [--block] [--tokens T] [--d-ff F]
+                    [--no-parity] [--no-cpu-baseline] [--no-ceilings]
     python bench.py --library-gemm      (torch.mm / hipBLASLt on the prefill's per-expert shapes, for context)
 
 A step is one pass of the whole layer (router, binning, fused up-projection with GELU product, down-projection,
-combine) over one batch of seeded synthetic tokens, with weights and inputs already resident in HBM.  The step
-calls the library's five step entry points in order (bit-identical to grok_moe_forward) on the current stream,
-so that HIP events can time the expert kernels inside the timed region.  Prints one JSON line.
+combine) over one batch of seeded synthetic tokens, with weights and inputs already resident in HBM.  The timed
+step calls the library's five step entry points in order (bit-identical to grok_moe_forward) on the current
+stream, so that HIP events on that stream time each kernel inside the timed region; the whole-layer entry point
+grok_moe_forward is timed as well ("entry_point_ms_per_step").
 
-The default workload is the Grok-1-shape decode step (T=8, d=6144, f=32768, E=8, top-2, bf16).  Unless
---no-prefill is given, the same run also times the T=8192 prefill on the same weights and reports it under
-"prefill".  The CPU oracle is timed on a bounded sample of the same workload ("cpu_baseline").
+The headline workload (--workload, default the Grok-1-shape decode step T=8, d=6144, f=32768, E=8, top-2, bf16)
+is timed for exactly --steps steps after --warmup untimed ones; its numbers are the top-level fields.  The other
+workloads of the layer (--configs, default all: prefill T=8192, skewed routing T=4096, int8 weights T=64, tiny
+fp32) follow under "configs", each with its own step count.  For every workload the same run reports:
+  * tokens/s, per-step median/min/p90, the per-kernel times and the roofline of the dominant kernel (HBM GB/s or
+    MFMA TFLOP/s against the published peaks and the measured ceilings), the shader clock during extra untimed
+    steps (a sampler kernel beside them), and the per-expert token counts;
+  * parity of that run's output against the CPU oracle (tests-only code, run here only as the check and the CPU
+    baseline): routing indices and counts bit for bit, max|gpu - oracle| / rms(oracle) on every row (256 seeded
+    rows for prefill and skewed routing), and the same against the oracle without the bf16 rounding of h;
+  * the oracle's own time on those rows (routing of all T tokens timed separately), on this host's cores.
+"ceilings" holds the practical limits measured by the probe library: a streaming HBM read and dense bf16 MFMA on
+random register operands (result checked), with the clock it ran at.  One JSON line on stdout.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -33,6 +47,9 @@ METRIC = "Grok-1 MoE layer tokens/s (T=8 decode, T=8192 prefill); % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_VALU_TFLOPS = 157.3       # MI355X fp32 vector ALU (published)
+CONFIG_STEPS = {"decode_bf16": 50, "prefill_bf16": 10, "skew_bf16": 10, "int8_w8": 50, "int8_w8_g8": 50,
+                "tiny_f32": 100}
+ALL_CONFIGS = ("decode_bf16", "prefill_bf16", "skew_bf16", "int8_w8", "tiny_f32")
 
 
 def log(msg):
@@ -52,10 +69,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode_bf16")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the companion T=8192 prefill measurement")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-steps", type=int, default=10, help="timed prefill steps (0: no prefill, as --no-prefill)")
+    ap.add_argument("--workload", default="decode_bf16", help="the headline workload (top-level fields)")
+    ap.add_argument("--configs", default="all",
+                    help="comma-separated workloads reported under 'configs' besides the headline one, 'all' "
+                         f"({', '.join(ALL_CONFIGS)}) or 'none'")
+    ap.add_argument("--config-steps", type=int, default=0, help="timed steps of every config (0: their defaults)")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle check (and the CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the single-thread oracle timing")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the HBM-read and MFMA ceiling probes")
     ap.add_argument("--block", action="store_true",
                     help="time the MoE block (pre-MoE RMSNorm, MoE, post-MoE RMSNorm, residual) instead of the layer")
     ap.add_argument("--weight-layout", choices=["in_out", "out_in"], default="in_out",
@@ -63,28 +84,26 @@ def parse():
     ap.add_argument("--library-gemm", action="store_true",
                     help="only time torch.matmul (hipBLASLt) bf16 on the prefill's per-expert GEMM shapes, for context")
     ap.add_argument("--tokens", type=int, default=0,
-                    help="run the workload at this many tokens instead of its own T (e.g. int8_w8 at 8192)")
+                    help="run the headline workload at this many tokens instead of its own T (e.g. int8_w8 at 8192)")
     ap.add_argument("--d-ff", type=int, default=0,
-                    help="run the workload at this d_ff instead of its own (e.g. 4096: one GPU's share of a layer "
-                         "split over 8 GPUs along d_ff)")
+                    help="run the headline workload at this d_ff instead of its own (e.g. 4096: one GPU's share of a "
+                         "layer split over 8 GPUs along d_ff)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     a = ap.parse_args()
-    if a.steps < 1 or a.warmup < 0 or a.prefill_steps < 0 or a.tokens < 0 or a.d_ff < 0:
-        ap.error("--steps must be >= 1; --warmup, --prefill-steps, --tokens and --d-ff >= 0")
+    if a.steps < 1 or a.warmup < 0 or a.tokens < 0 or a.d_ff < 0 or a.config_steps < 0:
+        ap.error("--steps must be >= 1; --warmup, --tokens, --d-ff and --config-steps >= 0")
     return a
 
+
+# ------------------------------------------------------------------------------------------------ the timed step
 
 class Layer:
     """Device-resident inputs and preallocated buffers of one workload, and the timed step."""
 
-    def __init__(self, gm, w, inp, dv, norms=None, weight_layout="in_out", transpose=True):
+    def __init__(self, gm, w, inp, dv, norms=None, weight_layout="in_out"):
         import torch
-        self.outin = weight_layout == "out_in"
-        if self.outin and transpose:  # the same weights stored [E, out, in] (transposed on the device, untimed)
-            dv = dict(dv)
-            for n in ("w1", "wv", "w2"):
-                dv[n] = dv[n].transpose(1, 2).contiguous()
+        self.outin = weight_layout == "out_in"  # dv holds the weights in this storage already
         self.gm, self.w, self.inp, self.dv = gm, w, inp, dv
         self.norms = norms  # (pre_scale, post_scale, eps) device tensors for the block form
         T, d, f, E = w.T, w.d, w.f, w.E
@@ -102,22 +121,23 @@ class Layer:
         self.out = torch.empty((T, d), dtype=torch.float32, device=dev)
         self.xn = torch.empty_like(dv["x"]) if norms is not None else None
         self.s1 = self.sv = self.s2 = None
-        self.grouped = None  # (scale_experts, groups_up, groups_down) of grouped int8 scales
+        self.scale_spec = (E, 1, 1)  # (scale_experts, groups_up, groups_down)
         if dv["scales"] is not None:
             self.s1, self.sv, self.s2 = dv["scales"]
             es = E if w.scale_experts is None else w.scale_experts
-            if (es, w.groups_up, w.groups_down) != (E, 1, 1):
-                self.grouped = (es, w.groups_up, w.groups_down)
-        mk = lambda: torch.cuda.Event(enable_timing=True)
-        self.ev = [mk() for _ in range(6)]
+            self.scale_spec = (es, w.groups_up, w.groups_down)
         self.lib = gm.lib()
+        mk = lambda: torch.cuda.Event(enable_timing=True)
+        self.ev = [mk() for _ in range(5)]
 
     def step(self, timed=False):
-        import ctypes
-        gm, dv, L, w = self.gm, self.dv, self.lib, self.w
+        import torch
+        dv, L, w = self.dv, self.lib, self.w
         P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-        s = ctypes.c_void_p(__import__("torch").cuda.current_stream().cuda_stream)
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         T, d, f, E, dt = w.T, w.d, w.f, w.E, w.dtype
+        lay = 1 if self.outin else 0
+        es, g1, g2 = self.scale_spec
         ev = self.ev
         if timed:
             ev[0].record()
@@ -132,30 +152,12 @@ class Layer:
         st |= L.grok_moe_bin(P(self.idx), T, E, 2, P(self.counts), P(self.offsets), P(self.perm), P(self.inv), s)
         if timed:
             ev[1].record()
-        es, g1, g2 = self.grouped if self.grouped is not None else (E, 1, 1)
-        if self.outin:
-            st |= L.grok_moe_expert_up_ex(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), 1, es, g1,
-                                          P(self.counts), P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h),
-                                          s)
-        elif self.grouped is None:
-            st |= L.grok_moe_expert_up(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), P(self.counts),
-                                       P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
-        else:
-            st |= L.grok_moe_expert_up_w8_grouped(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv),
-                                                  self.grouped[0], self.grouped[1], P(self.counts), P(self.offsets),
-                                                  P(self.perm), T, d, f, E, 2, P(self.h), s)
+        st |= L.grok_moe_expert_up(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), lay, es, g1,
+                                   P(self.counts), P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
         if timed:
             ev[2].record()
-        if self.outin:
-            st |= L.grok_moe_expert_down_ex(P(self.h), P(dv["w2"]), P(self.s2), 1, es, g2, P(self.counts),
-                                            P(self.offsets), T, d, f, E, 2, dt, self.S, P(self.y), s)
-        elif self.grouped is None:
-            st |= L.grok_moe_expert_down(P(self.h), P(dv["w2"]), P(self.s2), P(self.counts), P(self.offsets), T, d,
-                                         f, E, 2, dt, self.S, P(self.y), s)
-        else:
-            st |= L.grok_moe_expert_down_w8_grouped(P(self.h), P(dv["w2"]), P(self.s2), self.grouped[0],
-                                                    self.grouped[2], P(self.counts), P(self.offsets), T, d, f, E, 2,
-                                                    self.S, P(self.y), s)
+        st |= L.grok_moe_expert_down(P(self.h), P(dv["w2"]), P(self.s2), lay, es, g2, P(self.counts),
+                                     P(self.offsets), T, d, f, E, 2, dt, self.S, P(self.y), s)
         if timed:
             ev[3].record()
         if self.norms is None:
@@ -167,6 +169,17 @@ class Layer:
             ev[4].record()
         if st != 0:
             raise RuntimeError(f"library call failed (status bits {st})")
+
+    def forward_entry(self):
+        """The whole layer through the binding's entry point (grok_moe_forward, or its general form)."""
+        gm, dv = self.gm, self.dv
+        lay = gm.OUT_IN if self.outin else gm.IN_OUT
+        if self.norms is None:
+            return gm.forward(dv["x"], dv["router_w"], dv["w1"], dv["wv"], dv["w2"], scales=dv["scales"],
+                              router_bias=dv["router_bias"], return_routing=True, weight_layout=lay)
+        return gm.block_forward(dv["x"], self.norms[0], self.norms[1], self.norms[2], dv["router_w"], dv["w1"],
+                                dv["wv"], dv["w2"], scales=dv["scales"], router_bias=dv["router_bias"],
+                                return_routing=True, weight_layout=lay)
 
     def run_with_kernel_times(self, steps, warmup):
         """Time `steps` steps (wall, bracketed by synchronize) and the average per-launch duration of each expert
@@ -190,9 +203,22 @@ class Layer:
                            "p90": float(np.percentile(per_step, 90)), "n": int(steps)}
         return wall, k.mean(axis=0)  # ms: up, down, route+bin, combine
 
+    def time_entry_point(self, steps):
+        """ms per call of the whole-layer entry point (allocations of its outputs included)."""
+        import torch
+        self.forward_entry()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.forward_entry()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
 
-def n_hit(layer) -> int:
-    return int((layer.counts.cpu().numpy() > 0).sum())
+
+# ------------------------------------------------------------------------------------------------ rooflines
+
+def n_hit(counts) -> int:
+    return int((np.asarray(counts) > 0).sum())
 
 
 def up_bytes(w, nh, T):
@@ -231,39 +257,325 @@ def load_traffic(workload: str, kernel: str):
         return None
 
 
-def cpu_baseline(w, inp, oracle, synth, block=False):
-    """The oracle as it stands, on a bounded sample of the workload (routing for all tokens, expert path on a few
-    rows), timed on this host's cores; and the same for one row on a single thread."""
-    import torch
+def stream_path(w) -> bool:
+    return w.dtype != 0 and w.T <= (128 if w.dtype == 2 else 96)
 
-    def run(rows):
-        t0 = time.perf_counter()
-        if block:
-            ns = synth.make_norm_scales(w)
-            oracle.block_forward(inp, w.dtype, ns["pre_scale"], ns["post_scale"], ns["eps"], rows=rows)
+
+def roofline(w, layer, kms, ms, weight_layout, ceilings):
+    """Roofline of the dominant kernel (the up-projection) and the per-kernel rates."""
+    T, nh = w.T, n_hit(layer.counts.cpu().numpy())
+    oi = weight_layout == "out_in"
+    tname = w.name + ("_out_in" if oi else "")
+    kernels = {"expert_up_ms": kms[0], "expert_down_ms": kms[1], "route_bin_ms": kms[2], "combine_ms": kms[3]}
+    if w.dtype == 0:  # the fp32 layer: vector-ALU kernels (tiny shapes: launch latency in practice)
+        fl = up_flops(w, T)
+        ach = fl / (kms[0] * 1e-3) / 1e12
+        rl = {"bound": "alu", "kernel": "f32_tiled_kernel<2>", "achieved": ach, "peak": FP32_VALU_TFLOPS,
+              "unit": "TFLOP/s", "frac": ach / FP32_VALU_TFLOPS, "traffic": None, "algorithmic_flops": fl}
+    elif stream_path(w):  # weight-streaming kernels: HBM-bound
+        ub = up_bytes(w, nh, T)
+        ach = ub / (kms[0] * 1e-3) / 1e9
+        rl = {"bound": "hbm", "kernel": "oi_stream_kernel<2>" if oi else "up_stream_kernel", "achieved": ach,
+              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+              "traffic": load_traffic(tname, "up"), "algorithmic_bytes": ub}
+        if ceilings and ceilings.get("hbm_read_GBps"):
+            rl["frac_of_measured_read_ceiling"] = ach / ceilings["hbm_read_GBps"]
+        db = down_bytes(w, nh, T, layer.S)
+        kernels["expert_up_GBps"] = ach
+        kernels["expert_down_GBps"] = db / (kms[1] * 1e-3) / 1e9
+        kernels["layer_GBps"] = (ub + db) / (ms * 1e-3) / 1e9
+    else:  # LDS-tiled grouped GEMMs: MFMA-bound
+        fl = up_flops(w, T)
+        ach = fl / (kms[0] * 1e-3) / 1e12
+        grouped = w.groups_up > 1 or w.groups_down > 1
+        if w.dtype == 1 or (not grouped and not oi):
+            kname = (f"tiled_dma_kernel<2, {str(oi).lower()}, {'true' if w.dtype == 2 else 'false'}, 256> + "
+                     "tiled_dma_small_kernel")
+        elif grouped and not oi and w.groups_up <= 8:
+            kname = "tiled_dma_grouped_kernel<2>"
         else:
-            oracle.forward(inp, w.dtype, rows=rows)
-        return time.perf_counter() - t0
+            kname = f"tiled_reg_kernel<2, {'true' if grouped else 'false'}, {str(oi).lower()}>"
+        rl = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": ach / BF16_PEAK_TFLOPS, "traffic": load_traffic(tname, "up"), "algorithmic_flops": fl}
+        if ceilings and ceilings.get("mfma_sustained_TFLOPs"):
+            rl["frac_of_measured_mfma_ceiling"] = ach / ceilings["mfma_sustained_TFLOPs"]
+        kernels["expert_up_TFLOPs"] = ach
+        kernels["expert_down_TFLOPs"] = fl / 2 / (kms[1] * 1e-3) / 1e12
+        kernels["layer_TFLOPs"] = 3 * fl / 2 / (ms * 1e-3) / 1e12
+    return rl, kernels
 
-    # up to 8 seeded rows (every row of the decode batch), passes repeated until about 10 s of CPU work
-    rows = synth.sampled_rows(w.T, min(w.T, 8))
-    threads = torch.get_num_threads()
-    dt, reps = 0.0, 0
-    while reps < 20 and (reps == 0 or dt < 10.0):
-        dt += run(rows)
-        reps += 1
-    res = {"value": reps * len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-           "sample": f"{len(rows)} of {w.T} token rows of {w.name} through the float64 oracle (routing on all "
-                     f"{w.T} tokens, both selected experts per row), {reps} passes, {dt:.1f} s"}
-    torch.set_num_threads(1)
-    try:
-        dt1 = run(rows[:1])
-    finally:
-        torch.set_num_threads(threads)
-    res["single_thread"] = {"value": 1 / dt1, "unit": "tokens/s", "cores": 1,
-                            "sample": f"1 token row of {w.name} (routing on all {w.T} tokens), {dt1:.1f} s"}
+
+# ------------------------------------------------------------------------------------------------ probes
+
+class Probe:
+    """The measurement probes of libgrokmoe_probe.so (include/grok_moe_probe.h)."""
+
+    def __init__(self, gm):
+        path = os.path.join(os.path.dirname(gm.LIB_PATH), "libgrokmoe_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build with `python -m mixture_experts_transformer_gemv_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i, u64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
+        for name, args in (("grok_moe_probe_read", [vp, sz, i, i, vp, vp]),
+                           ("grok_moe_probe_mfma", [vp, i, vp, vp, vp]),
+                           ("grok_moe_probe_clock", [i, u64, vp, vp]),
+                           ("grok_moe_probe_wall_clock_khz", [])):
+            fn = getattr(L, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = args
+        self.L = L
+        self.wall_khz = L.grok_moe_probe_wall_clock_khz() or 100000
+
+    def ghz(self, clocks: np.ndarray) -> float:
+        c = clocks.reshape(-1, 4).astype(np.float64)
+        dc, dw = (c[:, 1] - c[:, 0]).sum(), (c[:, 3] - c[:, 2]).sum()
+        return float(dc / dw * self.wall_khz * 1e3 / 1e9) if dw > 0 else float("nan")
+
+    def clock_during(self, run, expected_ms: float) -> float | None:
+        """Shader clock (GHz) read by 8 single-wave sampler workgroups (one per XCD) on a second stream while
+        run() enqueues work on the current one, over 60% of the work's expected duration."""
+        import torch
+        out = torch.zeros(8 * 4, dtype=torch.int64, device="cuda")
+        side = torch.cuda.Stream()
+        ticks = int(0.6 * expected_ms * 1e-3 * self.wall_khz * 1e3)
+        if ticks < 1000:
+            return None
+        torch.cuda.synchronize()
+        run()
+        with torch.cuda.stream(side):
+            st = self.L.grok_moe_probe_clock(8, ticks, ctypes.c_void_p(out.data_ptr()),
+                                             ctypes.c_void_p(side.cuda_stream))
+        torch.cuda.synchronize()
+        if st != 0:
+            return None
+        return self.ghz(out.cpu().numpy().view(np.uint64))
+
+    def hbm_read(self, buf, reps=5):
+        import torch
+        nbytes = buf.numel() * buf.element_size()
+        nbytes -= nbytes % 16
+        wgs = 2048
+        sink = torch.zeros(wgs * 4, dtype=torch.int32, device="cuda")
+        res = {}
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for nt in (0, 1):
+            times = []
+            for _ in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                st = self.L.grok_moe_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, wgs, nt,
+                                                ctypes.c_void_p(sink.data_ptr()), s)
+                e1.record()
+                torch.cuda.synchronize()
+                if st != 0:
+                    raise RuntimeError(f"read probe failed ({st})")
+                times.append(e0.elapsed_time(e1))
+            res["nontemporal" if nt else "default"] = nbytes / (float(np.median(times[1:])) * 1e-3) / 1e9
+        return res, nbytes
+
+    def mfma(self, iters=200000):
+        """Sustained dense bf16 MFMA (TFLOP/s) on random operands, its clock, and a check of the result."""
+        import torch
+        g = torch.Generator(device="cuda").manual_seed(0)
+        ops = torch.randn(8 * 64 * 8, device="cuda", generator=g).to(torch.bfloat16)
+        chk = torch.zeros(1024 * 64, dtype=torch.float32, device="cuda")
+        clocks = torch.zeros(1024 * 4, dtype=torch.int64, device="cuda")
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        args = (ctypes.c_void_p(ops.data_ptr()), None, ctypes.c_void_p(chk.data_ptr()),
+                ctypes.c_void_p(clocks.data_ptr()), s)
+        self.L.grok_moe_probe_mfma(args[0], 1000, *args[2:])  # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st = self.L.grok_moe_probe_mfma(args[0], iters, *args[2:])
+        e1.record()
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError(f"mfma probe failed ({st})")
+        ms = e0.elapsed_time(e1)
+        flops = 1024.0 * iters * 16 * 32768
+        # expected checksum per lane, in float64 from the operands (fragment layouts in grok_moe_probe.h)
+        o = ops.float().cpu().numpy().astype(np.float64).reshape(8, 64, 8)
+        A = np.zeros((4, 32, 16))
+        B = np.zeros((4, 16, 32))
+        for f in range(4):
+            for lane in range(64):
+                A[f, lane & 31, 8 * (lane >> 5):8 * (lane >> 5) + 8] = o[f, lane]
+                B[f, 8 * (lane >> 5):8 * (lane >> 5) + 8, lane & 31] = o[4 + f, lane]
+        want = np.zeros(64)
+        scale = np.zeros(64)
+        rows = np.array([[(v & 3) + 8 * (v >> 2) + 4 * (lane >> 5) for v in range(16)] for lane in range(64)])
+        for i in range(4):
+            for j in range(4):
+                C = A[i] @ B[j]
+                for lane in range(64):
+                    vals = C[rows[lane], lane & 31]
+                    want[lane] += vals.sum()
+                    scale[lane] += np.abs(vals).sum()
+        got = chk.cpu().numpy().reshape(1024, 64).astype(np.float64)
+        err = float(np.max(np.abs(got - iters * want[None, :]) / (iters * scale[None, :])))
+        return {"mfma_sustained_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_ms": ms, "mfma_iters": iters,
+                "mfma_clock_GHz": self.ghz(clocks.cpu().numpy().view(np.uint64)),
+                "mfma_checksum_max_rel_err": err, "mfma_checksum_ok": bool(err < 1e-2),
+                "mfma_kernel": "1024 waves (one per SIMD), 16 v_mfma_f32_32x32x16_bf16 per round on register operands"}
+
+
+def ceilings(probe, buf):
+    """Practical ceilings of this GPU: streaming HBM read of a resident weight tensor and sustained MFMA."""
+    res = {}
+    rd, nbytes = probe.hbm_read(buf)
+    res["hbm_read_GBps_default"] = rd["default"]
+    res["hbm_read_GBps_nontemporal"] = rd["nontemporal"]
+    res["hbm_read_GBps"] = max(rd.values())
+    res["hbm_read_bytes"] = nbytes
+    res.update(probe.mfma())
+    res["mfma_frac_of_spec"] = res["mfma_sustained_TFLOPs"] / BF16_PEAK_TFLOPS
+    res["hbm_frac_of_spec"] = res["hbm_read_GBps"] / HBM_PEAK_GBS
     return res
 
+
+# ------------------------------------------------------------------------------------------------ oracle side
+
+def cpu_info():
+    """CPU model, logical CPUs this process may run on, their physical cores, and torch's thread count."""
+    import torch
+    try:
+        aff = sorted(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = list(range(os.cpu_count() or 1))
+    model, cores, cur = None, set(), {}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if ":" not in line:
+                if cur.get("processor") is not None and int(cur["processor"]) in aff:
+                    cores.add((cur.get("physical id", "0"), cur.get("core id", cur["processor"])))
+                cur = {}
+                continue
+            k, v = (s.strip() for s in line.split(":", 1))
+            cur[k] = v
+            if k == "model name" and model is None:
+                model = v
+        if cur.get("processor") is not None and int(cur["processor"]) in aff:
+            cores.add((cur.get("physical id", "0"), cur.get("core id", cur["processor"])))
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": len(aff), "physical_cores": len(cores) or None,
+            "threads": torch.get_num_threads()}
+
+
+def oracle_check(w, inp, layer, oracle, synth, timing=True):
+    """Parity of the run's output (layer.out / idx / p / counts after the timed steps) against the oracle, and the
+    oracle's time on the same rows."""
+    import torch
+    from synth.harness import TOL, rel_err, rms_rel_err
+    rows = None if w.sampled_rows is None else synth.sampled_rows(w.T, w.sampled_rows)
+    n_rows = w.T if rows is None else len(rows)
+    kind = "f32" if w.dtype == synth.F32 else "bf16"
+    res = {}
+    if timing:
+        bias = inp.get("router_bias")
+        t0 = time.perf_counter()
+        oracle.route(oracle.as_f64(inp["x"], kind), oracle.as_f64(inp["router_w"], kind),
+                     None if bias is None else torch.from_numpy(np.asarray(bias, np.float64)))
+        res["routing_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ref = oracle.forward(inp, w.dtype, rows=rows)
+    t_fwd = time.perf_counter() - t0
+    rows_t = ref["rows"].numpy()
+    out = layer.out.cpu().numpy()[rows_t]
+    idx, p, cnt = layer.idx.cpu().numpy(), layer.p.cpu().numpy(), layer.counts.cpu().numpy()
+    par = {"rows_checked": n_rows, "routing_tokens": w.T,
+           "idx_exact": bool(np.array_equal(idx, ref["idx"].numpy())),
+           "counts_exact": bool(np.array_equal(cnt, ref["counts"].numpy())),
+           "p_max_rel_err": float(np.max(np.abs(p - ref["p"].numpy()) / ref["p"].numpy())),
+           "max_err_over_rms": rel_err(out, ref["out"].numpy()),
+           "rms_err_over_rms": rms_rel_err(out, ref["out"].numpy()),
+           "tol": TOL[w.dtype], "min_logit_gap_cut": float(ref["min_gap_cut"])}
+    if w.dtype != synth.F32:  # against the plain definition, without the bf16 rounding of h
+        plain = oracle.forward(inp, w.dtype, rows=rows, round_h=False)["out"].numpy()
+        par["vs_unrounded"] = {"max_err_over_rms": rel_err(out, plain), "rms_err_over_rms": rms_rel_err(out, plain)}
+    par["pass"] = bool(par["idx_exact"] and par["counts_exact"] and par["p_max_rel_err"] < 1e-6
+                       and par["max_err_over_rms"] <= par["tol"])
+    res["parity"] = par
+    if timing:
+        info = cpu_info()
+        res["cpu_baseline"] = {
+            "value": n_rows / t_fwd, "unit": "tokens/s", "cores": info["threads"], "kind": "oracle",
+            "sample": (f"{n_rows} of {w.T} token rows of {w.name} through the float64 oracle (routing on all {w.T} "
+                       f"tokens, both selected experts per row), one pass, {t_fwd:.1f} s"),
+            "wall_s": t_fwd, "routing_s": res.pop("routing_s"), **info}
+        rt = res["cpu_baseline"]["routing_s"]
+        if t_fwd > rt:
+            res["cpu_baseline"]["expert_rows_tokens_per_s"] = n_rows / (t_fwd - rt)
+    return res
+
+
+def single_thread_baseline(w, inp, oracle):
+    import torch
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.forward(inp, w.dtype, rows=np.array([0]))
+        dt1 = time.perf_counter() - t0
+    finally:
+        torch.set_num_threads(threads)
+    return {"value": 1 / dt1, "unit": "tokens/s", "cores": 1,
+            "sample": f"1 token row of {w.name} (routing on all {w.T} tokens), {dt1:.1f} s"}
+
+
+# ------------------------------------------------------------------------------------------------ one workload
+
+def to_layout(dv, weight_layout):
+    """The device weights in the chosen storage: [E, in, out] as drawn, or their transposes [E, out, in] (the same
+    values; transposed once on the device, untimed)."""
+    if weight_layout != "out_in":
+        return dv
+    dv = dict(dv)
+    for n in ("w1", "wv", "w2"):
+        dv[n] = dv[n].transpose(1, 2).contiguous()
+    return dv
+
+
+def measure(gm, w, inp, dv, steps, warmup, a, probe, ceil, oracle, synth, norms=None):
+    import torch
+    layer = Layer(gm, w, inp, dv, norms, a.weight_layout)
+    wall, kms = layer.run_with_kernel_times(steps, warmup)
+    ms = wall * 1e3 / steps
+    counts = layer.counts.cpu().numpy()
+    rl, kernels = roofline(w, layer, kms, ms, a.weight_layout, ceil)
+    res = {"workload": w.name + ("_out_in" if a.weight_layout == "out_in" else "") + ("_block" if norms else ""),
+           "T": w.T, "d_model": w.d, "d_ff": w.f, "experts": w.E, "top_k": 2,
+           "dtype": {0: "f32", 1: "bf16", 2: "bf16 x int8-weight"}[w.dtype],
+           "value": w.T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms, "steps": steps, "warmup": warmup,
+           "step_ms": layer.step_stats, "roofline": rl, "kernels": kernels,
+           "routing": {"counts": counts.tolist(), "experts_hit": n_hit(counts)}, "down_splits": layer.S}
+    # the whole-layer entry point, and a check that it reproduces the timed steps bit for bit
+    out_e, idx_e, p_e, cnt_e = layer.forward_entry()
+    torch.cuda.synchronize()
+    res["entry_point_equal_to_steps"] = bool(torch.equal(out_e, layer.out) and torch.equal(idx_e, layer.idx)
+                                             and torch.equal(cnt_e, layer.counts))
+    del out_e, idx_e, p_e, cnt_e
+    res["entry_point_ms_per_step"] = layer.time_entry_point(max(3, min(steps, 20)))
+    if probe is not None:
+        nclk = max(3, int(np.ceil(40.0 / max(ms, 1e-3))))  # extra untimed steps, about 40 ms of work
+        res["clock_GHz"] = probe.clock_during(lambda: [layer.step() for _ in range(nclk)], nclk * ms)
+    log(f"{res['workload']}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down "
+        f"{kms[1]:.3f} ms, {rl['unit']} {rl['achieved']:.0f} ({100 * rl['frac']:.1f}% of peak), clock "
+        f"{res.get('clock_GHz')}")
+    if oracle is not None:
+        if norms is None:
+            res.update(oracle_check(w, inp, layer, oracle, synth))
+            par = res["parity"]
+            log(f"{res['workload']}: parity {'ok' if par['pass'] else 'FAILED'}: idx {par['idx_exact']}, counts "
+                f"{par['counts_exact']}, max err / rms {par['max_err_over_rms']:.2e} over {par['rows_checked']} rows"
+                + (f", unrounded {par['vs_unrounded']['max_err_over_rms']:.2e}" if "vs_unrounded" in par else ""))
+        else:
+            res["parity"] = None  # the block form's parity is a GPU test; not repeated here
+    return res, layer
+
+
+# ------------------------------------------------------------------------------------------------ context
 
 def library_gemm(steps, warmup):
     """torch.matmul (hipBLASLt) on dense bf16 GEMMs of the shapes one expert sees in the T=8192 prefill
@@ -300,6 +612,8 @@ def library_gemm(steps, warmup):
     print(json.dumps({"library_gemm": res, "library": "torch.mm (hipBLASLt)", "dtype": "bf16"}))
 
 
+# ------------------------------------------------------------------------------------------------ main
+
 def main():
     a = parse()
     if a.library_gemm:
@@ -314,22 +628,26 @@ def main():
 
     import mixture_experts_transformer_gemv_amd as gm
     import synth
-    from tests._helpers import dev_inputs
+    from synth.harness import dev_inputs
 
     gm.lib()
     torch.cuda.set_device(0)
+    oracle = None
+    if not a.no_parity:
+        import oracle  # noqa: F811  (the CPU check and baseline only; never on the timed path)
+    probe = Probe(gm)
+
     w = synth.WORKLOADS[a.workload]
-    if a.tokens or a.d_ff:
-        import dataclasses
-        if a.tokens:
-            w = dataclasses.replace(w, T=a.tokens, name=f"{w.name}_T{a.tokens}")
-        if a.d_ff:
-            w = dataclasses.replace(w, f=a.d_ff, name=f"{w.name}_f{a.d_ff}")
+    if a.tokens:
+        w = dataclasses.replace(w, T=a.tokens, name=f"{w.name}_T{a.tokens}",
+                                sampled_rows=w.sampled_rows or (256 if a.tokens > 256 else None))
+    if a.d_ff:
+        w = dataclasses.replace(w, f=a.d_ff, name=f"{w.name}_f{a.d_ff}")
     log(f"workload {w.name}: drawing weights")
     t0 = time.perf_counter()
-    wts = synth.make_weights(w)
-    inp = synth.make_inputs(w, weights=wts)
-    dv = dev_inputs(inp, w.dtype)
+    wts = {w.dtype: synth.make_weights(w)}
+    inp = synth.make_inputs(w, weights=wts[w.dtype])  # (host copies stay for the oracle)
+    dv = to_layout(dev_inputs(inp, w.dtype), a.weight_layout)
     log(f"inputs resident ({time.perf_counter() - t0:.1f} s)")
 
     if a.copy_probe_mib:
@@ -340,6 +658,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    ceil = None
+    if not a.no_ceilings and w.dtype != synth.F32 and dv["w1"].numel() * dv["w1"].element_size() >= (1 << 30):
+        log("ceilings: HBM read and MFMA probes")
+        ceil = ceilings(probe, dv["w1"])
+        log(f"ceilings: read {ceil['hbm_read_GBps']:.0f} GB/s, MFMA {ceil['mfma_sustained_TFLOPs']:.0f} TFLOP/s at "
+            f"{ceil['mfma_clock_GHz']:.2f} GHz (checksum {'ok' if ceil['mfma_checksum_ok'] else 'WRONG'})")
+
     norms = None
     if a.block:
         ns = synth.make_norm_scales(w)
@@ -348,86 +673,54 @@ def main():
         else:
             conv = lambda v: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
         norms = (conv(ns["pre_scale"]), conv(ns["post_scale"]), ns["eps"])
-    layer = Layer(gm, w, inp, dv, norms, a.weight_layout)
-    wall, kms = layer.run_with_kernel_times(a.steps, a.warmup)
-    ms = wall * 1e3 / a.steps
-    nh = n_hit(layer)
-    T = w.T
-    tname = w.name + ("_out_in" if a.weight_layout == "out_in" else "")  # the expert kernels' workload
-    wname = tname + ("_block" if a.block else "")
-    res = {"metric": METRIC, "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-           "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": {0: "f32", 1: "bf16", 2: "bf16 x int8-weight"}[w.dtype], "data": "synthetic",
-           "config": {"workload": wname, "T": T, "d_model": w.d, "d_ff": w.f,
-                      "experts": w.E, "top_k": 2, "experts_hit": nh, "down_splits": layer.S,
-                      "rmsnorm_residual": bool(a.block), "weight_layout": a.weight_layout}}
-    kernels = {"expert_up_ms": kms[0], "expert_down_ms": kms[1], "route_bin_ms": kms[2], "combine_ms": kms[3]}
-    if w.dtype == 0:  # the fp32 layer: vector-ALU kernels (tiny shapes: launch latency in practice)
-        fl = up_flops(w, T)
-        ach = fl / (kms[0] * 1e-3) / 1e12
-        res["roofline"] = {"bound": "alu", "kernel": "f32_tiled_kernel<2>", "achieved": ach,
-                           "peak": FP32_VALU_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP32_VALU_TFLOPS,
-                           "traffic": None, "algorithmic_flops": fl}
-    elif w.T <= (128 if w.dtype == synth.W8 else 96):  # weight-streaming kernels: HBM-bound, the up-projection
-        # (W1 and Wv) is the dominant kernel
-        ub = up_bytes(w, nh, T)
-        ach = ub / (kms[0] * 1e-3) / 1e9
-        kname = "oi_stream_kernel<2>" if a.weight_layout == "out_in" else "up_stream_kernel"
-        res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": load_traffic(tname, "up"), "algorithmic_bytes": ub}
-        db = down_bytes(w, nh, T, layer.S)
-        kernels["expert_down_GBps"] = db / (kms[1] * 1e-3) / 1e9
-        kernels["layer_GBps"] = (ub + db) / (ms * 1e-3) / 1e9
-    else:
-        fl = up_flops(w, T)
-        ach = fl / (kms[0] * 1e-3) / 1e12
-        oi = "true" if a.weight_layout == "out_in" else "false"
-        grouped = w.groups_up > 1 or w.groups_down > 1
-        if w.dtype == 1 or (not grouped and oi == "false"):  # 256-row tiles, then 128-row last tiles
-            kname = f"tiled_dma_kernel<2, {oi}, {'true' if w.dtype == 2 else 'false'}, 256> + tiled_dma_small_kernel"
-        elif grouped and oi == "false" and w.groups_up <= 8:  # grouped scales on the 128-row direct-to-LDS tiles
-            kname = "tiled_dma_grouped_kernel<2>"
+    head, hlayer = measure(gm, w, inp, dv, a.steps, a.warmup, a, probe, ceil, oracle, synth, norms)
+    res = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": {0: "f32", 1: "bf16", 2: "bf16 x int8-weight"}[w.dtype],
+           "data": "synthetic",
+           "config": {"workload": head["workload"], "T": w.T, "d_model": w.d, "d_ff": w.f, "experts": w.E,
+                      "top_k": 2, "experts_hit": head["routing"]["experts_hit"], "down_splits": head["down_splits"],
+                      "rmsnorm_residual": bool(a.block), "weight_layout": a.weight_layout},
+           "roofline": head["roofline"]}
+    if "cpu_baseline" in head:
+        res["cpu_baseline"] = head.pop("cpu_baseline")
+        if not a.no_cpu_baseline:
+            res["cpu_baseline"]["single_thread"] = single_thread_baseline(w, inp, oracle)
+    for k in ("kernels", "step_ms", "routing", "parity", "clock_GHz", "entry_point_ms_per_step",
+              "entry_point_equal_to_steps"):
+        if k in head:
+            res[k] = head[k]
+    if ceil is not None:
+        res["ceilings"] = ceil
+    del hlayer
+    torch.cuda.empty_cache()
+
+    names = [] if a.configs == "none" else (list(ALL_CONFIGS) if a.configs == "all" else a.configs.split(","))
+    names = [n for n in names if n != w.name]
+    if a.tokens or a.d_ff or a.block:
+        names = []  # variants of the headline workload stand alone
+    res["configs"] = {}
+    for name in names:
+        cw = synth.WORKLOADS[name]
+        log(f"config {name}")
+        share = cw.dtype == w.dtype and (cw.d, cw.f, cw.E, cw.groups_up, cw.groups_down, cw.scale_experts) == \
+            (w.d, w.f, w.E, w.groups_up, w.groups_down, w.scale_experts)
+        if share:  # the same weights (decode, prefill and skewed routing), already resident
+            cinp = synth.make_inputs(cw, weights=wts[w.dtype])
+            cdv = dict(dv)
+            part = dev_inputs({**cinp, "w1": None, "wv": None, "w2": None, "s1": None, "sv": None, "s2": None},
+                              cw.dtype)
+            cdv["x"], cdv["router_w"], cdv["router_bias"] = part["x"], part["router_w"], part["router_bias"]
         else:
-            kname = f"tiled_reg_kernel<2, {'true' if grouped else 'false'}, {oi}>"
-        res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
-                           "traffic": load_traffic(tname, "up"), "algorithmic_flops": fl}
-        kernels["layer_TFLOPs"] = 3 * fl / 2 / (ms * 1e-3) / 1e12
-    res["kernels"] = kernels
-    res["step_ms"] = layer.step_stats  # per step, first to last event on the stream: median, min, p90
-    log(f"{w.name}: {ms:.3f} ms/step, {res['value']:.1f} tokens/s, up {kms[0]:.3f} ms, down {kms[1]:.3f} ms")
-
-    if not a.no_prefill and a.prefill_steps > 0 and w.name == "decode_bf16" and not a.block:
-        pw = synth.WORKLOADS["prefill_bf16"]
-        pinp = synth.make_inputs(pw, weights=wts)
-        pdv = dict(layer.dv)  # the decode layer's weights, already in the chosen layout
-        pdv["x"] = dev_inputs({**pinp, "w1": None, "wv": None, "w2": None}, synth.BF16)["x"]
-        pl = Layer(gm, pw, pinp, pdv, None, a.weight_layout, transpose=False)
-        pname = pw.name + ("_out_in" if a.weight_layout == "out_in" else "")
-        pwall, pk = pl.run_with_kernel_times(a.prefill_steps, 2)
-        pms = pwall * 1e3 / a.prefill_steps
-        fl = up_flops(pw, pw.T)
-        res["prefill"] = {"workload": pname, "T": pw.T, "value": pw.T / (pms / 1e3), "unit": "tokens/s",
-                          "ms_per_step": pms, "steps": a.prefill_steps,
-                          "layer_TFLOPs": 3 * fl / 2 / (pms * 1e-3) / 1e12,
-                          "roofline": {"bound": "mfma",
-                                       "kernel": f"tiled_dma_kernel<2, {str(a.weight_layout == 'out_in').lower()}, false, 256> + tiled_dma_small_kernel",
-                                       "achieved": fl / (pk[0] * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                                       "unit": "TFLOP/s", "frac": fl / (pk[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                                       "traffic": load_traffic(pname, "up"), "algorithmic_flops": fl},
-                          "kernels": {"expert_up_ms": pk[0], "expert_down_ms": pk[1], "route_bin_ms": pk[2],
-                                      "combine_ms": pk[3],
-                                      "expert_down_TFLOPs": fl / 2 / (pk[1] * 1e-3) / 1e12},
-                          "step_ms": pl.step_stats}
-        log(f"prefill: {pms:.3f} ms/step, {res['prefill']['value']:.0f} tokens/s")
-        del pl, pdv
+            cinp = synth.make_inputs(cw)
+            cdv = to_layout(dev_inputs(cinp, cw.dtype), a.weight_layout)
+        steps = a.config_steps or CONFIG_STEPS.get(name, 10)
+        cres, clayer = measure(gm, cw, cinp, cdv, steps, 2, a, probe, ceil, oracle, synth)
+        res["configs"][name] = cres
+        del clayer, cdv
         torch.cuda.empty_cache()
-
-    if not a.no_cpu_baseline:
-        import oracle
-        log("timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(w, inp, oracle, synth, a.block)
+    if not res["configs"]:
+        del res["configs"]
     print(json.dumps(res), flush=True)
 
 

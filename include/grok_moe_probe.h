@@ -1,0 +1,55 @@
+/*
+ * grok_moe_probe.h -- measurement probes of one MI355X (gfx950): the practical ceilings that the Grok-1 MoE
+ * layer's kernels are compared with, beside the published peaks (HBM3E 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s at
+ * 2.4 GHz).  They are instruments, not steps of the layer: libgrokmoe_probe.so, built beside libgrokmoe.so.
+ *
+ * The shapes they are sized for come from the layer's weights ("Grok-1-BF16", section "Verification": expert
+ * tensors [32768, 6144] and [6144, 32768], 8 experts), which is what the read probe streams.
+ *
+ * Conventions: pointers are DEVICE pointers on the current HIP device, 16-byte aligned, owned by the caller;
+ * every call only enqueues on `stream` (0 = legacy default stream) and returns 0, or -1 for an invalid argument
+ * (nothing enqueued), or -4 if the launch failed.
+ */
+#ifndef GROK_MOE_PROBE_H
+#define GROK_MOE_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Streaming read of `bytes` bytes (a multiple of 16) at `buf` with 16-byte vector loads, grid-stride over
+ * `workgroups` workgroups of 256 threads; nontemporal != 0 sets the nontemporal hint on every load.  Each wave
+ * folds what it read by XOR into one word of sink [workgroups * 4] (so no load can be removed). */
+int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups, int nontemporal, uint32_t* sink,
+                        hipStream_t stream);
+
+/* Dense bf16 MFMA with nothing else: 256 workgroups of 4 waves (one wave per SIMD on every CU); each wave loads 4
+ * A and 4 B operand fragments of v_mfma_f32_32x32x16_bf16 (ops: 8 x 64 lanes x 8 bf16 = 4096 values, the same for
+ * every wave; A fragment i is ops[i], B fragment j is ops[4 + j], lane l holding elements 8 l .. 8 l + 7 of its
+ * fragment), then runs `iters` rounds of the 16 MFMAs of a 128 x 128 accumulator tile (4 x 4 blocks of 32 x 32)
+ * held in registers.  Lane l of wave w writes the sum over blocks (i, j) and accumulator elements v of its
+ * accumulators to checksum[64 w + l] (1024 waves), and clocks[4 w + {0,1,2,3}] = shader-clock counter at start and
+ * end, constant-rate counter at start and end.  Flops: 1024 waves x iters x 16 x 32768.  Operand layout of a
+ * 32x32x16 fragment: lane l holds row (A) or column (B) l & 31, k = 8 (l >> 5) .. +7; accumulator element v of
+ * lane l is row (v & 3) + 8 (v >> 2) + 4 (l >> 5), column l & 31. */
+int grok_moe_probe_mfma(const uint16_t* ops, int iters, float* checksum, uint64_t* clocks, hipStream_t stream);
+
+/* Clock sampler: `workgroups` single-wave workgroups each record the shader-clock counter and the constant-rate
+ * counter, sleep until `ticks` constant-rate ticks have passed (at most 2^20 sleeps of 8128 cycles each, so the
+ * kernel always ends), and record both again: out[4 w + {0,1,2,3}] as for grok_moe_probe_mfma.  Run beside other
+ * work on a second stream, it reads the shader clock that work runs at. */
+int grok_moe_probe_clock(int workgroups, uint64_t ticks, uint64_t* out, hipStream_t stream);
+
+/* Rate of the constant-rate counter in kHz (hipDeviceAttributeWallClockRate of the current device), or 0. */
+int grok_moe_probe_wall_clock_khz(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROK_MOE_PROBE_H */

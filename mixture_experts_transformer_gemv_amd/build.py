@@ -1,9 +1,11 @@
-"""Build libgrokmoe.so (the gfx950 HIP library behind include/grok_moe.h) in the package directory.
+"""Build libgrokmoe.so (the gfx950 HIP library behind include/grok_moe.h) and libgrokmoe_probe.so (the
+measurement probes behind include/grok_moe_probe.h) in the package directory.
 
     python -m mixture_experts_transformer_gemv_amd.build      # or build() from Python
 
 Every HIP source under csrc/ is compiled with hipcc for gfx950 into an object file, then linked into one
-shared library.  Packed-fp32 instructions are disabled for all device code.
+shared library; probe/ likewise into the probe library.  Packed-fp32 instructions are disabled for all device
+code.
 """
 from __future__ import annotations
 
@@ -15,8 +17,10 @@ from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
+PROBE_SRC = os.path.join(PKG, "probe")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgrokmoe.so")
+PROBE_LIB = os.path.join(PKG, "libgrokmoe_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -34,18 +38,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
 
 
-def sources() -> list[str]:
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(directory: str = CSRC) -> list[str]:
+    return sorted(os.path.join(directory, f) for f in os.listdir(directory) if f.endswith(".hip"))
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every HIP source and link libgrokmoe.so; returns the library path.  Always rebuilds."""
+    """Compile every HIP source and link libgrokmoe.so and libgrokmoe_probe.so; returns the layer library's path.
+    Always rebuilds."""
     cc = hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     flags = FLAGS + list(extra_flags or [])
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
+        sub = "probe_" if os.path.dirname(src) == PROBE_SRC else ""
+        obj = os.path.join(BUILD_DIR, sub + os.path.basename(src)[:-4] + ".o")
         cmd = [cc, *flags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
@@ -54,15 +60,19 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
             print(r.stderr, file=sys.stderr)
         return obj
 
-    srcs = sources()
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    def link(objs, out):
+        tmp = out + ".tmp"
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link of {out} failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, out)
+
+    srcs, psrcs = sources(CSRC), sources(PROBE_SRC)
+    with ThreadPoolExecutor(min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(compile_one, srcs + psrcs))
+    link(objs[:len(srcs)], LIB)
+    link(objs[len(srcs):], PROBE_LIB)
     return LIB
 
 

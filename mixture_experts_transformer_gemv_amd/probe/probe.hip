@@ -1,0 +1,135 @@
+// Measurement probes of the practical ceilings of one MI355X (gfx950); contracts in include/grok_moe_probe.h.
+//
+// Streaming HBM read (default or nontemporal 16-byte loads), dense bf16 MFMA on register operands with a
+// checkable result and the clock it ran at, and a clock sampler that runs beside other work.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/grok_moe_probe.h"
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+namespace {
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const u32x4_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(256) void read_kernel(const u32x4_t* __restrict__ p, size_t n16, uint32_t* sink) {
+  const size_t stride = size_t(gridDim.x) * 256;
+  size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {  // four independent loads in flight per lane
+    const u32x4_t a = ld16<NT>(p + i), b = ld16<NT>(p + i + stride), c = ld16<NT>(p + i + 2 * stride),
+                  d = ld16<NT>(p + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= ld16<NT>(p + i);
+  uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v ^= __shfl_xor(v, m, 64);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = v;
+}
+
+__device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void mfma_kernel(const u32x4_t* __restrict__ ops, int iters,
+                                                   float* __restrict__ checksum, uint64_t* __restrict__ clocks) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  u32x4_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = ops[i * 64 + lane];
+    b[i] = ops[(4 + i) * 64 + lane];
+  }
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const uint64_t c0 = clock64(), w0 = wall_clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
+  }
+  const uint64_t c1 = clock64(), w1 = wall_clock64();
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+  checksum[w * 64 + lane] = s;
+  if (lane == 0) {
+    clocks[4 * w + 0] = c0;
+    clocks[4 * w + 1] = c1;
+    clocks[4 * w + 2] = w0;
+    clocks[4 * w + 3] = w1;
+  }
+}
+
+__global__ __launch_bounds__(64) void clock_kernel(uint64_t ticks, uint64_t* out) {
+  const uint64_t c0 = clock64(), w0 = wall_clock64();
+  for (int i = 0; i < (1 << 20); ++i) {  // bounded: every workgroup ends
+    __builtin_amdgcn_s_sleep(127);
+    if (wall_clock64() - w0 >= ticks) break;
+  }
+  const uint64_t c1 = clock64(), w1 = wall_clock64();
+  if (threadIdx.x == 0) {
+    out[4 * blockIdx.x + 0] = c0;
+    out[4 * blockIdx.x + 1] = c1;
+    out[4 * blockIdx.x + 2] = w0;
+    out[4 * blockIdx.x + 3] = w1;
+  }
+}
+
+inline bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline int status(hipError_t e) { return e == hipSuccess ? 0 : -4; }
+
+}  // namespace
+
+extern "C" {
+
+int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups, int nontemporal, uint32_t* sink,
+                        hipStream_t stream) {
+  if (!aligned16(buf) || sink == nullptr || bytes % 16 != 0 || workgroups < 1 || workgroups > (1 << 20)) return -1;
+  const u32x4_t* p = static_cast<const u32x4_t*>(buf);
+  if (nontemporal) read_kernel<true><<<workgroups, 256, 0, stream>>>(p, bytes / 16, sink);
+  else read_kernel<false><<<workgroups, 256, 0, stream>>>(p, bytes / 16, sink);
+  return status(hipGetLastError());
+}
+
+int grok_moe_probe_mfma(const uint16_t* ops, int iters, float* checksum, uint64_t* clocks, hipStream_t stream) {
+  if (!aligned16(ops) || checksum == nullptr || clocks == nullptr || iters < 1) return -1;
+  mfma_kernel<<<256, 256, 0, stream>>>(reinterpret_cast<const u32x4_t*>(ops), iters, checksum, clocks);
+  return status(hipGetLastError());
+}
+
+int grok_moe_probe_clock(int workgroups, uint64_t ticks, uint64_t* out, hipStream_t stream) {
+  if (out == nullptr || workgroups < 1 || workgroups > 1024) return -1;
+  clock_kernel<<<workgroups, 64, 0, stream>>>(ticks, out);
+  return status(hipGetLastError());
+}
+
+int grok_moe_probe_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
+}
+
+}  // extern "C"
