@@ -20,8 +20,8 @@
  *     ENQUEUES work and returns without synchronising; results are visible after the stream reaches that point.
  *   - Argument errors are detected on the host before anything is enqueued: the call returns a negative
  *     status, enqueues nothing and writes nothing.  A failed kernel launch returns GROK_MOE_EHIP.
- *   - The library allocates no memory and keeps no mutable global state: calls on different streams with
- *     distinct workspaces may run concurrently.
+ *   - The library allocates no memory and, apart from the scratch array of grok_moe_forward_noalloc (below), keeps
+ *     no mutable global state: calls on different streams with distinct workspaces may run concurrently.
  *   - Weight layout, unless an entry point takes a grok_moe_layout: [E, in, out], W1 and Wv [E, d, f], W2 [E, f, d].
  *     int8 scales, unless an entry point takes a scale layout: [E, 1, f] for W1 and Wv, [E, 1, d] for W2 (one bf16
  *     scale per expert and output channel).
@@ -67,7 +67,8 @@ enum {
   GROK_MOE_EUNSUPPORTED = -2, /* valid but unsupported shape (k != 2, E outside [2,64], d/f granularity or
                                  size, more than one pass of tokens in an expert step, scale groups) */
   GROK_MOE_EWORKSPACE = -3,   /* workspace smaller than grok_moe_workspace_size() */
-  GROK_MOE_EHIP = -4          /* a HIP launch failed */
+  GROK_MOE_EHIP = -4,         /* a HIP launch failed */
+  GROK_MOE_ESCRATCH = -5      /* grok_moe_forward_noalloc: the batch needs more than GROK_MOE_SCRATCH_BYTES */
 };
 
 /* Human-readable text of a status code (static storage; never NULL). */
@@ -214,6 +215,26 @@ int grok_moe_route_norm(const void* x, const void* pre_scale, double eps, const 
 int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const int32_t* inv, const void* x,
                           const void* post_scale, double eps, int64_t T, int64_t d, int k, grok_moe_dtype dtype,
                           float* out, hipStream_t stream);
+
+/* ---- For callers that cannot allocate ------------------------------------------------------------------------
+ * Code under HIP graph capture, tight serving loops, or harnesses that forbid hipMalloc cannot provide a workspace
+ * from an allocation.  grok_moe_forward_noalloc is grok_moe_forward with the workspace taken from a static device
+ * array of GROK_MOE_SCRATCH_BYTES bytes inside the library (one copy on each GPU the library runs on, held until
+ * the process ends; its device address is looked up once per device, on the first call with that device current).
+ * The call allocates nothing.  It runs on the CURRENT device (`stream` must belong to it).  A batch whose workspace,
+ * grok_moe_workspace_size(T, d, f, E, k, dtype), exceeds GROK_MOE_SCRATCH_BYTES is rejected with
+ * GROK_MOE_ESCRATCH before anything is enqueued (at d = 6144, f = 32768: up to 292 tokens in bf16, 372 with int8
+ * weights).  No part of
+ * the array has to start at zero: every call writes what it reads.  All calls on one GPU share its array, so calls
+ * that overlap on one GPU (on different streams, or from different threads without ordering) RACE and give wrong
+ * results; order them on one stream.  Arguments, results and errors are otherwise those of grok_moe_forward, and
+ * the output is bit-identical to it. */
+#define GROK_MOE_SCRATCH_BYTES ((size_t)64 << 20)
+
+int grok_moe_forward_noalloc(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                             const void* s1, const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E,
+                             int k, grok_moe_dtype dtype, float* out, const float* router_bias, int32_t* topk_idx,
+                             float* topk_p, int32_t* expert_counts, hipStream_t stream);
 
 #ifdef __cplusplus
 }

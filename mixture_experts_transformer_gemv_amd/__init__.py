@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "F32", "BF16", "W8", "LIB_PATH", "lib", "forward", "route", "bin_tokens", "expert_up", "expert_down",
     "combine", "workspace_size", "down_splits", "strerror", "dtype_of", "GrokMoeError", "block_forward",
-    "block_workspace_size", "route_norm", "combine_norm", "IN_OUT", "OUT_IN", "scale_layout",
+    "block_workspace_size", "route_norm", "combine_norm", "IN_OUT", "OUT_IN", "scale_layout", "forward_noalloc",
+    "SCRATCH_BYTES",
 ]
 
 F32, BF16, W8 = 0, 1, 2
@@ -48,7 +49,11 @@ _SIGS = {
                                    _int, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "grok_moe_combine_norm": (_int, [_c_void_p, _int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, ctypes.c_double,
                                      _i64, _i64, _int, _int, _c_void_p, _c_void_p]),
+    "grok_moe_forward_noalloc": (_int, [_c_void_p] * 8 + [_i64, _i64, _i64, _int, _int, _int] + [_c_void_p] * 6),
 }
+
+# bytes of the static scratch array behind forward_noalloc (GROK_MOE_SCRATCH_BYTES)
+SCRATCH_BYTES = 64 << 20
 
 # weight storage: [E, in, out] (the checkpoint's JAX layout) or [E, out, in] (the converted PyTorch layout)
 IN_OUT, OUT_IN = "in_out", "out_in"
@@ -211,6 +216,29 @@ def forward(x, router_w, w1, wv, w2, scales=None, router_bias=None, return_routi
     if return_routing:
         return out, idx, pr, cnt
     return out
+
+
+def forward_noalloc(x, router_w, w1, wv, w2, scales=None, router_bias=None, out=None, routing=None):
+    """The whole layer through grok_moe_forward_noalloc: no workspace; the library's static scratch array on the
+    current device serves as one (calls that overlap on one GPU race).  [E, in, out] weights, scales [E, 1, out] for
+    int8.  out [T, d] fp32 and routing = (topk_idx, topk_p, expert_counts) may be given preallocated; returns out,
+    or (out, idx, p, counts) if routing is given."""
+    T, d, f, E = _layer_shapes(x, router_w, w1, wv, w2)
+    dt = dtype_of(x, w1)
+    for t, n in ((x, "x"), (router_w, "router_w"), (w1, "w1"), (wv, "wv"), (w2, "w2")):
+        _need(t, n)
+    s1 = sv = s2 = None
+    if dt == W8:
+        if scales is None or _grouped(scales, E, d, f) is not None:
+            raise GrokMoeError("forward_noalloc takes int8 scales of layout [E, 1, out]")
+        s1, sv, s2 = scales
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    idx, pr, cnt = routing if routing is not None else (None, None, None)
+    _check(lib().grok_moe_forward_noalloc(_p(x), _p(router_w), _p(w1), _p(wv), _p(w2), _p(s1), _p(sv), _p(s2),
+                                          T, d, f, E, 2, dt, _p(out), _p(router_bias), _p(idx), _p(pr), _p(cnt),
+                                          _stream()), "grok_moe_forward_noalloc")
+    return out if routing is None else (out, idx, pr, cnt)
 
 
 def route(x, router_w, router_bias=None):

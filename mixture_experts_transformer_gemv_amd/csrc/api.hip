@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/grok_moe.h"
 #include "launch.h"
@@ -292,6 +293,37 @@ int layer_entry(const void* x, const void* pre_scale, const void* post_scale, do
                    router_bias, topk_idx, topk_p, expert_counts, workspace, workspace_bytes, stream);
 }
 
+// ---- the scratch memory of grok_moe_forward_noalloc: one static device array, a copy on every GPU.  In host code
+// `scratch` is only a host-side stand-in for the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress with that GPU current, looked up once per device and kept here.
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch_slots[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[GROK_MOE_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of the current device's scratch array (resolved on the first call with that device current).
+hipError_t current_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch_slots[dev];
+  std::call_once(slot.once, [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess) return slot.err;
+  if (slot.ptr == nullptr || (reinterpret_cast<uintptr_t>(slot.ptr) & 255) != 0) return hipErrorInvalidSymbol;
+  *out = slot.ptr;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -306,6 +338,8 @@ const char* grok_moe_strerror(int status) {
                                        "points take at most one pass of tokens)";
     case GROK_MOE_EWORKSPACE: return "workspace too small";
     case GROK_MOE_EHIP: return "HIP kernel launch failed";
+    case GROK_MOE_ESCRATCH: return "the batch needs more workspace than the static scratch array of "
+                                   "grok_moe_forward_noalloc holds (GROK_MOE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -446,6 +480,20 @@ int grok_moe_combine_norm(const float* y, int splits, const float* topk_p, const
     return GROK_MOE_EINVAL;
   return hip_status(gm::launch_combine_norm(y, splits, topk_p, inv, int(T), int(d), x, dtype != GROK_MOE_F32,
                                             post_scale, eps, out, stream));
+}
+
+int grok_moe_forward_noalloc(const void* x, const void* router_w, const void* w1, const void* wv, const void* w2,
+                             const void* s1, const void* sv, const void* s2, int64_t T, int64_t d, int64_t f, int E,
+                             int k, grok_moe_dtype dtype, float* out, const float* router_bias, int32_t* topk_idx,
+                             float* topk_p, int32_t* expert_counts, hipStream_t stream) {
+  const int st = check_shape(T, d, f, E, k, dtype);
+  if (st != GROK_MOE_OK) return st;
+  if (T > 0 && workspace_need(T, d, f, E, dtype, false) > GROK_MOE_SCRATCH_BYTES) return GROK_MOE_ESCRATCH;
+  void* ws = nullptr;
+  if (T > 0 && current_scratch(&ws) != hipSuccess) return GROK_MOE_EHIP;
+  return layer_entry(x, nullptr, nullptr, 0.0, router_w, w1, wv, w2, s1, sv, s2, GROK_MOE_IN_OUT, E, 1, 1, T, d, f,
+                     E, k, dtype, out, router_bias, topk_idx, topk_p, expert_counts, ws, GROK_MOE_SCRATCH_BYTES,
+                     stream);
 }
 
 }  // extern "C"

@@ -230,3 +230,17 @@ def test_probe_library_exports_its_header():
     g.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
     assert g(0, 100, ctypes.c_void_p(0x200000), None) == -1
     assert gm.LIB_PATH != build.PROBE_LIB
+
+
+def test_noalloc_rejects_on_host(L):
+    """grok_moe_forward_noalloc: shape errors and batches beyond the static scratch array are rejected before
+    anything else (no device is touched)."""
+    import mixture_experts_transformer_gemv_amd as gm
+    fake = ctypes.c_void_p(0x100000)
+    args = lambda T, d, f, k=2, dt=1: (fake, fake, fake, fake, fake, None, None, None, T, d, f, 8, k, dt, fake, None,
+                                       None, None, None, None)
+    assert L.grok_moe_forward_noalloc(*args(8, 256, 512, k=3)) == -2
+    assert L.grok_moe_forward_noalloc(*args(300, 256, 65536)) == -5
+    assert L.grok_moe_forward_noalloc(*args(0, 256, 512)) == 0
+    assert gm.workspace_size(292, 6144, 32768) <= gm.SCRATCH_BYTES < gm.workspace_size(293, 6144, 32768)
+    assert "scratch" in gm.strerror(-5)
