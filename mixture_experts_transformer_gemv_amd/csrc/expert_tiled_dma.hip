@@ -66,7 +66,8 @@ constexpr int kScaleTableBytes = kDmaMaxGroups * BNT * 4;
 // tile_lds_bytes() bytes (plus kScaleTableBytes if GROUPED).  B_NT: nontemporal weight copies (for launches that
 // read each weight byte once).  GROUPED (int8, [in, out], 128-row tiles): int8 scales in groups of gsize rows of
 // K (at most kDmaMaxGroups groups); otherwise one scale per column, or none for bf16.
-template <int NMAT, bool OUTIN, bool INT8, int TBM, bool B_NT = (TBM == 128), bool GROUPED = false>
+template <int NMAT, bool OUTIN, bool INT8, int TBM, bool B_NT = (TBM == 128), bool GROUPED = false,
+          bool TRACE = false>
 __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, const void* __restrict__ B0,
                                                         const void* __restrict__ B1,
                                                         const uint16_t* __restrict__ s0,
@@ -75,7 +76,8 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ perm, uint32_t a_bytes, int K,
                                                         int N, void* __restrict__ out, int64_t split_stride, int e,
-                                                        int row0, int rows, int ntile, lds_u8* lds, int gsize = 0) {
+                                                        int row0, int rows, int ntile, lds_u8* lds, int gsize = 0,
+                                                        uint64_t* trace = nullptr) {
   static_assert(!(OUTIN && INT8), "int8 weights are tiled from [E, K, N] storage");
   static_assert(TBM == 256 || TBM == 192 || TBM == 128, "tiles of 256, 192 or 128 rows");
   static_assert(!GROUPED || (INT8 && !OUTIN && TBM == 128), "grouped scales: int8 [in, out] weights, 128-row tiles");
@@ -308,12 +310,17 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
 
   // ---- main loop.  Step kt: half-step 0 multiplies fragments buffer 0 while the 12 fragment pieces of
   // half-step 1 are read; then the wave waits for its copies of step kt+1 and joins the barrier; half-step 1
-  // multiplies buffer 1 while the copies of step kt+3 are issued and half-step 0 of step kt+1 is read.  Each MFMA
-  // is followed by at most one copy or one LDS read, in a fixed order.  Copies past the last step re-read the last
-  // step into a ring slot that is never read again, so every step issues CPS copies and the wait count is constant.
+  // multiplies buffer 1 while half-step 0 of step kt+1 is read.  Each MFMA is followed by at most one LDS read and
+  // at most one copy, in a fixed order.  Ring slot kt - 1 was last read before the barrier of step kt - 1, so the
+  // CPS copies of step kt + 3 (into that slot) are spread evenly over both half-steps of step kt: one copy every
+  // NSLOT / (CPS / 2) MFMAs.  Issued in bursts, the copies of a workgroup (16 KB within a few MFMAs) outrun what the
+  // vector memory path takes in, and the waves stall at issue with the MFMA pipes idle (measured on MI355X: MFMA
+  // density of the K loop 0.83 with the copies bunched around the barrier, 0.94-0.98 with no copies at all).
+  // Copies past the last step re-read the last step into a ring slot that is never read again, so every step
+  // issues CPS copies and the wait count is constant.
   // OUTIN: the weight copies of pair q are issued in the B slots of steps 2 q - 3 and 2 q - 2 (4 each), so that
-  // step kt issues copies 4 ((kt + 1) % 2) .. +3 of pair (kt + 3) / 2; the prologue issues pair 0 and the first
-  // half of pair 1.
+  // step kt issues copies 4 ((kt + 1) % 2) .. +3 of pair (kt + 3) / 2 at the end of half-step 0 and the activation
+  // copies of step kt + 3 at the start of half-step 1; the prologue issues pair 0 and the first half of pair 1.
   const int KT = Ks / BK;
   const lds_u8* bpairs = lds + NSTAGE * A_STG;
   // zeros in the A slots of rows past the expert's end, in every ring stage (written by this lane only; the
@@ -343,11 +350,11 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
 #pragma unroll
-      for (int n = 0; n < CPS; ++n)
-        if (s < NSTAGE - 2 || n < AP) copy_piece(s, min(s, KT - 1), n);
-    wait_vm<CPS * (NSTAGE - 3) + AP>();  // step 0 landed (step 1 and half of step 2 may be in flight)
+      for (int n = 0; n < CPS; ++n) copy_piece(s, min(s, KT - 1), n);
+    wait_vm<CPS * (NSTAGE - 2)>();  // step 0 landed (steps 1, 2 may be in flight)
   }
   lds_barrier();
+  if (TRACE && tid == 0) trace[2] = clock64();  // prologue done
   if constexpr (GROUPED) {  // the group of step 0 (kbase is a multiple of gsize or inside a group)
     const int g0 = kbase / gsize;
 #pragma unroll
@@ -385,30 +392,43 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     }
     const lds_u8* st = lds + (kt % NSTAGE) * A_STRIDE;
     const lds_u8* sb = bpairs + ((kt >> 1) % NPAIR) * B_PAIR;
-    // second half of the copies of step kt+2 (its first half was issued after the barrier of step kt-1); OUTIN:
-    // four copies of pair (kt + 3) / 2
-    const int pstage = (kt + NSTAGE - 2) % NSTAGE, pk = min(kt + NSTAGE - 2, KT - 1);
+    // [in, out]: the copies of step kt+3 into slot (kt+3) % NSTAGE, C0 of them in half-step 0 and the rest in
+    // half-step 1, at evenly spaced MFMA slots.  OUTIN: four copies of pair (kt + 3) / 2 in the last 4 slots of
+    // half-step 0, the activation copies of step kt+3 in the first AP slots of half-step 1.
+    constexpr int C0 = (CPS + 1) / 2, C1 = CPS - C0;
+    const int cstage = (kt + NSTAGE - 1) % NSTAGE, ck = min(kt + NSTAGE - 1, KT - 1);
 #pragma unroll
     for (int m = 0; m < NSLOT; ++m) {
       if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
       if (m < NPIECE) read_piece(1, st, sb, P, 1, m);
-      const int cb = m - (NSLOT - 4);  // the last 4 slots issue the weight copies
-      if (cb >= 0) {
-        if (OUTIN) copy_pair((kt + 3) >> 1, 4 * (1 - P) + cb);
-        else if (cb < BCOPIES) copy_piece(pstage, pk, AP + cb);
+      if constexpr (OUTIN) {
+        const int cb = m - (NSLOT - 4);  // the last 4 slots issue the weight copies
+        if (cb >= 0) copy_pair((kt + 3) >> 1, 4 * (1 - P) + cb);
+      } else {
+#pragma unroll
+        for (int c = 0; c < C0; ++c)
+          if (m == (c * NSLOT) / C0) copy_piece(cstage, ck, c);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(1, keep_cur);
-    wait_vm<CPS * (NSTAGE - 3)>();  // step kt+1 landed (steps kt+2 .. may be in flight)
-    lds_barrier();                       // ... for every wave; every wave finished reading step kt-1
-    const int cstage = (kt + NSTAGE - 1) % NSTAGE, ck = min(kt + NSTAGE - 1, KT - 1);
+    // step kt+1 landed (the copies of step kt+2 and the first C0 of step kt+3 may be in flight); OUTIN: steps kt+2
+    // and later may be in flight
+    if constexpr (OUTIN) wait_vm<CPS * (NSTAGE - 3)>();
+    else wait_vm<CPS * (NSTAGE - 3) + C0>();
+    lds_barrier();  // ... for every wave; every wave finished reading step kt
     const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * A_STRIDE;
     const lds_u8* nsb = bpairs + (((kt + 1) >> 1) % NPAIR) * B_PAIR;
 #pragma unroll
     for (int m = 0; m < NSLOT; ++m) {
       if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
-      if (m < AP) copy_piece(cstage, ck, m);
+      if constexpr (OUTIN) {
+        if (m < AP) copy_piece(cstage, ck, m);
+      } else {
+#pragma unroll
+        for (int c = 0; c < C1; ++c)
+          if (m == (c * NSLOT) / C1) copy_piece(cstage, ck, C0 + c);
+      }
       if (m < NPIECE) read_piece(0, nst, nsb, 1 - P, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -423,6 +443,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     for (int kt = 0; kt < KT; ++kt) kstep(kt, std::integral_constant<int, 0>{});  // parity unused
   }
   asm volatile("s_waitcnt vmcnt(0)");
+  if (TRACE && tid == 0) trace[3] = clock64();  // K loop done
 
   if constexpr (NMAT == 2) {
     // h tile [TBM rows][128 columns] bf16 staged in the (now idle) ring, then written as 16-byte row pieces
@@ -469,6 +490,10 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     tile::store_tile<NMAT, MI>(acc, wm, wn, lane, row0, rows, nbase, N,
                            static_cast<float*>(out) + blockIdx.y * split_stride);
   }
+  if (TRACE && tid == 0) {  // epilogue stores issued
+    trace[4] = clock64();
+    trace[6] = wall_clock64();
+  }
 }
 
 // The grouped GEMM: workgroup blockIdx.x takes the tile map_tile gives it among the row tiles R of TBM rows, in the
@@ -491,6 +516,42 @@ __global__ __launch_bounds__(256) void tiled_dma_kernel(const uint16_t* __restri
   tiled_dma_tile<NMAT, OUTIN, INT8, TBM>(A, B0, B1, s0, s1, s_estride, counts, offsets, perm, a_bytes, K, N, out,
                                          split_stride, e, row0, rows, ntile, (lds_u8*)(smem));
 }
+
+#ifdef GROK_MOE_TILE_TRACE
+// Timestamps of every tile of the 256-row launch (built into the measurement probes only): record b (workgroup
+// blockIdx.y * gridDim.x + blockIdx.x) holds [0] the hardware ids (HW_ID | XCC_ID << 32), shader-clock counter at
+// [1] start, [2] prologue done, [3] K loop done, [4] epilogue stores issued, constant-rate counter at [5] start and
+// [6] end, and [7] the tile (expert | row0 << 8 | rows << 32 | column tile << 44), or ~0 for a workgroup without one.
+template <int NMAT>
+__global__ __launch_bounds__(256) void tiled_dma_trace_kernel(const uint16_t* __restrict__ A,
+                                                              const void* __restrict__ B0,
+                                                              const void* __restrict__ B1,
+                                                              const int32_t* __restrict__ counts,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ perm, uint32_t a_bytes,
+                                                              int K, int N, int E, void* __restrict__ out,
+                                                              int64_t split_stride, uint64_t* __restrict__ trace) {
+  const uint64_t c0 = clock64(), w0 = wall_clock64();
+  uint64_t* rec = trace + 8 * (size_t(blockIdx.y) * gridDim.x + blockIdx.x);
+  int e, row0, rows, ntile;
+  const bool has = tile::map_tile<tile::Group<NMAT>::N, 256, tile::Rows::Main, NMAT == 2>(
+      counts, offsets, E, N / (BNT / NMAT), blockIdx.x, &e, &row0, &rows, &ntile);
+  if (threadIdx.x == 0) {
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+    rec[0] = uint64_t(hw) | (uint64_t(xcc) << 32);
+    rec[1] = c0;
+    rec[5] = w0;
+    rec[7] = has ? (uint64_t(e) | (uint64_t(row0) << 8) | (uint64_t(rows) << 32) | (uint64_t(ntile) << 44))
+                 : ~uint64_t(0);
+  }
+  if (!has) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<NMAT, false, false, 256>()];
+  tiled_dma_tile<NMAT, false, false, 256, false, false, true>(A, B0, B1, nullptr, nullptr, 0, counts, offsets, perm,
+                                                              a_bytes, K, N, out, split_stride, e, row0, rows, ntile,
+                                                              (lds_u8*)(smem), 0, rec);
+}
+#endif
 
 // The up-projection's second launch: the 192-row tiles (tile::Rows::Mid) and the 128-row tiles (tile::Rows::Tail)
 // in one grid, each workgroup running the body of its tile's height (one launch fewer than a launch per height:
