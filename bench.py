@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--d-ff", type=int, default=0,
                     help="run the headline workload at this d_ff instead of its own (e.g. 4096: one GPU's share of a "
                          "layer split over 8 GPUs along d_ff)")
+    ap.add_argument("--trace", action="store_true",
+                    help="also run the headline workload's 256-row tile launches once with per-tile timestamps (bf16 "
+                         "[in, out] weights, LDS-tiled batches) and report where their cycles go")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration under rocprofv3)")
     a = ap.parse_args()
@@ -316,9 +319,12 @@ class Probe:
             raise RuntimeError(f"{path} is missing: build with `python -m mixture_experts_transformer_gemv_amd.build`")
         L = ctypes.CDLL(path)
         vp, i, u64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
+        i64 = ctypes.c_int64
         for name, args in (("grok_moe_probe_read", [vp, sz, i, i, vp, vp]),
                            ("grok_moe_probe_mfma", [vp, i, vp, vp, vp]),
                            ("grok_moe_probe_clock", [i, u64, vp, vp]),
+                           ("grok_moe_probe_tile_trace", [i, vp, vp, vp, vp, vp, vp, i64, i, i, i, i, i, vp, vp, i64,
+                                                          vp]),
                            ("grok_moe_probe_wall_clock_khz", [])):
             fn = getattr(L, name)
             fn.restype = ctypes.c_int
@@ -418,6 +424,81 @@ class Probe:
                 "mfma_clock_GHz": self.ghz(clocks.cpu().numpy().view(np.uint64)),
                 "mfma_checksum_max_rel_err": err, "mfma_checksum_ok": bool(err < 1e-2),
                 "mfma_kernel": "1024 waves (one per SIMD), 16 v_mfma_f32_32x32x16_bf16 per round on register operands"}
+
+
+def tile_trace(probe, layer):
+    """Where the cycles of the prefill kernels go: the 256-row launch of each projection run once more with per-tile
+    timestamps (same kernel, trace points on), on the routing of the last timed step.  Per tile: prologue (start to
+    the first barrier: tile lookup, activation offsets, first copies), K loop, epilogue; the K loop's MFMA density
+    (K / 32 steps x 32 MFMAs x 32 cycles); per CU: the gaps between its consecutive tiles and its idle tail before
+    the launch ends."""
+    import torch
+    w, dv = layer.w, layer.dv
+    T, d, f, E = w.T, w.d, w.f, w.E
+    slots = 2 * T
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for nmat in (2, 1):
+        if nmat == 2:
+            a, b0, b1, perm, K, N, out, splits = dv["x"], dv["w1"], dv["wv"], layer.perm, d, f, layer.h, 1
+        else:
+            a, b0, b1, perm, K, N, out, splits = layer.h, dv["w2"], None, None, f, d, layer.y, layer.S
+        NT = N // (256 // nmat)
+        gx = ((slots // 256 + E) * NT + 7) // 8 * 8
+        nrec = gx * splits
+        tr = torch.zeros(nrec * 8, dtype=torch.int64, device="cuda")
+        torch.cuda.synchronize()
+        st = probe.L.grok_moe_probe_tile_trace(nmat, P(a), P(b0), None if b1 is None else P(b1), P(layer.counts),
+                                               P(layer.offsets), None if perm is None else P(perm),
+                                               a.numel() * a.element_size(), K, N, E, slots, splits, P(out), P(tr),
+                                               nrec, s)
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError(f"tile trace failed ({st})")
+        r = tr.cpu().numpy().view(np.uint64).reshape(nrec, 8)
+        r = r[r[:, 7] != np.uint64(0xFFFFFFFFFFFFFFFF)].astype(np.int64)
+        cyc = {"prologue": r[:, 2] - r[:, 1], "k_loop": r[:, 3] - r[:, 2], "epilogue": r[:, 4] - r[:, 3],
+               "tile": r[:, 4] - r[:, 1]}
+        wall = r[:, 6] - r[:, 5]
+        ghz = float(cyc["tile"].sum() / wall.sum() * probe.wall_khz * 1e3 / 1e9)
+        ticks_per_us = probe.wall_khz / 1e3
+        kt = K // splits // 32
+        mfma = kt * 32 * 32  # cycles of one wave's MFMAs per tile
+        hw, xcc = r[:, 0] & 0xFFFFFFFF, r[:, 0] >> 32
+        cu = (xcc & 0xF) * 1024 + ((hw >> 13) & 7) * 64 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 0xF)
+        t0, t1 = r[:, 5].min(), r[:, 6].max()
+        span = t1 - t0
+        gaps, tails, heads, busy = [], [], [], 0
+        for c in np.unique(cu):
+            m = cu == c
+            st_, en = r[m, 5], r[m, 6]
+            o = np.argsort(st_)
+            st_, en = st_[o], en[o]
+            gaps.extend((st_[1:] - en[:-1]).tolist())
+            heads.append(st_[0] - t0)
+            tails.append(t1 - en[-1])
+            busy += (en - st_).sum()
+        ncu = len(np.unique(cu))
+        gaps = np.array(gaps, dtype=np.float64)
+        res["up" if nmat == 2 else "down"] = {
+            "tiles": int(len(r)), "cus": ncu, "span_ms": span / ticks_per_us / 1e3, "clock_GHz": ghz,
+            "k_steps": kt, "mfma_cycles_per_tile": mfma,
+            "cycles_per_tile_mean": {k: float(v.mean()) for k, v in cyc.items()},
+            "cycles_per_tile_p10_p90": {k: [float(np.percentile(v, 10)), float(np.percentile(v, 90))]
+                                        for k, v in cyc.items()},
+            "k_loop_mfma_density": float(mfma / cyc["k_loop"].mean()),
+            "tile_mfma_density": float(mfma / cyc["tile"].mean()),
+            "share_of_tile": {k: float(cyc[k].mean() / cyc["tile"].mean()) for k in ("prologue", "k_loop",
+                                                                                      "epilogue")},
+            "gap_between_tiles_us": {"mean": float(gaps.mean() / ticks_per_us) if len(gaps) else None,
+                                     "p90": float(np.percentile(gaps, 90) / ticks_per_us) if len(gaps) else None},
+            "cu_busy_frac_of_span": float(busy / (ncu * span)),
+            "cu_head_idle_frac": float(np.mean(heads) / span), "cu_tail_idle_frac": float(np.mean(tails) / span),
+            "launch_mfma_density": float(len(r) * mfma / (ncu * span * ghz * 1e3 / ticks_per_us)),
+        }
+        del tr
+    return res
 
 
 def ceilings(probe, buf):
@@ -692,6 +773,15 @@ def main():
             res[k] = head[k]
     if ceil is not None:
         res["ceilings"] = ceil
+    if a.trace and w.dtype == synth.BF16 and a.weight_layout == "in_out" and not stream_path(w) and not a.block:
+        res["tile_trace"] = tile_trace(probe, hlayer)
+        for k, v in res["tile_trace"].items():
+            log(f"trace {k}: {v['tiles']} tiles, clock {v['clock_GHz']:.2f} GHz, cycles/tile "
+                f"{v['cycles_per_tile_mean']['tile']:.0f} (prologue {v['cycles_per_tile_mean']['prologue']:.0f}, "
+                f"loop {v['cycles_per_tile_mean']['k_loop']:.0f}, epilogue {v['cycles_per_tile_mean']['epilogue']:.0f});"
+                f" loop MFMA density {v['k_loop_mfma_density']:.3f}, tile {v['tile_mfma_density']:.3f}, launch "
+                f"{v['launch_mfma_density']:.3f}; gap {v['gap_between_tiles_us']['mean']:.2f} us; busy "
+                f"{v['cu_busy_frac_of_span']:.3f}")
     del hlayer
     torch.cuda.empty_cache()
 

@@ -52,7 +52,8 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     def compile_one(src):
         sub = "probe_" if os.path.dirname(src) == PROBE_SRC else ""
         obj = os.path.join(BUILD_DIR, sub + os.path.basename(src)[:-4] + ".o")
-        cmd = [cc, *flags, "-c", src, "-o", obj]
+        # the probes export only their C entry points (the trace probe compiles the layer's tile kernel source again)
+        cmd = [cc, *flags, *(["-fvisibility=hidden"] if sub else []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -102,9 +102,11 @@ inline int status(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 
 }  // namespace
 
+#define PROBE_API __attribute__((visibility("default")))
+
 extern "C" {
 
-int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups, int nontemporal, uint32_t* sink,
+PROBE_API int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups, int nontemporal, uint32_t* sink,
                         hipStream_t stream) {
   if (!aligned16(buf) || sink == nullptr || bytes % 16 != 0 || workgroups < 1 || workgroups > (1 << 20)) return -1;
   const u32x4_t* p = static_cast<const u32x4_t*>(buf);
@@ -113,19 +115,19 @@ int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups, int nonte
   return status(hipGetLastError());
 }
 
-int grok_moe_probe_mfma(const uint16_t* ops, int iters, float* checksum, uint64_t* clocks, hipStream_t stream) {
+PROBE_API int grok_moe_probe_mfma(const uint16_t* ops, int iters, float* checksum, uint64_t* clocks, hipStream_t stream) {
   if (!aligned16(ops) || checksum == nullptr || clocks == nullptr || iters < 1) return -1;
   mfma_kernel<<<256, 256, 0, stream>>>(reinterpret_cast<const u32x4_t*>(ops), iters, checksum, clocks);
   return status(hipGetLastError());
 }
 
-int grok_moe_probe_clock(int workgroups, uint64_t ticks, uint64_t* out, hipStream_t stream) {
+PROBE_API int grok_moe_probe_clock(int workgroups, uint64_t ticks, uint64_t* out, hipStream_t stream) {
   if (out == nullptr || workgroups < 1 || workgroups > 1024) return -1;
   clock_kernel<<<workgroups, 64, 0, stream>>>(ticks, out);
   return status(hipGetLastError());
 }
 
-int grok_moe_probe_wall_clock_khz(void) {
+PROBE_API int grok_moe_probe_wall_clock_khz(void) {
   int dev = 0, khz = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;

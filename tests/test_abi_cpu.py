@@ -219,7 +219,7 @@ def test_probe_library_exports_its_header():
     P = ctypes.CDLL(build.PROBE_LIB)
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "grok_moe_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(grok_moe_probe_[a-z_0-9]+)\s*\(", text)))
-    assert len(names) == 4
+    assert len(names) == 5
     for n in names:
         assert hasattr(P, n), n
     f = P.grok_moe_probe_read
