@@ -22,23 +22,31 @@ __device__ __forceinline__ uint32_t f2bf(float v) {
   uint32_t u = __float_as_uint(v);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
 
 // GELU in the exact (erf) form, 0.5 z (1 + erf(z / sqrt 2)), with erf evaluated by Abramowitz & Stegun,
 // Handbook of Mathematical Functions, formula 7.1.26 (|error of erf| <= 1.5e-7, far below the bf16 rounding of
-// h): erf(a) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-a^2), t = 1 / (1 + p a), for a >= 0, extended
-// by odd symmetry.  Branch-free.
+// h): erf(a) = 1 - P(t) exp(-a^2), P(t) = a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5, t = 1 / (1 + p a), for a >= 0,
+// extended by odd symmetry.  With a = |z| / sqrt 2 that gives GELU(z) = max(z, 0) - 0.5 |z| P(t) exp(-a^2) for
+// either sign of z (for z < 0 this avoids the cancellation of 1 + erf(z / sqrt 2)).  Branch-free.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float a = fabsf(z) * 0.70710678118654752440f;
+  const float az = fabsf(z);
+  const float a = az * 0.70710678118654752440f;
   const float t = __builtin_amdgcn_rcpf(__fmaf_rn(0.3275911f, a, 1.0f));
   float poly = __fmaf_rn(1.061405429f, t, -1.453152027f);
   poly = __fmaf_rn(poly, t, 1.421413741f);
   poly = __fmaf_rn(poly, t, -0.284496736f);
   poly = __fmaf_rn(poly, t, 0.254829592f);
   poly *= t;
-  const float erfa = 1.0f - poly * __expf(-a * a);
-  const float erfz = copysignf(erfa, z);
-  return 0.5f * z * (1.0f + erfz);
+  const float pe = poly * __expf(-a * a);
+  return __fmaf_rn(-0.5f * az, pe, fmaxf(z, 0.0f));
+}
+
+// Two floats -> two bf16 (round to nearest, ties to even, as f2bf for finite values; one v_cvt_pk_bf16_f32), lo
+// in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 // One gfx950 bf16 MFMA, 16x16 output, K = 32 (8 bf16 per lane in each operand).

@@ -459,11 +459,18 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {  // rows r and r + 1 of the column: one packed conversion
           const int r = wm * (TBM / 2) + i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;
-          const float a = INT8 ? acc[i][jn][v] * sa : acc[i][jn][v];
-          const float b = INT8 ? acc[i][2 + jn][v] * sb : acc[i][2 + jn][v];
-          ht[r * 128 + c] = uint16_t(f2bf(gelu_erf(a) * b));
+          float hv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float a = INT8 ? acc[i][jn][v + u] * sa : acc[i][jn][v + u];
+            const float b = INT8 ? acc[i][2 + jn][v + u] * sb : acc[i][2 + jn][v + u];
+            hv[u] = gelu_erf(a) * b;
+          }
+          const uint32_t pk = pack_bf16(hv[0], hv[1]);
+          ht[r * 128 + c] = uint16_t(pk);
+          ht[(r + 1) * 128 + c] = uint16_t(pk >> 16);
         }
     }
     lds_barrier();

@@ -69,9 +69,13 @@ __device__ __forceinline__ void tile_rows(int n, int m, int* r0, int* rows) {
 
 // Tile L (in the order below) among the row tiles R of TBM rows: (expert, first row slot, valid rows, column tile).
 // Order: expert -> group of NGROUP column tiles -> row tile -> column tile.
+// The expert's first slot is the running sum of the counts before it (offsets[e] as the binning step writes it),
+// so that no dependent load of offsets sits in the tile's prologue.
 template <int NGROUP, Rows R, int TBM, bool MID>
 __device__ __forceinline__ bool locate(const int32_t* counts, const int32_t* offsets, int E, int NT, int L,
                                        int* e_out, int* row0_out, int* rows_out, int* nt_out) {
+  (void)offsets;
+  int first = 0;
   for (int e = 0; e < E; ++e) {
     const int n = counts[e];
     const int mt = row_tiles<R, TBM, MID>(n);
@@ -85,11 +89,12 @@ __device__ __forceinline__ bool locate(const int32_t* counts, const int32_t* off
       *e_out = e;
       int r0, rows;
       tile_rows<R, TBM>(n, m, &r0, &rows);
-      *row0_out = offsets[e] + r0;
+      *row0_out = first + r0;
       *rows_out = rows;
       return true;
     }
     L -= te;
+    first += n;
   }
   return false;
 }
