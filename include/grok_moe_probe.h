@@ -23,8 +23,9 @@ extern "C" {
 #endif
 
 /* Streaming read of `bytes` bytes (a multiple of 16) at `buf` with 16-byte vector loads, grid-stride over
- * `workgroups` workgroups of 256 threads; nontemporal != 0 sets the nontemporal hint on every load.  Each wave
- * folds what it read by XOR into one word of sink [workgroups * 4] (so no load can be removed). */
+ * `workgroups` workgroups of 256 threads, 16 loads in flight per lane; nontemporal != 0 sets the nontemporal hint on
+ * every load.  Each wave folds what it read by XOR into one word of sink [workgroups * 4] (so no load can be
+ * removed). */
 int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups, int nontemporal, uint32_t* sink,
                         hipStream_t stream);
 

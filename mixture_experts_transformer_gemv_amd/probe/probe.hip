@@ -19,21 +19,24 @@ __device__ __forceinline__ u32x4_t ld16(const u32x4_t* p) {
   else return *p;
 }
 
-template <bool NT>
+// UNROLL independent 16-byte loads in flight per lane per iteration (the layer's weight streams keep about 16).
+template <bool NT, int UNROLL>
 __global__ __launch_bounds__(256) void read_kernel(const u32x4_t* __restrict__ p, size_t n16, uint32_t* sink) {
   const size_t stride = size_t(gridDim.x) * 256;
   size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   u32x4_t acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n16; i += 4 * stride) {  // four independent loads in flight per lane
-    const u32x4_t a = ld16<NT>(p + i), b = ld16<NT>(p + i + stride), c = ld16<NT>(p + i + 2 * stride),
-                  d = ld16<NT>(p + i + 3 * stride);
-    acc ^= a ^ b ^ c ^ d;
+  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+    u32x4_t v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = ld16<NT>(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc ^= v[u];
   }
   for (; i < n16; i += stride) acc ^= ld16<NT>(p + i);
-  uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v ^= __shfl_xor(v, m, 64);
-  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = v;
+  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m, 64);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
 }
 
 __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
@@ -110,8 +113,8 @@ PROBE_API int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups,
                         hipStream_t stream) {
   if (!aligned16(buf) || sink == nullptr || bytes % 16 != 0 || workgroups < 1 || workgroups > (1 << 20)) return -1;
   const u32x4_t* p = static_cast<const u32x4_t*>(buf);
-  if (nontemporal) read_kernel<true><<<workgroups, 256, 0, stream>>>(p, bytes / 16, sink);
-  else read_kernel<false><<<workgroups, 256, 0, stream>>>(p, bytes / 16, sink);
+  if (nontemporal) read_kernel<true, 16><<<workgroups, 256, 0, stream>>>(p, bytes / 16, sink);
+  else read_kernel<false, 16><<<workgroups, 256, 0, stream>>>(p, bytes / 16, sink);
   return status(hipGetLastError());
 }
 
