@@ -1,0 +1,329 @@
+// Persistent form of the 256-row up-projection tiles (bf16 weights stored [in, out]), gfx950.
+//
+// Expert FFN, page "A functional bridge between openai/grok and xai-org/grok-1" (architecture diagram):
+// h = GELU(x W1) (*) (x Wv), per assignment slot, rounded once to bf16.
+//
+// The tile body is that of expert_tiled_dma.hip (256 x 256 output tiles of W1|Wv columns, 32-deep K steps in a
+// 4-deep LDS ring filled by direct global -> LDS copies, LDS transpose reads of the weights, one barrier per K
+// step, copies spread over both half-steps).  What differs is the life of a workgroup: one workgroup per CU walks
+// the tiles of its XCD (tile i, i + W, i + 2 W, ... of the XCD's contiguous range in the order of tiles.h, W =
+// workgroups per XCD), and the K steps of consecutive tiles form one stream:
+//   * the last three K steps of a tile copy the first three steps of the next tile (in the ring slots that follow),
+//     so a tile starts with its first steps already in LDS, and the GELU epilogue of one tile runs while the next
+//     tile's first copies are in flight;
+//   * the epilogue stages the h tile in the ring slot of the tile's last K step (free: the next tile's first three
+//     steps take the other three slots) and in 32 KB beside the ring;
+//   * the activation row map (perm) of the tile after next is loaded during the epilogue, so its copy offsets are
+//     ready when its copies start.
+// The copy waits count vector memory operations in issue order, so every epilogue issues the same number of them:
+// 4 row-map loads (of row 0 when there is no tile after next) and 16 stores of 16 bytes per lane (buffer stores;
+// rows past the expert's end get an out-of-range offset and are dropped).  The first tile starts with the same
+// number of loads and dropped stores.  Workgroups never wait for each other.
+#include "common.h"
+#include "dma.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace gm {
+
+namespace {
+constexpr int PBK = 32;                       // K per ring stage
+constexpr int P_A = 256 * PBK * 2;            // bytes: activation stage [256 rows][32 k]
+constexpr int P_B = PBK * 128 * 2;            // bytes: one weight sub-tile [32 k][128 columns]
+constexpr int P_STAGE = P_A + 2 * P_B;        // 32 KB
+constexpr int P_EXTRA = 128 * 128 * 2;        // rows 128..255 of the staged h tile
+constexpr int P_LDS = 4 * P_STAGE + P_EXTRA;  // 160 KB
+constexpr int P_AP = 4, P_CPS = 8;            // activation copies, all copies per wave and K step
+constexpr int P_C0 = 4, P_C1 = 4;             // copies in half-step 0, 1
+constexpr int P_NMF = 16, P_NPIECE = 12, P_NSLOT = 16;
+constexpr int P_EPI = 4 + 16;                 // vector memory operations of one epilogue
+constexpr uint32_t P_OOR = 0x80000000u;       // out-of-range buffer offset (x and h are < 2^31 bytes)
+
+// One accumulator register read into a VGPR where it is used.  (Left to the compiler, the epilogue copies all 256
+// accumulators out of the AGPRs at once and spills.)  The caller keeps the MFMA result hazard: wait states between
+// the last MFMA and the first read.
+__device__ __forceinline__ float agpr_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+struct PTile {
+  int e, row0, rows, ntile;
+};
+
+// Copy parameters of one tile: activation offsets of the lane's 4 pieces, the wave's weight sub-tile base, and the
+// K of step s (k0 + s * kst; kst = 0 repeats one step: the copies past the last tile re-read a step nobody reads).
+struct PCopy {
+  uint32_t av[P_AP];
+  const uint16_t* bb;
+  int k0, kst;
+};
+}  // namespace
+
+__global__ __launch_bounds__(256) void tiled_up_persist_kernel(const uint16_t* __restrict__ A,
+                                                               const uint16_t* __restrict__ W1,
+                                                               const uint16_t* __restrict__ Wv,
+                                                               const int32_t* __restrict__ counts,
+                                                               const int32_t* __restrict__ perm, uint32_t a_bytes,
+                                                               int K, int N, int E, uint16_t* __restrict__ h,
+                                                               uint32_t h_bytes) {
+  constexpr int NG = tile::Group<2>::N;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[P_LDS];
+  lds_u8* lds = (lds_u8*)smem;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NT = N / 128;
+  const int KT = K / PBK;
+
+  // ---- this workgroup's tiles: XCD x = blockIdx.x % 8 owns tiles [x chunk, (x + 1) chunk) of the 256-row launch
+  int total = 0;
+  for (int e = 0; e < E; ++e) total += tile::row_tiles<tile::Rows::Main, 256, true>(counts[e]);
+  total *= NT;
+  const int chunk = (total + 7) >> 3;
+  const int x = blockIdx.x & 7, W = gridDim.x >> 3;
+  const int qend = min(chunk, total - x * chunk);  // tiles of this XCD
+  auto tile_at = [&](int q, PTile& t) {
+    tile::locate<NG, tile::Rows::Main, 256, true>(counts, nullptr, E, NT, x * chunk + q, &t.e, &t.row0, &t.rows,
+                                                  &t.ntile);
+  };
+  int q = blockIdx.x >> 3;
+  if (q >= qend) return;  // whole workgroup
+
+  // ---- copies (as expert_tiled_dma.hip, 256-row tiles, [in, out] bf16 weights)
+  const u32x4_t a_rsrc = buffer_rsrc(A, a_bytes);
+  const int sub = wave >> 1;
+  const uint16_t* bmat = sub ? Wv : W1;
+  const uint32_t b_voff = uint32_t(((lane >> 4) * N + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)))) * 2);
+  const uint32_t a_dst = lds0 + uint32_t(64 * wave) * (PBK * 2);
+  const uint32_t b_dst = lds0 + P_A + uint32_t(sub) * P_B + uint32_t(16 * (wave & 1)) * 256;
+  // activation row of the lane's piece i: tile row 64 wave + 16 i + lane / 4
+  auto piece_row = [&](int i) { return 64 * wave + 16 * i + (lane >> 2); };
+  auto make_copy = [&](const PTile& t, const int32_t (&pv)[P_AP], PCopy& c) {
+#pragma unroll
+    for (int i = 0; i < P_AP; ++i) {
+      const int r = piece_row(i);
+      c.av[i] = r < t.rows ? (uint32_t(pv[i]) * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u : P_OOR;
+    }
+    c.bb = bmat + size_t(t.e) * K * N + size_t(16 * (wave & 1)) * N + t.ntile * 128;
+    c.k0 = 0;
+    c.kst = PBK;
+  };
+  // the lane's 4 row-map entries of tile t (row 0 of the map if there is no tile: the loads always happen)
+  auto load_rows = [&](bool has, const PTile& t, int32_t (&pv)[P_AP]) {
+#pragma unroll
+    for (int i = 0; i < P_AP; ++i) {
+      const int r = min(piece_row(i), t.rows - 1);
+      pv[i] = perm[has ? t.row0 + r : 0];
+    }
+  };
+  // piece n of the copies of step s of tile c into ring slot `slot`
+  auto copy_piece = [&](const PCopy& c, int slot, int s, int n) {
+    const uint32_t so = uint32_t(slot) * P_STAGE;
+    const int k = c.k0 + s * c.kst;
+    if (n < P_AP)
+      b2lds16(a_rsrc, uint32_t(k) * 2u, c.av[n], a_dst + so + uint32_t(16 * n) * (PBK * 2));
+    else
+      g2lds16(c.bb + size_t(k) * N + size_t(4 * (n - P_AP)) * N, b_voff, b_dst + so + uint32_t(4 * (n - P_AP)) * 256);
+  };
+
+  // ---- fragments (waves 2 x 2: rows wm * 128 .. +127 as 4 blocks of 32, 4 column sub-tiles of 32)
+  const int wm = wave >> 1, wn = wave & 1;
+  // A fragment (block i, half ks): row wm * 128 + 32 i + (lane & 31), k chunk (2 ks + (lane >> 5)) ^ ((row >> 2) & 3);
+  // the block only adds 32 i rows and the swizzle depends on lane & 31 alone, so one base offset per ks.
+  int a_base[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int r = wm * 128 + (lane & 31);
+    a_base[ks] = r * (PBK * 2) + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
+  }
+  // B halves hh of sub-tile j, half-step ks: lane addresses k row 16 ks + 8 (G >> 1) + 4 hh + (s >> 2) and columns
+  // col .. +3 (G = lane >> 4, s = lane & 15, col = wn * 64 + 32 (j & 1) + 16 (G & 1) + 4 (s & 3), sub-tile j >> 1).
+  // k & 3 = (s >> 2) & 3 for every ks, hh, so ks and hh only add whole rows: one base per j & 1.
+  int b_base[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int G = lane >> 4, s = lane & 15;
+    const int col = wn * 64 + jj * 32 + 16 * (G & 1) + 4 * (s & 3);
+    const int k = 8 * (G >> 1) + (s >> 2);
+    b_base[jj] = P_A + k * 256 + 16 * ((col >> 3) ^ (4 * (k & 3))) + 2 * (col & 7);
+  }
+  u32x4_t fa[2][4], fb[2][4];
+  u32x2_t bh[2][4][2];
+  auto read_piece = [&](int buf, const lds_u8* st, int ks, int p) {
+    if (p == 0) {
+      fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_base[ks]);
+    } else if (p <= 8) {
+      const int j = (p - 1) >> 1, hh = (p - 1) & 1;
+      bh[buf][j][hh] = lds_tr16(st + b_base[j & 1] + (j >> 1) * P_B + (16 * ks + 4 * hh) * 256);
+    } else {
+      const int i = p - 8;
+      fa[buf][i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_base[ks] + i * 32 * (PBK * 2));
+    }
+  };
+  auto join_b = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[buf][j] = u32x4_t{bh[buf][j][0][0], bh[buf][j][0][1], bh[buf][j][1][0], bh[buf][j][1][1]};
+  };
+  f32x16_t acc[4][4];
+  const f32x16_t zero16 = {};
+
+  // One K step kt of the tile whose step 0 sits in ring slot r0, issuing the copies of step s of tile c into the
+  // slot of step kt + 3.  EX: vector memory operations issued between the copies of step kt + 2 and those of step
+  // kt + 3 (an epilogue's, for the first two steps of a tile).  FIRST: the tile's first step (accumulators start
+  // from zero).
+  int r0 = 0;
+  auto kstep = [&](int kt, const PCopy& c, int s, auto ex, auto first) {
+    constexpr int EX = decltype(ex)::value;
+    constexpr bool FIRST = decltype(first)::value;
+    const lds_u8* st = lds + ((r0 + kt) & 3) * P_STAGE;
+    const int cslot = (r0 + kt + 3) & 3;
+#pragma unroll
+    for (int m = 0; m < P_NSLOT; ++m) {
+      acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], FIRST ? zero16 : acc[m >> 2][m & 3]);
+      if (m < P_NPIECE) read_piece(1, st, 1, m);
+#pragma unroll
+      for (int cc = 0; cc < P_C0; ++cc)
+        if (m == (cc * P_NSLOT) / P_C0) copy_piece(c, cslot, s, cc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    join_b(1);
+    wait_vm<P_CPS + P_C0 + EX>();  // step kt + 1 landed
+    lds_barrier();
+    const lds_u8* nst = lds + ((r0 + kt + 1) & 3) * P_STAGE;
+#pragma unroll
+    for (int m = 0; m < P_NSLOT; ++m) {
+      acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
+#pragma unroll
+      for (int cc = 0; cc < P_C1; ++cc)
+        if (m == (cc * P_NSLOT) / P_C1) copy_piece(c, cslot, s, P_C0 + cc);
+      if (m < P_NPIECE) read_piece(0, nst, 0, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    join_b(0);
+  };
+
+  // ---- h stores: 16-byte buffer stores; an offset at or past h_bytes (rows past the tile's end) is dropped
+  const __amdgpu_buffer_rsrc_t h_rsrc = __builtin_amdgcn_make_buffer_rsrc(h, (short)0, int(h_bytes), 0x00020000);
+  auto store_h = [&](uint32_t voff, u32x4_t v) { __builtin_amdgcn_raw_buffer_store_b128(v, h_rsrc, int(voff), 0, 0); };
+
+  // ---- first tile: its row map, the copies of its first three steps, the row map of the next tile, and 16
+  // dropped stores, so that the wait counts of every tile are those of the steady state
+  PTile cur, nxt;
+  tile_at(q, cur);
+  nxt = cur;
+  int32_t pv[P_AP];
+  load_rows(true, cur, pv);
+  PCopy cc, nc;
+  make_copy(cur, pv, cc);
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int n = 0; n < P_CPS; ++n) copy_piece(cc, s, s, n);
+  bool has_next = q + W < qend;
+  if (has_next) tile_at(q + W, nxt);
+  load_rows(has_next, nxt, pv);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) store_h(P_OOR + 16u * uint32_t(i), u32x4_t{0u, 0u, 0u, 0u});  // distinct: all issued
+  wait_vm<2 * P_CPS + P_EPI>();  // step 0 landed
+  lds_barrier();
+
+  for (;;) {
+    // fragments of step 0, half 0 (landed and visible: the wait and barrier before)
+    const lds_u8* st0 = lds + r0 * P_STAGE;
+#pragma unroll
+    for (int p = 0; p < P_NPIECE; ++p) read_piece(0, st0, 0, p);
+    join_b(0);
+    kstep(0, cc, 3, std::integral_constant<int, P_EPI>{}, std::true_type{});
+    kstep(1, cc, 4, std::integral_constant<int, P_EPI>{}, std::false_type{});
+    for (int kt = 2; kt < KT - 3; ++kt) kstep(kt, cc, kt + 3, std::integral_constant<int, 0>{}, std::false_type{});
+    // the next tile's copy offsets (its row map was loaded during the last epilogue and has landed: the waits
+    // above cover every operation issued before the copies of step 3); past the last tile, the current tile's
+    // last step again
+    if (has_next) {
+      make_copy(nxt, pv, nc);
+    } else {
+      nc = cc;
+      nc.k0 = (KT - 1) * PBK;
+      nc.kst = 0;
+    }
+    for (int kt = KT - 3; kt < KT; ++kt)
+      kstep(kt, nc, kt + 3 - KT, std::integral_constant<int, 0>{}, std::false_type{});
+
+    // ---- epilogue: the row map of the tile after next, then the GELU product staged in LDS and stored.  32 wait
+    // states after the last MFMA before its accumulators are read.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    const int qn2 = q + 2 * W;
+    const bool has_next2 = has_next && qn2 < qend;
+    PTile nxt2 = nxt;
+    if (has_next2) tile_at(qn2, nxt2);
+    load_rows(has_next2, nxt2, pv);
+    // staging: rows wm * 128 .. +127 of the tile; wm = 0 in the ring slot of the last K step, wm = 1 beside the
+    // ring.  Every wave passed the barrier of the last K step, after which nobody reads that slot.
+    const int xslot = (r0 + KT - 1) & 3;
+    __attribute__((address_space(3))) uint16_t* ht0 = (__attribute__((address_space(3))) uint16_t*)(lds + xslot * P_STAGE);
+    __attribute__((address_space(3))) uint16_t* ht1 = (__attribute__((address_space(3))) uint16_t*)(lds + 4 * P_STAGE);
+    {
+      __attribute__((address_space(3))) uint16_t* ht = wm ? ht1 : ht0;
+      const int lr = lane & 31, rhalf = 4 * (lane >> 5);
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn) {
+        const int c = wn * 64 + jn * 32 + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {  // rows r and r + 1 of the column: one packed conversion
+            const int r = i * 32 + (v & 3) + 8 * (v >> 2) + rhalf;  // row within the wave's 128
+            const float a0 = agpr_read(acc[i][jn][v]), b0 = agpr_read(acc[i][2 + jn][v]);
+            const float a1 = agpr_read(acc[i][jn][v + 1]), b1 = agpr_read(acc[i][2 + jn][v + 1]);
+            const uint32_t pk = pack_bf16(gelu_erf(a0) * b0, gelu_erf(a1) * b1);
+            ht[r * 128 + c] = uint16_t(pk);
+            ht[(r + 1) * 128 + c] = uint16_t(pk >> 16);
+          }
+      }
+    }
+    lds_barrier();
+    const int nbase = cur.ntile * 128;
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      const int chunk16 = qq * 256 + tid;  // 16-byte chunk: tile row chunk16 / 16, columns 8 (chunk16 % 16) ..
+      const int r = chunk16 >> 4, c8 = (chunk16 & 15) * 8;
+      const __attribute__((address_space(3))) uint16_t* src = (qq < 8 ? ht0 + r * 128 : ht1 + (r - 128) * 128) + c8;
+      const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(src);
+      const uint32_t voff = r < cur.rows ? (uint32_t(cur.row0 + r) * uint32_t(N) + uint32_t(nbase + c8)) * 2u : P_OOR;
+      store_h(voff, v);
+    }
+    lds_barrier();  // every wave read its staged rows: the next tile may copy into that slot
+    if (!has_next) break;
+    r0 = (r0 + KT) & 3;
+    q += W;
+    cur = nxt;
+    cc = nc;
+    has_next = has_next2;
+    nxt = nxt2;
+  }
+}
+
+// The up-projection's 256-row tiles with the persistent kernel above: one workgroup per CU (a multiple of 8, so
+// that workgroup i runs on XCD i % 8).  Requires bf16 [in, out] weights, K = d a multiple of 32 with at least 8 K
+// steps, and x and h below 2^31 bytes (checked by the caller).
+hipError_t launch_up_persist(const uint16_t* x, const void* w1, const void* wv, const int32_t* counts,
+                             const int32_t* perm, int d, int f, int E, int slots, uint16_t* h, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const int wg = (cus / 8) * 8;
+  if (wg < 8 || d % PBK != 0 || d / PBK < 8) return hipErrorInvalidValue;
+  const size_t xbytes = size_t(slots / 2) * d * 2, hbytes = size_t(slots) * f * 2;
+  if (xbytes >= (size_t(1) << 31) || hbytes >= (size_t(1) << 31)) return hipErrorInvalidValue;
+  tiled_up_persist_kernel<<<dim3(wg), dim3(256), 0, s>>>(x, static_cast<const uint16_t*>(w1),
+                                                        static_cast<const uint16_t*>(wv), counts, perm,
+                                                        uint32_t(xbytes), d, f, E, h, uint32_t(hbytes));
+  return hipGetLastError();
+}
+
+}  // namespace gm

@@ -672,9 +672,18 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
     tiled_dma_small_kernel<OI, I8><<<grid_s, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, offsets, perm,  \
                                                              xb, d, f, E, h);                                   \
   } while (0)
-  if (int8) GM_UPD(false, true);
-  else if (outin) GM_UPD(true, false);
-  else GM_UPD(false, false);
+  if (int8) {
+    GM_UPD(false, true);
+  } else if (outin) {
+    GM_UPD(true, false);
+  } else if (d / BK >= 8) {  // bf16 [in, out]: the persistent form of the 256-row launch (expert_persist.hip)
+    const hipError_t err = launch_up_persist(x, w1, wv, counts, perm, d, f, E, slots, h, s);
+    if (err != hipSuccess) return err;
+    tiled_dma_small_kernel<false, false><<<grid_s, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, offsets, perm,
+                                                                  xb, d, f, E, h);
+  } else {
+    GM_UPD(false, false);
+  }
 #undef GM_UPD
   return hipGetLastError();
 }

@@ -89,6 +89,10 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
 hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const uint16_t* s2, int64_t s_estride, bool int8,
                                  bool outin, const int32_t* counts, const int32_t* offsets, int d, int f, int E,
                                  int slots, int S, float* y, hipStream_t s);
+// The up-projection's 256-row tiles for bf16 [in, out] weights in one persistent launch (one workgroup per CU;
+// d / 32 >= 8).
+hipError_t launch_up_persist(const uint16_t* x, const void* w1, const void* wv, const int32_t* counts,
+                             const int32_t* perm, int d, int f, int E, int slots, uint16_t* h, hipStream_t s);
 
 // fp32 layer (VALU, LDS tiles).
 hipError_t launch_up_f32(const float* x, const float* w1, const float* wv, bool outin, const int32_t* counts,

@@ -3,6 +3,7 @@
 // with its trace points enabled; the layer library itself carries none.
 #define GROK_MOE_TILE_TRACE 1
 #include "../csrc/expert_tiled_dma.hip"
+#include "../csrc/expert_persist.hip"  // the launchers above refer to it
 
 #include "../../include/grok_moe_probe.h"
 
