@@ -508,6 +508,8 @@ hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t*
   const dim3 grid((d + 511) / 512, S, E), block(256);
   const int64_t stride = int64_t(slots) * d;
   const bool grouped = int8 && sl.gsize < f;
+  if (int8 && !grouped && !outin)  // LDS-staged weights (expert_stream_lds.hip)
+    return launch_down_stream_lds(h, w2, s2, sl.estride, counts, offsets, d, f, E, slots, S, mt, y, s);
 #define GM_DOWN(I8, MT, GR, OI) down_stream_kernel<I8, MT, GR, OI><<<grid, block, 0, s>>>(h, w2, s2, sl, counts, \
                                                                                       offsets, d, f, S, stride, y)
 #define GM_DOWN_MT(I8, GR, OI) do { if (mt == 1) GM_DOWN(I8, 1, GR, OI); else GM_DOWN(I8, 2, GR, OI); } while (0)

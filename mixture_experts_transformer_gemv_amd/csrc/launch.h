@@ -49,6 +49,12 @@ hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t*
                               const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                               bool int8, int mt, float* y, hipStream_t s);
 
+// int8 [in, out] weights with one scale per column (scales at expert stride s_estride): the weight-streaming
+// down-projection with the weights staged in per-wave LDS rings (deeper streams than registers allow).
+hipError_t launch_down_stream_lds(const uint16_t* h, const void* w2, const uint16_t* s2, int64_t s_estride,
+                                  const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots,
+                                  int S, int mt, float* y, hipStream_t s);
+
 // Streaming kernels for weights stored [E, out, in]: weight rows staged in LDS by direct copies of 256-byte
 // pieces.  mt = 16-row token tiles per pass (1 or 2).  Usable when oi_stream_fits(K chunk, ...).
 bool oi_stream_fits(int Kc, bool int8, ScaleLayout sl, int K);
