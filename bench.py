@@ -291,7 +291,9 @@ def roofline(w, layer, kms, ms, weight_layout, ceilings):
         fl = up_flops(w, T)
         ach = fl / (kms[0] * 1e-3) / 1e12
         grouped = w.groups_up > 1 or w.groups_down > 1
-        if w.dtype == 1 or (not grouped and not oi):
+        if w.dtype == 1 and not oi:
+            kname = "tiled_up_persist_kernel + tiled_dma_small_kernel"
+        elif w.dtype == 1 or (not grouped and not oi):
             kname = (f"tiled_dma_kernel<2, {str(oi).lower()}, {'true' if w.dtype == 2 else 'false'}, 256> + "
                      "tiled_dma_small_kernel")
         elif grouped and not oi and w.groups_up <= 8:

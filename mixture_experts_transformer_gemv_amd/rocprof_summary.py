@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 output for the layer's kernels (CSV output of rocprofv3 --kernel-trace or --pmc).
 
-    python -m mixture_experts_transformer_gemv_amd.rocprof_summary trace DIR
-        per kernel and grid size: dispatches, average / min / max duration (us), share of GPU time (markdown)
+    python -m mixture_experts_transformer_gemv_amd.rocprof_summary trace DIR [--split REGEX:US]
+        per kernel and grid size: dispatches, average / min / max duration (us), share of GPU time (markdown);
+        --split lists a kernel's dispatches up to and above a duration in two rows
     python -m mixture_experts_transformer_gemv_amd.rocprof_summary traffic --fetch DIR --write DIR --workload W
             --kernel REGEX [--kernel REGEX] --algorithmic-bytes B --source FILE... --out RECORD.json
         HBM-side bytes per launch of a projection (the sum over its kernels matched by the regexes): FETCH_SIZE and
@@ -56,12 +57,18 @@ def short_name(name: str) -> str:
     return n.strip()
 
 
-def trace(directory: str) -> str:
+def trace(directory: str, split=()) -> str:
+    """split: (regex, microseconds) pairs; dispatches of a matching kernel are listed in two rows, up to and above
+    that duration (launches of one grid size by different workloads)."""
     per = defaultdict(list)
     for r in _rows(directory, "kernel_trace.csv"):
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         grid = r.get("Grid_Size") or r.get("Grid_Size_X") or ""
-        per[(short_name(r["Kernel_Name"]), grid)].append(dur)
+        name = short_name(r["Kernel_Name"])
+        for rx, us in split:
+            if re.search(rx, name):
+                name += f" ({'<=' if dur <= us else '>'} {us:g} us)"
+        per[(name, grid)].append(dur)
     total = sum(sum(v) for v in per.values())
     lines = ["| kernel | grid size | dispatches | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
              "|---|---:|---:|---:|---:|---:|---:|---:|"]
@@ -177,6 +184,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("dir")
+    t.add_argument("--split", action="append", default=[], metavar="REGEX:US",
+                   help="list the dispatches of the matching kernel up to and above US microseconds in two rows")
     c = sub.add_parser("counters")
     c.add_argument("dir")
     b = sub.add_parser("busy")
@@ -193,7 +202,7 @@ def main(argv=None):
     f.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace(a.dir))
+        print(trace(a.dir, [(x.rsplit(":", 1)[0], float(x.rsplit(":", 1)[1])) for x in a.split]))
     elif a.cmd == "counters":
         print(counters(a.dir))
     elif a.cmd == "busy":
