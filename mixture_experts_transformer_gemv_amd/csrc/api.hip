@@ -163,7 +163,7 @@ hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, 
   if (p.stream)
     return gm::launch_up_stream(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
                                 static_cast<const uint16_t*>(sv), up_layout(sp, d, f), sp.outin, counts, offsets,
-                                perm, int(d), int(f), E, i8, p.mt, static_cast<uint16_t*>(h), s);
+                                perm, int(d), int(f), E, int(p.slots), i8, p.mt, static_cast<uint16_t*>(h), s);
   return gm::launch_up_tiled(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
                              static_cast<const uint16_t*>(sv), up_layout(sp, d, f), sp.outin, counts, offsets, perm,
                              int(d), int(f), E, int(p.slots), i8, static_cast<uint16_t*>(h), s);

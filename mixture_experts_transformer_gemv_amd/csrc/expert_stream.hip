@@ -459,6 +459,94 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
   }
 }
 
+// bf16 [in, out] up-projection for 16-row token tiles with 64 columns per wave: lane l covers columns
+// n0 + 4 (l & 15) .. +3 and k rows 8 (l >> 4) .. +7 of each 32-deep step as 8-byte row pieces (a wave reads
+// 128-byte strips of each weight row), transposed in registers into 4 MFMA operands.  Half the accumulators of
+// up_stream_kernel, so two waves fit per SIMD.  With enough experts hit to fill the chip this streams the weights
+// faster (measured on MI355X at T = 8, Grok-1 shape: 6.8 -> 7.2 TB/s); with a few experts the 16-byte pieces
+// of up_stream_kernel keep more bytes in flight per wave and win.  Each output element is the same MFMA over the
+// same k in the same order as in up_stream_kernel: the results are bit-identical.
+__global__ __launch_bounds__(256, 2) void up_stream_narrow_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ w1,
+                                                                  const uint16_t* __restrict__ wv,
+                                                                  const int32_t* __restrict__ counts,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  const int32_t* __restrict__ perm, int d, int f,
+                                                                  uint16_t* __restrict__ h) {
+  const int e = blockIdx.y;
+  const int n_e = counts[e];
+  if (n_e == 0) return;
+  const int off = offsets[e];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int n0 = (blockIdx.x * 4 + wave) * 64;
+  if (n0 >= f) return;  // no workgroup barrier in this kernel
+  const int col = n0 + 4 * c16;
+  const size_t lane_base = size_t(e) * d * f + size_t(8 * g) * f + col;
+  struct Step {
+    u32x2_t b1[8], b2[8];
+    u32x4_t a;
+  };
+  // 8 rows of 4 bf16 columns -> 4 operands (column c: its 8 k values, two per dword)
+  auto transpose = [](const u32x2_t r[8], u32x4_t t[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t[c][q] = __builtin_amdgcn_perm(r[2 * q + 1][c >> 1], r[2 * q][c >> 1], sel);
+    }
+  };
+  for (int mb = 0; mb < n_e; mb += 16) {
+    const int m = mb + c16;
+    const bool aval = m < n_e;
+    const uint16_t* arow = x + size_t(aval ? perm[off + m] : 0) * d + 8 * g;
+    f32x4_t acc1[4], acc2[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc1[c] = f32x4_t{0, 0, 0, 0};
+      acc2[c] = f32x4_t{0, 0, 0, 0};
+    }
+    auto load = [&](Step& st, int k0) {
+      const size_t rb = lane_base + size_t(k0) * f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        st.b1[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(w1 + rb + size_t(r) * f));
+        st.b2[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(wv + rb + size_t(r) * f));
+      }
+      st.a = aval ? *reinterpret_cast<const u32x4_t*>(arow + k0) : u32x4_t{0, 0, 0, 0};
+    };
+    auto compute = [&](const Step& st) {
+      u32x4_t t[4];
+      transpose(st.b1, t);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc1[c] = mfma16x16x32(st.a, t[c], acc1[c]);
+      transpose(st.b2, t);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc2[c] = mfma16x16x32(st.a, t[c], acc2[c]);
+    };
+    // d is a multiple of 64: two 32-deep steps per iteration, the next step's loads in flight during compute
+    Step sa, sb;
+    load(sa, 0);
+    for (int k0 = 0; k0 < d; k0 += 64) {
+      load(sb, k0 + 32);
+      compute(sa);
+      if (k0 + 64 < d) load(sa, k0 + 64);
+      compute(sb);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = mb + 4 * g + v;
+      if (r < n_e) {
+        u32x2_t o;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          o[j] = pack_bf16(gelu_erf(acc1[2 * j][v]) * acc2[2 * j][v], gelu_erf(acc1[2 * j + 1][v]) * acc2[2 * j + 1][v]);
+        *reinterpret_cast<u32x2_t*>(h + size_t(off + r) * f + col) = o;
+      }
+    }
+  }
+}
+
 // The up-projection's split of the d axis over the 4 waves of a workgroup (KS = 4) when its grid of one workgroup
 // per 512 columns and expert would leave CUs idle (a layer's share of d_ff on one of several GPUs; measured at
 // f = 4096: 64 workgroups, 3.3 TB/s).  d / 4 a multiple of 128 (the stages of the [out, in] kernel, which splits
@@ -469,12 +557,27 @@ int up_stream_ksplit(int d, int f, int E) {
   return (d % 512 == 0 && ((f + 511) / 512) * E < 256) ? 4 : 1;
 }
 
+// The 64-column bf16 kernel: [in, out] weights, 16-row token tiles, the whole d axis per wave, and enough experts
+// that can be hit for min(slots, E) * f / 256 >= 1024 workgroups (at Grok-1 shape: four or more tokens; measured
+// up-projection ms, up_stream_kernel -> this kernel: T = 1 0.28 -> 0.28 (not taken), T = 2 0.36 -> 0.39, T = 4
+// 0.48 -> 0.45, T = 8 0.95 -> 0.90, T = 16 0.95 -> 0.90).
+bool up_stream_narrow(int d, int f, int E, int slots, bool int8, bool outin, int mt) {
+  return !int8 && !outin && mt == 1 && f % 256 == 0 && up_stream_ksplit(d, f, E) == 1 &&
+         int64_t(slots < E ? slots : E) * (f / 256) >= 1024;
+}
+
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                             const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
-                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, bool int8, int mt,
-                            uint16_t* h, hipStream_t s) {
+                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, bool int8,
+                            int mt, uint16_t* h, hipStream_t s) {
   const dim3 grid((f + 511) / 512, E), block(256);
   const bool grouped = int8 && sl.gsize < d;
+  if (up_stream_narrow(d, f, E, slots, int8, outin, mt)) {
+    up_stream_narrow_kernel<<<dim3(f / 256, E), block, 0, s>>>(x, static_cast<const uint16_t*>(w1),
+                                                               static_cast<const uint16_t*>(wv), counts, offsets,
+                                                               perm, d, f, h);
+    return hipGetLastError();
+  }
   if (up_stream_ksplit(d, f, E) == 4) {
     const dim3 grid4((f + 127) / 128, E);
 #define GM_UP4(I8, MT, GR, OI) up_stream_kernel<I8, MT, GR, OI, 4><<<grid4, block, 0, s>>>(x, w1, wv, s1, sv, sl, \

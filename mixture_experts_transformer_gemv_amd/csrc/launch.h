@@ -41,10 +41,12 @@ hipError_t launch_combine(const float* y, int S, const float* p, const int32_t* 
 // 4 if the streaming up-projection splits d over the waves of a workgroup (small f), else 1; the [in, out] and
 // [out, in] streaming kernels split alike.
 int up_stream_ksplit(int d, int f, int E);
+// true if launch_up_stream runs the 64-column bf16 kernel for this shape (slots = k T)
+bool up_stream_narrow(int d, int f, int E, int slots, bool int8, bool outin, int mt);
 hipError_t launch_up_stream(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                             const uint16_t* sv, ScaleLayout sl, bool outin, const int32_t* counts,
-                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, bool int8, int mt,
-                            uint16_t* h, hipStream_t s);
+                            const int32_t* offsets, const int32_t* perm, int d, int f, int E, int slots, bool int8,
+                            int mt, uint16_t* h, hipStream_t s);
 hipError_t launch_down_stream(const uint16_t* h, const void* w2, const uint16_t* s2, ScaleLayout sl, bool outin,
                               const int32_t* counts, const int32_t* offsets, int d, int f, int E, int slots, int S,
                               bool int8, int mt, float* y, hipStream_t s);
