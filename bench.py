@@ -264,6 +264,17 @@ def stream_path(w) -> bool:
     return w.dtype != 0 and w.T <= (128 if w.dtype == 2 else 96)
 
 
+def stream_up_kernel(w) -> str:
+    """The library's choice of streaming up-projection kernel for [in, out] weights (the rule of
+    up_stream_narrow in csrc/expert_stream.hip: bf16, 16-row token tiles, the whole d axis per wave, and
+    min(2T, E) * f / 256 >= 1024)."""
+    ksplit4 = w.d % 512 == 0 and ((w.f + 511) // 512) * w.E < 256
+    if (w.dtype == 1 and w.T <= 16 and w.f % 256 == 0 and not ksplit4
+            and min(2 * w.T, w.E) * (w.f // 256) >= 1024):
+        return "up_stream_narrow_kernel"
+    return "up_stream_kernel"
+
+
 def roofline(w, layer, kms, ms, weight_layout, ceilings):
     """Roofline of the dominant kernel (the up-projection) and the per-kernel rates."""
     T, nh = w.T, n_hit(layer.counts.cpu().numpy())
@@ -278,7 +289,7 @@ def roofline(w, layer, kms, ms, weight_layout, ceilings):
     elif stream_path(w):  # weight-streaming kernels: HBM-bound
         ub = up_bytes(w, nh, T)
         ach = ub / (kms[0] * 1e-3) / 1e9
-        rl = {"bound": "hbm", "kernel": "oi_stream_kernel<2>" if oi else "up_stream_kernel", "achieved": ach,
+        rl = {"bound": "hbm", "kernel": "oi_stream_kernel<2>" if oi else stream_up_kernel(w), "achieved": ach,
               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
               "traffic": load_traffic(tname, "up"), "algorithmic_bytes": ub}
         if ceilings and ceilings.get("hbm_read_GBps"):
