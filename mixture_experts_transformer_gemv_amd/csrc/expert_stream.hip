@@ -17,9 +17,13 @@
 // (int8: 8-byte) load, already the MFMA operand (int8 converted to bf16).  For one column the four 16-lane
 // groups read 64 contiguous bytes of the row; the next 32-deep step reads the next 64.
 //
-// Up-projection: one wave per 128 columns of both W1 and Wv over the whole d axis (GELU needs the full sum);
+// Up-projection: one wave per 128 columns of both W1 and Wv over the whole d axis (GELU needs the full sum; for bf16
+// 16-row tiles with enough experts hit, up_stream_narrow_kernel below takes 64 columns per wave);
 // h = bf16(GELU(a) * b) is written for the valid token rows.  Down-projection: one wave per 128 columns of W2
 // over one of S chunks of the f axis; fp32 partial sums go to y[S, slots, d] and are added by the combine.
+//
+// The int8 [in, out] down-projection with one scale group stages its weights in LDS instead
+// (expert_stream_lds.hip).
 //
 // int8 scales: with one group along the input axis the scale multiplies the fp32 accumulator once, in the
 // epilogue.  With several groups (GROUPED) the accumulator is kept in units of the current group's scale: on
