@@ -32,7 +32,6 @@ from __future__ import annotations
 import argparse
 import ctypes
 import dataclasses
-import hashlib
 import json
 import os
 import sys
@@ -54,14 +53,6 @@ ALL_CONFIGS = ("decode_bf16", "prefill_bf16", "skew_bf16", "int8_w8", "tiny_f32"
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-
-def source_hash(files) -> str:
-    h = hashlib.sha256()
-    for n in files:
-        with open(os.path.join(ROOT, "mixture_experts_transformer_gemv_amd", "csrc", n), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def parse():
@@ -253,6 +244,7 @@ def load_traffic(workload: str, kernel: str):
         return None
     try:
         rec = json.load(open(p))
+        from mixture_experts_transformer_gemv_amd.rocprof_summary import source_hash
         if rec.get("source_hash") != source_hash(rec["source_files"]):
             return None
         return rec.get("bytes_per_launch")

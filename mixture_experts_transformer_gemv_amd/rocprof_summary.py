@@ -108,11 +108,21 @@ def _sum_kernels(per: dict, regexes) -> tuple[float, list[str]]:
     return total, names
 
 
-def source_hash(files) -> str:
+def code_only(text: str) -> str:
+    """Source text without comments and blank lines, each line stripped: what a kernel is built from (string
+    literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).strip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
+def source_hash(files, directory: str = CSRC) -> str:
+    """Hash of the code (comments and blank lines left out) of a kernel's source files: a counter record stays valid
+    across edits of comments and becomes stale when the code changes."""
     h = hashlib.sha256()
     for n in files:
-        with open(os.path.join(CSRC, n), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(directory, n), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
