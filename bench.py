@@ -436,9 +436,10 @@ class Probe:
 
 
 def tile_trace(probe, layer):
-    """Where the cycles of the prefill kernels go: the 256-row launch of each projection run once more with per-tile
-    timestamps (same kernel, trace points on), on the routing of the last timed step.  Per tile: prologue (start to
-    the first barrier: tile lookup, activation offsets, first copies), K loop, epilogue; the K loop's MFMA density
+    """Where the cycles of the prefill kernels go: the 256-row tiles of each projection (the persistent up-projection,
+    the down-projection's 256-row launch) run once more with per-tile timestamps (same kernels, trace points on), on
+    the routing of the last timed step.  Per tile: prologue (up to the K loop: tile lookup, activation offsets, first
+    copies; for the persistent kernel only a workgroup's first tile has one), K loop, epilogue; the K loop's MFMA density
     (K / 32 steps x 32 MFMAs x 32 cycles); per CU: the gaps between its consecutive tiles and its idle tail before
     the launch ends."""
     import torch
@@ -466,7 +467,8 @@ def tile_trace(probe, layer):
         if st != 0:
             raise RuntimeError(f"tile trace failed ({st})")
         r = tr.cpu().numpy().view(np.uint64).reshape(nrec, 8)
-        r = r[r[:, 7] != np.uint64(0xFFFFFFFFFFFFFFFF)].astype(np.int64)
+        r = r[(r[:, 7] != np.uint64(0xFFFFFFFFFFFFFFFF)) & (((r[:, 7] >> np.uint64(32)) & np.uint64(0xFFF)) != 0)]
+        r = r.astype(np.int64)
         cyc = {"prologue": r[:, 2] - r[:, 1], "k_loop": r[:, 3] - r[:, 2], "epilogue": r[:, 4] - r[:, 3],
                "tile": r[:, 4] - r[:, 1]}
         wall = r[:, 6] - r[:, 5]

@@ -46,15 +46,18 @@ int grok_moe_probe_mfma(const uint16_t* ops, int iters, float* checksum, uint64_
  * work on a second stream, it reads the shader clock that work runs at. */
 int grok_moe_probe_clock(int workgroups, uint64_t ticks, uint64_t* out, hipStream_t stream);
 
-/* Per-tile timestamps of the prefill kernels: the 256-row launch of the up-projection (nmat = 2: a = x [T, d],
- * b0 = W1, b1 = Wv [E, d, f], perm the slot -> token map, K = d, N = f, out = h [slots, f] bf16) or of the
- * down-projection (nmat = 1: a = h [slots, f], b0 = W2 [E, f, d], b1 = perm = NULL, K = f, N = d, out = y
- * [splits, slots, d] f32), bf16 weights stored [in, out], with counts/offsets of the binning step; a_bytes = bytes
- * of a (< 2^31).  The same kernel as the layer's, with timestamps.  trace receives 8 words per workgroup b of the
- * launch (b = blockIdx.y * gridDim.x + blockIdx.x): [0] HW_ID | XCC_ID << 32, shader-clock counter at [1] start,
- * [2] prologue done, [3] K loop done, [4] epilogue stores issued, constant-rate counter at [5] start and [6] end,
- * [7] expert | row0 << 8 | rows << 32 | column tile << 44, or ~0 (and [2..4], [6] unset) for a workgroup without a
- * tile.  max_records bounds the launch (else -1). */
+/* Per-tile timestamps of the prefill kernels: the 256-row tiles of the up-projection (nmat = 2: a = x [T, d],
+ * b0 = W1, b1 = Wv [E, d, f], perm the slot -> token map, K = d, N = f, out = h [slots, f] bf16; the layer's
+ * persistent kernel, one workgroup per CU) or the 256-row launch of the down-projection (nmat = 1: a = h [slots, f],
+ * b0 = W2 [E, f, d], b1 = perm = NULL, K = f, N = d, out = y [splits, slots, d] f32), bf16 weights stored
+ * [in, out], with counts/offsets of the binning step; a_bytes = bytes of a (< 2^31).  The same kernels as the
+ * layer's, with timestamps.  trace receives 8 words per tile: nmat = 2, record L for the tile of index L in the tile
+ * order (records of indexes without a tile stay as they were); nmat = 1, record b of workgroup b = blockIdx.y *
+ * gridDim.x + blockIdx.x.  [0] HW_ID | XCC_ID << 32, shader-clock counter at [1] start (nmat = 2: the tile's start,
+ * for a workgroup's first tile the kernel's start), [2] prologue done (start of the K loop), [3] K loop done,
+ * [4] epilogue stores issued, constant-rate counter at [5] start (as [1]) and [6] end, [7] expert | row0 << 8 |
+ * rows << 32 | column tile << 44, or ~0 (nmat = 1, and [2..4], [6] unset) for a workgroup without a tile.
+ * max_records bounds the records (else -1). */
 int grok_moe_probe_tile_trace(int nmat, const void* a, const void* b0, const void* b1, const int32_t* counts,
                               const int32_t* offsets, const int32_t* perm, int64_t a_bytes, int K, int N, int E,
                               int slots, int splits, void* out, uint64_t* trace, int64_t max_records,

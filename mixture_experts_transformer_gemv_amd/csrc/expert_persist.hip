@@ -61,14 +61,24 @@ struct PCopy {
 };
 }  // namespace
 
+// TRACE (built into the measurement probes only): each tile's timestamps go to trace[8 L .. 8 L + 7] for its tile
+// index L in the order of tiles.h: [0] HW_ID | XCC_ID << 32, shader-clock counter at [1] the tile's start (for a
+// workgroup's first tile: the kernel's start, so that [2] - [1] is its prologue), [2] the start of its K loop,
+// [3] K loop done, [4] epilogue stores issued, constant-rate counter at [5] start (as [1]) and [6] end, [7] expert |
+// row0 << 8 | rows << 32 | column tile << 44.  One 64-byte buffer store per wave and epilogue (wave 0's four lanes
+// write, every other lane's offset is out of range), counted with the epilogue's other operations.
+template <bool TRACE>
 __global__ __launch_bounds__(256) void tiled_up_persist_kernel(const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ W1,
                                                                const uint16_t* __restrict__ Wv,
                                                                const int32_t* __restrict__ counts,
                                                                const int32_t* __restrict__ perm, uint32_t a_bytes,
                                                                int K, int N, int E, uint16_t* __restrict__ h,
-                                                               uint32_t h_bytes) {
+                                                               uint32_t h_bytes, uint64_t* __restrict__ trace,
+                                                               uint32_t trace_bytes) {
   constexpr int NG = tile::Group<2>::N;
+  constexpr int EPI = P_EPI + (TRACE ? 1 : 0);  // vector memory operations of one epilogue
+  uint64_t tc_start = TRACE ? clock64() : 0, tw_start = TRACE ? wall_clock64() : 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[P_LDS];
   lds_u8* lds = (lds_u8*)smem;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -226,18 +236,21 @@ __global__ __launch_bounds__(256) void tiled_up_persist_kernel(const uint16_t* _
   if (has_next) tile_at(q + W, nxt);
   load_rows(has_next, nxt, pv);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) store_h(P_OOR + 16u * uint32_t(i), u32x4_t{0u, 0u, 0u, 0u});  // distinct: all issued
-  wait_vm<2 * P_CPS + P_EPI>();  // step 0 landed
+  for (int i = 0; i < EPI - 4; ++i) store_h(P_OOR + 16u * uint32_t(i), u32x4_t{0u, 0u, 0u, 0u});  // distinct: all issued
+  wait_vm<2 * P_CPS + EPI>();  // step 0 landed
   lds_barrier();
+  const __amdgpu_buffer_rsrc_t t_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(TRACE ? trace : nullptr, (short)0, int(TRACE ? trace_bytes : 0), 0x00020000);
 
   for (;;) {
     // fragments of step 0, half 0 (landed and visible: the wait and barrier before)
     const lds_u8* st0 = lds + r0 * P_STAGE;
+    const uint64_t tc_loop = TRACE ? clock64() : 0;
 #pragma unroll
     for (int p = 0; p < P_NPIECE; ++p) read_piece(0, st0, 0, p);
     join_b(0);
-    kstep(0, cc, 3, std::integral_constant<int, P_EPI>{}, std::true_type{});
-    kstep(1, cc, 4, std::integral_constant<int, P_EPI>{}, std::false_type{});
+    kstep(0, cc, 3, std::integral_constant<int, EPI>{}, std::true_type{});
+    kstep(1, cc, 4, std::integral_constant<int, EPI>{}, std::false_type{});
     for (int kt = 2; kt < KT - 3; ++kt) kstep(kt, cc, kt + 3, std::integral_constant<int, 0>{}, std::false_type{});
     // the next tile's copy offsets (its row map was loaded during the last epilogue and has landed: the waits
     // above cover every operation issued before the copies of step 3); past the last tile, the current tile's
@@ -251,6 +264,7 @@ __global__ __launch_bounds__(256) void tiled_up_persist_kernel(const uint16_t* _
     }
     for (int kt = KT - 3; kt < KT; ++kt)
       kstep(kt, nc, kt + 3 - KT, std::integral_constant<int, 0>{}, std::false_type{});
+    const uint64_t tc_kdone = TRACE ? clock64() : 0;
 
     // ---- epilogue: the row map of the tile after next, then the GELU product staged in LDS and stored.  32 wait
     // states after the last MFMA before its accumulators are read.
@@ -296,6 +310,24 @@ __global__ __launch_bounds__(256) void tiled_up_persist_kernel(const uint16_t* _
       const uint32_t voff = r < cur.rows ? (uint32_t(cur.row0 + r) * uint32_t(N) + uint32_t(nbase + c8)) * 2u : P_OOR;
       store_h(voff, v);
     }
+    if constexpr (TRACE) {
+      const uint64_t tc_epi = clock64(), tw_end = wall_clock64();
+      const uint64_t hw = uint64_t(__builtin_amdgcn_s_getreg((31 << 11) | 4)) |
+                          (uint64_t(__builtin_amdgcn_s_getreg((31 << 11) | 20)) << 32);
+      const uint64_t code = uint64_t(cur.e) | (uint64_t(cur.row0) << 8) | (uint64_t(cur.rows) << 32) |
+                            (uint64_t(cur.ntile) << 44);
+      const uint64_t w[8] = {hw, tc_start, tc_loop, tc_kdone, tc_epi, tw_start, tw_end, code};
+      const int i = lane & 3;
+      uint64_t lo = w[0], hi = w[1];
+#pragma unroll
+      for (int k = 1; k < 4; ++k)
+        if (i == k) { lo = w[2 * k]; hi = w[2 * k + 1]; }
+      const uint32_t toff = (wave == 0 && lane < 4) ? uint32_t(x * chunk + q) * 64u + 16u * uint32_t(i) : P_OOR;
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)},
+                                             t_rsrc, int(toff), 0, 0);
+      tc_start = clock64();
+      tw_start = wall_clock64();
+    }
     lds_barrier();  // every wave read its staged rows: the next tile may copy into that slot
     if (!has_next) break;
     r0 = (r0 + KT) & 3;
@@ -320,9 +352,10 @@ hipError_t launch_up_persist(const uint16_t* x, const void* w1, const void* wv, 
   if (wg < 8 || d % PBK != 0 || d / PBK < 8) return hipErrorInvalidValue;
   const size_t xbytes = size_t(slots / 2) * d * 2, hbytes = size_t(slots) * f * 2;
   if (xbytes >= (size_t(1) << 31) || hbytes >= (size_t(1) << 31)) return hipErrorInvalidValue;
-  tiled_up_persist_kernel<<<dim3(wg), dim3(256), 0, s>>>(x, static_cast<const uint16_t*>(w1),
-                                                        static_cast<const uint16_t*>(wv), counts, perm,
-                                                        uint32_t(xbytes), d, f, E, h, uint32_t(hbytes));
+  tiled_up_persist_kernel<false><<<dim3(wg), dim3(256), 0, s>>>(x, static_cast<const uint16_t*>(w1),
+                                                               static_cast<const uint16_t*>(wv), counts, perm,
+                                                               uint32_t(xbytes), d, f, E, h, uint32_t(hbytes),
+                                                               nullptr, 0u);
   return hipGetLastError();
 }
 
