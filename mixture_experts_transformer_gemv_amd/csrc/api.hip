@@ -70,7 +70,7 @@ Passes passes(int64_t T, int64_t d, int64_t f, int dtype) {
   return Passes{n, T / n, T % n};
 }
 
-int down_splits(int64_t T, int64_t f, int dtype) {
+int down_splits(int64_t T, int64_t f, int E, int dtype) {
   // LDS-tiled bf16 down-projection: K split in two, so that its tiles fill the chip in more, shorter rounds
   if (dtype == GROK_MOE_BF16 && T > stream_max_tokens(dtype)) return 2;
   // fp32 layer: a small batch gives few tiles, each a long chain of 16-deep K steps: for T <= 256 split K into
@@ -81,10 +81,14 @@ int down_splits(int64_t T, int64_t f, int dtype) {
     return s;
   }
   if (T > stream_max_tokens(dtype)) return 1;
-  // near-equal chunks of at least 2048 rows of W2 with boundaries on multiples of 128 rows, at most 5 (measured
-  // against 2, 4, 6 and 8 chunks)
+  // near-equal chunks of at least 2048 rows of W2 with boundaries on multiples of 128 rows: at most 5 (measured
+  // against 3, 4, 6, 8 and 16 chunks), or 2 for bf16 16-row token tiles with at least as many tokens as experts
+  // (every expert likely hit: fewer, longer weight streams read faster there; measured on MI355X at Grok-1 shape,
+  // down-projection ms with 5 -> 2 chunks: T = 8 0.465 -> 0.452, T = 16 0.470 -> 0.456, but T = 4 0.329 -> 0.350,
+  // T = 64 0.484 -> 0.496, int8 with grouped scales 0.292 -> 0.389)
   if (f % 128 != 0) return 1;
-  return int(std::min<int64_t>(5, std::max<int64_t>(1, f / 2048)));
+  const int64_t most = (dtype == GROK_MOE_BF16 && T <= 16 && T >= E) ? 2 : 5;
+  return int(std::min<int64_t>(most, std::max<int64_t>(1, f / 2048)));
 }
 
 Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
@@ -93,7 +97,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int E, int dtype) {
   p.stream = dtype != GROK_MOE_F32 && T <= stream_max_tokens(dtype);
   p.mt = T <= 16 ? 1 : 2;
   p.mt_oi = T <= 16 ? 1 : 2;  // (4 tiles measured slower at T = 64: the token tile outgrows the weight tile)
-  p.splits = down_splits(T, f, dtype);
+  p.splits = down_splits(T, f, E, dtype);
   size_t o = 0;
   p.o_idx = o; o = align256(o + size_t(p.slots) * 4);
   p.o_p = o; o = align256(o + size_t(p.slots) * 4);
