@@ -163,7 +163,7 @@ hipError_t do_up(const void* x, const void* w1, const void* wv, const void* s1, 
   if (p.stream && sp.outin && gm::oi_stream_fits(int(d), i8, up_layout(sp, d, f), int(d)))
     return gm::launch_up_stream_oi(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
                                    static_cast<const uint16_t*>(sv), up_layout(sp, d, f), counts, offsets, perm,
-                                   int(d), int(f), E, i8, p.mt_oi, static_cast<uint16_t*>(h), s);
+                                   int(d), int(f), E, int(p.slots), i8, p.mt_oi, static_cast<uint16_t*>(h), s);
   if (p.stream)
     return gm::launch_up_stream(static_cast<const uint16_t*>(x), w1, wv, static_cast<const uint16_t*>(s1),
                                 static_cast<const uint16_t*>(sv), up_layout(sp, d, f), sp.outin, counts, offsets,

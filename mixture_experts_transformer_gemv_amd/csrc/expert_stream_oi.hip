@@ -84,7 +84,7 @@ __device__ __forceinline__ uint32_t lane_scale_bits(const u32x4_t& lo, const u32
 // KS = 4 (up-projection): the sums over the four quarters of K are kept apart and added in ascending quarter order
 // at the end, as the [in, out] kernel with its d axis split over 4 waves adds them (with grouped scales each
 // quarter's sum is first brought to the unit of the last quarter, by the same fused multiply-adds).
-template <int NMAT, bool INT8, bool GROUPED, int MT, int KS = 1>
+template <int NMAT, bool INT8, bool GROUPED, int MT, int KS = 1, int NB = 1>
 __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restrict__ A, const void* __restrict__ W0,
                                                         const void* __restrict__ W1, const uint16_t* __restrict__ sc0,
                                                         const uint16_t* __restrict__ sc1, ScaleLayout sl,
@@ -94,12 +94,13 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
                                                         int spw, void* __restrict__ out, int64_t split_stride) {
   typedef OiCfg<NMAT, INT8, MT> C;
   static_assert(INT8 || !GROUPED, "grouped scales belong to int8 weights");
+  static_assert(NB == 1 || (NMAT == 2 && !INT8 && KS == 1), "column blocks per workgroup: bf16 up-projection");
   constexpr int ESZ = INT8 ? 1 : 2;
   const int e = blockIdx.z;
   const int n_e = counts[e];
   if (n_e == 0) return;  // whole workgroup
   const int off = offsets[e];
-  const int nbase = blockIdx.x * OI_COLS;
+  const int nbase = blockIdx.x * OI_COLS * NB;
   const int kbeg = NMAT == 1 ? 0 : blockIdx.y * Kc;
   const int NS = (NMAT == 1 ? K : Kc) / OI_KS;  // stages
 
@@ -140,16 +141,19 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
       const uint32_t arow = (NMAT == 2) ? uint32_t(perm[off + rr]) : uint32_t(off + rr);
       a_voff[i] = arow * uint32_t(K * 2) + 16u * uint32_t(slot ^ (r & 15));
     }
-    auto copy_stage = [&](int slot, int s) {
+    // stage fs of the workgroup's stream: stage fs % NS of column block fs / NS
+    auto copy_stage = [&](int slot, int fs) {
       const uint32_t so = lds0 + uint32_t(slot * C::STAGE);
-      const int k0 = kbeg + s * OI_KS;
+      const int blk = fs / NS;
+      const int k0 = kbeg + (fs - blk * NS) * OI_KS;
+      const size_t wo = (size_t(blk) * OI_COLS * K + size_t(k0)) * ESZ;
 #pragma unroll
       for (int i = 0; i < C::W_PER_WAVE; ++i)
-        g2lds16_nt(wb0 + size_t(k0) * ESZ, w_voff[i], so + uint32_t((16 * wave + C::WROWS_PER_COPY * i) * C::ROWB));
+        g2lds16_nt(wb0 + wo, w_voff[i], so + uint32_t((16 * wave + C::WROWS_PER_COPY * i) * C::ROWB));
       if (NMAT == 2) {
 #pragma unroll
         for (int i = 0; i < C::W_PER_WAVE; ++i)
-          g2lds16_nt(wb1 + size_t(k0) * ESZ, w_voff[i],
+          g2lds16_nt(wb1 + wo, w_voff[i],
                   so + uint32_t(C::WTILE + (16 * wave + C::WROWS_PER_COPY * i) * C::ROWB));
       }
 #pragma unroll
@@ -185,9 +189,10 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) s_fix[m] = bf16f(uint16_t(lane_scale_bits(pend_lo[m], pend_hi[m], c16)));
     }
-    // results of the lane: column nbase + wrow, token rows mb + 16 mt + 4 g + v; NMAT = 1 stores chunk `split`
-    auto store = [&](int split) {
-      const int n = nbase + wrow;
+    // results of the lane: column nbase + OI_COLS blk + wrow, token rows mb + 16 mt + 4 g + v; NMAT = 1 stores
+    // chunk `split`
+    auto store = [&](int split, int blk) {
+      const int n = nbase + OI_COLS * blk + wrow;
       float s_m[NMAT];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) s_m[m] = GROUPED ? cur[m] : (INT8 ? s_fix[m] : 1.0f);
@@ -211,13 +216,24 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
 
     int chunk = 0, cnext = down_chunk_begin(1, K, spw);  // NMAT = 1: the chunk being summed and its end
     // ---- prologue: stages 0 .. NSTG-2 (past the end: the last stage again, into slots never read)
+    const int FS = NB * NS;  // stages of the stream
 #pragma unroll
-    for (int s = 0; s < C::NSTG - 1; ++s) copy_stage(s, min(s, NS - 1));
+    for (int s = 0; s < C::NSTG - 1; ++s) copy_stage(s, min(s, FS - 1));
 
-    for (int s = 0; s < NS; ++s) {
-      wait_vm<(C::NSTG - 2) * C::CPW>();  // this wave's copies of stage s landed
-      lds_barrier();                       // ... every wave's; every wave finished reading stage s - 1
-      copy_stage((s + C::NSTG - 1) % C::NSTG, min(s + C::NSTG - 1, NS - 1));
+    for (int fs = 0; fs < FS; ++fs) {
+      const int s = fs % NS;               // stage within the column block
+      wait_vm<(C::NSTG - 2) * C::CPW>();  // this wave's copies of stage fs landed
+      lds_barrier();                       // ... every wave's; every wave finished reading stage fs - 1
+      if constexpr (NB > 1) {
+        if (s == 0 && fs > 0) {
+          // the previous block's results (the stores add to the vector memory count: the copy waits only get
+          // stronger)
+          store(0, fs / NS - 1);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[0][mt] = acc[1][mt] = f32x4_t{0, 0, 0, 0};
+        }
+      }
+      copy_stage((fs + C::NSTG - 1) % C::NSTG, min(fs + C::NSTG - 1, FS - 1));
       const int k0 = kbeg + s * OI_KS;
       if constexpr (KS > 1) {
         if (s > 0 && s % (NS / KS) == 0) {  // stage s opens quarter q: keep the sum of quarter q - 1 apart
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
         gnext = gi * sl.gsize;
         if (gnext < kbeg + NS * OI_KS) fetch_group(gi);
       }
-      const lds_u8* st = lds + (s % C::NSTG) * C::STAGE;
+      const lds_u8* st = lds + (fs % C::NSTG) * C::STAGE;
 #pragma unroll
       for (int t = 0; t < OI_KS / 32; ++t) {
         u32x4_t a[MT], b[NMAT];
@@ -286,7 +302,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
           for (int mt = 0; mt < MT; ++mt) acc[m][mt] = mfma16x16x32(a[mt], b[m], acc[m][mt]);
       }
       if (NMAT == 1 && s + 1 < NS && (s + 1) * OI_KS == cnext) {  // end of a chunk that is not the last
-        store(chunk);
+        store(chunk, 0);
         cnext = down_chunk_begin(++chunk + 1, K, spw);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[0][mt] = f32x4_t{0, 0, 0, 0};
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(256) void oi_stream_kernel(const uint16_t* __restri
         for (int mt = 0; mt < MT; ++mt)
           acc[m][mt] = ((part[0][m][mt] + part[1][m][mt]) + part[2][m][mt]) + acc[m][mt];
     }
-    store(NMAT == 1 ? spw - 1 : 0);
+    store(NMAT == 1 ? spw - 1 : 0, NB - 1);
   }
 }
 
@@ -341,10 +357,19 @@ static void launch_oi_mt(int mt, dim3 grid, hipStream_t s, const uint16_t* A, co
                                                                     K, N, Kc, spw, out, split_stride);
 }
 
+// Column blocks of 64 per workgroup of the bf16 up-projection: 8 where f splits into whole 512-column ranges and
+// the experts that can be hit hold at least 512 of them, else 1.  Measured on MI355X at Grok-1 shape, up-projection
+// ms with 1 -> 8 blocks: T = 4 0.482 -> 0.471, T = 8 0.937 -> 0.917, T = 16 0.942 -> 0.924, T = 64 0.959 -> 0.941
+// (2 or 4 blocks in between); fewer tokens keep 1 (T = 2 with 4 blocks: 0.350 -> 0.376).
+int oi_up_blocks(int f, int E, int slots) {
+  const int64_t hit = slots < E ? slots : E;
+  return (f % (OI_COLS * 8) == 0 && hit * (f / (OI_COLS * 8)) >= 512) ? 8 : 1;
+}
+
 hipError_t launch_up_stream_oi(const uint16_t* x, const void* w1, const void* wv, const uint16_t* s1,
                                const uint16_t* sv, ScaleLayout sl, const int32_t* counts, const int32_t* offsets,
-                               const int32_t* perm, int d, int f, int E, bool int8, int mt, uint16_t* h,
-                               hipStream_t s) {
+                               const int32_t* perm, int d, int f, int E, int slots, bool int8, int mt,
+                               uint16_t* h, hipStream_t s) {
   const dim3 grid(f / OI_COLS, 1, E);  // one chunk: the whole d axis
   const bool grouped = int8 && sl.gsize < d;
   if (up_stream_ksplit(d, f, E) == 4) {  // the [in, out] kernel splits d: sum the same quarters
@@ -363,8 +388,17 @@ hipError_t launch_up_stream_oi(const uint16_t* x, const void* w1, const void* wv
     launch_oi_mt<2, true, true>(mt, grid, s, x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, d, 1, h, 0);
   else if (int8)
     launch_oi_mt<2, true, false>(mt, grid, s, x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, d, 1, h, 0);
-  else
-    launch_oi_mt<2, false, false>(mt, grid, s, x, w1, wv, s1, sv, sl, counts, offsets, perm, d, f, d, 1, h, 0);
+  else {
+    const int nb = oi_up_blocks(f, E, slots);
+    const dim3 gridb(f / (OI_COLS * nb), 1, E), block(256);
+#define GM_OIB(MT, NB) oi_stream_kernel<2, false, false, MT, 1, NB><<<gridb, block, 0, s>>>(x, w1, wv, s1, sv, sl, \
+                                                                                        counts, offsets, perm, d, f, d, 1, h, 0)
+#define GM_OIB_NB(MT) do { if (nb == 8) GM_OIB(MT, 8); else GM_OIB(MT, 1); } while (0)
+    if (mt == 1) GM_OIB_NB(1);
+    else GM_OIB_NB(2);
+#undef GM_OIB_NB
+#undef GM_OIB
+  }
   return hipGetLastError();
 }
 

@@ -72,6 +72,10 @@ CASES = [
     _w("oi_bf16_T24_uneven", 24, 256, 6400),               # down chunks of 2048, 2176 and 2176 rows
     _w("oi_bf16_T300", 300, 512, 1024),                    # direct-to-LDS tiles, down K split in 2
     _w("oi_bf16_T700_E4", 700, 768, 1536, E=4),
+    _w("oi_bf16_T16_E64_nb8", 16, 256, 8192, E=64),        # 8 column blocks per workgroup, 16-row tiles
+    _w("oi_bf16_T40_E64_nb8", 40, 256, 4096, E=64),        # 8 column blocks per workgroup, 32-row tiles
+    synth.Workload("oi_bf16_T96_skew_nb8", T=96, d=256, f=32768, router_bias=(4.0, 4.0, 0, 0, 0, 0, 0, 0)),
+    # ... 8 blocks, two busy experts in three passes of 32 rows, the other experts few or no rows
     _w("oi_w8_T40", 40, 512, 2048, dtype=W8),              # int8 streaming
     _w("oi_w8_T128", 128, 512, 1024, dtype=W8),            # int8 streaming, several passes
     _w("oi_w8_T300", 300, 512, 1024, dtype=W8),            # int8 register-staged tiles
