@@ -17,7 +17,10 @@
 //
 // A workgroup of 4 waves owns 64 output columns (16 per wave) of W1 and Wv (up) or of W2 (down: all spw chunks of
 // the f axis, a partial sum stored per chunk, so that one ring streams every chunk) for all token
-// rows of its expert (16 MT rows per pass), over a ring of NSTG stages with one workgroup barrier per stage.
+// rows of its expert (16 MT rows per pass), over a ring of NSTG stages with one workgroup barrier per stage.  The
+// bf16 up-projection's workgroups take NB consecutive blocks of 64 columns as one stream of stages (the last stages
+// of a block copy the first ones of the next), so a workgroup start, with its first copies' latency, comes once per
+// NB blocks.
 // Each (token, column) accumulates over k in 32-deep steps in ascending order, with the same lane-to-k
 // assignment as the [in, out] kernels, so the results are bit-identical to theirs.
 //
