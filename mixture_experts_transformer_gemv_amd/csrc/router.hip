@@ -4,9 +4,9 @@
 // logits come from a Dense gate with one output per expert, the gates are the softmax of the logits (no noise
 // at inference), and top_k with k = 2 returns the two largest gates with their indices.
 //
-// One workgroup per token.  For a small batch (a decode step) the workgroup has one thread per 8-element chunk
-// of d (up to 1024 threads), so every load of the token is issued at once and the kernel pays one memory latency;
-// for a large batch it has 4 waves, each thread striding over d.  Each thread accumulates its products in fp64:
+// One workgroup of 4 waves per token, each thread striding over d in 8-element chunks.  (One thread per chunk, up to
+// 1024 per workgroup, so that every load of the token is in flight at once, measured 1 us slower for routing and
+// binning together at Grok-1 shape, T = 1 to 64, on MI355X.)  Each thread accumulates its products in fp64:
 // a product of two bf16 (or two fp32) values is exact in fp64, so the only rounding is fp64 summation.  A fixed
 // butterfly inside each wave and a fixed order across the waves make the result deterministic.  Selection runs
 // on one wave with one lane per expert: the fp64 logits in descending order, the lower expert index first on
@@ -54,8 +54,7 @@ __device__ __forceinline__ void gate_fma(const void* __restrict__ rw, int d, int
   }
 }
 
-constexpr int kRouterMaxWaves = 16;
-constexpr int kRouterWideTokens = 256;  // batches up to this many tokens use the wide workgroups
+constexpr int kRouterWaves = 4;
 
 // (value, index) order of the top-k: larger value first, lower index first on equal values.
 __device__ __forceinline__ bool ranks_before(double a, int ia, double b, int ib) {
@@ -120,15 +119,12 @@ __device__ __forceinline__ void reduce_select(double (&acc)[EMAX], double (*part
   if (wave == 0) select_top2<EMAX>(part, nw, bias, E, t, lane, idx, p);
 }
 
-// Up to 1024 threads for E <= 16 experts; 256 (registers for 32 or 64 fp64 partial logits) beyond.
-template <int EMAX> constexpr int router_max_threads() { return EMAX <= 16 ? 1024 : 256; }
-
 template <bool BF16, int EMAX>
-__global__ __launch_bounds__(router_max_threads<EMAX>()) void router_topk_kernel(const void* __restrict__ x, const void* __restrict__ rw,
+__global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const void* __restrict__ x, const void* __restrict__ rw,
                                                            const float* __restrict__ bias, int T, int d, int E,
                                                            int32_t* __restrict__ idx, float* __restrict__ p) {
   // One workgroup per token; thread i accumulates the 8-element chunks 8 i, 8 (i + blockDim), ... of d.
-  __shared__ double part[kRouterMaxWaves][EMAX];
+  __shared__ double part[kRouterWaves][EMAX];
   const int t = blockIdx.x;
   double acc[EMAX];
 #pragma unroll
@@ -163,7 +159,7 @@ __global__ __launch_bounds__(256) void router_norm_kernel(const void* __restrict
                                                           const float* __restrict__ bias, int T, int d, int E,
                                                           void* __restrict__ xn, int32_t* __restrict__ idx,
                                                           float* __restrict__ p) {
-  __shared__ double part[kRouterMaxWaves][EMAX];
+  __shared__ double part[kRouterWaves][EMAX];
   __shared__ double ssq[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x;
@@ -222,9 +218,7 @@ __global__ __launch_bounds__(256) void router_norm_kernel(const void* __restrict
 template <bool BF16>
 static hipError_t launch_router_t(const void* x, const void* rw, const float* bias, int T, int d, int E, int32_t* idx,
                                   float* p, hipStream_t s) {
-  // small batches: one thread per 8-element chunk of d (all loads in flight at once); large: 4 waves per token
-  const int wide = (d / 8 + 63) / 64 * 64 < 1024 ? (d / 8 + 63) / 64 * 64 : 1024;
-  const dim3 grid(T), block(T <= kRouterWideTokens && E <= 16 ? wide : 256);
+  const dim3 grid(T), block(64 * kRouterWaves);
   if (E <= 8) router_topk_kernel<BF16, 8><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
   else if (E <= 16) router_topk_kernel<BF16, 16><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
   else if (E <= 32) router_topk_kernel<BF16, 32><<<grid, block, 0, s>>>(x, rw, bias, T, d, E, idx, p);
