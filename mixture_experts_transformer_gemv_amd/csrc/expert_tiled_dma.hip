@@ -677,7 +677,7 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
     GM_UPD(false, true);
   } else if (outin) {
     GM_UPD(true, false);
-  } else if (d / BK >= 8) {  // bf16 [in, out]: the persistent form of the 256-row launch (expert_persist.hip)
+  } else if (d / BK >= 8 && d % (2 * BK) == 0) {  // bf16 [in, out]: the persistent form of the 256-row launch
     const hipError_t err = launch_up_persist(x, w1, wv, counts, perm, d, f, E, slots, h, s);
     if (err != hipSuccess) return err;
     tiled_dma_small_kernel<false, false><<<grid_s, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, offsets, perm,
