@@ -6,7 +6,12 @@
 // Tile shape and order: tiles.h.  K steps of 32 in a 4-deep LDS ring (4 x 32 KB).  Both operands are copied
 // straight from global memory into LDS with global_load_lds_dwordx4 (no registers, no VALU), 16 bytes per lane,
 // addressed as a wave-uniform base plus a per-lane 32-bit offset:
-//   * A tile [256 rows][32 k], 64-byte rows; the 16-byte k chunk c of row r sits in slot c ^ ((r >> 2) & 3);
+//   * A (activations), [in, out] weights with one scale per column: copied per pair of K steps, [256 rows][64 k]
+//     with 128-byte rows (full cache lines), rows 0..127 in the A region of the pair's first ring slot and
+//     128..255 in that of its second; the 16-byte k chunk c of row r sits in slot c ^ ((r >> 1) & 7).  Even steps
+//     copy the activations of the pair two steps ahead, every step the weights of the step three ahead.  Otherwise
+//     (grouped int8 scales, [out, in] weights) per K step: [256 rows][32 k], 64-byte rows, chunk c of row r in
+//     slot c ^ ((r >> 2) & 3);
 //   * weights as two [32 k][128 column] sub-tiles (up: W1 and Wv; down: two halves of the W2 columns) with
 //     256-byte rows; the 8-column chunk c of row k sits in slot c ^ (4 (k & 3)).
 // The XOR swizzles are chosen on the global side (which chunk each lane fetches) so that the MFMA operand reads
@@ -93,6 +98,14 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   constexpr int BCOPIES = INT8 ? 2 : 4;        // 1 KB weight copies per wave and K step ([in, out])
   constexpr int CPS = AP + BCOPIES;            // copies per wave and K step ([out, in]: AP + 4)
   constexpr int A_STRIDE = OUTIN ? A_STG : STAGE;  // between ring slots of A
+  // [in, out] weights with one scale per column: the activations are copied per pair of K steps, 128 contiguous
+  // bytes (64 k) of each row per copy, so that a copy instruction reads 8 full 128-byte lines instead of 16 half
+  // lines (the vector memory path is the K loop's limit; measured on MI355X at Grok-1 shape, bit-identical:
+  // prefill down-projection 5.55 -> 5.32 ms, int8 weights at T = 8192 18.45 -> 17.88 ms per layer; with grouped
+  // int8 scales 7.15 -> 7.24 ms at T = 2048, so those keep per-step copies).  The pair's TBM rows x 128 bytes fill
+  // the A regions of the ring slots of its two steps: rows 0..TBM/2-1 in the first, the rest in the second.
+  constexpr bool PAIRA = !OUTIN && !GROUPED;
+  constexpr int APP = 2 * AP;                   // 1 KB activation copies per wave and step pair
   // Launches whose tiles read each weight byte once (one 128-row tile per expert and column tile) copy the weights
   // with the nontemporal hint; tiles that share weight columns through the caches keep the default policy.
   auto copy_b = [](const void* base, uint32_t voff, uint32_t dst) {
@@ -112,14 +125,18 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   // holds k chunk (lane & 3) ^ ((row >> 2) & 3).  Byte offsets from A (32 bits).  Rows past the expert's end (the
   // tail tile) get an out-of-range offset, so their copies write zeros: those rows are never stored, and
   // multiplying zeros takes markedly less power than multiplying data.
+  // PAIRA: piece i copies rows (TBM/4) w + 8 i + lane/8; lane's slot (lane & 7) of the 128-byte row holds k chunk
+  // (lane & 7) ^ ((row >> 1) & 7).
   const u32x4_t a_rsrc = buffer_rsrc(A, a_bytes);
-  uint32_t a_voff[AP];
+  constexpr int NAV = PAIRA ? APP : AP;
+  uint32_t a_voff[NAV];
 #pragma unroll
-  for (int i = 0; i < AP; ++i) {
-    const int r = (TBM / 4) * wave + 16 * i + (lane >> 2);
+  for (int i = 0; i < NAV; ++i) {
+    const int r = PAIRA ? (TBM / 4) * wave + 8 * i + (lane >> 3) : (TBM / 4) * wave + 16 * i + (lane >> 2);
     if (r < rows) {
       const uint32_t arow = (NMAT == 2) ? uint32_t(perm[row0 + r]) : uint32_t(row0 + r);
-      a_voff[i] = (arow * uint32_t(K) + 8u * uint32_t((lane & 3) ^ ((r >> 2) & 3))) * 2u;
+      const uint32_t chunk = PAIRA ? uint32_t((lane & 7) ^ ((r >> 1) & 7)) : uint32_t((lane & 3) ^ ((r >> 2) & 3));
+      a_voff[i] = (arow * uint32_t(K) + 8u * chunk) * 2u;
     } else {
       a_voff[i] = 0x80000000u;
     }
@@ -165,6 +182,15 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
       copy_b(b_base + size_t(kbase + kt * BK) * N + size_t(4 * (n - AP)) * N, b_voff,
               b_dst + so + uint32_t(4 * (n - AP)) * 256);
   };
+  // PAIRA: activation piece i of the step pair kd, kd + 1 (kd even) into the A regions of ring slots kd % NSTAGE
+  // (rows 0..TBM/2-1) and (kd + 1) % NSTAGE; weight piece n of step kt into ring slot stage
+  // (kd: the pair's first step, which places it in the ring; ks: the step its data is read from)
+  auto copy_apair = [&](int kd, int ks, int i) {
+    const uint32_t dst = lds0 + uint32_t(((kd + (wave >> 1)) % NSTAGE) * STAGE) +
+                         uint32_t((TBM / 4) * (wave & 1) + 8 * i) * 128u;
+    b2lds16(a_rsrc, uint32_t(kbase + ks * BK) * 2u, a_voff[i], dst);
+  };
+  auto copy_bpiece = [&](int stage, int kt, int n) { copy_piece(stage, kt, AP + n); };
   // OUTIN: copy c of K-step pair q into pair slot q % 3 (past the end: the last pair again, into a free slot)
   auto copy_pair = [&](int q, int c) {
     const int qd = min(q, (Ks / BK) / 2 - 1);
@@ -181,6 +207,17 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     for (int ks = 0; ks < 2; ++ks) {
       const int r = wm * (TBM / 2) + 32 * i + (lane & 31);
       a_off[i][ks] = r * (BK * 2) + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
+    }
+  // PAIRA: row 32 i + (lane & 31) of the wave's A region (that of the pair's first step for wm = 0, second for
+  // wm = 1), k chunk 4 (kt & 1) + 2 ks + (lane >> 5) of its 8; the block adds 32 i rows (4 KB) and leaves the
+  // swizzle unchanged, so one base offset per (kt & 1, ks)
+  int a_offp[2][2];
+#pragma unroll
+  for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r = lane & 31;
+      a_offp[hp][ks] = r * 128 + 16 * ((4 * hp + 2 * ks + (lane >> 5)) ^ ((r >> 1) & 7));
     }
   // B halves h: lane addresses k row 16 ks + 8 g + 4 h + (s >> 2) and columns col .. +3 of its sub-tile, where
   // G = lane >> 4, g = G >> 1, s = lane & 15 and col = (sub-tile column base) + 16 (G & 1) + 4 (s & 3)
@@ -235,24 +272,30 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   u32x4_t fa[2][MI], fb[2][4];
   u32x2_t bh[2][4][2];
   u32x2_t b8[2][4];
-  // st: the step's A slot (and, [in, out], its weight sub-tiles); sb, p2: OUTIN pair slot and step within it
-  auto read_piece = [&](int buf, const lds_u8* st, const lds_u8* sb, int p2, int ks, int p) {
+  // st: the step's A slot (and, [in, out], its weight sub-tiles); sb, p2: OUTIN pair slot and step within it;
+  // sa (PAIRA): the wave's A region of the step's pair, p2 the step within the pair
+  auto a_read = [&](int buf, int i, const lds_u8* st, const lds_u8* sa, int p2, int ks) {
+    if constexpr (PAIRA)
+      fa[buf][i] = *(const __attribute__((address_space(3))) u32x4_t*)(sa + a_offp[p2][ks] + i * 32 * 128);
+    else
+      fa[buf][i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[i][ks]);
+  };
+  auto read_piece = [&](int buf, const lds_u8* st, const lds_u8* sb, const lds_u8* sa, int p2, int ks, int p) {
     if (OUTIN) {
       if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
       else if (p <= 4)
         fb[buf][p - 1] = *(const __attribute__((address_space(3))) u32x4_t*)(sb + bt_off[p - 1][ks][p2]);
       else fa[buf][p - 4] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[p - 4][ks]);
     } else if (INT8) {
-      if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
+      if (p == 0) a_read(buf, 0, st, sa, p2, ks);
       else if (p <= 4) b8[buf][p - 1] = lds_tr8(st + b8_off[p - 1][ks]);
-      else fa[buf][p - 4] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[p - 4][ks]);
-    } else if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
+      else a_read(buf, p - 4, st, sa, p2, ks);
+    } else if (p == 0) a_read(buf, 0, st, sa, p2, ks);
     else if (p <= 8) {
       const int j = (p - 1) >> 1, h = (p - 1) & 1;
       bh[buf][j][h] = lds_tr16(st + b_off[j][ks][h]);
     } else {
-      const int i = p - 8;
-      fa[buf][i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[i][ks]);
+      a_read(buf, p - 8, st, sa, p2, ks);
     }
   };
   // keep (GROUPED): bit j clear masks the int8 values of fragment j's column (a zero scale in the step's group)
@@ -319,23 +362,52 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   // density of the K loop 0.83 with the copies bunched around the barrier, 0.94-0.98 with no copies at all).
   // Copies past the last step re-read the last step into a ring slot that is never read again, so every step
   // issues CPS copies and the wait count is constant.
+  // PAIRA: an even step kt issues the activations of the pair kt + 2, kt + 3 in half-step 0 and the weights of
+  // step kt + 3 in half-step 1; an odd step the weights of step kt + 3, half in each half-step (so the wait count
+  // alternates between the parities); the prologue issues the weights of step 0, the activations of pair 0 and
+  // the weights of steps 1 and 2.
   // OUTIN: the weight copies of pair q are issued in the B slots of steps 2 q - 3 and 2 q - 2 (4 each), so that
   // step kt issues copies 4 ((kt + 1) % 2) .. +3 of pair (kt + 3) / 2 at the end of half-step 0 and the activation
   // copies of step kt + 3 at the start of half-step 1; the prologue issues pair 0 and the first half of pair 1.
   const int KT = Ks / BK;
   const lds_u8* bpairs = lds + NSTAGE * A_STG;
+  // PAIRA: the wave's A region of step kt
+  auto a_region = [&](int kt) { return lds + (((kt & ~1) + wm) % NSTAGE) * STAGE; };
   // zeros in the A slots of rows past the expert's end, in every ring stage (written by this lane only; the
   // out-of-range copies leave them zero)
   if (rows < TBM) {
+    if constexpr (PAIRA) {
 #pragma unroll
-    for (int i = 0; i < AP; ++i)
-      if (a_voff[i] == 0x80000000u)
+      for (int i = 0; i < APP; ++i)
+        if (a_voff[i] == 0x80000000u)
 #pragma unroll
-        for (int st = 0; st < NSTAGE; ++st)
-          *(__attribute__((address_space(3))) u32x4_t*)(lds + (a_dst - lds0) + st * A_STRIDE + 16 * i * (BK * 2) +
-                                                        16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+          for (int pp = 0; pp < NSTAGE; pp += 2)  // the pairs' first slots: 0 and 2
+            *(__attribute__((address_space(3))) u32x4_t*)(lds + ((pp + (wave >> 1)) % NSTAGE) * STAGE +
+                                                          ((TBM / 4) * (wave & 1) + 8 * i) * 128 + 16 * lane) =
+                u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int i = 0; i < AP; ++i)
+        if (a_voff[i] == 0x80000000u)
+#pragma unroll
+          for (int st = 0; st < NSTAGE; ++st)
+            *(__attribute__((address_space(3))) u32x4_t*)(lds + (a_dst - lds0) + st * A_STRIDE + 16 * i * (BK * 2) +
+                                                          16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+    }
   }
-  if constexpr (OUTIN) {
+  if constexpr (PAIRA) {
+    // the weights of step 0, the activations of steps 0 and 1, the weights of steps 1 and 2 (the steady state's
+    // order)
+#pragma unroll
+    for (int n = 0; n < BCOPIES; ++n) copy_bpiece(0, 0, n);
+#pragma unroll
+    for (int i = 0; i < APP; ++i) copy_apair(0, 0, i);
+#pragma unroll
+    for (int st = 1; st < NSTAGE - 1; ++st)
+#pragma unroll
+      for (int n = 0; n < BCOPIES; ++n) copy_bpiece(st, min(st, KT - 1), n);
+    wait_vm<2 * BCOPIES>();  // step 0 landed (its weights and the activations of steps 0 and 1)
+  } else if constexpr (OUTIN) {
 #pragma unroll
     for (int n = 0; n < AP; ++n) copy_piece(0, 0, n);
 #pragma unroll
@@ -368,7 +440,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     gnext = (g0 + 1) * gsize;
   }
 #pragma unroll
-  for (int p = 0; p < NPIECE; ++p) read_piece(0, lds, bpairs, 0, 0, p);
+  for (int p = 0; p < NPIECE; ++p) read_piece(0, lds, bpairs, a_region(0), 0, 0, p);
   join_b(0, keep_cur);
   // One K step; P is the step's parity (kt & 1), a compile-time constant so that the [out, in] forms index their
   // pair-slot offset arrays with constants (a runtime index turns each into a chain of selects).
@@ -393,6 +465,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     }
     const lds_u8* st = lds + (kt % NSTAGE) * A_STRIDE;
     const lds_u8* sb = bpairs + ((kt >> 1) % NPAIR) * B_PAIR;
+    const lds_u8* sa = a_region(kt);
     // [in, out]: the copies of step kt+3 into slot (kt+3) % NSTAGE, C0 of them in half-step 0 and the rest in
     // half-step 1, at evenly spaced MFMA slots.  OUTIN: four copies of pair (kt + 3) / 2 in the last 4 slots of
     // half-step 0, the activation copies of step kt+3 in the first AP slots of half-step 1.
@@ -401,8 +474,18 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
 #pragma unroll
     for (int m = 0; m < NSLOT; ++m) {
       if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
-      if (m < NPIECE) read_piece(1, st, sb, P, 1, m);
-      if constexpr (OUTIN) {
+      if (m < NPIECE) read_piece(1, st, sb, sa, P, 1, m);
+      if constexpr (PAIRA) {
+        if constexpr (P == 0) {  // the activations of the pair kt + 2, kt + 3 (past the end: the last pair again)
+#pragma unroll
+          for (int c = 0; c < APP; ++c)
+            if (m == (c * NSLOT) / APP) copy_apair(kt + 2, min(kt + 2, KT - 2), c);
+        } else {
+#pragma unroll
+          for (int c = 0; c < BCOPIES / 2; ++c)
+            if (m == (c * NSLOT) / (BCOPIES / 2)) copy_bpiece(cstage, ck, c);
+        }
+      } else if constexpr (OUTIN) {
         const int cb = m - (NSLOT - 4);  // the last 4 slots issue the weight copies
         if (cb >= 0) copy_pair((kt + 3) >> 1, 4 * (1 - P) + cb);
       } else {
@@ -415,27 +498,36 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     join_b(1, keep_cur);
     // step kt+1 landed (the copies of step kt+2 and the first C0 of step kt+3 may be in flight); OUTIN: steps kt+2
     // and later may be in flight
-    if constexpr (OUTIN) wait_vm<CPS * (NSTAGE - 3)>();
+    // PAIRA: issued after the last copy step kt + 1 needs are, for kt even, the odd step kt - 1's weights and this
+    // step's activations, for kt odd, the even step kt - 1's weights and the first half of this step's
+    if constexpr (PAIRA) wait_vm<P == 0 ? BCOPIES + APP : BCOPIES + BCOPIES / 2>();
+    else if constexpr (OUTIN) wait_vm<CPS * (NSTAGE - 3)>();
     else wait_vm<CPS * (NSTAGE - 3) + C0>();
     lds_barrier();  // ... for every wave; every wave finished reading step kt
     const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * A_STRIDE;
     const lds_u8* nsb = bpairs + (((kt + 1) >> 1) % NPAIR) * B_PAIR;
+    const lds_u8* nsa = a_region(kt + 1);
 #pragma unroll
     for (int m = 0; m < NSLOT; ++m) {
       if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
-      if constexpr (OUTIN) {
+      if constexpr (PAIRA) {
+        constexpr int NB1 = P == 0 ? BCOPIES : BCOPIES / 2, B1 = P == 0 ? 0 : BCOPIES / 2;
+#pragma unroll
+        for (int c = 0; c < NB1; ++c)
+          if (m == (c * NSLOT) / NB1) copy_bpiece(cstage, ck, B1 + c);
+      } else if constexpr (OUTIN) {
         if (m < AP) copy_piece(cstage, ck, m);
       } else {
 #pragma unroll
         for (int c = 0; c < C1; ++c)
           if (m == (c * NSLOT) / C1) copy_piece(cstage, ck, C0 + c);
       }
-      if (m < NPIECE) read_piece(0, nst, nsb, 1 - P, 0, m);
+      if (m < NPIECE) read_piece(0, nst, nsb, nsa, 1 - P, 0, m);
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(0, (GROUPED && kbase + (kt + 1) * BK == gnext) ? keep_next : keep_cur);  // fragments of step kt+1
   };
-  if constexpr (OUTIN) {
+  if constexpr (OUTIN || PAIRA) {
     for (int kt = 0; kt < KT; kt += 2) {  // KT is even: K steps come in pairs
       kstep(kt, std::integral_constant<int, 0>{});
       kstep(kt + 1, std::integral_constant<int, 1>{});
@@ -624,7 +716,7 @@ hipError_t launch_up_tiled_dma_grouped(const uint16_t* x, const void* w1, const 
   const dim3 grid(tile::grid_tiles(slots, E, NT, 128)), block(256);
   const size_t xbytes = size_t(slots / 2) * d;  // x: [slots / 2 tokens, d] bf16
   if (2 * xbytes >= (size_t(1) << 31) || size_t(2) * slots * f >= (size_t(1) << 31) ||
-      !tiled_dma_grouped_fits(d, gsize))
+      !tiled_dma_grouped_fits(d, gsize) || d % (2 * BK) != 0)  // whole K-step pairs
     return hipErrorInvalidValue;
   tiled_dma_grouped_kernel<2><<<grid, block, 0, s>>>(x, w1, wv, s1, sv, s_estride, counts, offsets, perm,
                                                      uint32_t(2 * xbytes), d, f, E, h, 0, gsize);
@@ -637,7 +729,8 @@ hipError_t launch_down_tiled_dma_grouped(const uint16_t* h, const void* w2, cons
   const int NT = d / BNT;
   const dim3 grid(tile::grid_tiles(slots, E, NT, 128), S), block(256);
   const size_t hbytes = size_t(slots) * f * 2;  // h: [slots, f]
-  if (hbytes >= (size_t(1) << 31) || !tiled_dma_grouped_fits(f, gsize)) return hipErrorInvalidValue;
+  if (hbytes >= (size_t(1) << 31) || !tiled_dma_grouped_fits(f, gsize) || f % (2 * BK * S) != 0)
+    return hipErrorInvalidValue;  // whole K-step pairs in every split
   tiled_dma_grouped_kernel<1><<<grid, block, 0, s>>>(h, w2, nullptr, s2, nullptr, s_estride, counts, offsets,
                                                      nullptr, uint32_t(hbytes), f, d, E, y, int64_t(slots) * d,
                                                      gsize);
@@ -665,6 +758,7 @@ hipError_t launch_up_tiled_dma(const uint16_t* x, const void* w1, const void* wv
   const size_t xbytes = size_t(slots / 2) * d * 2;  // x: [slots / 2 tokens, d] (two slots per token)
   if (xbytes >= (size_t(1) << 31) || size_t(2) * slots * f >= (size_t(1) << 31)) return hipErrorInvalidValue;
   if (int8 && outin) return hipErrorInvalidValue;
+  if (d % (2 * BK) != 0) return hipErrorInvalidValue;  // whole K-step pairs
   const uint32_t xb = uint32_t(xbytes);
 #define GM_UPD(OI, I8)                                                                                           \
   do {                                                                                                         \
@@ -698,6 +792,7 @@ hipError_t launch_down_tiled_dma(const uint16_t* h, const void* w2, const uint16
   const size_t hbytes = size_t(slots) * f * 2;  // h: [slots, f]
   if (hbytes >= (size_t(1) << 31)) return hipErrorInvalidValue;
   if (int8 && outin) return hipErrorInvalidValue;
+  if (f % (2 * BK * S) != 0) return hipErrorInvalidValue;  // whole K-step pairs in every split
   const uint32_t hb = uint32_t(hbytes);
 #define GM_DND(OI, I8)                                                                                           \
   do {                                                                                                         \
