@@ -25,7 +25,8 @@ fp32) follow under "configs", each with its own step count.  For every workload 
     rows for prefill and skewed routing), and the same against the oracle without the bf16 rounding of h;
   * the oracle's own time on those rows (routing of all T tokens timed separately), on this host's cores.
 "ceilings" holds the practical limits measured by the probe library: a streaming HBM read and dense bf16 MFMA on
-random register operands (result checked), with the clock it ran at.  One JSON line on stdout.
+random register operands (result checked), with the clock it ran at, and the same MFMA loop with the A operands zero
+and in two other issue orders (what the MFMA rate depends on).  One JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -326,7 +327,8 @@ class Probe:
         vp, i, u64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
         i64 = ctypes.c_int64
         for name, args in (("grok_moe_probe_read", [vp, sz, i, i, vp, vp]),
-                           ("grok_moe_probe_mfma", [vp, i, vp, vp, vp]),
+                           ("grok_moe_probe_mfma", [vp, i, i, vp, vp, vp]),
+                           ("grok_moe_probe_mfma_feed", [vp, i64, i, i, vp, vp, vp]),
                            ("grok_moe_probe_clock", [i, u64, vp, vp]),
                            ("grok_moe_probe_tile_trace", [i, vp, vp, vp, vp, vp, vp, i64, i, i, i, i, i, vp, vp, i64,
                                                           vp]),
@@ -388,21 +390,29 @@ class Probe:
             res["nontemporal" if nt else "default"] = best
         return res, nbytes
 
-    def mfma(self, iters=200000):
-        """Sustained dense bf16 MFMA (TFLOP/s) on random operands, its clock, and a check of the result."""
+    # operand pair (A fragment, B fragment) of MFMA m of a round, for each issue order of grok_moe_probe_mfma
+    ORDERS = {0: [(m >> 2, m & 3) for m in range(16)],
+              1: [(m & 3, ((m >> 2) + m) & 3) for m in range(16)],
+              2: [(0, 0)] * 16}
+
+    def mfma(self, iters=200000, order=0, zero_a=False):
+        """Sustained dense bf16 MFMA (TFLOP/s) on N(0,1) operands (zero_a: the A fragments all zero, so every
+        product is zero), issued in `order`; its clock, and a check of the result."""
         import torch
         g = torch.Generator(device="cuda").manual_seed(0)
         ops = torch.randn(8 * 64 * 8, device="cuda", generator=g).to(torch.bfloat16)
+        if zero_a:
+            ops[:4 * 64 * 8] = 0
         chk = torch.zeros(1024 * 64, dtype=torch.float32, device="cuda")
         clocks = torch.zeros(1024 * 4, dtype=torch.int64, device="cuda")
         s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        args = (ctypes.c_void_p(ops.data_ptr()), None, ctypes.c_void_p(chk.data_ptr()),
-                ctypes.c_void_p(clocks.data_ptr()), s)
-        self.L.grok_moe_probe_mfma(args[0], 1000, *args[2:])  # warm-up
+        args = (ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(chk.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
+                s)
+        self.L.grok_moe_probe_mfma(args[0], 1000, order, *args[1:])  # warm-up
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        st = self.L.grok_moe_probe_mfma(args[0], iters, *args[2:])
+        st = self.L.grok_moe_probe_mfma(args[0], iters, order, *args[1:])
         e1.record()
         torch.cuda.synchronize()
         if st != 0:
@@ -420,19 +430,81 @@ class Probe:
         want = np.zeros(64)
         scale = np.zeros(64)
         rows = np.array([[(v & 3) + 8 * (v >> 2) + 4 * (lane >> 5) for v in range(16)] for lane in range(64)])
-        for i in range(4):
-            for j in range(4):
-                C = A[i] @ B[j]
-                for lane in range(64):
-                    vals = C[rows[lane], lane & 31]
-                    want[lane] += vals.sum()
-                    scale[lane] += np.abs(vals).sum()
+        for i, j in self.ORDERS[order]:
+            C = A[i] @ B[j]
+            for lane in range(64):
+                vals = C[rows[lane], lane & 31]
+                want[lane] += vals.sum()
+                scale[lane] += np.abs(vals).sum()
         got = chk.cpu().numpy().reshape(1024, 64).astype(np.float64)
-        err = float(np.max(np.abs(got - iters * want[None, :]) / (iters * scale[None, :])))
-        return {"mfma_sustained_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_ms": ms, "mfma_iters": iters,
-                "mfma_clock_GHz": self.ghz(clocks.cpu().numpy().view(np.uint64)),
-                "mfma_checksum_max_rel_err": err, "mfma_checksum_ok": bool(err < 1e-2),
-                "mfma_kernel": "1024 waves (one per SIMD), 16 v_mfma_f32_32x32x16_bf16 per round on register operands"}
+        if zero_a:
+            err = float(np.max(np.abs(got)))  # every product is exactly zero
+        else:
+            err = float(np.max(np.abs(got - iters * want[None, :]) / (iters * scale[None, :])))
+        return {"TFLOPs": flops / (ms * 1e-3) / 1e12, "ms": ms, "iters": iters,
+                "clock_GHz": self.ghz(clocks.cpu().numpy().view(np.uint64)),
+                "checksum_max_err": err, "checksum_ok": bool(err == 0.0 if zero_a else err < 1e-2)}
+
+
+    def feed(self, copies, iters=50000, images=64):
+        """The tile kernels' MFMA stream with its operand fragments read from an LDS ring (copies=0), and with the ring
+        fed by direct-to-LDS copies of the same bytes per flop from a source of `images` 32 KB stages that stays in
+        L2 (copies=1): TFLOP/s, clock, and a check of the sums.  Operands as in the prefill: A N(0,1), B N(0,0.02)."""
+        import torch
+        g = torch.Generator(device="cuda").manual_seed(1)
+        src = torch.randn(images, 2, 8192, device="cuda", generator=g)
+        src[:, 1] *= 0.02
+        src = src.to(torch.bfloat16).contiguous()
+        chk = torch.zeros(1024 * 64, dtype=torch.float32, device="cuda")
+        clocks = torch.zeros(1024 * 4, dtype=torch.int64, device="cuda")
+        st_ = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        call = lambda n: self.L.grok_moe_probe_mfma_feed(ctypes.c_void_p(src.data_ptr()), images * 32768, n, copies,
+                                                         ctypes.c_void_p(chk.data_ptr()),
+                                                         ctypes.c_void_p(clocks.data_ptr()), st_)
+        call(500)  # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st = call(iters)
+        e1.record()
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError(f"feed probe failed ({st})")
+        ms = e0.elapsed_time(e1)
+        want, scale = feed_expected(src.float().cpu().numpy().astype(np.float64), iters, copies)
+        got = chk.cpu().numpy().astype(np.float64).reshape(256, 2, 2, 64)
+        err = float(np.max(np.abs(got - want[None]) / scale[None]))
+        return {"TFLOPs": 1024.0 * iters * 32 * 32768 / (ms * 1e-3) / 1e12, "ms": ms, "iters": iters,
+                "clock_GHz": self.ghz(clocks.cpu().numpy().view(np.uint64)), "checksum_max_rel_err": err,
+                "checksum_ok": bool(err < 1e-3)}
+
+
+def feed_expected(src, iters, copies):
+    """Per (wm, wn, lane) of grok_moe_probe_mfma_feed: the sum of its accumulators (float64) and the sum of the
+    absolute values of the products in them, from the source images (src: [images, 16384] values; stage layout in
+    include/grok_moe_probe.h)."""
+    images = src.shape[0]
+    v = src.reshape(images, 32, 64, 8)  # [image, fragment, lane, 8 values]
+    A = np.zeros((images, 2, 2, 4, 32, 16))  # image, wm, ks, i, row, k
+    B = np.zeros((images, 2, 2, 4, 16, 32))  # image, wn, ks, j, k, column
+    for q in range(2):
+        for ks in range(2):
+            for i in range(4):
+                for h in range(2):
+                    A[:, q, ks, i][:, :, 8 * h:8 * h + 8] = v[:, (q * 2 + ks) * 4 + i, 32 * h:32 * h + 32]
+                    B[:, q, ks, i][:, 8 * h:8 * h + 8, :] = v[:, 16 + (q * 2 + ks) * 4 + i,
+                                                            32 * h:32 * h + 32].transpose(0, 2, 1)
+    n_img = images if copies else 4
+    C = np.einsum("gmsirk,gnsjkc->gmnsijrc", A[:n_img], B[:n_img])  # every block product of every step half
+    uses = np.bincount(np.arange(iters) % n_img, minlength=n_img).astype(np.float64)
+    want = np.zeros((2, 2, 64))
+    scale = np.zeros((2, 2, 64))
+    for h in range(2):
+        rows = np.array([(u & 3) + 8 * (u >> 2) + 4 * h for u in range(16)])  # accumulator rows of lanes 32 h ..
+        Ch = C[..., rows, :]  # g, wm, wn, ks, i, j, 16 rows, 32 columns
+        want[:, :, 32 * h:32 * h + 32] = np.tensordot(uses, Ch.sum(axis=(3, 4, 5, 6)), axes=1)
+        scale[:, :, 32 * h:32 * h + 32] = np.tensordot(uses, np.abs(Ch).sum(axis=(3, 4, 5, 6)), axes=1)
+    return want, scale
 
 
 def tile_trace(probe, layer):
@@ -520,8 +592,23 @@ def ceilings(probe, buf):
     res["hbm_read_GBps_nontemporal"] = rd["nontemporal"]
     res["hbm_read_GBps"] = max(rd.values())
     res["hbm_read_bytes"] = nbytes
-    res.update(probe.mfma())
+    m = probe.mfma()
+    res.update({"mfma_sustained_TFLOPs": m["TFLOPs"], "mfma_ms": m["ms"], "mfma_iters": m["iters"],
+                "mfma_clock_GHz": m["clock_GHz"], "mfma_checksum_max_rel_err": m["checksum_max_err"],
+                "mfma_checksum_ok": m["checksum_ok"],
+                "mfma_kernel": "1024 waves (one per SIMD), 16 v_mfma_f32_32x32x16_bf16 per round on register operands"})
     res["mfma_frac_of_spec"] = res["mfma_sustained_TFLOPs"] / BF16_PEAK_TFLOPS
+    # what the MFMA rate depends on: the operand values (A all zero: nothing toggles in the multipliers) and the
+    # issue order (A held for 4 MFMAs as in the tile kernels, both operands changing, or one pair throughout)
+    var = {}
+    for name, kw in (("zero_a", {"zero_a": True}), ("order_both_change", {"order": 1}),
+                     ("order_one_pair", {"order": 2})):
+        v = probe.mfma(iters=100000, **kw)
+        var[name] = {"TFLOPs": v["TFLOPs"], "clock_GHz": v["clock_GHz"], "checksum_ok": v["checksum_ok"]}
+    res["mfma_variants"] = var
+    # the tile kernels' K loop alone: fragments from LDS, then also the copies that feed the ring (L2-resident source)
+    res["mfma_feed"] = {name: probe.feed(copies=c) for name, c in (("lds_fragments", 0),
+                                                                   ("lds_fragments_and_copies", 1))}
     res["hbm_frac_of_spec"] = res["hbm_read_GBps"] / HBM_PEAK_GBS
     return res
 

@@ -44,6 +44,15 @@ __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, con
                                                  c, 0, 0, 0);
 }
 
+// Operand pair of MFMA m (0..15) of a round: ORDER 0 (the layer's tile kernels): blocks (i, j) row by row, so A
+// fragment i stays for 4 MFMAs while B changes; ORDER 1: both fragments change at every MFMA, (m & 3, (m/4 + m) & 3);
+// ORDER 2: the pair (0, 0) for all 16 (the operands never change).
+template <int ORDER>
+__device__ __forceinline__ int pair_a(int m) { return ORDER == 0 ? m >> 2 : ORDER == 1 ? m & 3 : 0; }
+template <int ORDER>
+__device__ __forceinline__ int pair_b(int m) { return ORDER == 0 ? m & 3 : ORDER == 1 ? ((m >> 2) + m) & 3 : 0; }
+
+template <int ORDER>
 __global__ __launch_bounds__(256) void mfma_kernel(const u32x4_t* __restrict__ ops, int iters,
                                                    float* __restrict__ checksum, uint64_t* __restrict__ clocks) {
   const int lane = threadIdx.x & 63;
@@ -54,28 +63,22 @@ __global__ __launch_bounds__(256) void mfma_kernel(const u32x4_t* __restrict__ o
     a[i] = ops[i * 64 + lane];
     b[i] = ops[(4 + i) * 64 + lane];
   }
-  f32x16_t acc[4][4];
+  f32x16_t acc[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int m = 0; m < 16; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) acc[m][v] = 0.0f;
   const uint64_t c0 = clock64(), w0 = wall_clock64();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
+    for (int m = 0; m < 16; ++m) acc[m] = mfma(a[pair_a<ORDER>(m)], b[pair_b<ORDER>(m)], acc[m]);
   }
   const uint64_t c1 = clock64(), w1 = wall_clock64();
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int m = 0; m < 16; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+    for (int v = 0; v < 16; ++v) s += acc[m][v];
   checksum[w * 64 + lane] = s;
   if (lane == 0) {
     clocks[4 * w + 0] = c0;
@@ -118,9 +121,13 @@ PROBE_API int grok_moe_probe_read(const void* buf, size_t bytes, int workgroups,
   return status(hipGetLastError());
 }
 
-PROBE_API int grok_moe_probe_mfma(const uint16_t* ops, int iters, float* checksum, uint64_t* clocks, hipStream_t stream) {
-  if (!aligned16(ops) || checksum == nullptr || clocks == nullptr || iters < 1) return -1;
-  mfma_kernel<<<256, 256, 0, stream>>>(reinterpret_cast<const u32x4_t*>(ops), iters, checksum, clocks);
+PROBE_API int grok_moe_probe_mfma(const uint16_t* ops, int iters, int order, float* checksum, uint64_t* clocks,
+                                  hipStream_t stream) {
+  if (!aligned16(ops) || checksum == nullptr || clocks == nullptr || iters < 1 || order < 0 || order > 2) return -1;
+  const u32x4_t* o = reinterpret_cast<const u32x4_t*>(ops);
+  if (order == 0) mfma_kernel<0><<<256, 256, 0, stream>>>(o, iters, checksum, clocks);
+  else if (order == 1) mfma_kernel<1><<<256, 256, 0, stream>>>(o, iters, checksum, clocks);
+  else mfma_kernel<2><<<256, 256, 0, stream>>>(o, iters, checksum, clocks);
   return status(hipGetLastError());
 }
 

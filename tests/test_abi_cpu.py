@@ -224,7 +224,7 @@ def test_probe_library_exports_its_header():
     P = ctypes.CDLL(build.PROBE_LIB)
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "grok_moe_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(grok_moe_probe_[a-z_0-9]+)\s*\(", text)))
-    assert len(names) == 5
+    assert len(names) == 6
     for n in names:
         assert hasattr(P, n), n
     f = P.grok_moe_probe_read
@@ -234,6 +234,20 @@ def test_probe_library_exports_its_header():
     g = P.grok_moe_probe_clock
     g.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
     assert g(0, 100, ctypes.c_void_p(0x200000), None) == -1
+    m = P.grok_moe_probe_mfma
+    m.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    ok = (ctypes.c_void_p(0x100000), 10)
+    assert m(*ok, 3, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000), None) == -1  # no such issue order
+    assert m(*ok, -1, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000), None) == -1
+    assert m(ctypes.c_void_p(0x100000), 0, 0, ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000), None) == -1
+    fd = P.grok_moe_probe_mfma_feed
+    fd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    out = (ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000), None)
+    assert fd(ctypes.c_void_p(0x100000), 3 * 32768, 10, 1, *out) == -1  # fewer than 4 stage images
+    assert fd(ctypes.c_void_p(0x100000), 4 * 32768 + 16, 10, 1, *out) == -1  # not whole images
+    assert fd(ctypes.c_void_p(0x100000), 4 * 32768, 10, 2, *out) == -1  # copies is 0 or 1
+    assert fd(ctypes.c_void_p(0x100008), 4 * 32768, 10, 0, *out) == -1  # misaligned
     assert gm.LIB_PATH != build.PROBE_LIB
 
 
