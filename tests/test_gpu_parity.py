@@ -206,19 +206,20 @@ def test_layer_all_tokens_to_two_experts(gm):
 
 def test_layer_tile_heights(gm):
     """router_w = 0 puts all T tokens on experts 0 and 1, so each has exactly T slots.  The tiled kernels pick the
-    tile height from the count: T = 150, 315, 384 and 550 run as 1, 2, 2 and 3 tiles of 192 rows; T = 1100 and 1152
-    as 4 full 256-row tiles plus a last tile of 76 / 128 rows run as a 128-row tile; T = 1153 keeps its 129-row last
-    tile in the 256-row launch.  Both weight types, and the [out, in] layout."""
+    tile height from the count: T = 150, 315, 384 and 550 run as 1, 2, 2 and 3 tiles of 192 rows; T = 420, 600 and
+    1230 as 2, 3 and 5 tiles of 256 rows, the last partly filled; T = 1100 and 1152 as 4 full 256-row tiles plus a
+    last tile of 76 / 128 rows run as a 128-row tile; T = 1153 keeps its 129-row last tile in the 256-row launch.
+    Both weight types, and the [out, in] layout."""
     from tests.test_gpu_layout import check_layout
-    cases = [(150, BF16), (315, BF16), (384, BF16), (550, BF16), (1100, BF16), (1152, BF16), (1153, BF16),
-             (315, W8), (1100, W8)]
+    cases = [(150, BF16), (315, BF16), (384, BF16), (420, BF16), (550, BF16), (600, BF16), (1100, BF16),
+             (1152, BF16), (1153, BF16), (1230, BF16), (315, W8), (600, W8), (1100, W8), (1153, W8)]
     for T, dtype in cases:
         w = synth.Workload(f"tiles_T{T}_{dtype}", T=T, d=256, f=512, dtype=dtype, w_std=0.1)
         inp = synth.make_inputs(w)
         inp["router_w"] = np.zeros_like(inp["router_w"])
         _, ref = check_layer(gm, w, inp=inp)
         assert ref["counts"].tolist() == [T, T, 0, 0, 0, 0, 0, 0]
-    for T in (315, 1100):
+    for T in (315, 600, 1100, 1153):
         w = synth.Workload(f"oi_tiles_T{T}", T=T, d=256, f=512, w_std=0.1)
         inp = synth.make_inputs(w)
         inp["router_w"] = np.zeros_like(inp["router_w"])
