@@ -71,7 +71,9 @@ def check_layer(gm, w: synth.Workload, inp=None, rows=None, name=None, dv=None, 
     (1, 256, 8, BF16, False), (77, 512, 8, BF16, True), (1000, 256, 8, BF16, False), (50, 256, 16, BF16, False),
     (30, 256, 64, BF16, True), (64, 128, 8, F32, False), (129, 192, 8, F32, True), (20, 6144, 8, BF16, False),
     # batches above 256 tokens, ragged sizes, 2 and 4 experts
-    (1003, 256, 8, BF16, True), (300, 512, 4, F32, True), (777, 6144, 8, BF16, False), (260, 256, 2, BF16, False)])
+    (1003, 256, 8, BF16, True), (300, 512, 4, F32, True), (777, 6144, 8, BF16, False), (260, 256, 2, BF16, False),
+    # larger batches
+    (2048, 256, 8, BF16, True), (2051, 6144, 8, BF16, False), (3001, 192, 8, F32, True), (2500, 256, 4, BF16, True)])
 def test_router_step(gm, T, d, E, dtype, bias):
     say(f"[case] router T={T} d={d} E={E} dtype={dtype} bias={bias}")
     w = synth.Workload("r", T=T, d=d, f=256, E=E, dtype=dtype)
@@ -88,7 +90,23 @@ def test_router_step(gm, T, d, E, dtype, bias):
     assert np.allclose(p.cpu().numpy(), ref["p"].numpy(), rtol=1e-6, atol=0)
 
 
-@pytest.mark.parametrize("T", [40, 603])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_router_batch_forms_agree(gm, dtype):
+    """Routing is per token: a token's indices and probabilities are bit-identical whether it is routed in a batch
+    of 2051 tokens or in a smaller batch holding it."""
+    say(f"[case] router forms dtype={dtype}")
+    w = synth.Workload("rf", T=2051, d=6144 if dtype == BF16 else 512, f=256, dtype=dtype)
+    inp = synth.make_inputs(w)
+    inp["router_bias"] = np.linspace(-1, 2, 8).astype(np.float32)
+    dv = dev_inputs(inp, dtype)
+    idx, p = gm.route(dv["x"], dv["router_w"], dv["router_bias"])
+    for a, b in ((0, 1000), (1000, 2000), (2000, 2051)):
+        idx_s, p_s = gm.route(dv["x"][a:b].contiguous(), dv["router_w"], dv["router_bias"])
+        assert torch.equal(idx_s, idx[a:b])
+        assert torch.equal(p_s.view(torch.int32), p[a:b].view(torch.int32))
+
+
+@pytest.mark.parametrize("T", [40, 603, 2049])
 def test_router_ties_take_lower_index(gm, T):
     x = torch.randn(T, 256, device="cuda").to(torch.bfloat16)
     rw = torch.zeros(8, 256, device="cuda", dtype=torch.bfloat16)
