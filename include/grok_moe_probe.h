@@ -57,7 +57,7 @@ int grok_moe_probe_mfma(const uint16_t* ops, int iters, int order, float* checks
  * once before the loop, and step s reads image s mod 4 (no global traffic in the loop).  Lane l of wave w of the
  * grid (1024 waves) writes the sum of its 256 accumulator values to checksum[64 w + l], and clocks as
  * grok_moe_probe_mfma (around the loop).  Flops: 1024 waves x iters x 32 x 32768.  Returns -1 for a null or
- * misaligned pointer, iters < 1, src_bytes not a multiple of 32768, below 4 images or above 2^30, or copies not
+ * misaligned pointer, iters outside 1 .. 2^30, src_bytes not a multiple of 32768, below 4 images or above 2^30, or copies not
  * 0 or 1. */
 int grok_moe_probe_mfma_feed(const void* src, int64_t src_bytes, int iters, int copies, float* checksum,
                              uint64_t* clocks, hipStream_t stream);

@@ -248,6 +248,7 @@ def test_probe_library_exports_its_header():
     assert fd(ctypes.c_void_p(0x100000), 4 * 32768 + 16, 10, 1, *out) == -1  # not whole images
     assert fd(ctypes.c_void_p(0x100000), 4 * 32768, 10, 2, *out) == -1  # copies is 0 or 1
     assert fd(ctypes.c_void_p(0x100008), 4 * 32768, 10, 0, *out) == -1  # misaligned
+    assert fd(ctypes.c_void_p(0x100000), 4 * 32768, (1 << 30) + 1, 0, *out) == -1  # step index would overflow
     assert gm.LIB_PATH != build.PROBE_LIB
 
 
