@@ -116,8 +116,8 @@ extern "C" __attribute__((visibility("default"))) int grok_moe_probe_mfma_feed(c
                                                                                uint64_t* clocks, hipStream_t stream) {
   using namespace gm;
   if (src == nullptr || (reinterpret_cast<uintptr_t>(src) & 15) != 0 || checksum == nullptr || clocks == nullptr ||
-      iters < 1 || iters > (1 << 30) || src_bytes % F_STAGE != 0 || src_bytes < 4 * F_STAGE || src_bytes > (int64_t(1) << 30) ||
-      (copies != 0 && copies != 1))
+      iters < 1 || iters > (1 << 30) || src_bytes % F_STAGE != 0 || src_bytes < 4 * F_STAGE ||
+      src_bytes > (int64_t(1) << 30) || (copies != 0 && copies != 1))
     return -1;
   const int nimg = int(src_bytes / F_STAGE);
   const uint8_t* s = static_cast<const uint8_t*>(src);
