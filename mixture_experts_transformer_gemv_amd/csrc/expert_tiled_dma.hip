@@ -6,12 +6,11 @@
 // Tile shape and order: tiles.h.  K steps of 32 in a 4-deep LDS ring (4 x 32 KB).  Both operands are copied
 // straight from global memory into LDS with global_load_lds_dwordx4 (no registers, no VALU), 16 bytes per lane,
 // addressed as a wave-uniform base plus a per-lane 32-bit offset:
-//   * A (activations), [in, out] weights with one scale per column: copied per pair of K steps, [256 rows][64 k]
-//     with 128-byte rows (full cache lines), rows 0..127 in the A region of the pair's first ring slot and
-//     128..255 in that of its second; the 16-byte k chunk c of row r sits in slot c ^ ((r >> 1) & 7).  Even steps
-//     copy the activations of the pair two steps ahead, every step the weights of the step three ahead.  Otherwise
-//     (grouped int8 scales, [out, in] weights) per K step: [256 rows][32 k], 64-byte rows, chunk c of row r in
-//     slot c ^ ((r >> 2) & 3);
+//   * A (activations): copied per pair of K steps, [256 rows][64 k] with 128-byte rows (full cache lines), rows
+//     0..127 in the A region of the pair's first ring slot and 128..255 in that of its second; the 16-byte k chunk
+//     c of row r sits in slot c ^ ((r >> 1) & 7).  Even steps copy the activations of the pair two steps ahead.
+//     With grouped int8 scales per K step instead: [256 rows][32 k], 64-byte rows, chunk c of row r in slot
+//     c ^ ((r >> 2) & 3);
 //   * weights as two [32 k][128 column] sub-tiles (up: W1 and Wv; down: two halves of the W2 columns) with
 //     256-byte rows; the 8-column chunk c of row k sits in slot c ^ (4 (k & 3)).
 // The XOR swizzles are chosen on the global side (which chunk each lane fetches) so that the MFMA operand reads
@@ -24,7 +23,8 @@
 // the HBM traffic and 64-byte row pieces read ~15% slower).  So their tile is copied per pair of K steps,
 // [256 weight rows][64 k] with 128-byte rows (16-byte chunk c of row r in slot c ^ ((r >> 1) & 7)), into one of
 // three pair slots beside a 4-deep ring of A stages (4 x 16 KB + 3 x 32 KB = 160 KB); a pair's copies are issued
-// during the two steps three and two steps ahead of it, so the per-step copy count and waits are unchanged.
+// during the steps four and three steps ahead of it (half-step 1 of the even one, both half-steps of the odd one),
+// so that they are spread over the half-steps the activation copies leave free.
 // Schedule: one workgroup barrier per K step, between its two 16-deep halves; every MFMA is followed by at most
 // one LDS fragment read or one copy (pinned with sched_barrier), so the copies (half of step kt+3 after the
 // barrier, the other half in the next half-step) and the fragments of the next half-step are issued in the
@@ -87,6 +87,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   static_assert(!(OUTIN && INT8), "int8 weights are tiled from [E, K, N] storage");
   static_assert(TBM == 256 || TBM == 192 || TBM == 128, "tiles of 256, 192 or 128 rows");
   static_assert(!GROUPED || (INT8 && !OUTIN && TBM == 128), "grouped scales: int8 [in, out] weights, 128-row tiles");
+  static_assert(!OUTIN || !GROUPED, "[out, in] tiles copy their activations per K-step pair");
   constexpr int BNM = BNT / NMAT;  // columns per matrix
   constexpr int MI = TBM / 64;     // row blocks of 32 per wave (waves 2 x 2: TBM / 2 rows each)
   constexpr int AP = TBM / 64;     // 1 KB activation copies per wave and K step
@@ -98,13 +99,13 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   constexpr int BCOPIES = INT8 ? 2 : 4;        // 1 KB weight copies per wave and K step ([in, out])
   constexpr int CPS = AP + BCOPIES;            // copies per wave and K step ([out, in]: AP + 4)
   constexpr int A_STRIDE = OUTIN ? A_STG : STAGE;  // between ring slots of A
-  // [in, out] weights with one scale per column: the activations are copied per pair of K steps, 128 contiguous
-  // bytes (64 k) of each row per copy, so that a copy instruction reads 8 full 128-byte lines instead of 16 half
-  // lines (the vector memory path is the K loop's limit; measured on MI355X at Grok-1 shape, bit-identical:
-  // prefill down-projection 5.55 -> 5.32 ms, int8 weights at T = 8192 18.45 -> 17.88 ms per layer; with grouped
-  // int8 scales 7.15 -> 7.24 ms at T = 2048, so those keep per-step copies).  The pair's TBM rows x 128 bytes fill
-  // the A regions of the ring slots of its two steps: rows 0..TBM/2-1 in the first, the rest in the second.
-  constexpr bool PAIRA = !OUTIN && !GROUPED;
+  // The activations are copied per pair of K steps, 128 contiguous bytes (64 k) of each row per copy, so that a
+  // copy instruction reads 8 full 128-byte lines instead of 16 half lines (the vector memory path is the K loop's
+  // limit; measured on MI355X at Grok-1 shape, bit-identical: prefill down-projection 5.55 -> 5.32 ms, int8
+  // weights at T = 8192 18.45 -> 17.88 ms per layer, [out, in] weights 17.5 -> 16.9 ms; with grouped int8 scales
+  // 7.15 -> 7.24 ms at T = 2048, so those keep per-step copies).  The pair's TBM rows x 128 bytes fill the A
+  // regions of the ring slots of its two steps: rows 0..TBM/2-1 in the first, the rest in the second.
+  constexpr bool PAIRA = !GROUPED;
   constexpr int APP = 2 * AP;                   // 1 KB activation copies per wave and step pair
   // Launches whose tiles read each weight byte once (one 128-row tile per expert and column tile) copy the weights
   // with the nontemporal hint; tiles that share weight columns through the caches keep the default policy.
@@ -186,7 +187,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   // (rows 0..TBM/2-1) and (kd + 1) % NSTAGE; weight piece n of step kt into ring slot stage
   // (kd: the pair's first step, which places it in the ring; ks: the step its data is read from)
   auto copy_apair = [&](int kd, int ks, int i) {
-    const uint32_t dst = lds0 + uint32_t(((kd + (wave >> 1)) % NSTAGE) * STAGE) +
+    const uint32_t dst = lds0 + uint32_t(((kd + (wave >> 1)) % NSTAGE) * A_STRIDE) +
                          uint32_t((TBM / 4) * (wave & 1) + 8 * i) * 128u;
     b2lds16(a_rsrc, uint32_t(kbase + ks * BK) * 2u, a_voff[i], dst);
   };
@@ -282,10 +283,10 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   };
   auto read_piece = [&](int buf, const lds_u8* st, const lds_u8* sb, const lds_u8* sa, int p2, int ks, int p) {
     if (OUTIN) {
-      if (p == 0) fa[buf][0] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[0][ks]);
+      if (p == 0) a_read(buf, 0, st, sa, p2, ks);
       else if (p <= 4)
         fb[buf][p - 1] = *(const __attribute__((address_space(3))) u32x4_t*)(sb + bt_off[p - 1][ks][p2]);
-      else fa[buf][p - 4] = *(const __attribute__((address_space(3))) u32x4_t*)(st + a_off[p - 4][ks]);
+      else a_read(buf, p - 4, st, sa, p2, ks);
     } else if (INT8) {
       if (p == 0) a_read(buf, 0, st, sa, p2, ks);
       else if (p <= 4) b8[buf][p - 1] = lds_tr8(st + b8_off[p - 1][ks]);
@@ -366,13 +367,16 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
   // step kt + 3 in half-step 1; an odd step the weights of step kt + 3, half in each half-step (so the wait count
   // alternates between the parities); the prologue issues the weights of step 0, the activations of pair 0 and
   // the weights of steps 1 and 2.
-  // OUTIN: the weight copies of pair q are issued in the B slots of steps 2 q - 3 and 2 q - 2 (4 each), so that
-  // step kt issues copies 4 ((kt + 1) % 2) .. +3 of pair (kt + 3) / 2 at the end of half-step 0 and the activation
-  // copies of step kt + 3 at the start of half-step 1; the prologue issues pair 0 and the first half of pair 1.
+  // OUTIN: as PAIRA for the activations; the weight copies of pair q are issued in half-step 1 of step 2 q - 4
+  // (copies 0..3) and in both half-steps of step 2 q - 3 (4, 5 and 6, 7), so every half-step but the one with the
+  // activation copies issues some, and the pair has landed two steps before it is read; the prologue issues the
+  // weights of pairs 0 and 1 and the activations of pair 0.  (Copying the weights of pair q at the end of half-step
+  // 0 of steps 2 q - 3 and 2 q - 2, in one burst with the activations on even steps, ran the [out, in] prefill
+  // down-projection 6.13 -> 6.59 ms; this order 6.21 -> 5.77 ms, measured on MI355X.)
   const int KT = Ks / BK;
   const lds_u8* bpairs = lds + NSTAGE * A_STG;
   // PAIRA: the wave's A region of step kt
-  auto a_region = [&](int kt) { return lds + (((kt & ~1) + wm) % NSTAGE) * STAGE; };
+  auto a_region = [&](int kt) { return lds + (((kt & ~1) + wm) % NSTAGE) * A_STRIDE; };
   // zeros in the A slots of rows past the expert's end, in every ring stage (written by this lane only; the
   // out-of-range copies leave them zero)
   if (rows < TBM) {
@@ -382,7 +386,7 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
         if (a_voff[i] == 0x80000000u)
 #pragma unroll
           for (int pp = 0; pp < NSTAGE; pp += 2)  // the pairs' first slots: 0 and 2
-            *(__attribute__((address_space(3))) u32x4_t*)(lds + ((pp + (wave >> 1)) % NSTAGE) * STAGE +
+            *(__attribute__((address_space(3))) u32x4_t*)(lds + ((pp + (wave >> 1)) % NSTAGE) * A_STRIDE +
                                                           ((TBM / 4) * (wave & 1) + 8 * i) * 128 + 16 * lane) =
                 u32x4_t{0u, 0u, 0u, 0u};
     } else {
@@ -395,7 +399,17 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
                                                           16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  if constexpr (PAIRA) {
+  if constexpr (OUTIN) {
+    // the weights of pair 0, the activations of pair 0, the first half of the weights of pair 1 (the steady
+    // state's order)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) copy_pair(0, c);
+#pragma unroll
+    for (int i = 0; i < APP; ++i) copy_apair(0, 0, i);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) copy_pair(1, c);
+    wait_vm<8>();  // pair 0 landed
+  } else if constexpr (PAIRA) {
     // the weights of step 0, the activations of steps 0 and 1, the weights of steps 1 and 2 (the steady state's
     // order)
 #pragma unroll
@@ -407,18 +421,6 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
 #pragma unroll
       for (int n = 0; n < BCOPIES; ++n) copy_bpiece(st, min(st, KT - 1), n);
     wait_vm<2 * BCOPIES>();  // step 0 landed (its weights and the activations of steps 0 and 1)
-  } else if constexpr (OUTIN) {
-#pragma unroll
-    for (int n = 0; n < AP; ++n) copy_piece(0, 0, n);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) copy_pair(0, c);
-#pragma unroll
-    for (int n = 0; n < AP; ++n) copy_piece(1, min(1, KT - 1), n);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) copy_pair(1, c);
-#pragma unroll
-    for (int n = 0; n < AP; ++n) copy_piece(2, min(2, KT - 1), n);
-    wait_vm<2 * AP + 4>();  // step 0 (A and pair 0) landed
   } else {
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
@@ -475,7 +477,17 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
     for (int m = 0; m < NSLOT; ++m) {
       if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[0][m >> 2], fb[0][m & 3], acc[m >> 2][m & 3]);
       if (m < NPIECE) read_piece(1, st, sb, sa, P, 1, m);
-      if constexpr (PAIRA) {
+      if constexpr (OUTIN) {
+        if constexpr (P == 0) {  // the activations of the pair kt + 2, kt + 3 (past the end: the last pair again)
+#pragma unroll
+          for (int c = 0; c < APP; ++c)
+            if (m == (c * NSLOT) / APP) copy_apair(kt + 2, min(kt + 2, KT - 2), c);
+        } else {  // the second half of the weights of pair (kt + 3) / 2: copies 4, 5 here, 6, 7 in half-step 1
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            if (m == (c * NSLOT) / 2) copy_pair((kt + 3) >> 1, 4 + c);
+        }
+      } else if constexpr (PAIRA) {
         if constexpr (P == 0) {  // the activations of the pair kt + 2, kt + 3 (past the end: the last pair again)
 #pragma unroll
           for (int c = 0; c < APP; ++c)
@@ -485,9 +497,6 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
           for (int c = 0; c < BCOPIES / 2; ++c)
             if (m == (c * NSLOT) / (BCOPIES / 2)) copy_bpiece(cstage, ck, c);
         }
-      } else if constexpr (OUTIN) {
-        const int cb = m - (NSLOT - 4);  // the last 4 slots issue the weight copies
-        if (cb >= 0) copy_pair((kt + 3) >> 1, 4 * (1 - P) + cb);
       } else {
 #pragma unroll
         for (int c = 0; c < C0; ++c)
@@ -496,12 +505,14 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
       __builtin_amdgcn_sched_barrier(0);
     }
     join_b(1, keep_cur);
-    // step kt+1 landed (the copies of step kt+2 and the first C0 of step kt+3 may be in flight); OUTIN: steps kt+2
-    // and later may be in flight
+    // step kt+1 landed (the copies of step kt+2 and the first C0 of step kt+3 may be in flight)
     // PAIRA: issued after the last copy step kt + 1 needs are, for kt even, the odd step kt - 1's weights and this
     // step's activations, for kt odd, the even step kt - 1's weights and the first half of this step's
-    if constexpr (PAIRA) wait_vm<P == 0 ? BCOPIES + APP : BCOPIES + BCOPIES / 2>();
-    else if constexpr (OUTIN) wait_vm<CPS * (NSTAGE - 3)>();
+    // OUTIN: issued after the activations of the pair kt + 1 belongs to (the last copy it needs: its weights came
+    // earlier) are, for kt even (pair kt / 2), the weights of step kt - 2 (4), step kt - 1 (4) and this step's
+    // activations; for kt odd (pair (kt + 1) / 2), the weights of step kt - 1 (4) and half-step 0 of this step (2)
+    if constexpr (OUTIN) wait_vm<P == 0 ? APP + 8 : 6>();
+    else if constexpr (PAIRA) wait_vm<P == 0 ? BCOPIES + APP : BCOPIES + BCOPIES / 2>();
     else wait_vm<CPS * (NSTAGE - 3) + C0>();
     lds_barrier();  // ... for every wave; every wave finished reading step kt
     const lds_u8* nst = lds + ((kt + 1) % NSTAGE) * A_STRIDE;
@@ -510,13 +521,21 @@ __device__ __forceinline__ void tiled_dma_tile(const uint16_t* __restrict__ A, c
 #pragma unroll
     for (int m = 0; m < NSLOT; ++m) {
       if (m < NMF) acc[m >> 2][m & 3] = mfma32x32x16(fa[1][m >> 2], fb[1][m & 3], acc[m >> 2][m & 3]);
-      if constexpr (PAIRA) {
+      if constexpr (OUTIN) {
+        if constexpr (P == 0) {  // the first half of the weights of pair kt / 2 + 2
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (m == (c * NSLOT) / 4) copy_pair((kt >> 1) + 2, c);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            if (m == (c * NSLOT) / 2) copy_pair((kt + 3) >> 1, 6 + c);
+        }
+      } else if constexpr (PAIRA) {
         constexpr int NB1 = P == 0 ? BCOPIES : BCOPIES / 2, B1 = P == 0 ? 0 : BCOPIES / 2;
 #pragma unroll
         for (int c = 0; c < NB1; ++c)
           if (m == (c * NSLOT) / NB1) copy_bpiece(cstage, ck, B1 + c);
-      } else if constexpr (OUTIN) {
-        if (m < AP) copy_piece(cstage, ck, m);
       } else {
 #pragma unroll
         for (int c = 0; c < C1; ++c)
