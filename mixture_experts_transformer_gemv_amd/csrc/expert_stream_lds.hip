@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256, 2) void down_stream_lds_kernel(const uint16_t*
                                                                  const int32_t* __restrict__ offsets, uint32_t h_bytes,
                                                                  int d, int f, int S, int64_t split_stride,
                                                                  float* __restrict__ y) {
+  static_assert(!SH || MT == 2, "shared activation rows: waves 0 and 1 copy the two 16-row blocks");
   constexpr int STG = SH ? L_W : L_W + MT * 1024;  // bytes of one stage of a wave's ring
   constexpr int NSA = NST + 1;                        // SH: shared activation slots
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * NST * STG + (SH ? NSA * MT * 1024 : 0)];
