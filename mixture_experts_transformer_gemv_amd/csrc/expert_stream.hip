@@ -165,8 +165,8 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
         st.b2[r] = W::load(wv, rb + size_t(r) * rs);
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
+      for (int mt = 0; mt < MT; ++mt)  // rows past the expert's end read its first row; they are never stored
+        st.a[mt] = *reinterpret_cast<const u32x4_t*>(arow[mt] + k0);
     };
     // GROUPED: the current group's scales (zero replaced by one), the byte masks of its columns with a non-zero
     // scale, and the raw scales of the next group (loaded a group ahead)
@@ -208,7 +208,9 @@ __global__ __launch_bounds__(256) void up_stream_kernel(const uint16_t* __restri
       for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
         load(sb, k0 + 32);
         compute(sa);
-        if (k0 + 64 < khi) load(sa, k0 + 64);
+        // past the end the last step is loaded again and not used: no branch around the loads, whose join
+        // would make the compiler wait for every load in flight
+        load(sa, min(k0 + 64, khi - 32));
         compute(sb);
       }
     };
@@ -380,8 +382,8 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 #pragma unroll
       for (int r = 0; r < 8; ++r) st.b[r] = W::load(w2, rb + size_t(r) * rs);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        st.a[mt] = aval[mt] ? *reinterpret_cast<const u32x4_t*>(arow[mt] + k0) : u32x4_t{0, 0, 0, 0};
+      for (int mt = 0; mt < MT; ++mt)  // rows past the expert's end read its first row; they are never stored
+        st.a[mt] = *reinterpret_cast<const u32x4_t*>(arow[mt] + k0);
     };
     // GROUPED: the current group's scales (zero replaced by one), the byte mask of its columns with a non-zero
     // scale, and the raw scales of the next group (loaded a group ahead)
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
       for (int k0 = klo; k0 < khi; k0 += 64) {
         load(sb, k0 + 32);
         compute(sa);
-        if (k0 + 64 < kend) load(sa, k0 + 64);
+        load(sa, min(k0 + 64, kend - 32));  // unused past the end: no branch, as in up_stream_kernel
         compute(sb);
       }
     };
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void up_stream_narrow_kernel(const uint16_t
         st.b1[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(w1 + rb + size_t(r) * f));
         st.b2[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(wv + rb + size_t(r) * f));
       }
-      st.a = aval ? *reinterpret_cast<const u32x4_t*>(arow + k0) : u32x4_t{0, 0, 0, 0};
+      st.a = *reinterpret_cast<const u32x4_t*>(arow + k0);  // past the expert's end: its first row, not stored
     };
     auto compute = [&](const Step& st) {
       u32x4_t t[4];
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void up_stream_narrow_kernel(const uint16_t
     for (int k0 = 0; k0 < d; k0 += 64) {
       load(sb, k0 + 32);
       compute(sa);
-      if (k0 + 64 < d) load(sa, k0 + 64);
+      load(sa, min(k0 + 64, d - 32));  // unused past the end: no branch, as in up_stream_kernel
       compute(sb);
     }
 #pragma unroll
