@@ -10,8 +10,10 @@
 A step is one pass of the whole layer (router, binning, fused up-projection with GELU product, down-projection,
 combine) over one batch of seeded synthetic tokens, with weights and inputs already resident in HBM.  The timed
 step calls the library's five step entry points in order (bit-identical to grok_moe_forward) on the current
-stream, so that HIP events on that stream time each kernel inside the timed region; the whole-layer entry point
-grok_moe_forward is timed as well ("entry_point_ms_per_step").
+stream, so that HIP events on that stream time the dominant kernel (the up-projection) inside the timed region;
+the other kernels are timed by as many untimed steps with events between every launch (each event costs a few
+microseconds of GPU time, which the timed steps do not carry).  The whole-layer entry point grok_moe_forward is
+timed as well ("entry_point_ms_per_step").
 
 The headline workload (--workload, default the Grok-1-shape decode step T=8, d=6144, f=32768, E=8, top-2, bf16)
 is timed for exactly --steps steps after --warmup untimed ones; its numbers are the top-level fields.  The other
@@ -125,7 +127,9 @@ class Layer:
         mk = lambda: torch.cuda.Event(enable_timing=True)
         self.ev = [mk() for _ in range(5)]
 
-    def step(self, timed=False):
+    def step(self, marks=()):
+        """One step; records the events whose indices are in marks (0 before the router, 1 after binning, 2 after the
+        up-projection, 3 after the down-projection, 4 after the combine)."""
         import torch
         dv, L, w = self.dv, self.lib, self.w
         P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
@@ -134,7 +138,7 @@ class Layer:
         lay = 1 if self.outin else 0
         es, g1, g2 = self.scale_spec
         ev = self.ev
-        if timed:
+        if 0 in marks:
             ev[0].record()
         if self.norms is None:
             xa = dv["x"]
@@ -145,22 +149,22 @@ class Layer:
             st = L.grok_moe_route_norm(P(dv["x"]), P(self.norms[0]), self.norms[2], P(dv["router_w"]),
                                        P(dv["router_bias"]), T, d, E, 2, dt, P(self.xn), P(self.idx), P(self.p), s)
         st |= L.grok_moe_bin(P(self.idx), T, E, 2, P(self.counts), P(self.offsets), P(self.perm), P(self.inv), s)
-        if timed:
+        if 1 in marks:
             ev[1].record()
         st |= L.grok_moe_expert_up(P(xa), P(dv["w1"]), P(dv["wv"]), P(self.s1), P(self.sv), lay, es, g1,
                                    P(self.counts), P(self.offsets), P(self.perm), T, d, f, E, 2, dt, P(self.h), s)
-        if timed:
+        if 2 in marks:
             ev[2].record()
         st |= L.grok_moe_expert_down(P(self.h), P(dv["w2"]), P(self.s2), lay, es, g2, P(self.counts),
                                      P(self.offsets), T, d, f, E, 2, dt, self.S, P(self.y), s)
-        if timed:
+        if 3 in marks:
             ev[3].record()
         if self.norms is None:
             st |= L.grok_moe_combine(P(self.y), self.S, P(self.p), P(self.inv), T, d, 2, P(self.out), s)
         else:
             st |= L.grok_moe_combine_norm(P(self.y), self.S, P(self.p), P(self.inv), P(dv["x"]), P(self.norms[1]),
                                           self.norms[2], T, d, 2, dt, P(self.out), s)
-        if timed:
+        if 4 in marks:
             ev[4].record()
         if st != 0:
             raise RuntimeError(f"library call failed (status bits {st})")
@@ -177,8 +181,11 @@ class Layer:
                                 return_routing=True, weight_layout=lay)
 
     def run_with_kernel_times(self, steps, warmup):
-        """Time `steps` steps (wall, bracketed by synchronize) and the average per-launch duration of each expert
-        kernel (HIP events on the launch stream, read after the timed region)."""
+        """Time `steps` steps (wall, bracketed by synchronize) with HIP events on the launch stream around the
+        up-projection only (the dominant kernel: its average per-launch duration comes from the timed steps); then,
+        untimed, as many steps with events between every launch give the other kernels' times and the per-step
+        spread.  Each event between launches costs a few microseconds of GPU time, so the timed steps carry only
+        the two that the dominant kernel needs."""
         import torch
         for _ in range(warmup):
             self.step()
@@ -188,15 +195,22 @@ class Layer:
         t0 = time.perf_counter()
         for i in range(steps):
             self.ev = evs[i]
-            self.step(timed=True)
+            self.step(marks=(1, 2))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        k = np.array([[e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]), e[0].elapsed_time(e[1]),
-                       e[3].elapsed_time(e[4])] for e in evs])
+        up = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        evs = [[mk() for _ in range(5)] for _ in range(steps)]
+        for i in range(steps):
+            self.ev = evs[i]
+            self.step(marks=(0, 1, 2, 3, 4))
+        torch.cuda.synchronize()
+        k = np.array([[e[2].elapsed_time(e[3]), e[0].elapsed_time(e[1]), e[3].elapsed_time(e[4])] for e in evs])
         per_step = np.array([e[0].elapsed_time(e[4]) for e in evs])  # first to last event of each step, ms
         self.step_stats = {"median": float(np.median(per_step)), "min": float(per_step.min()),
-                           "p90": float(np.percentile(per_step, 90)), "n": int(steps)}
-        return wall, k.mean(axis=0)  # ms: up, down, route+bin, combine
+                           "p90": float(np.percentile(per_step, 90)), "n": int(steps),
+                           "with_events_between_every_launch": True}
+        down, rb, comb = k.mean(axis=0)
+        return wall, np.array([up, down, rb, comb])  # ms: up, down, route+bin, combine
 
     def time_entry_point(self, steps):
         """ms per call of the whole-layer entry point (allocations of its outputs included)."""
