@@ -95,6 +95,45 @@ def parse():
 
 # ------------------------------------------------------------------------------------------------ the timed step
 
+class FenceFreeEvent:
+    """A HIP event created with hipEventDisableSystemFence in the HIP runtime torch has loaded, recorded on torch's
+    current stream: unlike torch.cuda.Event, recording it adds no system-scope release (a write-back of the caches)
+    between the launches around it.  Same interface as the two torch.cuda.Event methods used here."""
+    _hip = None
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            L = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)  # the runtime already in the process
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = L
+        return cls._hip
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        if self._lib().hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self):
+        import torch
+        if self._lib().hipEventRecord(self.h, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        ms = ctypes.c_float()
+        if self._lib().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if self.h and self._hip is not None:
+            self._hip.hipEventDestroy(self.h)
+
+
 class Layer:
     """Device-resident inputs and preallocated buffers of one workload, and the timed step."""
 
@@ -184,14 +223,15 @@ class Layer:
         """Time `steps` steps (wall, bracketed by synchronize) with HIP events on the launch stream around the
         up-projection only (the dominant kernel: its average per-launch duration comes from the timed steps); then,
         untimed, as many steps with events between every launch give the other kernels' times and the per-step
-        spread.  Each event between launches costs a few microseconds of GPU time, so the timed steps carry only
-        the two that the dominant kernel needs."""
+        spread.  Each torch event between launches costs a few microseconds of GPU time (its system-scope
+        release writes the caches back), so the timed steps carry only the two that the dominant kernel needs, and
+        those without that release (FenceFreeEvent)."""
         import torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
         mk = lambda: torch.cuda.Event(enable_timing=True)
-        evs = [[mk() for _ in range(5)] for _ in range(steps)]
+        evs = [[None, FenceFreeEvent(), FenceFreeEvent(), None, None] for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
             self.ev = evs[i]
