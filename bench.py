@@ -223,14 +223,13 @@ class Layer:
         """Time `steps` steps (wall, bracketed by synchronize) with HIP events on the launch stream around the
         up-projection only (the dominant kernel: its average per-launch duration comes from the timed steps); then,
         untimed, as many steps with events between every launch give the other kernels' times and the per-step
-        spread.  Each torch event between launches costs a few microseconds of GPU time (its system-scope
-        release writes the caches back), so the timed steps carry only the two that the dominant kernel needs, and
-        those without that release (FenceFreeEvent)."""
+        spread.  A torch event between launches costs a few microseconds of GPU time (its system-scope release
+        writes the caches back), so every event here is a FenceFreeEvent, and the timed steps carry only the two
+        that the dominant kernel needs."""
         import torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        mk = lambda: torch.cuda.Event(enable_timing=True)
         evs = [[None, FenceFreeEvent(), FenceFreeEvent(), None, None] for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
@@ -239,7 +238,7 @@ class Layer:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         up = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        evs = [[mk() for _ in range(5)] for _ in range(steps)]
+        evs = [[FenceFreeEvent() for _ in range(5)] for _ in range(steps)]
         for i in range(steps):
             self.ev = evs[i]
             self.step(marks=(0, 1, 2, 3, 4))
